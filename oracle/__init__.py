@@ -1,0 +1,167 @@
+"""Plain fp64 CPU oracle for uncertainty-routed heterogeneous attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, the smoke check in
+``__graft_entry__.py`` and the CPU-baseline leg of ``bench.py`` may import
+this package.  It shares no code with the HIP path and the HIP path never
+calls it.
+
+[HetA] = "Where Compute Matters: Heterogeneous Attention for Efficient Video
+Diffusion" (HetA-DiT, arXiv 2609.31050), full text.
+
+The arithmetic lives in ``hetattn_oracle.c`` (double precision, plain loops);
+this module only marshals numpy arrays through ctypes.  Functions:
+
+* :func:`route_top_rho`  -- dense set = the round(rho*N) largest u, ties by
+  token index (quantile reading of [HetA §3.2.2 Eqs. 11-12]).
+* :func:`route_mean_std` -- T = mu + c*sigma, m_i = 1[u_i < T]
+  ([HetA §3.2.2 Eqs. 11-12]).
+* :func:`attend_rows`    -- Eq. 13 for chosen rows: dense rows use Eq. 2 over
+  all N keys, local rows use Eq. 3 over the 3D window ([HetA §3.1.1]).
+* :func:`forward`        -- :func:`attend_rows` over every token.
+* :func:`attention_weights` -- the softmax weights of one (row, head).
+
+Parity pins for every function are in ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hetattn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# Tests that plant mistakes in a copy of the oracle point this at the copy.
+_LIB_OVERRIDE = os.environ.get("HETATTN_ORACLE_LIB")
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (OpenMP, -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+             "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        lib.oracle_route_top_rho.argtypes = [P, i, i, ctypes.c_double, P, P, P, P, P]
+        lib.oracle_route_mean_std.argtypes = [P, i, i, ctypes.c_double, P, P, P, P, P]
+        lib.oracle_window_axis.argtypes = [i, i, i, P, P]
+        lib.oracle_attend_rows.argtypes = [P, P, P, i, i, i, i, i, i, i, i, i,
+                                           ctypes.c_double, P, P, ctypes.c_long, P, i]
+        lib.oracle_attention_weights.argtypes = [P, P, i, i, i, i, i, i, i, i, i,
+                                                 ctypes.c_double, P, ctypes.c_long, i, P]
+        for fn in (lib.oracle_route_top_rho, lib.oracle_route_mean_std, lib.oracle_window_axis,
+                   lib.oracle_attend_rows, lib.oracle_attention_weights):
+            fn.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+@dataclass
+class Route:
+    mask: np.ndarray       # uint8 [B, N], 1 = local
+    dense_idx: np.ndarray  # int32 [B, N], ascending, -1 past the count
+    local_idx: np.ndarray  # int32 [B, N], ascending, -1 past the count
+    counts: np.ndarray     # int32 [B, 2] = (dense, local)
+    thresh: np.ndarray     # float64 [B]
+
+
+def _route(fn_name: str, u: np.ndarray, param: float) -> Route:
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    if u.ndim != 2:
+        raise ValueError("u must be [B, N]")
+    B, N = u.shape
+    mask = np.empty((B, N), np.uint8)
+    di = np.empty((B, N), np.int32)
+    li = np.empty((B, N), np.int32)
+    counts = np.empty((B, 2), np.int32)
+    thresh = np.empty(B, np.float64)
+    rc = getattr(_load(), fn_name)(_ptr(u), B, N, float(param), _ptr(mask), _ptr(di),
+                                   _ptr(li), _ptr(counts), _ptr(thresh))
+    if rc != 0:
+        raise ValueError(f"{fn_name} rejected its arguments (rc={rc})")
+    return Route(mask, di, li, counts, thresh)
+
+
+def route_top_rho(u: np.ndarray, rho: float) -> Route:
+    return _route("oracle_route_top_rho", u, rho)
+
+
+def route_mean_std(u: np.ndarray, c: float) -> Route:
+    return _route("oracle_route_mean_std", u, c)
+
+
+def window_axis(S: int, k: int, pos: int) -> tuple[int, int]:
+    start = ctypes.c_int()
+    length = ctypes.c_int()
+    rc = _load().oracle_window_axis(S, k, pos, ctypes.addressof(start), ctypes.addressof(length))
+    if rc != 0:
+        raise ValueError("bad window arguments")
+    return start.value, length.value
+
+
+def _as_f32(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def attend_rows(q, k, v, grid, window, scale, mask, rows, nthreads: int = 0) -> np.ndarray:
+    """Outputs [len(rows), heads, D] (float64) for rows = b*N + n."""
+    q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
+    B, N, H, D = q.shape
+    T, Hg, Wg = grid
+    if T * Hg * Wg != N or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("shape mismatch")
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, H, D), np.float64)
+    wt, wh, ww = window
+    rc = _load().oracle_attend_rows(_ptr(q), _ptr(k), _ptr(v), B, H, D, T, Hg, Wg, wt, wh, ww,
+                                    float(scale), _ptr(mask), _ptr(rows), rows.size, _ptr(out),
+                                    int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_attend_rows rejected its arguments (rc={rc})")
+    return out
+
+
+def forward(q, k, v, grid, window, scale, mask, nthreads: int = 0) -> np.ndarray:
+    """Outputs [B, N, heads, D] (float64) for every token."""
+    B, N, H, D = q.shape
+    rows = np.arange(B * N, dtype=np.int64)
+    return attend_rows(q, k, v, grid, window, scale, mask, rows, nthreads).reshape(B, N, H, D)
+
+
+def attention_weights(q, k, grid, window, scale, mask, row: int, head: int) -> np.ndarray:
+    q, k = _as_f32(q), _as_f32(k)
+    B, N, H, D = q.shape
+    T, Hg, Wg = grid
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    w = np.empty(N, np.float64)
+    wt, wh, ww = window
+    rc = _load().oracle_attention_weights(_ptr(q), _ptr(k), B, H, D, T, Hg, Wg, wt, wh, ww,
+                                          float(scale), _ptr(mask), int(row), int(head), _ptr(w))
+    if rc != 0:
+        raise ValueError("oracle_attention_weights rejected its arguments")
+    return w

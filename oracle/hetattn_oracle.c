@@ -1,0 +1,285 @@
+/*
+ * hetattn_oracle.c -- plain fp64 CPU oracle for uncertainty-routed
+ * heterogeneous attention.  TEST INFRASTRUCTURE ONLY (see the header).
+ *
+ * [HetA] = "Where Compute Matters: Heterogeneous Attention for Efficient
+ * Video Diffusion" (HetA-DiT, arXiv 2609.31050), full text.
+ *
+ * Each function writes the definition out directly: a library sort for the
+ * ranking, explicit loops for every sum.  Nothing is blocked, fused or
+ * reordered beyond what the definitions state.
+ */
+#include "hetattn_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* u as used for ranking: u_i >= 0 on the pages ([HetA §3.2.1 Eq. 7]); a -0
+ * is the same value as +0 and a NaN is read as the most uncertain value. */
+static double mapped_u(float x)
+{
+    if (isnan(x)) return INFINITY;
+    if (x == 0.0f) return 0.0;
+    return (double)x;
+}
+
+typedef struct {
+    double u;
+    int idx;
+} ranked_token;
+
+/* Larger u first; equal u -> smaller token index first. */
+static int rank_cmp(const void *pa, const void *pb)
+{
+    const ranked_token *a = (const ranked_token *)pa;
+    const ranked_token *b = (const ranked_token *)pb;
+    if (a->u > b->u) return -1;
+    if (a->u < b->u) return 1;
+    return (a->idx < b->idx) ? -1 : (a->idx > b->idx) ? 1 : 0;
+}
+
+/* From a per-token dense flag, write the mask (1 = local, [HetA §3.2.2
+ * Eq. 12]) and the two ascending index lists with their counts. */
+static void write_route(const unsigned char *dense, int N, unsigned char *mask,
+                        int *dense_idx, int *local_idx, int *counts)
+{
+    int nd = 0, nl = 0;
+    for (int i = 0; i < N; i++) {
+        if (dense[i]) {
+            mask[i] = 0;
+            dense_idx[nd++] = i;
+        } else {
+            mask[i] = 1;
+            local_idx[nl++] = i;
+        }
+    }
+    for (int i = nd; i < N; i++) dense_idx[i] = -1;
+    for (int i = nl; i < N; i++) local_idx[i] = -1;
+    counts[0] = nd;
+    counts[1] = nl;
+}
+
+int oracle_route_top_rho(const float *u, int B, int N, double rho,
+                         unsigned char *mask, int *dense_idx, int *local_idx,
+                         int *counts, double *thresh)
+{
+    if (!u || !mask || !dense_idx || !local_idx || !counts || !thresh) return -1;
+    if (B <= 0 || N <= 0) return -1;
+    if (!(rho >= 0.0 && rho <= 1.0)) return -1;
+
+    long K = (long)floor(rho * (double)N + 0.5);
+    if (K < 0) K = 0;
+    if (K > N) K = N;
+
+    ranked_token *order = (ranked_token *)malloc(sizeof(ranked_token) * (size_t)N);
+    unsigned char *dense = (unsigned char *)malloc((size_t)N);
+    if (!order || !dense) {
+        free(order);
+        free(dense);
+        return -2;
+    }
+    for (int b = 0; b < B; b++) {
+        const float *ub = u + (size_t)b * N;
+        for (int i = 0; i < N; i++) {
+            order[i].u = mapped_u(ub[i]);
+            order[i].idx = i;
+        }
+        qsort(order, (size_t)N, sizeof(ranked_token), rank_cmp);
+        memset(dense, 0, (size_t)N);
+        for (long r = 0; r < K; r++) dense[order[r].idx] = 1;
+        thresh[b] = (K == 0) ? INFINITY : order[K - 1].u;
+        write_route(dense, N, mask + (size_t)b * N, dense_idx + (size_t)b * N,
+                    local_idx + (size_t)b * N, counts + 2 * b);
+    }
+    free(order);
+    free(dense);
+    return 0;
+}
+
+int oracle_route_mean_std(const float *u, int B, int N, double c,
+                          unsigned char *mask, int *dense_idx, int *local_idx,
+                          int *counts, double *thresh)
+{
+    if (!u || !mask || !dense_idx || !local_idx || !counts || !thresh) return -1;
+    if (B <= 0 || N <= 0) return -1;
+    if (!isfinite(c)) return -1;
+
+    unsigned char *dense = (unsigned char *)malloc((size_t)N);
+    if (!dense) return -2;
+    for (int b = 0; b < B; b++) {
+        const float *ub = u + (size_t)b * N;
+        /* Eq. 11: mean and (population) standard deviation over the sample. */
+        double sum = 0.0;
+        for (int i = 0; i < N; i++) sum += mapped_u(ub[i]);
+        double mu = sum / (double)N;
+        double ss = 0.0;
+        for (int i = 0; i < N; i++) {
+            double dlt = mapped_u(ub[i]) - mu;
+            ss += dlt * dlt;
+        }
+        double sigma = sqrt(ss / (double)N);
+        double T = mu + c * sigma;
+        /* Eq. 12: m_i = 1[u_i < T]; the dense tokens are those with m_i = 0. */
+        for (int i = 0; i < N; i++) dense[i] = (mapped_u(ub[i]) < T) ? 0 : 1;
+        thresh[b] = T;
+        write_route(dense, N, mask + (size_t)b * N, dense_idx + (size_t)b * N,
+                    local_idx + (size_t)b * N, counts + 2 * b);
+    }
+    free(dense);
+    return 0;
+}
+
+int oracle_window_axis(int S, int k, int pos, int *start, int *len)
+{
+    if (S <= 0 || k <= 0 || (k % 2) == 0 || pos < 0 || pos >= S || !start || !len)
+        return -1;
+    int L = (k < S) ? k : S;
+    int s = pos - (k - 1) / 2; /* window centred on pos ... */
+    if (s > S - L) s = S - L;  /* ... moved back inside the grid */
+    if (s < 0) s = 0;
+    *start = s;
+    *len = L;
+    return 0;
+}
+
+/* Softmax attention of one query over an explicit key list, in double:
+ * s_j = scale * q.k_j, a_j = exp(s_j - max s) / sum exp(s - max s),
+ * o = sum_j a_j v_j ([HetA §3.1.1 Eqs. 2-3]).  Subtracting the maximum only
+ * keeps exp() in range; it does not change a_j. */
+static void attend_one(const float *qrow, const float *kbase, const float *vbase,
+                       long key_stride, int D, const int *keys, int nkeys,
+                       double scale, double *s, double *o, double *w_out)
+{
+    double smax = -INFINITY;
+    for (int j = 0; j < nkeys; j++) {
+        const float *kr = kbase + (long)keys[j] * key_stride;
+        double dot = 0.0;
+        for (int d = 0; d < D; d++) dot += (double)qrow[d] * (double)kr[d];
+        s[j] = scale * dot;
+        if (s[j] > smax) smax = s[j];
+    }
+    double denom = 0.0;
+    for (int j = 0; j < nkeys; j++) {
+        s[j] = exp(s[j] - smax);
+        denom += s[j];
+    }
+    for (int d = 0; d < D; d++) o[d] = 0.0;
+    for (int j = 0; j < nkeys; j++) {
+        double a = s[j] / denom;
+        if (w_out) w_out[j] = a;
+        if (vbase) {
+            const float *vr = vbase + (long)keys[j] * key_stride;
+            for (int d = 0; d < D; d++) o[d] += a * (double)vr[d];
+        }
+    }
+}
+
+/* The key set of token n: every token of the sample when dense (mask 0),
+ * else the 3D box of [HetA §3.1.1 Eq. 3] in t-major order. */
+static int key_set(int n, unsigned char is_local, int T, int Hg, int Wg,
+                   int wt, int wh, int ww, int *keys)
+{
+    int N = T * Hg * Wg;
+    if (!is_local) {
+        for (int j = 0; j < N; j++) keys[j] = j;
+        return N;
+    }
+    int t = n / (Hg * Wg), y = (n / Wg) % Hg, x = n % Wg;
+    int t0, lt, y0, ly, x0, lx;
+    oracle_window_axis(T, wt, t, &t0, &lt);
+    oracle_window_axis(Hg, wh, y, &y0, &ly);
+    oracle_window_axis(Wg, ww, x, &x0, &lx);
+    int m = 0;
+    for (int a = t0; a < t0 + lt; a++)
+        for (int bb = y0; bb < y0 + ly; bb++)
+            for (int c = x0; c < x0 + lx; c++) keys[m++] = (a * Hg + bb) * Wg + c;
+    return m;
+}
+
+static int check_shape(int B, int heads, int D, int T, int Hg, int Wg, int wt,
+                       int wh, int ww)
+{
+    if (B <= 0 || heads <= 0 || D <= 0 || T <= 0 || Hg <= 0 || Wg <= 0) return -1;
+    if (wt <= 0 || wh <= 0 || ww <= 0) return -1;
+    if (wt % 2 == 0 || wh % 2 == 0 || ww % 2 == 0) return -1;
+    return 0;
+}
+
+int oracle_attend_rows(const float *q, const float *k, const float *v,
+                       int B, int heads, int D,
+                       int T, int Hg, int Wg, int wt, int wh, int ww,
+                       double scale, const unsigned char *mask,
+                       const long *rows, long nrows, double *out, int nthreads)
+{
+    if (!q || !k || !v || !mask || !rows || !out) return -1;
+    if (check_shape(B, heads, D, T, Hg, Wg, wt, wh, ww)) return -1;
+    const long N = (long)T * Hg * Wg;
+    for (long r = 0; r < nrows; r++)
+        if (rows[r] < 0 || rows[r] >= (long)B * N) return -1;
+    const long tok_stride = (long)heads * D; /* [B, N, heads, D] */
+    int err = 0;
+
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel reduction(| : err)
+    {
+        int *keys = (int *)malloc(sizeof(int) * (size_t)N);
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        if (!keys || !s) {
+            err = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long r = 0; r < nrows; r++) {
+                long b = rows[r] / N, n = rows[r] % N;
+                int nk = key_set((int)n, mask[b * N + n], T, Hg, Wg, wt, wh, ww, keys);
+                for (int h = 0; h < heads; h++) {
+                    const float *qrow = q + (b * N + n) * tok_stride + (long)h * D;
+                    const float *kb = k + b * N * tok_stride + (long)h * D;
+                    const float *vb = v + b * N * tok_stride + (long)h * D;
+                    attend_one(qrow, kb, vb, tok_stride, D, keys, nk, scale, s,
+                               out + (r * heads + h) * (long)D, NULL);
+                }
+            }
+        }
+        free(keys);
+        free(s);
+    }
+    return err ? -2 : 0;
+}
+
+int oracle_attention_weights(const float *q, const float *k,
+                             int B, int heads, int D,
+                             int T, int Hg, int Wg, int wt, int wh, int ww,
+                             double scale, const unsigned char *mask,
+                             long row, int head, double *weights)
+{
+    if (!q || !k || !mask || !weights) return -1;
+    if (check_shape(B, heads, D, T, Hg, Wg, wt, wh, ww)) return -1;
+    const long N = (long)T * Hg * Wg;
+    if (row < 0 || row >= (long)B * N || head < 0 || head >= heads) return -1;
+    const long tok_stride = (long)heads * D;
+    long b = row / N, n = row % N;
+    int *keys = (int *)malloc(sizeof(int) * (size_t)N);
+    double *s = (double *)malloc(sizeof(double) * (size_t)N);
+    double *w = (double *)malloc(sizeof(double) * (size_t)N);
+    double *o = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!keys || !s || !w || !o) {
+        free(keys); free(s); free(w); free(o);
+        return -2;
+    }
+    int nk = key_set((int)n, mask[b * N + n], T, Hg, Wg, wt, wh, ww, keys);
+    const float *qrow = q + (b * N + n) * tok_stride + (long)head * D;
+    const float *kb = k + b * N * tok_stride + (long)head * D;
+    attend_one(qrow, kb, NULL, tok_stride, D, keys, nk, scale, s, o, w);
+    for (long j = 0; j < N; j++) weights[j] = 0.0;
+    for (int j = 0; j < nk; j++) weights[keys[j]] = w[j];
+    free(keys); free(s); free(w); free(o);
+    return 0;
+}

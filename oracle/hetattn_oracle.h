@@ -1,0 +1,78 @@
+/*
+ * hetattn_oracle.h -- plain fp64 CPU oracle for uncertainty-routed
+ * heterogeneous attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the HIP path, and the HIP path never calls it.
+ *
+ * [HetA] = "Where Compute Matters: Heterogeneous Attention for Efficient
+ * Video Diffusion" (HetA-DiT, arXiv 2609.31050), full text.
+ *
+ * Conventions shared with the product boundary only through their written
+ * definition (not through code):
+ *   - tokens of sample b are flattened t-major: n = (t*Hg + y)*Wg + x;
+ *   - Q, K, V, O are [B, N, heads, D] row-major;
+ *   - mask[b*N + n] = 1 for a local ("certain") token, 0 for a dense one,
+ *     as in [HetA §3.2.2 Eq. 12];
+ *   - inputs arrive as float32 (bf16 values widen to float32 exactly) and every
+ *     arithmetic step is done in double.
+ *
+ * Every function returns 0 on success and a negative value on a bad argument.
+ */
+#ifndef HETATTN_ORACLE_H
+#define HETATTN_ORACLE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Top-rho routing (the quantile reading of the threshold in [HetA §3.2.2
+ * Eqs. 11-12]; rho is the dense fraction of [HetA §3.2.2, text of Eq. 14]).
+ * K = floor(rho*N + 1/2) tokens per sample are dense: the K largest u, with
+ * equal u ordered by ascending token index.  NaN counts as +inf and -0 as +0.
+ * thresh[b] = the (mapped) u of the K-th ranked token, +inf when K = 0.
+ * counts[2b] = K, counts[2b+1] = N - K.  dense_idx/local_idx rows are
+ * ascending token indices; entries past the count are set to -1. */
+int oracle_route_top_rho(const float *u, int B, int N, double rho,
+                         unsigned char *mask, int *dense_idx, int *local_idx,
+                         int *counts, double *thresh);
+
+/* Mean-std routing, [HetA §3.2.2 Eqs. 11-12] as printed:
+ * mu = mean(u), sigma = population standard deviation (1/N, two passes),
+ * T = mu + c*sigma, and token i is local iff u_i < T (so dense iff not).
+ * u values are mapped as in top-rho before use. */
+int oracle_route_mean_std(const float *u, int B, int N, double c,
+                          unsigned char *mask, int *dense_idx, int *local_idx,
+                          int *counts, double *thresh);
+
+/* The local neighbourhood of [HetA §3.1.1 Eq. 3] along one axis of extent S
+ * for an odd window k at coordinate pos: length min(k, S), start shifted so
+ * the box stays inside [0, S). */
+int oracle_window_axis(int S, int k, int pos, int *start, int *len);
+
+/* Heterogeneous attention [HetA §3.2.2 Eq. 13] for a list of rows.
+ * rows[r] = b*N + n selects the token; out[r*heads*D + h*D + d] receives the
+ * output of every head.  A token with mask 0 attends to all N tokens of its
+ * sample ([HetA §3.1.1 Eq. 2]); a token with mask 1 attends to its 3D window
+ * ([HetA §3.1.1 Eq. 3]).  Softmax is taken over the key set with the given
+ * scale.  nthreads <= 0 uses the OpenMP default. */
+int oracle_attend_rows(const float *q, const float *k, const float *v,
+                       int B, int heads, int D,
+                       int T, int Hg, int Wg, int wt, int wh, int ww,
+                       double scale, const unsigned char *mask,
+                       const long *rows, long nrows, double *out, int nthreads);
+
+/* Same as oracle_attend_rows, but also returns the attention weights of one
+ * (row, head) pair over all N tokens of the row's sample (zero outside the
+ * key set).  Used to check support and normalisation. */
+int oracle_attention_weights(const float *q, const float *k,
+                             int B, int heads, int D,
+                             int T, int Hg, int Wg, int wt, int wh, int ww,
+                             double scale, const unsigned char *mask,
+                             long row, int head, double *weights);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,53 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a copy of ``oracle/hetattn_oracle.c`` (on the
+CPU, in a temporary directory), builds it, and runs the oracle pin tests
+against the copy.  The pins pass on the real oracle; here at least one must
+fail for every planted mistake.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "hetattn_oracle.c")
+
+MUTANTS = {
+    "window_centre_off_by_one": ("int s = pos - (k - 1) / 2;", "int s = pos - (k + 1) / 2;"),
+    "window_not_shifted_at_far_border": ("if (s > S - L) s = S - L;", ""),
+    "ties_to_higher_index": ("return (a->idx < b->idx) ? -1 : (a->idx > b->idx) ? 1 : 0;",
+                             "return (a->idx < b->idx) ? 1 : (a->idx > b->idx) ? -1 : 0;"),
+    "rho_n_truncated": ("floor(rho * (double)N + 0.5)", "floor(rho * (double)N)"),
+    "mean_std_non_strict": ("(mapped_u(ub[i]) < T) ? 0 : 1", "(mapped_u(ub[i]) <= T) ? 0 : 1"),
+    "sample_std": ("sqrt(ss / (double)N)", "sqrt(ss / (double)(N - 1))"),
+    "scale_dropped": ("s[j] = scale * dot;", "s[j] = dot;"),
+    "key_row_stride": ("const float *kr = kbase + (long)keys[j] * key_stride;",
+                       "const float *kr = kbase + (long)keys[j] * D;"),
+    "window_axes_swapped": ("oracle_window_axis(Hg, wh, y, &y0, &ly);",
+                            "oracle_window_axis(Hg, ww, y, &y0, &ly);"),
+    "nan_least_uncertain": ("if (isnan(x)) return INFINITY;", "if (isnan(x)) return -INFINITY;"),
+    "value_from_query_row": ("const float *vr = vbase + (long)keys[j] * key_stride;",
+                             "const float *vr = vbase;"),
+    "local_mask_inverted": ("if (!is_local) {", "if (is_local) {"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mutant = tmp_path / "hetattn_oracle.c"
+    mutant.write_text(src.replace(old, new))
+    (tmp_path / "hetattn_oracle.h").write_text(open(SRC[:-1] + "h").read())
+    lib = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-w",
+                           str(mutant), "-o", str(lib), "-lm"])
+    env = dict(os.environ, HETATTN_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_route.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_attention.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"planted mistake {name!r} passed every pin:\n{r.stdout[-2000:]}"
