@@ -1,0 +1,146 @@
+/*
+ * hetattn.h -- C ABI of the uncertainty-routed heterogeneous attention
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * [HetA] = "Where Compute Matters: Heterogeneous Attention for Efficient
+ * Video Diffusion" (HetA-DiT, arXiv 2609.31050), full text.
+ *
+ * The library computes one heterogeneous self-attention layer, [HetA §3.2.2
+ * Eq. 13]: given Q, K, V of N spatio-temporal tokens ([HetA §3.1.1 Eq. 1])
+ * and a per-token uncertainty u_i >= 0 ([HetA §3.2.1 Eq. 7]) predicted at
+ * the previous denoising step ([HetA §3.2.2], mask reused at step tau-Delta;
+ * [HetA §4] no extra pass at inference), it
+ *   1. picks one threshold per sample ([HetA §3.2.2 Eq. 11]) and the binary
+ *      mask m_i = 1[u_i < T] ([HetA §3.2.2 Eq. 12]): m = 1 is a "certain"
+ *      token (local attention), m = 0 an "uncertain" one (dense attention);
+ *   2. compacts the dense and the local token indices into ascending lists;
+ *   3. computes dense softmax attention over all N keys for the dense tokens
+ *      ([HetA §3.1.1 Eq. 2]) and softmax attention over a 3D window of the
+ *      (T, H, W) latent grid for the local tokens ([HetA §3.1.1 Eq. 3]);
+ *   4. writes both into one output: row i of O is the dense result when
+ *      m_i = 0 and the local result when m_i = 1.
+ *
+ * Layout.  Tokens of a sample are flattened t-major: n = (t*grid_h + y)*grid_w
+ * + x, N = grid_t*grid_h*grid_w.  Q, K, V and O are contiguous
+ * [batch, N, heads, head_dim] arrays of one element type (bf16 or f32).
+ *
+ * Threshold forms.  HET_TOP_RHO makes exactly K = floor(rho*N + 1/2) tokens of
+ * every sample dense (rho is the dense fraction of [HetA §3.2.2], text of
+ * Eq. 14): the K largest u, equal u ranked by ascending token index.
+ * HET_MEAN_STD is [HetA §3.2.2 Eq. 11] as printed: T = mu + c*sigma with the
+ * mean and population standard deviation of the sample's u (fp64), dense iff
+ * u_i >= T.  In both forms a NaN u counts as +inf and -0 as +0.
+ *
+ * Window.  Along each axis of extent S, an odd window k covers min(k, S)
+ * positions starting at clamp(pos - (k-1)/2, 0, S - min(k, S)): it is shifted,
+ * not cut, at the grid border, so every local token sees the same number of
+ * keys M (the constant M of [HetA §3.2.2 Eq. 14]).  A window at least as large
+ * as the grid covers the whole axis.
+ *
+ * Memory.  All tensor arguments are device pointers owned by the caller; the
+ * library allocates and frees nothing and keeps no state between calls.
+ * Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
+ * return without waiting for it.  `shape` and `route` themselves are host
+ * structs read during the call only.
+ *
+ * Errors.  Argument errors are detected on the host before anything is
+ * enqueued and returned as a status; nothing is written then.  A failed launch
+ * returns HET_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ * synchronisation.  No call throws across the ABI.
+ */
+#ifndef HETATTN_H
+#define HETATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HETATTN_ABI_VERSION 1
+
+typedef enum {
+    HET_OK = 0,
+    HET_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, even window, bad param */
+    HET_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, window too wide, index overflow */
+    HET_ERR_WORKSPACE = 3,   /* workspace smaller than het_attn_workspace_bytes() */
+    HET_ERR_HIP = 4          /* a HIP launch failed */
+} het_status;
+
+typedef enum { HET_BF16 = 0, HET_F32 = 1 } het_dtype;
+
+typedef enum {
+    HET_TOP_RHO = 0,  /* param = rho in [0, 1] */
+    HET_MEAN_STD = 1  /* param = c, finite */
+} het_thresh_mode;
+
+typedef struct {
+    int32_t batch;     /* B >= 1 */
+    int32_t heads;     /* >= 1 */
+    int32_t head_dim;  /* 64 or 128 */
+    int32_t grid_t, grid_h, grid_w;  /* latent grid; N = product */
+    int32_t win_t, win_h, win_w;     /* odd, >= 1 */
+    int32_t dtype;     /* het_dtype of Q, K, V and O */
+    float scale;       /* softmax scale; <= 0 selects 1/sqrt(head_dim) ([HetA §3.1.1 Eq. 2]) */
+} het_attn_shape;
+
+typedef struct {
+    uint8_t *mask;       /* [B, N]: 1 = local (m_i = 1), 0 = dense (m_i = 0) */
+    int32_t *dense_idx;  /* [B, N]: dense tokens ascending, then -1 */
+    int32_t *local_idx;  /* [B, N]: local tokens ascending, then -1 */
+    int32_t *counts;     /* [B, 2]: (dense count, local count) per sample */
+    double *thresh;      /* [B]: T_b (TOP_RHO: u of the K-th ranked token, +inf if K = 0) */
+    int32_t dense_count_host; /* set by het_attn_route: K in TOP_RHO mode, -1 in MEAN_STD mode */
+} het_route;
+
+/* HETATTN_ABI_VERSION of the loaded library. */
+int het_attn_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char *het_status_string(int status);
+
+/* Device workspace het_attn_forward needs for this shape, in bytes (may be 0).
+ * Returns 0 for an invalid shape as well; het_attn_forward reports that. */
+size_t het_attn_workspace_bytes(const het_attn_shape *shape);
+
+/* Threshold selection, mask and stable compaction ([HetA §3.2.2 Eqs. 11-12]).
+ *   u      device, float32 [B, N], read only.
+ *   mode   het_thresh_mode; param = rho (TOP_RHO) or c (MEAN_STD).
+ *   out    host struct of caller-owned device buffers, all written;
+ *          out->dense_count_host is written on the host.
+ * Deterministic: the same u gives bit-identical outputs. */
+int het_attn_route(const het_attn_shape *shape, const float *u, int mode, double param,
+                   het_route *out, void *stream);
+
+/* Heterogeneous attention ([HetA §3.2.2 Eq. 13]) with the route of
+ * het_attn_route for the same shape.
+ *   q, k, v  device, [B, N, heads, head_dim] of shape->dtype, read only.
+ *   o        device, same layout and type; every row is written exactly once.
+ *            Must not overlap q, k, v or the route buffers.
+ *   workspace, workspace_bytes: device scratch of at least
+ *            het_attn_workspace_bytes(shape) bytes (NULL allowed when 0).
+ * Dense rows use fp32 accumulation and an fp32 online softmax; with bf16
+ * inputs the probabilities are rounded to bf16 before the P*V product. */
+int het_attn_forward(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                     const het_route *route, void *o, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* The two halves of het_attn_forward, same arguments and rules.
+ * het_attn_dense writes only the rows with m_i = 0 (dense attention over all
+ * N keys, [HetA §3.1.1 Eq. 2]); het_attn_local writes only the rows with
+ * m_i = 1 (the 3D window, [HetA §3.1.1 Eq. 3]).  Together they write every
+ * row once, as het_attn_forward does ([HetA §3.2.2 Eq. 13]); since their
+ * rows are disjoint, a caller may issue them on two streams that both wait
+ * for the route. */
+int het_attn_dense(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                   const het_route *route, void *o, void *workspace, size_t workspace_bytes,
+                   void *stream);
+int het_attn_local(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                   const het_route *route, void *o, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HETATTN_H */

@@ -1,0 +1,135 @@
+"""The C ABI of include/hetattn.h: symbols, version, status strings and the
+host-side argument checks.  Nothing here launches a kernel: every call below
+is rejected on the host before any HIP call, so these run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import uncertainty_routed_heterogeneous_amd as het
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hetattn.h")
+FAKE = 0x1000  # never dereferenced: each call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(het_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(het.LIB_PATH):
+        import uncertainty_routed_heterogeneous_amd.build as b
+        b.build()
+    return het.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names == sorted(het.SIGNATURES), "binding and header disagree"
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.het_attn_abi_version() == het.ABI_VERSION == 1
+    for st in range(5):
+        assert het.status_string(st)
+    assert het.status_string(99) == "unknown status"
+
+
+def good_shape(**kw):
+    d = dict(batch=1, heads=2, head_dim=64, grid=(4, 8, 8), window=(3, 3, 3), dtype=het.HET_F32)
+    d.update(kw)
+    return het.make_shape(d["batch"], d["heads"], d["head_dim"], d["grid"], d["window"], d["dtype"])
+
+
+def fake_route():
+    return het.RouteStruct(FAKE, FAKE, FAKE, FAKE, FAKE, -1)
+
+
+def call_route(lib, shape, mode=het.HET_TOP_RHO, param=0.2, u=FAKE, route=None):
+    r = route if route is not None else fake_route()
+    return lib.het_attn_route(ctypes.byref(shape) if shape is not None else None, u, mode, param,
+                              ctypes.byref(r), None)
+
+
+def call_forward(lib, shape, route=None, q=FAKE, o=FAKE, ws=None, ws_bytes=0):
+    r = route if route is not None else fake_route()
+    return lib.het_attn_forward(ctypes.byref(shape) if shape is not None else None, q, FAKE, FAKE,
+                                ctypes.byref(r), o, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(batch=0), het.HET_ERR_INVALID_ARG),
+    (dict(heads=-1), het.HET_ERR_INVALID_ARG),
+    (dict(grid=(0, 8, 8)), het.HET_ERR_INVALID_ARG),
+    (dict(window=(2, 3, 3)), het.HET_ERR_INVALID_ARG),
+    (dict(window=(3, 3, 0)), het.HET_ERR_INVALID_ARG),
+    (dict(dtype=7), het.HET_ERR_INVALID_ARG),
+    (dict(head_dim=96), het.HET_ERR_UNSUPPORTED),
+    (dict(head_dim=256), het.HET_ERR_UNSUPPORTED),
+    (dict(grid=(64, 64, 64), heads=64, head_dim=128, batch=8), het.HET_ERR_UNSUPPORTED),
+    (dict(grid=(4, 8, 64), window=(3, 3, 27)), het.HET_ERR_UNSUPPORTED),
+])
+def test_shape_errors(lib, bad, status):
+    s = good_shape(**bad)
+    assert call_route(lib, s) == status
+    assert call_forward(lib, s) == status
+    assert lib.het_attn_workspace_bytes(ctypes.byref(s)) == 0
+
+
+def test_null_and_bad_scale(lib):
+    assert call_route(lib, None) == het.HET_ERR_INVALID_ARG
+    assert call_forward(lib, None) == het.HET_ERR_INVALID_ARG
+    s = good_shape()
+    s.scale = float("nan")
+    assert call_route(lib, s) == het.HET_ERR_INVALID_ARG
+    s.scale = float("inf")
+    assert call_forward(lib, s) == het.HET_ERR_INVALID_ARG
+
+
+def test_route_argument_errors(lib):
+    s = good_shape()
+    assert call_route(lib, s, u=None) == het.HET_ERR_INVALID_ARG
+    for field in ("mask", "dense_idx", "local_idx", "counts", "thresh"):
+        r = fake_route()
+        setattr(r, field, None)
+        assert call_route(lib, s, route=r) == het.HET_ERR_INVALID_ARG, field
+    for rho in (-0.01, 1.01, float("nan"), float("inf")):
+        assert call_route(lib, s, het.HET_TOP_RHO, rho) == het.HET_ERR_INVALID_ARG
+    for c in (float("nan"), float("inf"), float("-inf")):
+        assert call_route(lib, s, het.HET_MEAN_STD, c) == het.HET_ERR_INVALID_ARG
+    assert call_route(lib, s, mode=5) == het.HET_ERR_INVALID_ARG
+
+
+def test_forward_argument_errors(lib):
+    s = good_shape()
+    assert call_forward(lib, s, q=None) == het.HET_ERR_INVALID_ARG
+    assert call_forward(lib, s, o=None) == het.HET_ERR_INVALID_ARG
+    r = fake_route()
+    r.dense_count_host = 257  # N = 256
+    assert call_forward(lib, s, route=r) == het.HET_ERR_INVALID_ARG
+    r.dense_count_host = -2
+    assert call_forward(lib, s, route=r) == het.HET_ERR_INVALID_ARG
+    r = fake_route()
+    r.counts = None
+    assert call_forward(lib, s, route=r) == het.HET_ERR_INVALID_ARG
+
+
+def test_workspace_size(lib):
+    assert lib.het_attn_workspace_bytes(None) == 0
+    assert lib.het_attn_workspace_bytes(ctypes.byref(good_shape())) >= 0
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    u = torch.zeros(1, 256)
+    with pytest.raises(ValueError):
+        het.route(u, (4, 8, 8), (3, 3, 3), 2, 64, torch.float32, rho=0.2)  # not on a GPU
+    with pytest.raises(ValueError):
+        het.route(u, (4, 8, 8), (3, 3, 3), 2, 64, torch.float32)  # neither rho nor c

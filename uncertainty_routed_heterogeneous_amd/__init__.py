@@ -1,0 +1,185 @@
+"""Uncertainty-routed heterogeneous attention on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding of ``libhetattn.so`` (C ABI in ``include/hetattn.h``).
+This module only marshals arguments: every step of the layer runs in the HIP
+kernels of ``csrc/``.  PyTorch supplies device memory and the current stream.
+
+[HetA] = "Where Compute Matters: Heterogeneous Attention for Efficient Video
+Diffusion" (HetA-DiT, arXiv 2609.31050).
+
+    r = route(u, grid, window, q.shape, rho=0.2)   # §3.2.2 Eqs. 11-12
+    o = forward(q, k, v, r)                        # §3.2.2 Eq. 13
+
+The library is loaded on first use; if it is missing the call raises -- there
+is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhetattn.so")
+
+HET_OK, HET_ERR_INVALID_ARG, HET_ERR_UNSUPPORTED, HET_ERR_WORKSPACE, HET_ERR_HIP = range(5)
+HET_BF16, HET_F32 = 0, 1
+HET_TOP_RHO, HET_MEAN_STD = 0, 1
+ABI_VERSION = 1
+
+
+class HetAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("grid_t", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("win_t", ctypes.c_int32), ("win_h", ctypes.c_int32), ("win_w", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class RouteStruct(ctypes.Structure):
+    _fields_ = [("mask", ctypes.c_void_p), ("dense_idx", ctypes.c_void_p),
+                ("local_idx", ctypes.c_void_p), ("counts", ctypes.c_void_p),
+                ("thresh", ctypes.c_void_p), ("dense_count_host", ctypes.c_int32)]
+
+
+# Exported symbols and their ctypes signatures (the names of include/hetattn.h).
+SIGNATURES = {
+    "het_attn_abi_version": (ctypes.c_int, []),
+    "het_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "het_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
+    "het_attn_route": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_double, ctypes.POINTER(RouteStruct), ctypes.c_void_p]),
+}
+_ATTN_ARGS = [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+              ctypes.POINTER(RouteStruct), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+              ctypes.c_void_p]
+for _name in ("het_attn_forward", "het_attn_dense", "het_attn_local"):
+    SIGNATURES[_name] = (ctypes.c_int, _ATTN_ARGS)
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libhetattn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m uncertainty_routed_heterogeneous_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if lib.het_attn_abi_version() != ABI_VERSION:
+            raise RuntimeError("libhetattn.so ABI version mismatch")
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().het_status_string(int(status)).decode()
+
+
+def make_shape(batch, heads, head_dim, grid, window, dtype, scale=0.0) -> Shape:
+    return Shape(int(batch), int(heads), int(head_dim), *[int(g) for g in grid],
+                 *[int(w) for w in window], int(dtype), float(scale))
+
+
+def _stream_handle(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+@dataclass
+class Route:
+    """Result of :func:`route`: device tensors plus the host-side dense count."""
+    mask: "object"        # uint8 [B, N], 1 = local
+    dense_idx: "object"   # int32 [B, N]
+    local_idx: "object"   # int32 [B, N]
+    counts: "object"      # int32 [B, 2]
+    thresh: "object"      # float64 [B]
+    dense_count_host: int
+    grid: tuple
+    window: tuple
+
+    def as_struct(self) -> RouteStruct:
+        return RouteStruct(self.mask.data_ptr(), self.dense_idx.data_ptr(), self.local_idx.data_ptr(),
+                           self.counts.data_ptr(), self.thresh.data_ptr(), int(self.dense_count_host))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t == torch.bfloat16:
+        return HET_BF16
+    if t == torch.float32:
+        return HET_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def route(u, grid, window, heads: int, head_dim: int, dtype, rho: float | None = None,
+          c: float | None = None, stream=None) -> Route:
+    """Threshold, mask and compaction for u [B, N] (float32, on the GPU)."""
+    import torch
+    if (rho is None) == (c is None):
+        raise ValueError("give exactly one of rho (top-rho) or c (mean-std)")
+    if u.dtype != torch.float32 or u.dim() != 2 or not u.is_cuda or not u.is_contiguous():
+        raise ValueError("u must be a contiguous float32 [B, N] CUDA tensor")
+    B, N = u.shape
+    if math.prod(grid) != N:
+        raise ValueError("grid does not match N")
+    dev = u.device
+    r = Route(torch.empty((B, N), dtype=torch.uint8, device=dev),
+              torch.empty((B, N), dtype=torch.int32, device=dev),
+              torch.empty((B, N), dtype=torch.int32, device=dev),
+              torch.empty((B, 2), dtype=torch.int32, device=dev),
+              torch.empty((B,), dtype=torch.float64, device=dev), -1, tuple(grid), tuple(window))
+    shape = make_shape(B, heads, head_dim, grid, window, _dtype_code(dtype))
+    rs = r.as_struct()
+    mode, param = (HET_TOP_RHO, rho) if rho is not None else (HET_MEAN_STD, c)
+    st = load_library().het_attn_route(ctypes.byref(shape), u.data_ptr(), mode, float(param),
+                                       ctypes.byref(rs), _stream_handle(stream))
+    if st != HET_OK:
+        raise HetAttnError(st, "het_attn_route")
+    r.dense_count_host = rs.dense_count_host
+    return r
+
+
+def workspace_bytes(shape: Shape) -> int:
+    return int(load_library().het_attn_workspace_bytes(ctypes.byref(shape)))
+
+
+def forward(q, k, v, r: Route, scale: float | None = None, out=None, stream=None,
+            part: str = "both"):
+    """Heterogeneous attention for contiguous [B, N, heads, D] CUDA tensors.
+
+    part = "both" (het_attn_forward), "dense" (het_attn_dense: rows with
+    m_i = 0 only) or "local" (het_attn_local: rows with m_i = 1 only)."""
+    import torch
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v must be contiguous [B, N, heads, D] CUDA tensors")
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    B, N, H, D = q.shape
+    shape = make_shape(B, H, D, r.grid, r.window, _dtype_code(q.dtype), scale or 0.0)
+    if out is None:
+        out = torch.empty_like(q)
+    ws_n = workspace_bytes(shape)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device) if ws_n else None
+    rs = r.as_struct()
+    name = {"both": "het_attn_forward", "dense": "het_attn_dense", "local": "het_attn_local"}[part]
+    st = getattr(load_library(), name)(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                       ctypes.byref(rs), out.data_ptr(),
+                                       ws.data_ptr() if ws is not None else None, ws_n,
+                                       _stream_handle(stream))
+    if st != HET_OK:
+        raise HetAttnError(st, name)
+    return out

@@ -1,0 +1,176 @@
+// api.cpp -- the C ABI of include/hetattn.h: argument validation on the host,
+// then launches on the caller's stream.  No allocation, no state, no
+// device-to-host traffic.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "hetattn.h"
+#include "kernels.hpp"
+
+namespace {
+
+using hetattn::AttnArgs;
+using hetattn::RouteArgs;
+
+struct Dims {
+    int64_t B, N, H, D;
+};
+
+// Validates the shape; on success fills dims and the effective scale.
+het_status check_shape(const het_attn_shape *s, Dims &d, float &scale) {
+    if (!s) return HET_ERR_INVALID_ARG;
+    if (s->batch <= 0 || s->heads <= 0 || s->head_dim <= 0) return HET_ERR_INVALID_ARG;
+    if (s->grid_t <= 0 || s->grid_h <= 0 || s->grid_w <= 0) return HET_ERR_INVALID_ARG;
+    if (s->win_t <= 0 || s->win_h <= 0 || s->win_w <= 0) return HET_ERR_INVALID_ARG;
+    if (s->win_t % 2 == 0 || s->win_h % 2 == 0 || s->win_w % 2 == 0) return HET_ERR_INVALID_ARG;
+    if (s->dtype != HET_BF16 && s->dtype != HET_F32) return HET_ERR_INVALID_ARG;
+    if (std::isnan(s->scale) || std::isinf(s->scale)) return HET_ERR_INVALID_ARG;
+    if (s->head_dim != 64 && s->head_dim != 128) return HET_ERR_UNSUPPORTED;
+    d.B = s->batch;
+    d.H = s->heads;
+    d.D = s->head_dim;
+    d.N = (int64_t)s->grid_t * s->grid_h * s->grid_w;
+    // Element offsets inside the kernels stay below 2^31 per tensor.
+    if (d.N > INT32_MAX / 2 || d.B * d.N * d.H * d.D >= ((int64_t)1 << 31)) return HET_ERR_UNSUPPORTED;
+    const int lw = s->win_w < s->grid_w ? s->win_w : s->grid_w;
+    if (lw > hetattn::kLocalMaxWinW) return HET_ERR_UNSUPPORTED;
+    scale = s->scale > 0.0f ? s->scale : 1.0f / std::sqrt((float)s->head_dim);
+    return HET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int het_attn_abi_version(void) { return HETATTN_ABI_VERSION; }
+
+const char *het_status_string(int status) {
+    switch (status) {
+        case HET_OK: return "ok";
+        case HET_ERR_INVALID_ARG: return "invalid argument";
+        case HET_ERR_UNSUPPORTED: return "unsupported shape";
+        case HET_ERR_WORKSPACE: return "workspace too small";
+        case HET_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t het_attn_workspace_bytes(const het_attn_shape *shape) {
+    Dims d;
+    float scale;
+    if (check_shape(shape, d, scale) != HET_OK) return 0;
+    return 0;
+}
+
+int het_attn_route(const het_attn_shape *shape, const float *u, int mode, double param,
+                   het_route *out, void *stream) {
+    Dims d;
+    float scale;
+    const het_status st = check_shape(shape, d, scale);
+    if (st != HET_OK) return st;
+    if (!u || !out || !out->mask || !out->dense_idx || !out->local_idx || !out->counts || !out->thresh)
+        return HET_ERR_INVALID_ARG;
+    RouteArgs a;
+    a.u = u;
+    a.batch = (int)d.B;
+    a.n = (int)d.N;
+    a.mask = out->mask;
+    a.dense_idx = out->dense_idx;
+    a.local_idx = out->local_idx;
+    a.counts = out->counts;
+    a.thresh = out->thresh;
+    a.c = 0.0;
+    a.k = 0;
+    if (mode == HET_TOP_RHO) {
+        if (!(param >= 0.0 && param <= 1.0)) return HET_ERR_INVALID_ARG;
+        double kk = std::floor(param * (double)d.N + 0.5);
+        if (kk < 0.0) kk = 0.0;
+        if (kk > (double)d.N) kk = (double)d.N;
+        a.mode = 0;
+        a.k = (int)kk;
+    } else if (mode == HET_MEAN_STD) {
+        if (!std::isfinite(param)) return HET_ERR_INVALID_ARG;
+        a.mode = 1;
+        a.c = param;
+    } else {
+        return HET_ERR_INVALID_ARG;
+    }
+    if (hetattn::launch_route(a, (hipStream_t)stream) != hipSuccess) return HET_ERR_HIP;
+    out->dense_count_host = (a.mode == 0) ? a.k : -1;
+    return HET_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+enum Part { kBoth = 3, kDenseOnly = 1, kLocalOnly = 2 };
+
+int run_attention(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                  const het_route *route, void *o, void *workspace, size_t workspace_bytes,
+                  void *stream, int parts) {
+    Dims d;
+    float scale;
+    const het_status st = check_shape(shape, d, scale);
+    if (st != HET_OK) return st;
+    if (!q || !k || !v || !o || !route || !route->mask || !route->dense_idx || !route->counts)
+        return HET_ERR_INVALID_ARG;
+    if (route->dense_count_host < -1 || route->dense_count_host > d.N) return HET_ERR_INVALID_ARG;
+    const size_t need = het_attn_workspace_bytes(shape);
+    if (workspace_bytes < need) return HET_ERR_WORKSPACE;
+    if (need > 0 && !workspace) return HET_ERR_INVALID_ARG;
+
+    AttnArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.mask = route->mask;
+    a.dense_idx = route->dense_idx;
+    a.counts = route->counts;
+    a.batch = (int)d.B;
+    a.n = (int)d.N;
+    a.heads = (int)d.H;
+    a.head_dim = (int)d.D;
+    a.grid_t = shape->grid_t;
+    a.grid_h = shape->grid_h;
+    a.grid_w = shape->grid_w;
+    a.win_t = shape->win_t;
+    a.win_h = shape->win_h;
+    a.win_w = shape->win_w;
+    a.bf16 = shape->dtype == HET_BF16;
+    a.scale = scale;
+    a.max_dense = route->dense_count_host >= 0 ? route->dense_count_host : (int)d.N;
+
+    hipStream_t s = (hipStream_t)stream;
+    // The two kernels write disjoint rows of o (Eq. 13 with m in {0, 1}).
+    if ((parts & kLocalOnly) && hetattn::launch_local(a, s) != hipSuccess) return HET_ERR_HIP;
+    if ((parts & kDenseOnly) && hetattn::launch_dense(a, s) != hipSuccess) return HET_ERR_HIP;
+    return HET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int het_attn_forward(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                     const het_route *route, void *o, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    return run_attention(shape, q, k, v, route, o, workspace, workspace_bytes, stream, kBoth);
+}
+
+int het_attn_dense(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                   const het_route *route, void *o, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    return run_attention(shape, q, k, v, route, o, workspace, workspace_bytes, stream, kDenseOnly);
+}
+
+int het_attn_local(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                   const het_route *route, void *o, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    return run_attention(shape, q, k, v, route, o, workspace, workspace_bytes, stream, kLocalOnly);
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of the
+// heterogeneous attention library: vector types, MFMA wrappers and the lane
+// layouts they imply, bf16 packing and a few cross-lane reductions.
+//
+// MFMA lane layouts used throughout (wave64, gfx950):
+//   v_mfma_f32_32x32x16_bf16   A: lane l holds row l%32, k = 8*(l/32) + j (j < 8)
+//                              B: lane l holds col l%32, k = 8*(l/32) + j
+//                              C: lane l, reg i -> col l%32, row 8*(i/4) + 4*(l/32) + i%4
+//   v_mfma_f32_32x32x2_f32     A: row l%32, k = l/32;  B: col l%32, k = l/32;  C as above
+// ds_read_b64_tr_b16: inside each 16-lane group, lane j supplies the address
+// of 4 consecutive 16-bit elements M_j; lane i receives M_{4e + i/4}[i%4] as
+// element e (e < 4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hetattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define HET_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed (lo = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2 r = __builtin_convertvector((f32x2_t){a, b}, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Value of lane l^32 (the other half of the wave).
+__device__ __forceinline__ float other_half(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    // r[0] = [x_lo, x_lo], r[1] = [x_hi, x_hi]: the partner is r[1] below lane 32, r[0] above.
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ float half_pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr16(const HET_LDS void *p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HET_LDS s16x4 *)p);
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 concat8(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
+
+// Window start along one axis (shifted inside the grid), see hetattn.h.
+__device__ __forceinline__ int window_start(int pos, int k, int len, int S) {
+    int s = pos - (k - 1) / 2;
+    s = imin(s, S - len);
+    return imax(s, 0);
+}
+
+}  // namespace hetattn

@@ -1,0 +1,41 @@
+// kernels.hpp -- host-side launchers of the gfx950 kernels (internal; the
+// public boundary is include/hetattn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hetattn {
+
+struct RouteArgs {
+    const float *u;
+    int batch, n;
+    int mode;       // 0 = top-rho, 1 = mean-std
+    int k;          // dense count (top-rho)
+    double c;       // mean-std coefficient
+    uint8_t *mask;
+    int32_t *dense_idx, *local_idx, *counts;
+    double *thresh;
+};
+
+struct AttnArgs {
+    const void *q, *k, *v;
+    void *o;
+    const uint8_t *mask;
+    const int32_t *dense_idx, *counts;
+    int batch, n, heads, head_dim;
+    int grid_t, grid_h, grid_w;
+    int win_t, win_h, win_w;   // odd, requested
+    bool bf16;
+    float scale;               // softmax scale (> 0)
+    int max_dense;             // upper bound on any sample's dense count
+};
+
+// Largest effective window along w that the local kernel's key tiling holds.
+constexpr int kLocalMaxWinW = 25;
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t stream);
+hipError_t launch_dense(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_local(const AttnArgs &a, hipStream_t stream);
+
+}  // namespace hetattn

@@ -1,0 +1,288 @@
+// local.hip -- softmax attention over a 3D window for the local tokens.
+//
+// [HetA] = "Where Compute Matters: Heterogeneous Attention for Efficient
+// Video Diffusion" (HetA-DiT): local attention of §3.1.1 Eq. 3 over a fixed
+// 3D neighbourhood of the latent grid (§5.1, "predefined 3D neighborhood")
+// for the tokens with m_i = 1 (§3.2.2 Eqs. 12-13).  This is the
+// (1-rho)*N*M*d_h term of the cost model (§3.2.2 Eq. 14).
+//
+// One wave = one query tile of 4 (h) x 8 (w) grid positions at one t, for
+// one (sample, head).  Because the window is shifted rather than cut at the
+// border, the union of the tile's windows is a box: lt frames x ny rows x nx
+// columns.  That box is walked in key blocks of 32 slots, each block holding
+// 32/SR box rows of SR column slots (SR = 16 when nx <= 16, else 32), so every
+// key block is one 32x32 MFMA tile; per (query, key) a mask keeps only the
+// query's own window.  Dense tokens inside a tile ride along and are not
+// stored.  K is fed to the MFMA straight from global memory (each lane reads
+// its key's row); V goes through a per-wave LDS slab and is read transposed.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace hetattn {
+
+constexpr int kLocalQY = 4;
+constexpr int kLocalQX = 8;
+
+struct LocalGeom {
+    int T, Hg, Wg;     // grid
+    int wt, wh, ww;    // requested (odd) window
+    int lt, lh, lw;    // effective window lengths, min(w, extent)
+    int tiles_y, tiles_x;
+    int slot_row;      // SR: 16 or 32 column slots per box row
+};
+
+// Decode slot s (0..31) of key block kb into a token index, or -1.
+__device__ __forceinline__ int local_slot_token(int s, int kb, int SR, int rows, int ny, int nx,
+                                                int t0, int y0, int x0, const LocalGeom &g) {
+    const int r = kb * (32 / SR) + s / SR;
+    const int xo = s % SR;
+    if (r >= rows || xo >= nx) return -1;
+    const int tt = t0 + r / ny, yy = y0 + r % ny;
+    return (tt * g.Hg + yy) * g.Wg + (x0 + xo);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void local_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                   const T *__restrict__ v, T *__restrict__ o,
+                                                   const uint8_t *__restrict__ mask, int N, int H,
+                                                   float scale_log2, LocalGeom g) {
+    constexpr bool kBf16 = sizeof(T) == 2;
+    constexpr int kPitchV = kBf16 ? D + 16 : D + 4;
+    __shared__ __attribute__((aligned(16))) T Vs[32 * kPitchV];
+
+    const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int tile = blockIdx.x;
+    const int t = tile / (g.tiles_y * g.tiles_x);
+    const int ty = (tile / g.tiles_x) % g.tiles_y, tx = tile % g.tiles_x;
+    const int ybase = ty * kLocalQY, xbase = tx * kLocalQX;
+
+    // The query of this lane (col = query within the tile).
+    const int y = ybase + col / kLocalQX, x = xbase + col % kLocalQX;
+    const bool in_grid = y < g.Hg && x < g.Wg;
+    const int tok = in_grid ? (t * g.Hg + y) * g.Wg + x : 0;
+    const bool is_local = in_grid && mask[(size_t)b * N + tok] != 0;
+    if (!__any(is_local)) return;
+
+    // Window of this query, and the union box of the tile.
+    const int t0 = window_start(t, g.wt, g.lt, g.T);
+    const int qy0 = window_start(imin(y, g.Hg - 1), g.wh, g.lh, g.Hg);
+    const int qx0 = window_start(imin(x, g.Wg - 1), g.ww, g.lw, g.Wg);
+    const int ylast = imin(ybase + kLocalQY - 1, g.Hg - 1), xlast = imin(xbase + kLocalQX - 1, g.Wg - 1);
+    const int uy0 = window_start(ybase, g.wh, g.lh, g.Hg);
+    const int ux0 = window_start(xbase, g.ww, g.lw, g.Wg);
+    const int ny = window_start(ylast, g.wh, g.lh, g.Hg) + g.lh - uy0;
+    const int nx = window_start(xlast, g.ww, g.lw, g.Wg) + g.lw - ux0;
+    const int SR = g.slot_row;
+    const int rows = g.lt * ny;
+    const int n_blocks = (rows + (32 / SR) - 1) / (32 / SR);
+
+    const size_t tok_stride = (size_t)H * D;
+    const T *kb_ = k + (size_t)b * N * tok_stride + (size_t)h * D;
+    const T *vb_ = v + (size_t)b * N * tok_stride + (size_t)h * D;
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+    float m_run = -__builtin_inff();
+    float l_part = 0.0f;
+
+    if constexpr (kBf16) {
+        bf16x8 qf[D / 16];
+        const __bf16 *qp = (const __bf16 *)q + ((size_t)b * N + tok) * tok_stride + (size_t)h * D + 8 * half;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) qf[c] = is_local ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
+
+        for (int kb = 0; kb < n_blocks; ++kb) {
+            // Stage the block's V rows (slot s = row of the slab) into LDS.
+            constexpr int kChunks = D / 8;
+#pragma unroll
+            for (int it = 0; it < 32 * kChunks / 64; ++it) {
+                const int e = lane + 64 * it, s = e / kChunks, ch = e % kChunks;
+                const int j = local_slot_token(s, kb, SR, rows, ny, nx, t0, uy0, ux0, g);
+                u32x4 val = u32x4{0, 0, 0, 0};
+                if (j >= 0) val = *(const u32x4 *)((const __bf16 *)vb_ + (size_t)j * tok_stride + 8 * ch);
+                *(u32x4 *)((__bf16 *)Vs + s * kPitchV + 8 * ch) = val;
+            }
+            // S^T = K Q^T with the K rows read straight from global memory.
+            const int jk = local_slot_token(col, kb, SR, rows, ny, nx, t0, uy0, ux0, g);
+            f32x16 s = f32x16{};
+            {
+                const __bf16 *kp = (const __bf16 *)kb_ + (size_t)(jk < 0 ? 0 : jk) * tok_stride + 8 * half;
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) {
+                    const bf16x8 a = (jk >= 0) ? *(const bf16x8 *)(kp + 16 * c) : bf16x8{};
+                    s = mfma32_bf16(a, qf[c], s);
+                }
+            }
+            // Keep only keys inside this query's window.
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int slot = 8 * (i / 4) + 4 * half + (i % 4);
+                const int r = kb * (32 / SR) + slot / SR, xo = slot % SR;
+                const int yy = uy0 + r % ny, xx = ux0 + xo;
+                const bool ok = r < rows && xo < nx && yy >= qy0 && yy < qy0 + g.lh && xx >= qx0 &&
+                                xx < qx0 + g.lw;
+                const float xv = ok ? s[i] * scale_log2 : -__builtin_inff();
+                s[i] = xv;
+                mx = fmaxf(mx, xv);
+            }
+            mx = half_pair_max(mx);
+            const float m_new = fmaxf(m_run, mx);
+            // A block may hold none of this query's keys yet: keep exp2 finite.
+            const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            m_run = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+            bf16x8 pf[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                u32x4 w;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float p0 = __builtin_amdgcn_exp2f(s[8 * c + 2 * jj] - m_use);
+                    const float p1 = __builtin_amdgcn_exp2f(s[8 * c + 2 * jj + 1] - m_use);
+                    l_part += p0 + p1;
+                    w[jj] = pack_bf16x2(p0, p1);
+                }
+                pf[c] = __builtin_bit_cast(bf16x8, w);
+            }
+            __syncthreads();  // V slab visible to the whole wave
+            const int gq = lane >> 4, j16 = lane & 15;
+            const int v_key_off = 4 * half + (j16 >> 2);
+            const int v_col_off = 16 * (gq & 1) + 4 * (j16 & 3);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const __bf16 *base = (const __bf16 *)Vs + (16 * c + v_key_off) * kPitchV + db * 32 + v_col_off;
+                    const bf16x4 lo = lds_read_tr16((const HET_LDS void *)base);
+                    const bf16x4 hi = lds_read_tr16((const HET_LDS void *)(base + 8 * kPitchV));
+                    oacc[db] = mfma32_bf16(concat8(lo, hi), pf[c], oacc[db]);
+                }
+            }
+            __syncthreads();  // slab free for the next block
+        }
+    } else {
+        float qf[D / 2];
+        const float *qp = (const float *)q + ((size_t)b * N + tok) * tok_stride + (size_t)h * D + half;
+#pragma unroll
+        for (int c = 0; c < D / 2; ++c) qf[c] = is_local ? qp[2 * c] : 0.0f;
+
+        for (int kb = 0; kb < n_blocks; ++kb) {
+            constexpr int kChunks = D / 4;
+#pragma unroll
+            for (int it = 0; it < 32 * kChunks / 64; ++it) {
+                const int e = lane + 64 * it, s = e / kChunks, ch = e % kChunks;
+                const int j = local_slot_token(s, kb, SR, rows, ny, nx, t0, uy0, ux0, g);
+                u32x4 val = u32x4{0, 0, 0, 0};
+                if (j >= 0) val = *(const u32x4 *)((const float *)vb_ + (size_t)j * tok_stride + 4 * ch);
+                *(u32x4 *)((float *)Vs + s * kPitchV + 4 * ch) = val;
+            }
+            const int jk = local_slot_token(col, kb, SR, rows, ny, nx, t0, uy0, ux0, g);
+            f32x16 s = f32x16{};
+            {
+                const float *kp = (const float *)kb_ + (size_t)(jk < 0 ? 0 : jk) * tok_stride + half;
+#pragma unroll
+                for (int c = 0; c < D / 2; ++c) s = mfma32_f32(jk >= 0 ? kp[2 * c] : 0.0f, qf[c], s);
+            }
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int slot = 8 * (i / 4) + 4 * half + (i % 4);
+                const int r = kb * (32 / SR) + slot / SR, xo = slot % SR;
+                const int yy = uy0 + r % ny, xx = ux0 + xo;
+                const bool ok = r < rows && xo < nx && yy >= qy0 && yy < qy0 + g.lh && xx >= qx0 &&
+                                xx < qx0 + g.lw;
+                const float xv = ok ? s[i] * scale_log2 : -__builtin_inff();
+                s[i] = xv;
+                mx = fmaxf(mx, xv);
+            }
+            mx = half_pair_max(mx);
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            m_run = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
+                l_part += s[i];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float a = ((const float *)Vs)[(8 * (i / 4) + 4 * half + (i % 4)) * kPitchV + db * 32 + col];
+                    oacc[db] = mfma32_f32(a, s[i], oacc[db]);
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    if (!is_local) return;
+    const float inv_l = 1.0f / half_pair_sum(l_part);
+    T *op = o + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int d = db * 32 + 8 * i4 + 4 * half;
+            if constexpr (kBf16) {
+                u32x2 w;
+                w[0] = pack_bf16x2(oacc[db][4 * i4 + 0] * inv_l, oacc[db][4 * i4 + 1] * inv_l);
+                w[1] = pack_bf16x2(oacc[db][4 * i4 + 2] * inv_l, oacc[db][4 * i4 + 3] * inv_l);
+                *(u32x2 *)((__bf16 *)op + d) = w;
+            } else {
+                f32x4 w = {oacc[db][4 * i4 + 0] * inv_l, oacc[db][4 * i4 + 1] * inv_l,
+                           oacc[db][4 * i4 + 2] * inv_l, oacc[db][4 * i4 + 3] * inv_l};
+                *(f32x4 *)((float *)op + d) = w;
+            }
+        }
+    }
+}
+
+hipError_t launch_local(const AttnArgs &a, hipStream_t stream) {
+    LocalGeom g;
+    g.T = a.grid_t; g.Hg = a.grid_h; g.Wg = a.grid_w;
+    g.wt = a.win_t; g.wh = a.win_h; g.ww = a.win_w;
+    g.lt = a.win_t < a.grid_t ? a.win_t : a.grid_t;
+    g.lh = a.win_h < a.grid_h ? a.win_h : a.grid_h;
+    g.lw = a.win_w < a.grid_w ? a.win_w : a.grid_w;
+    g.tiles_y = (a.grid_h + kLocalQY - 1) / kLocalQY;
+    g.tiles_x = (a.grid_w + kLocalQX - 1) / kLocalQX;
+    const int nx_max = kLocalQX + g.lw - 1;
+    g.slot_row = nx_max <= 16 ? 16 : 32;
+    if (nx_max > 32) return hipErrorInvalidValue;  // rejected earlier by the ABI layer
+    const dim3 grid(g.T * g.tiles_y * g.tiles_x, a.heads, a.batch);
+    const float sl2 = a.scale * kLog2e;
+    if (a.bf16) {
+        auto q = (const __bf16 *)a.q, k = (const __bf16 *)a.k, v = (const __bf16 *)a.v;
+        auto o = (__bf16 *)a.o;
+        if (a.head_dim == 128)
+            hipLaunchKernelGGL((local_kernel<__bf16, 128>), grid, dim3(64), 0, stream, q, k, v, o, a.mask,
+                               a.n, a.heads, sl2, g);
+        else
+            hipLaunchKernelGGL((local_kernel<__bf16, 64>), grid, dim3(64), 0, stream, q, k, v, o, a.mask,
+                               a.n, a.heads, sl2, g);
+    } else {
+        auto q = (const float *)a.q, k = (const float *)a.k, v = (const float *)a.v;
+        auto o = (float *)a.o;
+        if (a.head_dim == 128)
+            hipLaunchKernelGGL((local_kernel<float, 128>), grid, dim3(64), 0, stream, q, k, v, o, a.mask,
+                               a.n, a.heads, sl2, g);
+        else
+            hipLaunchKernelGGL((local_kernel<float, 64>), grid, dim3(64), 0, stream, q, k, v, o, a.mask,
+                               a.n, a.heads, sl2, g);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hetattn
