@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of one uncertainty-routed heterogeneous attention layer on one
+MI355X.
+
+A step is one pass of the whole layer over one batch of synthetic inputs
+already resident in HBM: threshold + mask + compaction (het_attn_route), the
+local 3D-window rows (het_attn_local) and the gathered dense rows
+(het_attn_dense) -- i.e. het_attn_route + het_attn_forward, issued as its two
+halves so that HIP events can time the dense kernel by itself inside the
+timed region.  Default workload: the Wan2.1-1.3B-shaped layer (B=1, 12
+heads, head_dim 128, 21x30x52 latent grid, rho = 0.2, 3x7x7 window).
+
+Prints ONE JSON line on stdout.  Extra detail goes to stderr.
+
+[HetA] = "Where Compute Matters: Heterogeneous Attention for Efficient Video
+Diffusion" (HetA-DiT): effective FLOPs follow the cost model of §3.2.2 Eq. 14.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms/attn layer + effective TFLOP/s at rho=0.2 (Wan-1.3B shape); % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+DENSE_KERNEL_SOURCES = ("uncertainty_routed_heterogeneous_amd/csrc/dense.hip",
+                        "uncertainty_routed_heterogeneous_amd/csrc/common.hpp")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "dense_bf16_wan13b_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(dense_launch_units: float):
+    """HBM bytes per dense launch from the committed counter summary, if it
+    was taken on the current dense kernel source; else None."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    text = open(TRAFFIC_PROFILE).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(DENSE_KERNEL_SOURCES):
+        return None
+    return float(m_bytes.group(1))
+
+
+class Layer:
+    """Pre-built ctypes arguments for one workload, so the timed loop issues
+    three library calls per step and nothing else."""
+
+    def __init__(self, het, w, q, k, v, u, rho):
+        import torch
+        self.het, self.lib, self.w = het, het.load_library(), w
+        B, N = w.batch, w.n_tokens
+        dev = q.device
+        self.q, self.k, self.v, self.u = q, k, v, u
+        self.o = torch.empty_like(q)
+        self.mask = torch.empty((B, N), dtype=torch.uint8, device=dev)
+        self.didx = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.lidx = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.counts = torch.empty((B, 2), dtype=torch.int32, device=dev)
+        self.thresh = torch.empty((B,), dtype=torch.float64, device=dev)
+        self.shape = het.make_shape(B, w.heads, w.head_dim, w.grid, w.window, het.HET_BF16)
+        self.rs = het.RouteStruct(self.mask.data_ptr(), self.didx.data_ptr(), self.lidx.data_ptr(),
+                                  self.counts.data_ptr(), self.thresh.data_ptr(), -1)
+        self.rho = float(rho)
+        self.stream = torch.cuda.current_stream().cuda_stream
+        ws = het.workspace_bytes(self.shape)
+        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.ws_bytes = ws
+        self.args = (ctypes.byref(self.shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                     ctypes.byref(self.rs), self.o.data_ptr(), self.ws.data_ptr(), ws, self.stream)
+
+    def route(self):
+        st = self.lib.het_attn_route(ctypes.byref(self.shape), self.u.data_ptr(), self.het.HET_TOP_RHO,
+                                     self.rho, ctypes.byref(self.rs), self.stream)
+        if st != 0:
+            raise self.het.HetAttnError(st, "het_attn_route")
+
+    def local(self):
+        st = self.lib.het_attn_local(*self.args)
+        if st != 0:
+            raise self.het.HetAttnError(st, "het_attn_local")
+
+    def dense(self):
+        st = self.lib.het_attn_dense(*self.args)
+        if st != 0:
+            raise self.het.HetAttnError(st, "het_attn_dense")
+
+
+def time_layer(layer, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` steps; per-kernel times come from
+    events recorded between the launches on the same stream."""
+    import torch
+    for _ in range(warmup):
+        layer.route(); layer.local(); layer.dense()
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[E(), E(), E(), E()] for _ in range(steps)]
+    start, end = E(), E()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(steps):
+        ev[s][0].record(); layer.route()
+        ev[s][1].record(); layer.local()
+        ev[s][2].record(); layer.dense()
+        ev[s][3].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    per = [[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in ev]
+    mean = lambda xs: sum(xs) / len(xs)
+    return dict(ms_per_step=total_ms / steps, wall_ms_per_step=1e3 * wall / steps,
+                route_ms=mean([p[0] for p in per]), local_ms=mean([p[1] for p in per]),
+                dense_ms=mean([p[2] for p in per]))
+
+
+def cpu_baseline(w, q, k, v, u, rho, stride: int):
+    """The fp64 oracle on the host cores, on a bounded sample of the same
+    layer: the full route plus every `stride`-th dense and local row."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    r = oracle.route_top_rho(u, rho)
+    rows = []
+    n_dense = n_local = 0
+    for b in range(w.batch):
+        d = r.dense_idx[b, : r.counts[b, 0]][::stride]
+        l = r.local_idx[b, : r.counts[b, 1]][::stride]
+        n_dense += d.size
+        n_local += l.size
+        rows.append(b * w.n_tokens + np.concatenate([d, l]).astype(np.int64))
+    oracle.attend_rows(q, k, v, w.grid, w.window, w.softmax_scale, r.mask, np.concatenate(rows),
+                       nthreads=threads)
+    sec = time.perf_counter() - t0
+    T, H, Wd = w.grid
+    M = min(w.window[0], T) * min(w.window[1], H) * min(w.window[2], Wd)
+    flop = 4.0 * w.head_dim * w.heads * (n_dense * w.n_tokens + n_local * M)
+    return {"value": round(flop / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"{w.name}: full route of {w.batch}x{w.n_tokens} tokens plus every "
+                       f"{stride}th dense and local row ({n_dense} dense, {n_local} local rows, "
+                       f"all {w.heads} heads) in fp64; {sec:.1f} s, effective FLOPs of the sample "
+                       f"per second; est. {W.effective_flops(w.with_(rho=rho)) / (flop / sec):.1f} s "
+                       f"for the whole layer")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="wan13b", choices=["wan13b", "wan5b", "long", "tiny"])
+    ap.add_argument("--rho", type=float, default=None, help="override the workload's rho")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense-baseline", action="store_true")
+    ap.add_argument("--cpu-stride", type=int, default=4)
+    ap.add_argument("--lib", default=None, help="load this libhetattn.so instead of the in-tree one")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(the layer shards by (sample, head) with no collectives; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import uncertainty_routed_heterogeneous_amd as het
+    import workloads as W
+
+    if args.lib:
+        het.load_library(os.path.abspath(args.lib))
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = W.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        w = w.with_(dtype="bf16")
+    rho = w.rho if args.rho is None else args.rho
+    log(f"[bench] workload={w.name} grid={w.grid} B={w.batch} heads={w.heads} D={w.head_dim} "
+        f"rho={rho} window={w.window}")
+    qn, kn, vn = W.make_qkv(w)
+    un = W.make_u(w)
+    to_bf16 = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    q, k, v = to_bf16(qn), to_bf16(kn), to_bf16(vn)
+    u = torch.from_numpy(un).cuda()
+    torch.cuda.synchronize()
+
+    layer = Layer(het, w, q, k, v, u, rho)
+    res = time_layer(layer, args.steps, args.warmup)
+    n_dense = [W.dense_count(w.n_tokens, rho)] * w.batch
+    eff_flop = W.effective_flops(w, n_dense)
+    dense_flop = 4.0 * w.head_dim * w.heads * sum(kd * w.n_tokens for kd in n_dense)
+    bytes_el = 2
+    BNHD = w.batch * w.n_tokens * w.heads * w.head_dim
+    n_local = sum(w.n_tokens - kd for kd in n_dense)
+    local_bytes = 2 * BNHD * bytes_el + 2 * n_local * w.heads * w.head_dim * bytes_el
+    route_bytes = 13 * w.batch * w.n_tokens
+    value = eff_flop / (res["ms_per_step"] * 1e-3) / 1e12
+    dense_tflops = dense_flop / (res["dense_ms"] * 1e-3) / 1e12
+    traffic = read_traffic(dense_flop / (4.0 * w.head_dim))
+    log(f"[bench] ms/step={res['ms_per_step']:.4f} route={res['route_ms']:.4f} "
+        f"local={res['local_ms']:.4f} dense={res['dense_ms']:.4f} -> {value:.1f} TFLOP/s effective, "
+        f"dense kernel {dense_tflops:.1f} TFLOP/s")
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: HetA attention layer, B={w.batch}, {w.heads} heads, "
+                               f"head_dim {w.head_dim}, grid {w.grid[0]}x{w.grid[1]}x{w.grid[2]}",
+                   "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim, "grid": list(w.grid),
+                   "tokens": w.n_tokens, "rho": rho, "dense_tokens": n_dense,
+                   "window": list(w.window), "u": w.u_kind, "effective_flop": eff_flop},
+        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "dense_bf16_kernel<128>",
+                     "achieved": round(dense_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(dense_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "avg_launch_ms": round(res["dense_ms"], 5),
+                     "flop_per_launch": dense_flop},
+        "kernels": {
+            "route_ms": round(res["route_ms"], 5),
+            "route_GBps": round(route_bytes / (res["route_ms"] * 1e-3) / 1e9, 1),
+            "local_ms": round(res["local_ms"], 5),
+            "local_GBps": round(local_bytes / (res["local_ms"] * 1e-3) / 1e9, 1),
+            "local_frac_hbm": round(local_bytes / (res["local_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "dense_ms": round(res["dense_ms"], 5),
+        },
+    }
+
+    if not args.no_dense_baseline and rho < 1.0:
+        dl = Layer(het, w, q, k, v, u, 1.0)
+        rd = time_layer(dl, max(5, args.steps // 5), max(2, args.warmup // 5))
+        out["dense_rho1"] = {"ms_per_step": round(rd["ms_per_step"], 5),
+                             "dense_kernel_TFLOPs": round(4.0 * w.head_dim * w.heads * w.batch *
+                                                          w.n_tokens ** 2 / (rd["dense_ms"] * 1e-3) / 1e12, 2),
+                             "speedup_vs_rho1": round(rd["ms_per_step"] / res["ms_per_step"], 3)}
+        log(f"[bench] rho=1 dense path: {rd['ms_per_step']:.4f} ms/step "
+            f"({out['dense_rho1']['speedup_vs_rho1']}x slower than rho={rho})")
+        del dl
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 CPU oracle on a sample ...")
+        out["cpu_baseline"] = cpu_baseline(w, qn, kn, vn, un, rho, args.cpu_stride)
+        log(f"[bench] cpu baseline: {out['cpu_baseline']}")
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
