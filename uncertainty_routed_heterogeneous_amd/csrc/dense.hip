@@ -36,17 +36,35 @@ struct DenseTile {
 };
 
 // ---------------------------------------------------------------- bf16 ----
+// Lazy rescaling: the running reference max m_ref only moves when a tile's
+// max exceeds it by more than kRescaleSlack (log2 units).  Probabilities are
+// then at most 2^kRescaleSlack, which bf16 and fp32 hold exactly as well as
+// values <= 1, and O / l is unchanged because both use the same reference.
+constexpr float kRescaleSlack = 8.0f;
+
+// Workgroup -> (sample, head, query tile).  Workgroups are dealt to the 8 XCDs
+// round-robin; remapping gives each XCD a contiguous run of tiles, so the
+// tiles streaming one head's K/V run on one XCD and share its L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+    const int per_xcd = nwg >> 3;  // nwg is a multiple of 8
+    return (bid & 7) * per_xcd + (bid >> 3);
+}
+
 template <int D>
-__global__ __launch_bounds__(kDenseThreads) void dense_bf16_kernel(
+__global__ __launch_bounds__(kDenseThreads, 2) void dense_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const int32_t *__restrict__ dense_idx,
-    const int32_t *__restrict__ counts, int N, int H, float scale_log2) {
+    const int32_t *__restrict__ counts, int N, int H, float scale_log2, int tiles_per_bh,
+    int n_units) {
     constexpr int BN = 64;
     using Tl = DenseTile<__bf16, D, BN>;
     __shared__ __attribute__((aligned(16))) __bf16 Ks[BN * Tl::kPitchK];
     __shared__ __attribute__((aligned(16))) __bf16 Vs[BN * Tl::kPitchV];
 
-    const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int unit = xcd_remap(blockIdx.x, gridDim.x);
+    if (unit >= n_units) return;
+    const int tile = unit % tiles_per_bh, bh = unit / tiles_per_bh;
+    const int h = bh % H, b = bh / H;
     const int n_dense = counts[2 * b];
     if (tile * kDenseBM >= n_dense) return;
 
@@ -97,8 +115,13 @@ __global__ __launch_bounds__(kDenseThreads) void dense_bf16_kernel(
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-    float m_run = -__builtin_inff();
+    float m_ref = -__builtin_inff();  // reference max, log2 units
     float l_part = 0.0f;
+
+    // Transposed-read coordinates of V (see the O^T update below).
+    const int g16 = lane >> 4, j16 = lane & 15;
+    const int v_key_off = 4 * half + (j16 >> 2);
+    const int v_col_off = 16 * (g16 & 1) + 4 * (j16 & 3);
 
     const int n_tiles = (N + BN - 1) / BN;
     fetch(0);
@@ -107,7 +130,7 @@ __global__ __launch_bounds__(kDenseThreads) void dense_bf16_kernel(
     for (int kt = 0; kt < n_tiles; ++kt) {
         if (kt + 1 < n_tiles) fetch(kt + 1);
 
-        // ---- S^T = K Q^T for two 32-key blocks
+        // ---- S^T = K Q^T for two 32-key blocks (raw scores)
         f32x16 s[2];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
@@ -119,30 +142,33 @@ __global__ __launch_bounds__(kDenseThreads) void dense_bf16_kernel(
                 s[blk] = mfma32_bf16(a, qf[c], s[blk]);
             }
         }
+        if (kt == n_tiles - 1 && (kt + 1) * BN > N) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kt * BN + blk * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+                    if (key >= N) s[blk][i] = -__builtin_inff();
+                }
+        }
 
-        // ---- online softmax (base 2)
-        const bool ragged = (kt + 1) * BN > N;
+        // ---- online softmax (base 2, lazy rescale)
         float mx = -__builtin_inff();
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float x = s[blk][i] * scale_log2;
-                if (ragged) {
-                    const int key = kt * BN + blk * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-                    if (key >= N) x = -__builtin_inff();
-                }
-                s[blk][i] = x;
-                mx = fmaxf(mx, x);
-            }
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[blk][i]);
+        mx = half_pair_max(mx) * scale_log2;
+        const bool grow = mx > m_ref + kRescaleSlack;
+        if (__any(grow)) {
+            const float m_new = grow ? mx : m_ref;
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            m_ref = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
         }
-        mx = half_pair_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        const float neg_m = -m_ref;
 
         // P as the B operand of O^T += V^T P^T: chunk c of block blk = registers 8c..8c+7,
         // i.e. keys 16c + 8(j/4) + 4*half + j%4 (j < 8) of the block.
@@ -154,8 +180,8 @@ __global__ __launch_bounds__(kDenseThreads) void dense_bf16_kernel(
                 u32x4 w;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float p0 = __builtin_amdgcn_exp2f(s[blk][8 * c + 2 * j] - m_new);
-                    const float p1 = __builtin_amdgcn_exp2f(s[blk][8 * c + 2 * j + 1] - m_new);
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][8 * c + 2 * j], scale_log2, neg_m));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][8 * c + 2 * j + 1], scale_log2, neg_m));
                     l_part += p0 + p1;
                     w[j] = pack_bf16x2(p0, p1);
                 }
@@ -166,9 +192,6 @@ __global__ __launch_bounds__(kDenseThreads) void dense_bf16_kernel(
         // ---- O^T += V^T P^T.  A operand rows = d, k = the 8 keys above; read
         // transposed from the row-major V tile: lane j of each 16-lane group
         // points at key (base + j/4), columns 4*(j%4) .. +3 of its 16-column slab.
-        const int g = lane >> 4, j16 = lane & 15;
-        const int v_key_off = 4 * half + (j16 >> 2);
-        const int v_col_off = 16 * (g & 1) + 4 * (j16 & 3);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -342,12 +365,15 @@ hipError_t launch_dense(const AttnArgs &a, hipStream_t stream) {
     if (a.bf16) {
         auto q = (const __bf16 *)a.q, k = (const __bf16 *)a.k, v = (const __bf16 *)a.v;
         auto o = (__bf16 *)a.o;
+        const int tiles = (a.max_dense + kDenseBM - 1) / kDenseBM;
+        const int units = tiles * a.heads * a.batch;
+        const dim3 g1d((units + 7) / 8 * 8);
         if (a.head_dim == 128)
-            hipLaunchKernelGGL(dense_bf16_kernel<128>, grid, dim3(kDenseThreads), 0, stream, q, k, v, o,
-                               a.dense_idx, a.counts, a.n, a.heads, sl2);
+            hipLaunchKernelGGL(dense_bf16_kernel<128>, g1d, dim3(kDenseThreads), 0, stream, q, k, v, o,
+                               a.dense_idx, a.counts, a.n, a.heads, sl2, tiles, units);
         else
-            hipLaunchKernelGGL(dense_bf16_kernel<64>, grid, dim3(kDenseThreads), 0, stream, q, k, v, o,
-                               a.dense_idx, a.counts, a.n, a.heads, sl2);
+            hipLaunchKernelGGL(dense_bf16_kernel<64>, g1d, dim3(kDenseThreads), 0, stream, q, k, v, o,
+                               a.dense_idx, a.counts, a.n, a.heads, sl2, tiles, units);
     } else {
         auto q = (const float *)a.q, k = (const float *)a.k, v = (const float *)a.v;
         auto o = (float *)a.o;
