@@ -74,6 +74,15 @@ __device__ __forceinline__ bf16x8 concat8(bf16x4 a, bf16x4 b) {
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 
+// Workgroup -> work unit.  The hardware deals consecutive workgroups to the 8
+// XCDs round-robin; this remap gives each XCD a contiguous run of units so
+// that units sharing K/V (one head, neighbouring tiles) share that XCD's L2.
+// nwg must be a multiple of 8.
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+    const int per_xcd = nwg >> 3;
+    return (bid & 7) * per_xcd + (bid >> 3);
+}
+
 // Window start along one axis (shifted inside the grid), see hetattn.h.
 __device__ __forceinline__ int window_start(int pos, int k, int len, int S) {
     int s = pos - (k - 1) / 2;

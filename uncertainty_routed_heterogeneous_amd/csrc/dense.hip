@@ -42,14 +42,6 @@ struct DenseTile {
 // values <= 1, and O / l is unchanged because both use the same reference.
 constexpr float kRescaleSlack = 8.0f;
 
-// Workgroup -> (sample, head, query tile).  Workgroups are dealt to the 8 XCDs
-// round-robin; remapping gives each XCD a contiguous run of tiles, so the
-// tiles streaming one head's K/V run on one XCD and share its L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
-    const int per_xcd = nwg >> 3;  // nwg is a multiple of 8
-    return (bid & 7) * per_xcd + (bid >> 3);
-}
-
 template <int D>
 __global__ __launch_bounds__(kDenseThreads, 2) void dense_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,

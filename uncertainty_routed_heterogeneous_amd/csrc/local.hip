@@ -13,8 +13,16 @@
 // 32/SR box rows of SR column slots (SR = 16 when nx <= 16, else 32), so every
 // key block is one 32x32 MFMA tile; per (query, key) a mask keeps only the
 // query's own window.  Dense tokens inside a tile ride along and are not
-// stored.  K is fed to the MFMA straight from global memory (each lane reads
-// its key's row); V goes through a per-wave LDS slab and is read transposed.
+// stored.
+//
+// Memory: the layer is bandwidth-bound (about 65 flop per byte), so the
+// tiles are ordered (sample, head, t, y, x) and dealt to XCDs in contiguous
+// runs: neighbouring tiles, whose key boxes overlap, share one L2.  K rows
+// feed the MFMA straight from global memory; V goes through a per-wave LDS
+// slab and is read transposed.  The next key block's K and V are fetched into
+// registers while the current block computes.  Slots outside the box load a
+// clamped in-grid address and are zeroed (V) or masked (scores), so no load
+// is predicated.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,30 +39,29 @@ struct LocalGeom {
     int slot_row;      // SR: 16 or 32 column slots per box row
 };
 
-// Decode slot s (0..31) of key block kb into a token index, or -1.
-__device__ __forceinline__ int local_slot_token(int s, int kb, int SR, int rows, int ny, int nx,
-                                                int t0, int y0, int x0, const LocalGeom &g) {
-    const int r = kb * (32 / SR) + s / SR;
-    const int xo = s % SR;
-    if (r >= rows || xo >= nx) return -1;
-    const int tt = t0 + r / ny, yy = y0 + r % ny;
-    return (tt * g.Hg + yy) * g.Wg + (x0 + xo);
-}
-
 template <typename T, int D>
-__global__ __launch_bounds__(64) void local_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                   const T *__restrict__ v, T *__restrict__ o,
-                                                   const uint8_t *__restrict__ mask, int N, int H,
-                                                   float scale_log2, LocalGeom g) {
+__global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                      const T *__restrict__ v, T *__restrict__ o,
+                                                      const uint8_t *__restrict__ mask, int N, int H,
+                                                      float scale_log2, LocalGeom g, int n_units) {
     constexpr bool kBf16 = sizeof(T) == 2;
+    constexpr int kVec = 16 / sizeof(T);          // elements per 16-byte load
+    constexpr int kChunks = D / kVec;             // 16-byte chunks per row
+    constexpr int kStage = 32 * kChunks / 64;     // V chunks staged per lane per block
     constexpr int kPitchV = kBf16 ? D + 16 : D + 4;
     __shared__ __attribute__((aligned(16))) T Vs[32 * kPitchV];
 
+    const int unit = xcd_remap(blockIdx.x, gridDim.x);
+    if (unit >= n_units) return;
+    const int tx = unit % g.tiles_x;
+    int rest = unit / g.tiles_x;
+    const int ty = rest % g.tiles_y;
+    rest /= g.tiles_y;
+    const int t = rest % g.T;
+    rest /= g.T;
+    const int h = rest % H, b = rest / H;
+
     const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int tile = blockIdx.x;
-    const int t = tile / (g.tiles_y * g.tiles_x);
-    const int ty = (tile / g.tiles_x) % g.tiles_y, tx = tile % g.tiles_x;
     const int ybase = ty * kLocalQY, xbase = tx * kLocalQX;
 
     // The query of this lane (col = query within the tile).
@@ -73,13 +80,26 @@ __global__ __launch_bounds__(64) void local_kernel(const T *__restrict__ q, cons
     const int ux0 = window_start(xbase, g.ww, g.lw, g.Wg);
     const int ny = window_start(ylast, g.wh, g.lh, g.Hg) + g.lh - uy0;
     const int nx = window_start(xlast, g.ww, g.lw, g.Wg) + g.lw - ux0;
-    const int SR = g.slot_row;
+    const int SR = g.slot_row, rpb = 32 / SR;
     const int rows = g.lt * ny;
-    const int n_blocks = (rows + (32 / SR) - 1) / (32 / SR);
+    const int n_blocks = (rows + rpb - 1) / rpb;
 
     const size_t tok_stride = (size_t)H * D;
-    const T *kb_ = k + (size_t)b * N * tok_stride + (size_t)h * D;
-    const T *vb_ = v + (size_t)b * N * tok_stride + (size_t)h * D;
+    const T *kbase = k + (size_t)b * N * tok_stride + (size_t)h * D;
+    const T *vbase = v + (size_t)b * N * tok_stride + (size_t)h * D;
+
+    // Box row r -> token of its first column (rows past the box clamp to the last row).
+    auto row_token = [&](int r) -> int {
+        r = imin(r, rows - 1);
+        const int tt = t0 + r / ny, yy = uy0 + r % ny;
+        return (tt * g.Hg + yy) * g.Wg + ux0;
+    };
+    // Slot s of block kb -> token (clamped into the box) and whether it is a real key.
+    auto slot = [&](int kb, int s, int &tokj) -> bool {
+        const int r = kb * rpb + s / SR, xo = s % SR;
+        tokj = row_token(r) + imin(xo, nx - 1);
+        return r < rows && xo < nx;
+    };
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -87,56 +107,110 @@ __global__ __launch_bounds__(64) void local_kernel(const T *__restrict__ q, cons
     float m_run = -__builtin_inff();
     float l_part = 0.0f;
 
-    if constexpr (kBf16) {
-        bf16x8 qf[D / 16];
-        const __bf16 *qp = (const __bf16 *)q + ((size_t)b * N + tok) * tok_stride + (size_t)h * D + 8 * half;
+    // Staging of one block: this lane's K row (A operand) and its share of V rows.
+    constexpr int kKRegs = kBf16 ? D / 16 : D / 2;
+    typedef typename std::conditional<kBf16, bf16x8, float>::type KFrag;
+    KFrag kf[kKRegs], kn[kKRegs];
+    u32x4 vst[kStage];
+    bool vok[kStage];
+    auto fetch = [&](int kb, KFrag *kdst) {
+        int jk;
+        slot(kb, col, jk);
+        const T *kp = kbase + (size_t)jk * tok_stride;
+        if constexpr (kBf16) {
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) qf[c] = is_local ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
+            for (int c = 0; c < kKRegs; ++c) kdst[c] = *(const bf16x8 *)((const __bf16 *)kp + 16 * c + 8 * half);
+        } else {
+#pragma unroll
+            for (int c = 0; c < kKRegs; ++c) kdst[c] = ((const float *)kp)[2 * c + half];
+        }
+#pragma unroll
+        for (int it = 0; it < kStage; ++it) {
+            const int e = lane + 64 * it, s = e / kChunks, ch = e % kChunks;
+            int jv;
+            vok[it] = slot(kb, s, jv);
+            vst[it] = *(const u32x4 *)(vbase + (size_t)jv * tok_stride + kVec * ch);
+        }
+    };
+    auto stage_v = [&]() {
+#pragma unroll
+        for (int it = 0; it < kStage; ++it) {
+            const int e = lane + 64 * it, s = e / kChunks, ch = e % kChunks;
+            const u32x4 val = vok[it] ? vst[it] : u32x4{0, 0, 0, 0};
+            *(u32x4 *)(Vs + s * kPitchV + kVec * ch) = val;
+        }
+    };
 
-        for (int kb = 0; kb < n_blocks; ++kb) {
-            // Stage the block's V rows (slot s = row of the slab) into LDS.
-            constexpr int kChunks = D / 8;
+    // Query operand.
+    typedef typename std::conditional<kBf16, bf16x8, float>::type QFrag;
+    QFrag qf[kKRegs];
+    {
+        const T *qp = q + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
+        if constexpr (kBf16) {
 #pragma unroll
-            for (int it = 0; it < 32 * kChunks / 64; ++it) {
-                const int e = lane + 64 * it, s = e / kChunks, ch = e % kChunks;
-                const int j = local_slot_token(s, kb, SR, rows, ny, nx, t0, uy0, ux0, g);
-                u32x4 val = u32x4{0, 0, 0, 0};
-                if (j >= 0) val = *(const u32x4 *)((const __bf16 *)vb_ + (size_t)j * tok_stride + 8 * ch);
-                *(u32x4 *)((__bf16 *)Vs + s * kPitchV + 8 * ch) = val;
-            }
-            // S^T = K Q^T with the K rows read straight from global memory.
-            const int jk = local_slot_token(col, kb, SR, rows, ny, nx, t0, uy0, ux0, g);
-            f32x16 s = f32x16{};
-            {
-                const __bf16 *kp = (const __bf16 *)kb_ + (size_t)(jk < 0 ? 0 : jk) * tok_stride + 8 * half;
+            for (int c = 0; c < kKRegs; ++c)
+                qf[c] = is_local ? *(const bf16x8 *)((const __bf16 *)qp + 16 * c + 8 * half) : bf16x8{};
+        } else {
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c) {
-                    const bf16x8 a = (jk >= 0) ? *(const bf16x8 *)(kp + 16 * c) : bf16x8{};
-                    s = mfma32_bf16(a, qf[c], s);
-                }
-            }
-            // Keep only keys inside this query's window.
-            float mx = -__builtin_inff();
+            for (int c = 0; c < kKRegs; ++c) qf[c] = is_local ? ((const float *)qp)[2 * c + half] : 0.0f;
+        }
+    }
+
+    const int gq = lane >> 4, j16 = lane & 15;
+    const int v_key_off = 4 * half + (j16 >> 2);
+    const int v_col_off = 16 * (gq & 1) + 4 * (j16 & 3);
+
+    fetch(0, kf);
+    for (int kb = 0; kb < n_blocks; ++kb) {
+        stage_v();
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int slot = 8 * (i / 4) + 4 * half + (i % 4);
-                const int r = kb * (32 / SR) + slot / SR, xo = slot % SR;
-                const int yy = uy0 + r % ny, xx = ux0 + xo;
-                const bool ok = r < rows && xo < nx && yy >= qy0 && yy < qy0 + g.lh && xx >= qx0 &&
-                                xx < qx0 + g.lw;
-                const float xv = ok ? s[i] * scale_log2 : -__builtin_inff();
-                s[i] = xv;
-                mx = fmaxf(mx, xv);
-            }
-            mx = half_pair_max(mx);
-            const float m_new = fmaxf(m_run, mx);
-            // A block may hold none of this query's keys yet: keep exp2 finite.
-            const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            m_run = m_new;
-            l_part *= alpha;
+        for (int c = 0; c < kKRegs; ++c) kn[c] = kf[c];
+        if (kb + 1 < n_blocks) fetch(kb + 1, kf);
+
+        // S^T = K Q^T for this block.
+        f32x16 s = f32x16{};
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        for (int c = 0; c < kKRegs; ++c) {
+            if constexpr (kBf16) s = mfma32_bf16(kn[c], qf[c], s);
+            else s = mfma32_f32(kn[c], qf[c], s);
+        }
+
+        // Keep only keys inside this query's window.  Register i holds slot
+        // 8(i/4) + 4*half + i%4; its box row is kb*rpb + slot/SR.
+        int ry[2];
+        bool rv[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int r = kb * rpb + rr;
+            rv[rr] = r < rows && rr < rpb;
+            ry[rr] = uy0 + imin(r, rows - 1) % ny;
+        }
+        const bool y_in0 = rv[0] && ry[0] >= qy0 && ry[0] < qy0 + g.lh;
+        const bool y_in1 = rv[1] && ry[1] >= qy0 && ry[1] < qy0 + g.lh;
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int sl = 8 * (i / 4) + 4 * half + (i % 4);
+            const int xo = sl % SR;
+            const bool y_in = (sl / SR == 0) ? y_in0 : y_in1;
+            const int xx = ux0 + xo;
+            const bool ok = y_in && xo < nx && xx >= qx0 && xx < qx0 + g.lw;
+            const float xv = ok ? s[i] * scale_log2 : -__builtin_inff();
+            s[i] = xv;
+            mx = fmaxf(mx, xv);
+        }
+        mx = half_pair_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        // A block may hold none of this query's keys yet: keep exp2 finite.
+        const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_run = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+
+        __syncthreads();  // V slab of this block visible to the whole wave
+        if constexpr (kBf16) {
             bf16x8 pf[2];
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
@@ -150,10 +224,6 @@ __global__ __launch_bounds__(64) void local_kernel(const T *__restrict__ q, cons
                 }
                 pf[c] = __builtin_bit_cast(bf16x8, w);
             }
-            __syncthreads();  // V slab visible to the whole wave
-            const int gq = lane >> 4, j16 = lane & 15;
-            const int v_key_off = 4 * half + (j16 >> 2);
-            const int v_col_off = 16 * (gq & 1) + 4 * (j16 & 3);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -164,57 +234,12 @@ __global__ __launch_bounds__(64) void local_kernel(const T *__restrict__ q, cons
                     oacc[db] = mfma32_bf16(concat8(lo, hi), pf[c], oacc[db]);
                 }
             }
-            __syncthreads();  // slab free for the next block
-        }
-    } else {
-        float qf[D / 2];
-        const float *qp = (const float *)q + ((size_t)b * N + tok) * tok_stride + (size_t)h * D + half;
-#pragma unroll
-        for (int c = 0; c < D / 2; ++c) qf[c] = is_local ? qp[2 * c] : 0.0f;
-
-        for (int kb = 0; kb < n_blocks; ++kb) {
-            constexpr int kChunks = D / 4;
-#pragma unroll
-            for (int it = 0; it < 32 * kChunks / 64; ++it) {
-                const int e = lane + 64 * it, s = e / kChunks, ch = e % kChunks;
-                const int j = local_slot_token(s, kb, SR, rows, ny, nx, t0, uy0, ux0, g);
-                u32x4 val = u32x4{0, 0, 0, 0};
-                if (j >= 0) val = *(const u32x4 *)((const float *)vb_ + (size_t)j * tok_stride + 4 * ch);
-                *(u32x4 *)((float *)Vs + s * kPitchV + 4 * ch) = val;
-            }
-            const int jk = local_slot_token(col, kb, SR, rows, ny, nx, t0, uy0, ux0, g);
-            f32x16 s = f32x16{};
-            {
-                const float *kp = (const float *)kb_ + (size_t)(jk < 0 ? 0 : jk) * tok_stride + half;
-#pragma unroll
-                for (int c = 0; c < D / 2; ++c) s = mfma32_f32(jk >= 0 ? kp[2 * c] : 0.0f, qf[c], s);
-            }
-            float mx = -__builtin_inff();
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int slot = 8 * (i / 4) + 4 * half + (i % 4);
-                const int r = kb * (32 / SR) + slot / SR, xo = slot % SR;
-                const int yy = uy0 + r % ny, xx = ux0 + xo;
-                const bool ok = r < rows && xo < nx && yy >= qy0 && yy < qy0 + g.lh && xx >= qx0 &&
-                                xx < qx0 + g.lw;
-                const float xv = ok ? s[i] * scale_log2 : -__builtin_inff();
-                s[i] = xv;
-                mx = fmaxf(mx, xv);
-            }
-            mx = half_pair_max(mx);
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            m_run = m_new;
-            l_part *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 s[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
                 l_part += s[i];
             }
-            __syncthreads();
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -223,8 +248,8 @@ __global__ __launch_bounds__(64) void local_kernel(const T *__restrict__ q, cons
                     oacc[db] = mfma32_f32(a, s[i], oacc[db]);
                 }
             }
-            __syncthreads();
         }
+        __syncthreads();  // slab free for the next block
     }
 
     if (!is_local) return;
@@ -261,26 +286,27 @@ hipError_t launch_local(const AttnArgs &a, hipStream_t stream) {
     const int nx_max = kLocalQX + g.lw - 1;
     g.slot_row = nx_max <= 16 ? 16 : 32;
     if (nx_max > 32) return hipErrorInvalidValue;  // rejected earlier by the ABI layer
-    const dim3 grid(g.T * g.tiles_y * g.tiles_x, a.heads, a.batch);
+    const int units = a.batch * a.heads * g.T * g.tiles_y * g.tiles_x;
+    const dim3 grid((units + 7) / 8 * 8);
     const float sl2 = a.scale * kLog2e;
     if (a.bf16) {
         auto q = (const __bf16 *)a.q, k = (const __bf16 *)a.k, v = (const __bf16 *)a.v;
         auto o = (__bf16 *)a.o;
         if (a.head_dim == 128)
             hipLaunchKernelGGL((local_kernel<__bf16, 128>), grid, dim3(64), 0, stream, q, k, v, o, a.mask,
-                               a.n, a.heads, sl2, g);
+                               a.n, a.heads, sl2, g, units);
         else
             hipLaunchKernelGGL((local_kernel<__bf16, 64>), grid, dim3(64), 0, stream, q, k, v, o, a.mask,
-                               a.n, a.heads, sl2, g);
+                               a.n, a.heads, sl2, g, units);
     } else {
         auto q = (const float *)a.q, k = (const float *)a.k, v = (const float *)a.v;
         auto o = (float *)a.o;
         if (a.head_dim == 128)
             hipLaunchKernelGGL((local_kernel<float, 128>), grid, dim3(64), 0, stream, q, k, v, o, a.mask,
-                               a.n, a.heads, sl2, g);
+                               a.n, a.heads, sl2, g, units);
         else
             hipLaunchKernelGGL((local_kernel<float, 64>), grid, dim3(64), 0, stream, q, k, v, o, a.mask,
-                               a.n, a.heads, sl2, g);
+                               a.n, a.heads, sl2, g, units);
     }
     return hipGetLastError();
 }
