@@ -30,6 +30,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Lazy rescaling of the online softmax: the running reference max only moves
+// when a tile's max exceeds it by more than kRescaleSlack (log2 units).
+// Probabilities are then at most 2^kRescaleSlack, which bf16 and fp32 hold
+// with the same relative precision as values <= 1, and O / l is unchanged
+// because both are taken against the same reference.
+constexpr float kRescaleSlack = 8.0f;
+
 __device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -36,11 +36,6 @@ struct DenseTile {
 };
 
 // ---------------------------------------------------------------- bf16 ----
-// Lazy rescaling: the running reference max m_ref only moves when a tile's
-// max exceeds it by more than kRescaleSlack (log2 units).  Probabilities are
-// then at most 2^kRescaleSlack, which bf16 and fp32 hold exactly as well as
-// values <= 1, and O / l is unchanged because both use the same reference.
-constexpr float kRescaleSlack = 8.0f;
 
 template <int D>
 __global__ __launch_bounds__(kDenseThreads, 2) void dense_bf16_kernel(
@@ -154,7 +149,7 @@ __global__ __launch_bounds__(kDenseThreads, 2) void dense_bf16_kernel(
         const bool grow = mx > m_ref + kRescaleSlack;
         if (__any(grow)) {
             const float m_new = grow ? mx : m_ref;
-            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
             m_ref = m_new;
             l_part *= alpha;
 #pragma unroll

@@ -39,12 +39,12 @@ struct LocalGeom {
     int slot_row;      // SR: 16 or 32 column slots per box row
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                      const T *__restrict__ v, T *__restrict__ o,
-                                                      const uint8_t *__restrict__ mask, int N, int H,
-                                                      float scale_log2, LocalGeom g, int n_units) {
+template <typename T, int D, int SR>
+__global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
+    const uint8_t *__restrict__ mask, int N, int H, float scale_log2, LocalGeom g, int n_units) {
     constexpr bool kBf16 = sizeof(T) == 2;
+    constexpr int rpb = 32 / SR;                  // box rows per key block
     constexpr int kVec = 16 / sizeof(T);          // elements per 16-byte load
     constexpr int kChunks = D / kVec;             // 16-byte chunks per row
     constexpr int kStage = 32 * kChunks / 64;     // V chunks staged per lane per block
@@ -80,7 +80,6 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(const
     const int ux0 = window_start(xbase, g.ww, g.lw, g.Wg);
     const int ny = window_start(ylast, g.wh, g.lh, g.Hg) + g.lh - uy0;
     const int nx = window_start(xlast, g.ww, g.lw, g.Wg) + g.lw - ux0;
-    const int SR = g.slot_row, rpb = 32 / SR;
     const int rows = g.lt * ny;
     const int n_blocks = (rows + rpb - 1) / rpb;
 
@@ -88,17 +87,12 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(const
     const T *kbase = k + (size_t)b * N * tok_stride + (size_t)h * D;
     const T *vbase = v + (size_t)b * N * tok_stride + (size_t)h * D;
 
-    // Box row r -> token of its first column (rows past the box clamp to the last row).
+    // Box row r -> token of its first column (rows past the box clamp to the
+    // last row).  r is the same for the whole wave, so this runs on the SALU.
     auto row_token = [&](int r) -> int {
         r = imin(r, rows - 1);
         const int tt = t0 + r / ny, yy = uy0 + r % ny;
         return (tt * g.Hg + yy) * g.Wg + ux0;
-    };
-    // Slot s of block kb -> token (clamped into the box) and whether it is a real key.
-    auto slot = [&](int kb, int s, int &tokj) -> bool {
-        const int r = kb * rpb + s / SR, xo = s % SR;
-        tokj = row_token(r) + imin(xo, nx - 1);
-        return r < rows && xo < nx;
     };
 
     f32x16 oacc[D / 32];
@@ -113,9 +107,12 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(const
     KFrag kf[kKRegs], kn[kKRegs];
     u32x4 vst[kStage];
     bool vok[kStage];
+    // Slot s = rr*SR + xo of a block lies in box row rr of the block; slots
+    // past the row (xo >= nx) or past the box load a clamped in-box address.
     auto fetch = [&](int kb, KFrag *kdst) {
-        int jk;
-        slot(kb, col, jk);
+        const int rt0 = row_token(kb * rpb), rt1 = row_token(kb * rpb + 1);
+        const bool ok0 = kb * rpb < rows, ok1 = rpb > 1 && kb * rpb + 1 < rows;
+        const int jk = ((col / SR) ? rt1 : rt0) + imin(col % SR, nx - 1);
         const T *kp = kbase + (size_t)jk * tok_stride;
         if constexpr (kBf16) {
 #pragma unroll
@@ -124,12 +121,16 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(const
 #pragma unroll
             for (int c = 0; c < kKRegs; ++c) kdst[c] = ((const float *)kp)[2 * c + half];
         }
+        // Lane stages slot (P*it + lane/kChunks), chunk lane%kChunks, P = 64/kChunks;
+        // P*it % SR + P - 1 < SR, so the slot's row (P*it)/SR is known per it.
+        constexpr int P = 64 / kChunks;
 #pragma unroll
         for (int it = 0; it < kStage; ++it) {
-            const int e = lane + 64 * it, s = e / kChunks, ch = e % kChunks;
-            int jv;
-            vok[it] = slot(kb, s, jv);
-            vst[it] = *(const u32x4 *)(vbase + (size_t)jv * tok_stride + kVec * ch);
+            const int rr = (P * it) / SR;
+            const int xo = (P * it) % SR + lane / kChunks;
+            const int jv = (rr ? rt1 : rt0) + imin(xo, nx - 1);
+            vok[it] = (rr ? ok1 : ok0) && xo < nx;
+            vst[it] = *(const u32x4 *)(vbase + (size_t)jv * tok_stride + kVec * (lane % kChunks));
         }
     };
     auto stage_v = [&]() {
@@ -176,38 +177,40 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(const
         }
 
         // Keep only keys inside this query's window.  Register i holds slot
-        // 8(i/4) + 4*half + i%4; its box row is kb*rpb + slot/SR.
-        int ry[2];
-        bool rv[2];
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int r = kb * rpb + rr;
-            rv[rr] = r < rows && rr < rpb;
-            ry[rr] = uy0 + imin(r, rows - 1) % ny;
-        }
-        const bool y_in0 = rv[0] && ry[0] >= qy0 && ry[0] < qy0 + g.lh;
-        const bool y_in1 = rv[1] && ry[1] >= qy0 && ry[1] < qy0 + g.lh;
+        // 8(i/4) + 4*half + i%4 of the block: box row (i/4 >= 2 && SR == 16),
+        // column 8*((i/4) % (SR/8)) + 4*half + i%4.
+        const int r0 = kb * rpb;
+        const int yy0 = uy0 + imin(r0, rows - 1) % ny, yy1 = uy0 + imin(r0 + 1, rows - 1) % ny;
+        const bool y_in0 = r0 < rows && yy0 >= qy0 && yy0 < qy0 + g.lh;
+        const bool y_in1 = rpb > 1 && r0 + 1 < rows && yy1 >= qy0 && yy1 < qy0 + g.lh;
+        // Columns of the query's window relative to the box, intersected with the box.
+        const int xlo = qx0 - ux0, xhi = imin(qx0 - ux0 + g.lw, nx);
         float mx = -__builtin_inff();
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int sl = 8 * (i / 4) + 4 * half + (i % 4);
-            const int xo = sl % SR;
-            const bool y_in = (sl / SR == 0) ? y_in0 : y_in1;
-            const int xx = ux0 + xo;
-            const bool ok = y_in && xo < nx && xx >= qx0 && xx < qx0 + g.lw;
-            const float xv = ok ? s[i] * scale_log2 : -__builtin_inff();
+            const int xo = 8 * ((i / 4) % (SR / 8)) + 4 * half + (i % 4);
+            const bool y_in = (SR == 16 && i >= 8) ? y_in1 : y_in0;
+            const bool ok = y_in && xo >= xlo && xo < xhi;
+            const float xv = ok ? s[i] : -__builtin_inff();
             s[i] = xv;
             mx = fmaxf(mx, xv);
         }
-        mx = half_pair_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        // A block may hold none of this query's keys yet: keep exp2 finite.
-        const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        l_part *= alpha;
+        // Online softmax in base 2 with a lazily moved reference max (see the
+        // dense kernel): the reference moves only when a block's max exceeds
+        // it by more than kRescaleSlack.  A block may hold none of this
+        // query's keys (mx = -inf); the reference then stays put.
+        mx = half_pair_max(mx) * scale_log2;
+        const bool grow = mx > m_run + kRescaleSlack;
+        if (__any(grow)) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            m_run = m_new;
+            l_part *= alpha;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        }
+        const float m_use = (m_run == -__builtin_inff()) ? 0.0f : m_run;
+        const float neg_m = -m_use;
 
         __syncthreads();  // V slab of this block visible to the whole wave
         if constexpr (kBf16) {
@@ -217,8 +220,8 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(const
                 u32x4 w;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const float p0 = __builtin_amdgcn_exp2f(s[8 * c + 2 * jj] - m_use);
-                    const float p1 = __builtin_amdgcn_exp2f(s[8 * c + 2 * jj + 1] - m_use);
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + 2 * jj], scale_log2, neg_m));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + 2 * jj + 1], scale_log2, neg_m));
                     l_part += p0 + p1;
                     w[jj] = pack_bf16x2(p0, p1);
                 }
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(const
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                s[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
+                s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, neg_m));
                 l_part += s[i];
             }
 #pragma unroll
@@ -289,25 +292,24 @@ hipError_t launch_local(const AttnArgs &a, hipStream_t stream) {
     const int units = a.batch * a.heads * g.T * g.tiles_y * g.tiles_x;
     const dim3 grid((units + 7) / 8 * 8);
     const float sl2 = a.scale * kLog2e;
+#define HET_LOCAL_LAUNCH(T_, D_, SR_)                                                             \
+    hipLaunchKernelGGL((local_kernel<T_, D_, SR_>), grid, dim3(64), 0, stream, (const T_ *)a.q,   \
+                       (const T_ *)a.k, (const T_ *)a.v, (T_ *)a.o, a.mask, a.n, a.heads, sl2, g, units)
+    const bool sr16 = g.slot_row == 16;
     if (a.bf16) {
-        auto q = (const __bf16 *)a.q, k = (const __bf16 *)a.k, v = (const __bf16 *)a.v;
-        auto o = (__bf16 *)a.o;
-        if (a.head_dim == 128)
-            hipLaunchKernelGGL((local_kernel<__bf16, 128>), grid, dim3(64), 0, stream, q, k, v, o, a.mask,
-                               a.n, a.heads, sl2, g, units);
-        else
-            hipLaunchKernelGGL((local_kernel<__bf16, 64>), grid, dim3(64), 0, stream, q, k, v, o, a.mask,
-                               a.n, a.heads, sl2, g, units);
+        if (a.head_dim == 128) {
+            if (sr16) HET_LOCAL_LAUNCH(__bf16, 128, 16); else HET_LOCAL_LAUNCH(__bf16, 128, 32);
+        } else {
+            if (sr16) HET_LOCAL_LAUNCH(__bf16, 64, 16); else HET_LOCAL_LAUNCH(__bf16, 64, 32);
+        }
     } else {
-        auto q = (const float *)a.q, k = (const float *)a.k, v = (const float *)a.v;
-        auto o = (float *)a.o;
-        if (a.head_dim == 128)
-            hipLaunchKernelGGL((local_kernel<float, 128>), grid, dim3(64), 0, stream, q, k, v, o, a.mask,
-                               a.n, a.heads, sl2, g, units);
-        else
-            hipLaunchKernelGGL((local_kernel<float, 64>), grid, dim3(64), 0, stream, q, k, v, o, a.mask,
-                               a.n, a.heads, sl2, g, units);
+        if (a.head_dim == 128) {
+            if (sr16) HET_LOCAL_LAUNCH(float, 128, 16); else HET_LOCAL_LAUNCH(float, 128, 32);
+        } else {
+            if (sr16) HET_LOCAL_LAUNCH(float, 64, 16); else HET_LOCAL_LAUNCH(float, 64, 32);
+        }
     }
+#undef HET_LOCAL_LAUNCH
     return hipGetLastError();
 }
 
