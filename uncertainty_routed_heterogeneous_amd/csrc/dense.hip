@@ -36,6 +36,39 @@ struct DenseTile {
 };
 
 // ---------------------------------------------------------------- bf16 ----
+// K and V tiles move global -> LDS by DMA (global_load_lds_dwordx4: each wave
+// writes one contiguous 1 KB run, lane l at byte 16*l), double-buffered in
+// four separate LDS arrays so that reads of one buffer never wait on DMA into
+// another.  Rows are unpadded; the 16-byte chunk c of key row r is stored at
+// chunk c ^ swz<D>(r).  The LDS has 64 banks of 4 bytes (256 B per cycle):
+// a 16-lane ds_read_b128 of 16 consecutive rows at one chunk (K, A operand)
+// and a 32-lane transposed read of 4 consecutive rows x 4 consecutive chunks
+// (V) then both touch every bank exactly once.
+//
+// Per iteration kt (one barrier):
+//   wait for own DMA, barrier      K(kt+1), V(kt) now in LDS; previous reads done
+//   DMA K(kt+2), V(kt+1)           into the buffers freed by the barrier
+//   S(kt+1) = K(kt+1) Q^T          MFMA, overlaps the softmax of S(kt) below
+//   P = softmax(S(kt)), O^T += V(kt)^T P^T
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);  // 16 chunks per row
+    else return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);              // 8 chunks, 2 rows per 256 B
+}
+
+template <int D>
+struct DenseBf16Geom {
+    static constexpr int BN = 64;                  // keys per tile
+    static constexpr int kCpr = D / 8;             // 16-byte chunks per row
+    static constexpr int kRowsPerLoad = 64 / kCpr; // rows per wave DMA (1 KB)
+    static constexpr int kLoadsPerWave = BN / kRowsPerLoad / 4;
+    static constexpr int kTileElems = BN * D;
+};
+
+template <int D>
+__device__ __forceinline__ const HET_LDS void *lds_chunk(const __bf16 *buf, int row, int chunk) {
+    return (const HET_LDS void *)(buf + row * D + 8 * (chunk ^ swz<D>(row)));
+}
 
 template <int D>
 __global__ __launch_bounds__(kDenseThreads, 2) void dense_bf16_kernel(
@@ -43,10 +76,12 @@ __global__ __launch_bounds__(kDenseThreads, 2) void dense_bf16_kernel(
     __bf16 *__restrict__ o, const int32_t *__restrict__ dense_idx,
     const int32_t *__restrict__ counts, int N, int H, float scale_log2, int tiles_per_bh,
     int n_units) {
-    constexpr int BN = 64;
-    using Tl = DenseTile<__bf16, D, BN>;
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[BN * Tl::kPitchK];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[BN * Tl::kPitchV];
+    using G = DenseBf16Geom<D>;
+    constexpr int BN = G::BN;
+    __shared__ __attribute__((aligned(1024))) __bf16 K0[G::kTileElems];
+    __shared__ __attribute__((aligned(1024))) __bf16 K1[G::kTileElems];
+    __shared__ __attribute__((aligned(1024))) __bf16 V0[G::kTileElems];
+    __shared__ __attribute__((aligned(1024))) __bf16 V1[G::kTileElems];
 
     const int unit = xcd_remap(blockIdx.x, gridDim.x);
     if (unit >= n_units) return;
@@ -57,7 +92,7 @@ __global__ __launch_bounds__(kDenseThreads, 2) void dense_bf16_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
-    const size_t tok_stride = (size_t)H * D;
+    const int tok_stride = H * D;
     const __bf16 *kb = k + (size_t)b * N * tok_stride + (size_t)h * D;
     const __bf16 *vb = v + (size_t)b * N * tok_stride + (size_t)h * D;
 
@@ -69,33 +104,42 @@ __global__ __launch_bounds__(kDenseThreads, 2) void dense_bf16_kernel(
     {
         const __bf16 *qp = q + ((size_t)b * N + tok) * tok_stride + (size_t)h * D + 8 * half;
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-            qf[c] = q_valid ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
-        }
+        for (int c = 0; c < D / 16; ++c) qf[c] = q_valid ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
     }
 
-    // Register staging of one K/V tile.
-    u32x4 kreg[Tl::kPasses], vreg[Tl::kPasses];
-    const int ld_row = tid / Tl::kChunksPerRow, ld_chunk = tid % Tl::kChunksPerRow;
-    auto fetch = [&](int kt) {
+    // DMA geometry: load j of this wave fills tile rows r0_j .. r0_j + kRowsPerLoad.
+    int dma_row[G::kLoadsPerWave], dma_off[G::kLoadsPerWave];
 #pragma unroll
-        for (int p = 0; p < Tl::kPasses; ++p) {
-            const int key = kt * BN + p * Tl::kRowsPerPass + ld_row;
-            if (key < N) {
-                kreg[p] = *(const u32x4 *)(kb + (size_t)key * tok_stride + ld_chunk * Tl::kVec);
-                vreg[p] = *(const u32x4 *)(vb + (size_t)key * tok_stride + ld_chunk * Tl::kVec);
-            } else {
-                kreg[p] = u32x4{0, 0, 0, 0};
-                vreg[p] = u32x4{0, 0, 0, 0};
-            }
+    for (int j = 0; j < G::kLoadsPerWave; ++j) {
+        const int r0 = (wave * G::kLoadsPerWave + j) * G::kRowsPerLoad;
+        const int r = r0 + lane / G::kCpr, p = lane % G::kCpr;
+        dma_row[j] = r;
+        dma_off[j] = 8 * (p ^ swz<D>(r));
+    }
+    const int n_tiles = (N + BN - 1) / BN;
+    auto dma = [&](const __bf16 *src, __bf16 *dst, int kt) {
+        const int key0 = kt * BN;
+        const bool ragged = key0 + BN > N;
+#pragma unroll
+        for (int j = 0; j < G::kLoadsPerWave; ++j) {
+            const int key = ragged ? imin(key0 + dma_row[j], N - 1) : key0 + dma_row[j];
+            const __bf16 *gp = src + (size_t)key * tok_stride + dma_off[j];
+            __bf16 *lp = dst + (wave * G::kLoadsPerWave + j) * G::kRowsPerLoad * D;
+            __builtin_amdgcn_global_load_lds((const void *)gp, (HET_LDS void *)lp, 16, 0, 0);
         }
     };
-    auto stash = [&]() {
+
+    // S^T = K Q^T for the two 32-key blocks of a tile (raw scores).
+    auto qk = [&](const __bf16 *Kt, f32x16 (&s)[2]) {
 #pragma unroll
-        for (int p = 0; p < Tl::kPasses; ++p) {
-            const int r = p * Tl::kRowsPerPass + ld_row;
-            *(u32x4 *)(Ks + r * Tl::kPitchK + ld_chunk * Tl::kVec) = kreg[p];
-            *(u32x4 *)(Vs + r * Tl::kPitchV + ld_chunk * Tl::kVec) = vreg[p];
+        for (int blk = 0; blk < 2; ++blk) {
+            s[blk] = f32x16{};
+            const int row = blk * 32 + col;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                const bf16x8 a = *(const HET_LDS bf16x8 *)lds_chunk<D>(Kt, row, 2 * c + half);
+                s[blk] = mfma32_bf16(a, qf[c], s[blk]);
+            }
         }
     };
 
@@ -105,31 +149,17 @@ __global__ __launch_bounds__(kDenseThreads, 2) void dense_bf16_kernel(
     float m_ref = -__builtin_inff();  // reference max, log2 units
     float l_part = 0.0f;
 
-    // Transposed-read coordinates of V (see the O^T update below).
+    // Transposed V read: lane j16 of each 16-lane group points at tile row
+    // (base + 4*half + j16/4), element column 16*(g16&1) + 4*(j16&3) of a
+    // 32-column slab, i.e. chunk 2*(g16&1) + (j16&3)/2, byte 8*(j16&1).
     const int g16 = lane >> 4, j16 = lane & 15;
-    const int v_key_off = 4 * half + (j16 >> 2);
-    const int v_col_off = 16 * (g16 & 1) + 4 * (j16 & 3);
+    const int v_row_off = 4 * half + (j16 >> 2);
+    const int v_chunk_off = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+    const int v_elem_off = 4 * (j16 & 1);
 
-    const int n_tiles = (N + BN - 1) / BN;
-    fetch(0);
-    stash();
-    __syncthreads();
-    for (int kt = 0; kt < n_tiles; ++kt) {
-        if (kt + 1 < n_tiles) fetch(kt + 1);
-
-        // ---- S^T = K Q^T for two 32-key blocks (raw scores)
-        f32x16 s[2];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            s[blk] = f32x16{};
-            const __bf16 *krow = Ks + (blk * 32 + col) * Tl::kPitchK + 8 * half;
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 a = *(const bf16x8 *)(krow + 16 * c);
-                s[blk] = mfma32_bf16(a, qf[c], s[blk]);
-            }
-        }
-        if (kt == n_tiles - 1 && (kt + 1) * BN > N) {
+    // softmax(S(kt)) and O^T += V(kt)^T P^T.
+    auto softmax_pv = [&](f32x16 (&s)[2], const __bf16 *Vt, int kt) {
+        if (kt == n_tiles - 1 && kt * BN + BN > N) {
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -138,8 +168,6 @@ __global__ __launch_bounds__(kDenseThreads, 2) void dense_bf16_kernel(
                     if (key >= N) s[blk][i] = -__builtin_inff();
                 }
         }
-
-        // ---- online softmax (base 2, lazy rescale)
         float mx = -__builtin_inff();
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
@@ -156,12 +184,11 @@ __global__ __launch_bounds__(kDenseThreads, 2) void dense_bf16_kernel(
             for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
         }
         const float neg_m = -m_ref;
-
-        // P as the B operand of O^T += V^T P^T: chunk c of block blk = registers 8c..8c+7,
+        // P as the B operand: chunk c of block blk = registers 8c..8c+7,
         // i.e. keys 16c + 8(j/4) + 4*half + j%4 (j < 8) of the block.
         bf16x8 pf[2][2];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 u32x4 w;
@@ -174,30 +201,45 @@ __global__ __launch_bounds__(kDenseThreads, 2) void dense_bf16_kernel(
                 }
                 pf[blk][c] = __builtin_bit_cast(bf16x8, w);
             }
-        }
-
-        // ---- O^T += V^T P^T.  A operand rows = d, k = the 8 keys above; read
-        // transposed from the row-major V tile: lane j of each 16-lane group
-        // points at key (base + j/4), columns 4*(j%4) .. +3 of its 16-column slab.
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
+            for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    const __bf16 *base = Vs + (blk * 32 + 16 * c + v_key_off) * Tl::kPitchV + db * 32 + v_col_off;
-                    const bf16x4 lo = lds_read_tr16((const HET_LDS void *)base);
-                    const bf16x4 hi = lds_read_tr16((const HET_LDS void *)(base + 8 * Tl::kPitchV));
+                    const int row = blk * 32 + 16 * c + v_row_off;
+                    const int chunk = 4 * db + v_chunk_off;
+                    const bf16x4 lo = lds_read_tr16((const HET_LDS void *)(Vt + row * D + 8 * (chunk ^ swz<D>(row)) + v_elem_off));
+                    const bf16x4 hi = lds_read_tr16((const HET_LDS void *)(Vt + (row + 8) * D + 8 * (chunk ^ swz<D>(row + 8)) + v_elem_off));
                     oacc[db] = mfma32_bf16(concat8(lo, hi), pf[blk][c], oacc[db]);
                 }
-            }
-        }
+    };
 
-        __syncthreads();
+    // Prologue: K(0), V(0), K(1) in flight; S(0) from K(0).
+    dma(kb, K0, 0);
+    dma(vb, V0, 0);
+    if (n_tiles > 1) dma(kb, K1, 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    f32x16 s_cur[2], s_nxt[2];
+    qk(K0, s_cur);
+
+    // One step: Kc holds K(kt+1), Kn receives K(kt+2), Vc holds V(kt), Vn receives V(kt+1).
+    auto step = [&](int kt, const __bf16 *Kc, __bf16 *Kn, const __bf16 *Vc, __bf16 *Vn) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        if (kt + 2 < n_tiles) dma(kb, Kn, kt + 2);
         if (kt + 1 < n_tiles) {
-            stash();
-            __syncthreads();
+            dma(vb, Vn, kt + 1);
+            qk(Kc, s_nxt);
         }
+        softmax_pv(s_cur, Vc, kt);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) s_cur[blk] = s_nxt[blk];
+    };
+    for (int kt = 0; kt < n_tiles; kt += 2) {
+        step(kt, K1, K0, V0, V1);
+        if (kt + 1 < n_tiles) step(kt + 1, K0, K1, V1, V0);
     }
 
     if (!q_valid) return;
