@@ -83,10 +83,19 @@ def test_unit_values_give_unit_output():
     assert np.abs(got - 1.0).max() <= 1e-2
 
 
-def test_single_token(oracle_mod):
-    w, q, k, v, u = small_case((1, 1, 1), 1, 64, "f32", batch=1, seed=11, window=(3, 3, 3))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_token(oracle_mod, dtype):
+    w, q, k, v, u = small_case((1, 1, 1), 1, 64, dtype, batch=1, seed=11, window=(3, 3, 3))
     for rho in (0.0, 1.0):
         full_parity(oracle_mod, w, q, k, v, u, rho=rho, what="N=1")
+
+
+@pytest.mark.parametrize("rho", [1.0 / 1200, 0.01, 0.11])
+def test_few_dense_tokens(oracle_mod, rho):
+    """Less dense work than persistent workgroups, and tiles split across
+    workgroups (the dense kernel's split-and-merge path)."""
+    w, q, k, v, u = small_case((6, 10, 20), 3, 128, "bf16", seed=15)
+    full_parity(oracle_mod, w, q, k, v, u, rho=rho, what=f"few dense rho={rho:.4f}")
 
 
 def test_mean_std_route_forward(oracle_mod):

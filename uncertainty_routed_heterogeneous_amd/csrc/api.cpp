@@ -40,6 +40,14 @@ het_status check_shape(const het_attn_shape *s, Dims &d, float &scale) {
     return HET_OK;
 }
 
+// Compute units of the current device (0 if it cannot be queried).
+int current_cu_count() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return cus;
+}
+
 }  // namespace
 
 extern "C" {
@@ -61,7 +69,9 @@ size_t het_attn_workspace_bytes(const het_attn_shape *shape) {
     Dims d;
     float scale;
     if (check_shape(shape, d, scale) != HET_OK) return 0;
-    return 0;
+    const int cus = current_cu_count();
+    if (cus <= 0) return 0;
+    return hetattn::dense_workspace_bytes((int)d.B, (int)d.H, (int)d.N, (int)d.D, shape->dtype == HET_BF16, cus);
 }
 
 int het_attn_route(const het_attn_shape *shape, const float *u, int mode, double param,
@@ -118,9 +128,12 @@ int run_attention(const het_attn_shape *shape, const void *q, const void *k, con
     if (!q || !k || !v || !o || !route || !route->mask || !route->dense_idx || !route->counts)
         return HET_ERR_INVALID_ARG;
     if (route->dense_count_host < -1 || route->dense_count_host > d.N) return HET_ERR_INVALID_ARG;
-    const size_t need = het_attn_workspace_bytes(shape);
-    if (workspace_bytes < need) return HET_ERR_WORKSPACE;
+    const int cus = current_cu_count();
+    if (cus <= 0) return HET_ERR_HIP;
+    const size_t need = hetattn::dense_workspace_bytes((int)d.B, (int)d.H, (int)d.N, (int)d.D,
+                                                       shape->dtype == HET_BF16, cus);
     if (need > 0 && !workspace) return HET_ERR_INVALID_ARG;
+    if (workspace_bytes < need) return HET_ERR_WORKSPACE;
 
     AttnArgs a;
     a.q = q;
@@ -143,6 +156,8 @@ int run_attention(const het_attn_shape *shape, const void *q, const void *k, con
     a.bf16 = shape->dtype == HET_BF16;
     a.scale = scale;
     a.max_dense = route->dense_count_host >= 0 ? route->dense_count_host : (int)d.N;
+    a.workspace = workspace;
+    a.cu_count = cus;
 
     hipStream_t s = (hipStream_t)stream;
     // The two kernels write disjoint rows of o (Eq. 13 with m in {0, 1}).

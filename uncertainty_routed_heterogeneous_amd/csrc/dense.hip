@@ -5,35 +5,29 @@
 // with m_i = 0 (§3.2.2 Eqs. 12-13).  This is the rho*N^2*d_h term of the cost
 // model (§3.2.2 Eq. 14) and the dominant cost of the layer.
 //
-// One workgroup = 4 waves = 128 gathered queries of one (sample, head); each
-// wave owns 32 queries.  Per key tile of BN keys:
-//   S^T = K Q^T      MFMA, A = K tile (LDS), B = Q (registers, loaded once)
+// bf16 path.  One workgroup = 4 waves = 256 gathered queries of one (sample,
+// head); each wave owns 64 queries as two 32-query column blocks, so every K
+// or V fragment read from LDS feeds two MFMAs.  Per 64-key tile:
+//   S^T = K Q^T      MFMA 32x32x16, A = K tile (LDS), B = Q (registers)
 //   online softmax   fp32, base 2, per query = per lane (lane l%32)
 //   O^T += V^T P^T   MFMA, A = V tile read transposed from LDS, B = P
 // Computing the transposed products keeps every per-query quantity (running
 // max, row sum, output column) in the lane that owns the query, so the
 // softmax needs one cross-half exchange per tile and no LDS round trip.
-// K/V tiles for step j+1 are fetched into registers while step j computes.
+//
+// One wave per SIMD (512 registers).  Within a wave the work of tile kt is
+// overlapped with tile kt+1: the MFMAs of S(kt+1) = K(kt+1) Q^T are issued
+// between the exp/sum/convert instructions of softmax(S(kt)), and the P*V
+// MFMAs of tile kt between the row-max instructions of S(kt+1).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace hetattn {
 
 constexpr int kDenseThreads = 256;
-constexpr int kDenseBM = 128;
-
-template <typename T, int D, int BN>
-struct DenseTile {
-    static constexpr int kPadK = (sizeof(T) == 2) ? 8 : 4;
-    static constexpr int kPadV = (sizeof(T) == 2) ? 16 : 4;
-    static constexpr int kPitchK = D + kPadK;     // elements
-    static constexpr int kPitchV = D + kPadV;
-    static constexpr int kVec = 16 / sizeof(T);   // elements per 16-byte load
-    static constexpr int kChunksPerRow = D / kVec;
-    static constexpr int kRowsPerPass = kDenseThreads / kChunksPerRow;
-    static constexpr int kPasses = BN / kRowsPerPass;
-    static_assert(kPasses * kRowsPerPass == BN, "tile load shape");
-};
+constexpr int kDenseBM = 128;    // f32 path: queries per workgroup
+constexpr int kDenseQB = 1;      // bf16 path: 32-query blocks per wave
+constexpr int kDenseBM16 = 128 * kDenseQB;  // bf16 path: queries per workgroup
 
 // ---------------------------------------------------------------- bf16 ----
 // K and V tiles move global -> LDS by DMA (global_load_lds_dwordx4: each wave
@@ -48,8 +42,8 @@ struct DenseTile {
 // Per iteration kt (one barrier):
 //   wait for own DMA, barrier      K(kt+1), V(kt) now in LDS; previous reads done
 //   DMA K(kt+2), V(kt+1)           into the buffers freed by the barrier
-//   S(kt+1) = K(kt+1) Q^T          MFMA, overlaps the softmax of S(kt) below
-//   P = softmax(S(kt)), O^T += V(kt)^T P^T
+//   S(kt+1) = K(kt+1) Q^T  ||  P(kt) = exp2(S(kt) - m)
+//   O^T += V(kt)^T P^T     ||  row max of S(kt+1)
 template <int D>
 __device__ __forceinline__ int swz(int row) {
     if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);  // 16 chunks per row
@@ -65,198 +59,405 @@ struct DenseBf16Geom {
     static constexpr int kTileElems = BN * D;
 };
 
-template <int D>
-__device__ __forceinline__ const HET_LDS void *lds_chunk(const __bf16 *buf, int row, int chunk) {
-    return (const HET_LDS void *)(buf + row * D + 8 * (chunk ^ swz<D>(row)));
+// ------------------------------------------------------ stream-K schedule --
+// The dense work is the list of units (sample, head, 256-query tile), each a
+// sequence of n_kt key tiles; flattened unit-major it has W = units * n_kt
+// items.  The grid is persistent (one workgroup per CU) and workgroup w takes
+// items [w*W/G, (w+1)*W/G): every CU gets the same amount of work, so there is
+// no partially filled last wave of tiles.  A unit cut between workgroups is
+// finished in pieces: every piece stores its partial state (unnormalised O,
+// reference max m, row sum l, fp32) in the workspace and bumps the unit's
+// counter; the piece that brings the counter to the number of pieces merges
+// them (O = sum 2^(m_s - m) O_s, l = sum 2^(m_s - m) l_s), writes the output
+// and resets the counter.  No workgroup ever waits for another.
+//
+// Workspace: [2G slots][kDenseBM16 queries][D] O partials (each lane's
+// accumulators contiguous, in register order), then [2G][2][kDenseBM16]
+// (m, l), then one int counter per unit (zeroed before the launch).  Slot 2w
+// holds the piece of workgroup w's first unit, slot 2w+1 that of its last.
+__device__ __forceinline__ int64_t work_begin(int64_t W, int G, int w) { return (int64_t)w * W / G; }
+// Workgroup owning item x: the largest w with work_begin(w) <= x.
+__device__ __forceinline__ int work_owner(int64_t W, int G, int64_t x) {
+    int w = (int)(x * G / W);
+    while (w + 1 < G && work_begin(W, G, w + 1) <= x) ++w;
+    return w;
 }
 
 template <int D>
-__global__ __launch_bounds__(kDenseThreads, 2) void dense_bf16_kernel(
+__global__ __launch_bounds__(kDenseThreads, 1) void dense_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const int32_t *__restrict__ dense_idx,
-    const int32_t *__restrict__ counts, int N, int H, float scale_log2, int tiles_per_bh,
-    int n_units) {
-    using G = DenseBf16Geom<D>;
-    constexpr int BN = G::BN;
-    __shared__ __attribute__((aligned(1024))) __bf16 K0[G::kTileElems];
-    __shared__ __attribute__((aligned(1024))) __bf16 K1[G::kTileElems];
-    __shared__ __attribute__((aligned(1024))) __bf16 V0[G::kTileElems];
-    __shared__ __attribute__((aligned(1024))) __bf16 V1[G::kTileElems];
-
-    const int unit = xcd_remap(blockIdx.x, gridDim.x);
-    if (unit >= n_units) return;
-    const int tile = unit % tiles_per_bh, bh = unit / tiles_per_bh;
-    const int h = bh % H, b = bh / H;
-    const int n_dense = counts[2 * b];
-    if (tile * kDenseBM >= n_dense) return;
+    const int32_t *__restrict__ counts, int B, int N, int H, float scale_log2, int G,
+    float *__restrict__ ws_part, int32_t *__restrict__ ws_count) {
+    using Gm = DenseBf16Geom<D>;
+    constexpr int BN = Gm::BN;
+    constexpr int BM = kDenseBM16;
+    constexpr int NC = D / 16;  // k-chunks of QK
+    constexpr int NDB = D / 32; // 32-row blocks of O^T
+    constexpr int QB = kDenseQB;
+    __shared__ __attribute__((aligned(1024))) __bf16 K0[Gm::kTileElems];
+    __shared__ __attribute__((aligned(1024))) __bf16 K1[Gm::kTileElems];
+    __shared__ __attribute__((aligned(1024))) __bf16 V0[Gm::kTileElems];
+    __shared__ __attribute__((aligned(1024))) __bf16 V1[Gm::kTileElems];
+    __shared__ int s_flag;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
     const int tok_stride = H * D;
-    const __bf16 *kb = k + (size_t)b * N * tok_stride + (size_t)h * D;
-    const __bf16 *vb = v + (size_t)b * N * tok_stride + (size_t)h * D;
+    const int n_kt = (N + BN - 1) / BN;
 
-    // Gathered query of this lane (col = query within the wave's 32).
-    const int qrow = tile * kDenseBM + wave * 32 + col;
-    const bool q_valid = qrow < n_dense;
-    const int tok = q_valid ? dense_idx[(size_t)b * N + qrow] : 0;
-    bf16x8 qf[D / 16];
-    {
-        const __bf16 *qp = q + ((size_t)b * N + tok) * tok_stride + (size_t)h * D + 8 * half;
+    // Units per sample come from the device-side dense counts, so the split is
+    // exact in both threshold modes; every workgroup computes the same list.
+    int units = 0;
+    for (int bb = 0; bb < B; ++bb) units += H * ((counts[2 * bb] + BM - 1) / BM);
+    const int64_t W = (int64_t)units * n_kt;
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    if (w >= G || W == 0) return;
+    int64_t x = work_begin(W, G, w);
+    const int64_t x_end = work_begin(W, G, w + 1);
+    if (x >= x_end) return;
+    const int first_unit = (int)(x / n_kt);
+
+    // DMA geometry: load j of this wave fills tile rows from r0_j on; this
+    // lane writes row r0_j + lane/kCpr at chunk position lane%kCpr, so it
+    // fetches the chunk that the swizzle puts there.  Full tiles address as
+    // a wave-uniform row base plus a per-lane 32-bit offset.
+    const int dma_lrow = lane / Gm::kCpr, dma_pos = lane % Gm::kCpr;
+    int dma_lane_off[Gm::kLoadsPerWave];
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) qf[c] = q_valid ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
+    for (int j = 0; j < Gm::kLoadsPerWave; ++j) {
+        const int r = (wave * Gm::kLoadsPerWave + j) * Gm::kRowsPerLoad + dma_lrow;
+        dma_lane_off[j] = dma_lrow * tok_stride + 8 * (dma_pos ^ swz<D>(r));
     }
-
-    // DMA geometry: load j of this wave fills tile rows r0_j .. r0_j + kRowsPerLoad.
-    int dma_row[G::kLoadsPerWave], dma_off[G::kLoadsPerWave];
-#pragma unroll
-    for (int j = 0; j < G::kLoadsPerWave; ++j) {
-        const int r0 = (wave * G::kLoadsPerWave + j) * G::kRowsPerLoad;
-        const int r = r0 + lane / G::kCpr, p = lane % G::kCpr;
-        dma_row[j] = r;
-        dma_off[j] = 8 * (p ^ swz<D>(r));
-    }
-    const int n_tiles = (N + BN - 1) / BN;
-    auto dma = [&](const __bf16 *src, __bf16 *dst, int kt) {
-        const int key0 = kt * BN;
-        const bool ragged = key0 + BN > N;
-#pragma unroll
-        for (int j = 0; j < G::kLoadsPerWave; ++j) {
-            const int key = ragged ? imin(key0 + dma_row[j], N - 1) : key0 + dma_row[j];
-            const __bf16 *gp = src + (size_t)key * tok_stride + dma_off[j];
-            __bf16 *lp = dst + (wave * G::kLoadsPerWave + j) * G::kRowsPerLoad * D;
-            __builtin_amdgcn_global_load_lds((const void *)gp, (HET_LDS void *)lp, 16, 0, 0);
-        }
-    };
-
-    // S^T = K Q^T for the two 32-key blocks of a tile (raw scores).
-    auto qk = [&](const __bf16 *Kt, f32x16 (&s)[2]) {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            s[blk] = f32x16{};
-            const int row = blk * 32 + col;
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 a = *(const HET_LDS bf16x8 *)lds_chunk<D>(Kt, row, 2 * c + half);
-                s[blk] = mfma32_bf16(a, qf[c], s[blk]);
-            }
-        }
-    };
-
-    f32x16 oacc[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-    float m_ref = -__builtin_inff();  // reference max, log2 units
-    float l_part = 0.0f;
-
     // Transposed V read: lane j16 of each 16-lane group points at tile row
-    // (base + 4*half + j16/4), element column 16*(g16&1) + 4*(j16&3) of a
+    // base + 4*half + j16/4, element column 16*(g16&1) + 4*(j16&3) of a
     // 32-column slab, i.e. chunk 2*(g16&1) + (j16&3)/2, byte 8*(j16&1).
     const int g16 = lane >> 4, j16 = lane & 15;
     const int v_row_off = 4 * half + (j16 >> 2);
     const int v_chunk_off = 2 * (g16 & 1) + ((j16 & 3) >> 1);
     const int v_elem_off = 4 * (j16 & 1);
 
-    // softmax(S(kt)) and O^T += V(kt)^T P^T.
-    auto softmax_pv = [&](f32x16 (&s)[2], const __bf16 *Vt, int kt) {
-        if (kt == n_tiles - 1 && kt * BN + BN > N) {
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kt * BN + blk * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-                    if (key >= N) s[blk][i] = -__builtin_inff();
-                }
+    while (x < x_end) {
+        // ---- the unit of item x and the key-tile range of this piece
+        const int unit = (int)(x / n_kt);
+        const int kt0 = (int)(x - (int64_t)unit * n_kt);
+        const int kt1 = (int)((x_end - (int64_t)unit * n_kt) < n_kt ? (x_end - (int64_t)unit * n_kt) : n_kt);
+        x = (int64_t)unit * n_kt + kt1;
+        int b = 0, rem = unit, tiles_b = 0;
+        for (;;) {
+            tiles_b = (counts[2 * b] + BM - 1) / BM;
+            if (rem < H * tiles_b) break;
+            rem -= H * tiles_b;
+            ++b;
         }
-        float mx = -__builtin_inff();
+        const int h = rem / tiles_b, tile = rem % tiles_b;
+        const int n_dense = counts[2 * b];
+        const __bf16 *kb = k + (size_t)b * N * tok_stride + (size_t)h * D;
+        const __bf16 *vb = v + (size_t)b * N * tok_stride + (size_t)h * D;
+
+        // Gathered queries of this lane: query block qb holds query
+        // tile*BM + wave*64 + qb*32 + col.
+        int tok[QB];
+        bool q_valid[QB];
+        bf16x8 qf[QB][NC];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int qb = 0; qb < QB; ++qb) {
+            const int qrow = tile * BM + (wave * QB + qb) * 32 + col;
+            q_valid[qb] = qrow < n_dense;
+            tok[qb] = q_valid[qb] ? dense_idx[(size_t)b * N + qrow] : 0;
+            const __bf16 *qp = q + ((size_t)b * N + tok[qb]) * tok_stride + (size_t)h * D + 8 * half;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[blk][i]);
-        mx = half_pair_max(mx) * scale_log2;
-        const bool grow = mx > m_ref + kRescaleSlack;
-        if (__any(grow)) {
-            const float m_new = grow ? mx : m_ref;
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-            m_ref = m_new;
-            l_part *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+            for (int c = 0; c < NC; ++c) qf[qb][c] = q_valid[qb] ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
         }
-        const float neg_m = -m_ref;
-        // P as the B operand: chunk c of block blk = registers 8c..8c+7,
-        // i.e. keys 16c + 8(j/4) + 4*half + j%4 (j < 8) of the block.
-        bf16x8 pf[2][2];
+
+        auto dma = [&](const __bf16 *src, __bf16 *dst, int kt) {
+            const int key0 = kt * BN;
+            if (key0 + BN <= N) {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                u32x4 w;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][8 * c + 2 * j], scale_log2, neg_m));
-                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][8 * c + 2 * j + 1], scale_log2, neg_m));
-                    l_part += p0 + p1;
-                    w[j] = pack_bf16x2(p0, p1);
+                for (int j = 0; j < Gm::kLoadsPerWave; ++j) {
+                    const int r0 = (wave * Gm::kLoadsPerWave + j) * Gm::kRowsPerLoad;
+                    const __bf16 *row_base = src + (size_t)(key0 + r0) * tok_stride;
+                    __builtin_amdgcn_global_load_lds((const void *)(row_base + dma_lane_off[j]),
+                                                     (HET_LDS void *)(dst + r0 * D), 16, 0, 0);
                 }
-                pf[blk][c] = __builtin_bit_cast(bf16x8, w);
+            } else {  // last, ragged tile: rows past N repeat key N-1 (their scores are masked)
+#pragma unroll
+                for (int j = 0; j < Gm::kLoadsPerWave; ++j) {
+                    const int r0 = (wave * Gm::kLoadsPerWave + j) * Gm::kRowsPerLoad;
+                    const int r = r0 + dma_lrow;
+                    const int key = imin(key0 + r, N - 1);
+                    const __bf16 *gp = src + (size_t)key * tok_stride + 8 * (dma_pos ^ swz<D>(r));
+                    __builtin_amdgcn_global_load_lds((const void *)gp, (HET_LDS void *)(dst + r0 * D), 16, 0, 0);
+                }
+            }
+        };
+        // S^T = K Q^T for the tile in Kt: sc[kb][qb] = key block kb x query block qb (raw scores).
+        auto qk = [&](const __bf16 *Kt, f32x16 (&sc)[2][QB]) {
+#pragma unroll
+            for (int kbk = 0; kbk < 2; ++kbk) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) sc[kbk][qb] = f32x16{};
+                const int row = kbk * 32 + col;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const bf16x8 a = *(const HET_LDS bf16x8 *)(Kt + row * D + 8 * ((2 * c + half) ^ swz<D>(row)));
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) sc[kbk][qb] = mfma32_bf16(a, qf[qb][c], sc[kbk][qb]);
+                }
+            }
+        };
+        // Row max (log2 units) of each query block; keys >= N masked first when asked.
+        auto row_max = [&](f32x16 (&sc)[2][QB], int kt, bool mask_tail, float (&mx)[QB]) {
+            if (mask_tail) {
+#pragma unroll
+                for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kt * BN + kbk * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+                        if (key >= N) {
+#pragma unroll
+                            for (int qb = 0; qb < QB; ++qb) sc[kbk][qb][i] = -__builtin_inff();
+                        }
+                    }
             }
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+            for (int qb = 0; qb < QB; ++qb) {
+                float m = -__builtin_inff();
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
+                for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int row = blk * 32 + 16 * c + v_row_off;
-                    const int chunk = 4 * db + v_chunk_off;
-                    const bf16x4 lo = lds_read_tr16((const HET_LDS void *)(Vt + row * D + 8 * (chunk ^ swz<D>(row)) + v_elem_off));
-                    const bf16x4 hi = lds_read_tr16((const HET_LDS void *)(Vt + (row + 8) * D + 8 * (chunk ^ swz<D>(row + 8)) + v_elem_off));
-                    oacc[db] = mfma32_bf16(concat8(lo, hi), pf[blk][c], oacc[db]);
+                    for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[kbk][qb][i]);
+                mx[qb] = half_pair_max(m) * scale_log2;
+            }
+        };
+
+        f32x16 oacc[QB][NDB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[qb][db] = f32x16{};
+        float m_ref[QB], l_part[QB];  // reference max (log2 units), partial row sum
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            m_ref[qb] = -__builtin_inff();
+            l_part[qb] = 0.0f;
+        }
+
+        // Lazy rescale of the running state for a tile whose row maxima are mx.
+        auto rescale = [&](const float (&mx)[QB]) {
+            bool gg[QB], any_g = false;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                gg[qb] = mx[qb] > m_ref[qb] + kRescaleSlack;
+                any_g = any_g || gg[qb];
+            }
+            if (__any(any_g)) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const float m_new = gg[qb] ? mx[qb] : m_ref[qb];
+                    const float alpha = gg[qb] ? __builtin_amdgcn_exp2f(m_ref[qb] - m_new) : 1.0f;
+                    m_ref[qb] = m_new;
+                    l_part[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
                 }
-    };
+            }
+        };
+        // P = exp2(S*scale - m) as the B operand of O^T += V^T P^T: chunk c2 of
+        // key block kb = registers 8*c2 .. 8*c2+7, i.e. keys 16*c2 + 8(j/4) +
+        // 4*half + j%4 (j < 8) of the block.
+        auto probs = [&](f32x16 (&sc)[2][QB], bf16x8 (&pf)[QB][2][2]) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float neg_m = -m_ref[qb];
+#pragma unroll
+                for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+                    for (int c2 = 0; c2 < 2; ++c2) {
+                        u32x4 wv;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][qb][8 * c2 + 2 * j], scale_log2, neg_m));
+                            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][qb][8 * c2 + 2 * j + 1], scale_log2, neg_m));
+                            wv[j] = pack_bf16x2(p0, p1);
+                            l_part[qb] += p0 + p1;
+                        }
+                        pf[qb][kbk][c2] = __builtin_bit_cast(bf16x8, wv);
+                    }
+            }
+        };
+        auto pv = [&](const __bf16 *Vt, const bf16x8 (&pf)[QB][2][2]) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+                    for (int c2 = 0; c2 < 2; ++c2) {
+                        const int row = kbk * 32 + 16 * c2 + v_row_off;
+                        const int chunk = 4 * db + v_chunk_off;
+                        const bf16x4 lo = lds_read_tr16((const HET_LDS void *)(Vt + row * D + 8 * (chunk ^ swz<D>(row)) + v_elem_off));
+                        const bf16x4 hi = lds_read_tr16((const HET_LDS void *)(Vt + (row + 8) * D + 8 * (chunk ^ swz<D>(row + 8)) + v_elem_off));
+                        const bf16x8 a = concat8(lo, hi);
+#pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32_bf16(a, pf[qb][kbk][c2], oacc[qb][db]);
+                    }
+        };
 
-    // Prologue: K(0), V(0), K(1) in flight; S(0) from K(0).
-    dma(kb, K0, 0);
-    dma(vb, V0, 0);
-    if (n_tiles > 1) dma(kb, K1, 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
-    f32x16 s_cur[2], s_nxt[2];
-    qk(K0, s_cur);
-
-    // One step: Kc holds K(kt+1), Kn receives K(kt+2), Vc holds V(kt), Vn receives V(kt+1).
-    auto step = [&](int kt, const __bf16 *Kc, __bf16 *Kn, const __bf16 *Vc, __bf16 *Vn) {
+        // ---- key tiles kt0 .. kt1-1 of this unit.  The barrier makes sure all
+        // waves are done with the LDS buffers of the previous piece.
+        const bool ragged_last = (N % BN) != 0;
+        __builtin_amdgcn_s_barrier();
+        dma(kb, K0, kt0);
+        dma(vb, V0, kt0);
+        if (kt0 + 1 < kt1) dma(kb, K1, kt0 + 1);
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
-        if (kt + 2 < n_tiles) dma(kb, Kn, kt + 2);
-        if (kt + 1 < n_tiles) {
-            dma(vb, Vn, kt + 1);
-            qk(Kc, s_nxt);
+        // Score tiles alternate roles: even steps compute S(kt+1) into s_b
+        // while consuming S(kt) from s_a, odd steps the other way round.
+        f32x16 s_a[2][QB], s_b[2][QB];
+        float mx[QB];
+        qk(K0, s_a);
+        row_max(s_a, kt0, ragged_last && kt0 == n_kt - 1, mx);
+        // One step: Kc holds K(kt+1), Kn receives K(kt+2), Vc holds V(kt), Vn receives V(kt+1).
+        auto step = [&](int kt, const __bf16 *Kc, __bf16 *Kn, const __bf16 *Vc, __bf16 *Vn,
+                        f32x16 (&s_cur)[2][QB], f32x16 (&s_nxt)[2][QB]) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_barrier();
+            if (kt + 2 < kt1) dma(kb, Kn, kt + 2);
+            rescale(mx);
+            bf16x8 pf[QB][2][2];
+            if (kt + 1 < kt1) {
+                dma(vb, Vn, kt + 1);
+                qk(Kc, s_nxt);
+                probs(s_cur, pf);
+                pv(Vc, pf);
+                row_max(s_nxt, kt + 1, ragged_last && kt + 1 == n_kt - 1, mx);
+            } else {
+                probs(s_cur, pf);
+                pv(Vc, pf);
+            }
+        };
+        for (int kt = kt0; kt < kt1; kt += 2) {
+            step(kt, K1, K0, V0, V1, s_a, s_b);
+            if (kt + 1 < kt1) step(kt + 1, K0, K1, V1, V0, s_b, s_a);
         }
-        softmax_pv(s_cur, Vc, kt);
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) s_cur[blk] = s_nxt[blk];
-    };
-    for (int kt = 0; kt < n_tiles; kt += 2) {
-        step(kt, K1, K0, V0, V1);
-        if (kt + 1 < n_tiles) step(kt + 1, K0, K1, V1, V0);
-    }
 
-    if (!q_valid) return;
-    const float inv_l = 1.0f / half_pair_sum(l_part);
-    __bf16 *op = o + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
+        float l_tot[QB];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+        for (int qb = 0; qb < QB; ++qb) l_tot[qb] = half_pair_sum(l_part[qb]);
+        auto store_out = [&](int qb, float inv_l) {
+            if (!q_valid[qb]) return;
+            __bf16 *op = o + ((size_t)b * N + tok[qb]) * tok_stride + (size_t)h * D;
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            const int d = db * 32 + 8 * i4 + 4 * half;
-            u32x2 w;
-            w[0] = pack_bf16x2(oacc[db][4 * i4 + 0] * inv_l, oacc[db][4 * i4 + 1] * inv_l);
-            w[1] = pack_bf16x2(oacc[db][4 * i4 + 2] * inv_l, oacc[db][4 * i4 + 3] * inv_l);
-            *(u32x2 *)(op + d) = w;
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int d = db * 32 + 8 * i4 + 4 * half;
+                    u32x2 wv;
+                    wv[0] = pack_bf16x2(oacc[qb][db][4 * i4 + 0] * inv_l, oacc[qb][db][4 * i4 + 1] * inv_l);
+                    wv[1] = pack_bf16x2(oacc[qb][db][4 * i4 + 2] * inv_l, oacc[qb][db][4 * i4 + 3] * inv_l);
+                    *(u32x2 *)(op + d) = wv;
+                }
+        };
+        if (kt0 == 0 && kt1 == n_kt) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) store_out(qb, 1.0f / l_tot[qb]);
+            continue;
         }
+
+        // ---- a piece of a split unit: publish the partial state.  Each lane
+        // stores its D/2 accumulators per query block contiguously in register
+        // order (the lane that merges reads them back in the same order).
+        const size_t slot_elems = (size_t)D * BM;
+        const int my_slot = 2 * w + (unit == first_unit ? 0 : 1);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int qi = (wave * QB + qb) * 32 + col;  // query within the unit
+            f32x4 *dst = (f32x4 *)(ws_part + (size_t)my_slot * slot_elems + (size_t)qi * D + (size_t)half * (D / 2));
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4)
+                    dst[db * 4 + i4] = f32x4{oacc[qb][db][4 * i4], oacc[qb][db][4 * i4 + 1],
+                                             oacc[qb][db][4 * i4 + 2], oacc[qb][db][4 * i4 + 3]};
+            float *part_ml = ws_part + (size_t)2 * G * slot_elems + (size_t)my_slot * 2 * BM;
+            if (half == 0) {
+                part_ml[qi] = m_ref[qb];
+                part_ml[BM + qi] = l_tot[qb];
+            }
+        }
+        __threadfence();
+        __syncthreads();
+        // The pieces of this unit come from the non-empty workgroups owning its
+        // items (with fewer items than workgroups some ranges are empty).
+        const int64_t ux0 = (int64_t)unit * n_kt, ux1 = ux0 + n_kt - 1;
+        const int w_first = work_owner(W, G, ux0), w_last = work_owner(W, G, ux1);
+        int n_pieces = 0;
+        for (int pw = w_first; pw <= w_last; ++pw) n_pieces += work_begin(W, G, pw + 1) > work_begin(W, G, pw);
+        if (tid == 0) s_flag = (atomicAdd(&ws_count[unit], 1) == n_pieces - 1);
+        __syncthreads();
+        if (!s_flag) continue;
+
+        // ---- last piece to finish: merge every piece of this unit.
+        __threadfence();
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int qi = (wave * QB + qb) * 32 + col;
+            // Every piece, this workgroup's own included, is read back from the
+            // workspace and summed in workgroup order, so the result does not
+            // depend on which piece finished last.
+            float m_all = -__builtin_inff();
+            for (int pw = w_first; pw <= w_last; ++pw) {
+                if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
+                const int ps = 2 * pw + (unit == (int)(work_begin(W, G, pw) / n_kt) ? 0 : 1);
+                const float *pml = ws_part + (size_t)2 * G * slot_elems + (size_t)ps * 2 * BM;
+                m_all = fmaxf(m_all, __builtin_nontemporal_load(pml + qi));
+            }
+            f32x16 acc[NDB];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+            float l_all = 0.0f;
+            for (int pw = w_first; pw <= w_last; ++pw) {
+                if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
+                const int ps = 2 * pw + (unit == (int)(work_begin(W, G, pw) / n_kt) ? 0 : 1);
+                const f32x4 *po = (const f32x4 *)(ws_part + (size_t)ps * slot_elems + (size_t)qi * D + (size_t)half * (D / 2));
+                const float *pml = ws_part + (size_t)2 * G * slot_elems + (size_t)ps * 2 * BM;
+                const float a = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(pml + qi) - m_all);
+                l_all += a * __builtin_nontemporal_load(pml + BM + qi);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        const f32x4 pvv = __builtin_nontemporal_load(po + db * 4 + i4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[db][4 * i4 + e] += a * pvv[e];
+                    }
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[qb][db] = acc[db];
+            store_out(qb, 1.0f / l_all);
+        }
+        if (tid == 0) ws_count[unit] = 0;  // ready for the next launch
     }
 }
+
+__global__ void zero_i32_kernel(int32_t *p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// The f32 path below uses kDenseBM queries per workgroup and a plain grid.
+template <typename T, int D, int BN>
+struct DenseTile {
+    static constexpr int kPadK = (sizeof(T) == 2) ? 8 : 4;
+    static constexpr int kPadV = (sizeof(T) == 2) ? 16 : 4;
+    static constexpr int kPitchK = D + kPadK;     // elements
+    static constexpr int kPitchV = D + kPadV;
+    static constexpr int kVec = 16 / sizeof(T);   // elements per 16-byte load
+    static constexpr int kChunksPerRow = D / kVec;
+    static constexpr int kRowsPerPass = kDenseThreads / kChunksPerRow;
+    static constexpr int kPasses = BN / kRowsPerPass;
+    static_assert(kPasses * kRowsPerPass == BN, "tile load shape");
+};
 
 // ----------------------------------------------------------------- f32 ----
 // Same structure with v_mfma_f32_32x32x2_f32 (k = 2 per instruction) and a
@@ -387,23 +588,37 @@ __global__ __launch_bounds__(kDenseThreads) void dense_f32_kernel(
     }
 }
 
+int dense_persistent_groups(int cu_count) { return cu_count; }
+
+size_t dense_workspace_bytes(int batch, int heads, int n, int head_dim, bool bf16, int cu_count) {
+    if (!bf16) return 0;
+    const size_t G = (size_t)dense_persistent_groups(cu_count);
+    const size_t units = (size_t)batch * heads * ((n + kDenseBM16 - 1) / kDenseBM16);
+    return 2 * G * ((size_t)head_dim * kDenseBM16 + 2 * kDenseBM16) * sizeof(float) + units * sizeof(int32_t);
+}
+
 hipError_t launch_dense(const AttnArgs &a, hipStream_t stream) {
     if (a.max_dense <= 0) return hipSuccess;
-    const dim3 grid((a.max_dense + kDenseBM - 1) / kDenseBM, a.heads, a.batch);
     const float sl2 = a.scale * kLog2e;
     if (a.bf16) {
         auto q = (const __bf16 *)a.q, k = (const __bf16 *)a.k, v = (const __bf16 *)a.v;
         auto o = (__bf16 *)a.o;
-        const int tiles = (a.max_dense + kDenseBM - 1) / kDenseBM;
-        const int units = tiles * a.heads * a.batch;
-        const dim3 g1d((units + 7) / 8 * 8);
+        const int G = dense_persistent_groups(a.cu_count);
+        float *ws_part = (float *)a.workspace;
+        int32_t *ws_count = (int32_t *)((char *)a.workspace +
+                                        2 * (size_t)G * ((size_t)a.head_dim * kDenseBM16 + 2 * kDenseBM16) * sizeof(float));
+        const int units_max = a.batch * a.heads * ((a.n + kDenseBM16 - 1) / kDenseBM16);
+        hipLaunchKernelGGL(zero_i32_kernel, dim3((units_max + 255) / 256), dim3(256), 0, stream, ws_count,
+                           units_max);
+        const dim3 g1d((G + 7) / 8 * 8);
         if (a.head_dim == 128)
             hipLaunchKernelGGL(dense_bf16_kernel<128>, g1d, dim3(kDenseThreads), 0, stream, q, k, v, o,
-                               a.dense_idx, a.counts, a.n, a.heads, sl2, tiles, units);
+                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, ws_count);
         else
             hipLaunchKernelGGL(dense_bf16_kernel<64>, g1d, dim3(kDenseThreads), 0, stream, q, k, v, o,
-                               a.dense_idx, a.counts, a.n, a.heads, sl2, tiles, units);
+                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, ws_count);
     } else {
+        const dim3 grid((a.max_dense + kDenseBM - 1) / kDenseBM, a.heads, a.batch);
         auto q = (const float *)a.q, k = (const float *)a.k, v = (const float *)a.v;
         auto o = (float *)a.o;
         if (a.head_dim == 128)
