@@ -5,9 +5,8 @@
 // with m_i = 0 (§3.2.2 Eqs. 12-13).  This is the rho*N^2*d_h term of the cost
 // model (§3.2.2 Eq. 14) and the dominant cost of the layer.
 //
-// bf16 path.  One workgroup = 4 waves = 256 gathered queries of one (sample,
-// head); each wave owns 64 queries as two 32-query column blocks, so every K
-// or V fragment read from LDS feeds two MFMAs.  Per 64-key tile:
+// bf16 path.  One workgroup = 8 waves = 256 gathered queries of one
+// (sample, head), 32 per wave.  Per 64-key tile:
 //   S^T = K Q^T      MFMA 32x32x16, A = K tile (LDS), B = Q (registers)
 //   online softmax   fp32, base 2, per query = per lane (lane l%32)
 //   O^T += V^T P^T   MFMA, A = V tile read transposed from LDS, B = P
@@ -15,19 +14,20 @@
 // max, row sum, output column) in the lane that owns the query, so the
 // softmax needs one cross-half exchange per tile and no LDS round trip.
 //
-// One wave per SIMD (512 registers).  Within a wave the work of tile kt is
-// overlapped with tile kt+1: the MFMAs of S(kt+1) = K(kt+1) Q^T are issued
-// between the exp/sum/convert instructions of softmax(S(kt)), and the P*V
-// MFMAs of tile kt between the row-max instructions of S(kt+1).
+// Ping-pong: waves 0-3 (group 0) and 4-7 (group 1) put one wave of each
+// group on every SIMD.  Each wave alternates an MFMA burst (P*V of the
+// previous tile, then S of this tile) with a VALU burst (softmax of this
+// tile), and the two groups run half a round apart, so while one wave of a
+// SIMD computes exponentials the other keeps the matrix unit busy.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace hetattn {
 
-constexpr int kDenseThreads = 256;
-constexpr int kDenseBM = 128;    // f32 path: queries per workgroup
-constexpr int kDenseQB = 1;      // bf16 path: 32-query blocks per wave
-constexpr int kDenseBM16 = 128 * kDenseQB;  // bf16 path: queries per workgroup
+constexpr int kDenseThreads = 256;  // f32 path
+constexpr int kDenseBM = 128;       // f32 path: queries per workgroup
+constexpr int kDenseThreads16 = 512;  // bf16 path: 8 waves
+constexpr int kDenseBM16 = 256;       // bf16 path: queries per workgroup
 
 // ---------------------------------------------------------------- bf16 ----
 // K and V tiles move global -> LDS by DMA (global_load_lds_dwordx4: each wave
@@ -53,9 +53,10 @@ __device__ __forceinline__ int swz(int row) {
 template <int D>
 struct DenseBf16Geom {
     static constexpr int BN = 64;                  // keys per tile
+    static constexpr int kWaves = 8;
     static constexpr int kCpr = D / 8;             // 16-byte chunks per row
     static constexpr int kRowsPerLoad = 64 / kCpr; // rows per wave DMA (1 KB)
-    static constexpr int kLoadsPerWave = BN / kRowsPerLoad / 4;
+    static constexpr int kLoadsPerWave = BN / kRowsPerLoad / kWaves;
     static constexpr int kTileElems = BN * D;
 };
 
@@ -84,7 +85,7 @@ __device__ __forceinline__ int work_owner(int64_t W, int G, int64_t x) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kDenseThreads, 1) void dense_bf16_kernel(
+__global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const int32_t *__restrict__ dense_idx,
     const int32_t *__restrict__ counts, int B, int N, int H, float scale_log2, int G,
@@ -94,7 +95,6 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_bf16_kernel(
     constexpr int BM = kDenseBM16;
     constexpr int NC = D / 16;  // k-chunks of QK
     constexpr int NDB = D / 32; // 32-row blocks of O^T
-    constexpr int QB = kDenseQB;
     __shared__ __attribute__((aligned(1024))) __bf16 K0[Gm::kTileElems];
     __shared__ __attribute__((aligned(1024))) __bf16 K1[Gm::kTileElems];
     __shared__ __attribute__((aligned(1024))) __bf16 V0[Gm::kTileElems];
@@ -102,6 +102,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_bf16_kernel(
     __shared__ int s_flag;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = wave >> 2;  // ping-pong group
     const int half = lane >> 5, col = lane & 31;
     const int tok_stride = H * D;
     const int n_kt = (N + BN - 1) / BN;
@@ -155,19 +156,15 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_bf16_kernel(
         const __bf16 *kb = k + (size_t)b * N * tok_stride + (size_t)h * D;
         const __bf16 *vb = v + (size_t)b * N * tok_stride + (size_t)h * D;
 
-        // Gathered queries of this lane: query block qb holds query
-        // tile*BM + wave*64 + qb*32 + col.
-        int tok[QB];
-        bool q_valid[QB];
-        bf16x8 qf[QB][NC];
+        // Gathered query of this lane.
+        const int qrow = tile * BM + wave * 32 + col;
+        const bool q_valid = qrow < n_dense;
+        const int tok = q_valid ? dense_idx[(size_t)b * N + qrow] : 0;
+        bf16x8 qf[NC];
+        {
+            const __bf16 *qp = q + ((size_t)b * N + tok) * tok_stride + (size_t)h * D + 8 * half;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int qrow = tile * BM + (wave * QB + qb) * 32 + col;
-            q_valid[qb] = qrow < n_dense;
-            tok[qb] = q_valid[qb] ? dense_idx[(size_t)b * N + qrow] : 0;
-            const __bf16 *qp = q + ((size_t)b * N + tok[qb]) * tok_stride + (size_t)h * D + 8 * half;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) qf[qb][c] = q_valid[qb] ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
+            for (int c = 0; c < NC; ++c) qf[c] = q_valid ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
         }
 
         auto dma = [&](const __bf16 *src, __bf16 *dst, int kt) {
@@ -191,199 +188,153 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_bf16_kernel(
                 }
             }
         };
-        // S^T = K Q^T for the tile in Kt: sc[kb][qb] = key block kb x query block qb (raw scores).
-        auto qk = [&](const __bf16 *Kt, f32x16 (&sc)[2][QB]) {
+
+        f32x16 oacc[NDB];
 #pragma unroll
-            for (int kbk = 0; kbk < 2; ++kbk) {
+        for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+        float m_ref = -__builtin_inff();  // reference max, log2 units
+        float l_part = 0.0f;
+        f32x16 sc[2];                     // S^T of the current tile: key block x 32 queries
+        bf16x8 pf[2][2];                  // P of the current tile as the B operand
+
+        // MFMA burst of round r: O^T += V(r-1)^T P(r-1)^T, then S(r) = K(r) Q^T.
+        auto burst = [&](bool do_pv, const __bf16 *Vt, bool do_qk, const __bf16 *Kt) {
+            if (do_pv) {
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) sc[kbk][qb] = f32x16{};
-                const int row = kbk * 32 + col;
+                for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    const bf16x8 a = *(const HET_LDS bf16x8 *)(Kt + row * D + 8 * ((2 * c + half) ^ swz<D>(row)));
+                    for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) sc[kbk][qb] = mfma32_bf16(a, qf[qb][c], sc[kbk][qb]);
+                        for (int c2 = 0; c2 < 2; ++c2) {
+                            const int row = kbk * 32 + 16 * c2 + v_row_off;
+                            const int chunk = 4 * db + v_chunk_off;
+                            const bf16x4 lo = lds_read_tr16((const HET_LDS void *)(Vt + row * D + 8 * (chunk ^ swz<D>(row)) + v_elem_off));
+                            const bf16x4 hi = lds_read_tr16((const HET_LDS void *)(Vt + (row + 8) * D + 8 * (chunk ^ swz<D>(row + 8)) + v_elem_off));
+                            oacc[db] = mfma32_bf16(concat8(lo, hi), pf[kbk][c2], oacc[db]);
+                        }
+            }
+            if (do_qk) {
+#pragma unroll
+                for (int kbk = 0; kbk < 2; ++kbk) {
+                    sc[kbk] = f32x16{};
+                    const int row = kbk * 32 + col;
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        const bf16x8 a = *(const HET_LDS bf16x8 *)(Kt + row * D + 8 * ((2 * c + half) ^ swz<D>(row)));
+                        sc[kbk] = mfma32_bf16(a, qf[c], sc[kbk]);
+                    }
                 }
             }
         };
-        // Row max (log2 units) of each query block; keys >= N masked first when asked.
-        auto row_max = [&](f32x16 (&sc)[2][QB], int kt, bool mask_tail, float (&mx)[QB]) {
-            if (mask_tail) {
+        // VALU burst of round r: softmax of S(r) into P(r) (lazy rescale, base 2).
+        auto softmax = [&](int kt) {
+            if (kt == n_kt - 1 && kt * BN + BN > N) {
 #pragma unroll
                 for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int key = kt * BN + kbk * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-                        if (key >= N) {
-#pragma unroll
-                            for (int qb = 0; qb < QB; ++qb) sc[kbk][qb][i] = -__builtin_inff();
-                        }
+                        if (key >= N) sc[kbk][i] = -__builtin_inff();
                     }
             }
+            float mx = -__builtin_inff();
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float m = -__builtin_inff();
+            for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-                for (int kbk = 0; kbk < 2; ++kbk)
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kbk][i]);
+            mx = half_pair_max(mx) * scale_log2;
+            const bool grow = mx > m_ref + kRescaleSlack;
+            if (__any(grow)) {
+                const float m_new = grow ? mx : m_ref;
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+                m_ref = m_new;
+                l_part *= alpha;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[kbk][qb][i]);
-                mx[qb] = half_pair_max(m) * scale_log2;
+                for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
             }
-        };
-
-        f32x16 oacc[QB][NDB];
+            const float neg_m = -m_ref;
+            // chunk c2 of key block kb = registers 8*c2 .. 8*c2+7, i.e. keys
+            // 16*c2 + 8(j/4) + 4*half + j%4 (j < 8) of the block.
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+            for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) oacc[qb][db] = f32x16{};
-        float m_ref[QB], l_part[QB];  // reference max (log2 units), partial row sum
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    u32x4 wv;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            m_ref[qb] = -__builtin_inff();
-            l_part[qb] = 0.0f;
-        }
-
-        // Lazy rescale of the running state for a tile whose row maxima are mx.
-        auto rescale = [&](const float (&mx)[QB]) {
-            bool gg[QB], any_g = false;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                gg[qb] = mx[qb] > m_ref[qb] + kRescaleSlack;
-                any_g = any_g || gg[qb];
-            }
-            if (__any(any_g)) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const float m_new = gg[qb] ? mx[qb] : m_ref[qb];
-                    const float alpha = gg[qb] ? __builtin_amdgcn_exp2f(m_ref[qb] - m_new) : 1.0f;
-                    m_ref[qb] = m_new;
-                    l_part[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
+                    for (int j = 0; j < 4; ++j) {
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][8 * c2 + 2 * j], scale_log2, neg_m));
+                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][8 * c2 + 2 * j + 1], scale_log2, neg_m));
+                        l_part += p0 + p1;
+                        wv[j] = pack_bf16x2(p0, p1);
+                    }
+                    pf[kbk][c2] = __builtin_bit_cast(bf16x8, wv);
                 }
-            }
-        };
-        // P = exp2(S*scale - m) as the B operand of O^T += V^T P^T: chunk c2 of
-        // key block kb = registers 8*c2 .. 8*c2+7, i.e. keys 16*c2 + 8(j/4) +
-        // 4*half + j%4 (j < 8) of the block.
-        auto probs = [&](f32x16 (&sc)[2][QB], bf16x8 (&pf)[QB][2][2]) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float neg_m = -m_ref[qb];
-#pragma unroll
-                for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-                    for (int c2 = 0; c2 < 2; ++c2) {
-                        u32x4 wv;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][qb][8 * c2 + 2 * j], scale_log2, neg_m));
-                            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][qb][8 * c2 + 2 * j + 1], scale_log2, neg_m));
-                            wv[j] = pack_bf16x2(p0, p1);
-                            l_part[qb] += p0 + p1;
-                        }
-                        pf[qb][kbk][c2] = __builtin_bit_cast(bf16x8, wv);
-                    }
-            }
-        };
-        auto pv = [&](const __bf16 *Vt, const bf16x8 (&pf)[QB][2][2]) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-                    for (int c2 = 0; c2 < 2; ++c2) {
-                        const int row = kbk * 32 + 16 * c2 + v_row_off;
-                        const int chunk = 4 * db + v_chunk_off;
-                        const bf16x4 lo = lds_read_tr16((const HET_LDS void *)(Vt + row * D + 8 * (chunk ^ swz<D>(row)) + v_elem_off));
-                        const bf16x4 hi = lds_read_tr16((const HET_LDS void *)(Vt + (row + 8) * D + 8 * (chunk ^ swz<D>(row + 8)) + v_elem_off));
-                        const bf16x8 a = concat8(lo, hi);
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32_bf16(a, pf[qb][kbk][c2], oacc[qb][db]);
-                    }
         };
 
-        // ---- key tiles kt0 .. kt1-1 of this unit.  The barrier makes sure all
-        // waves are done with the LDS buffers of the previous piece.
-        const bool ragged_last = (N % BN) != 0;
-        __builtin_amdgcn_s_barrier();
+        // ---- rounds kt0 .. kt1 of this piece.  Round r holds K(r) and
+        // V(r-1) in LDS and fetches K(r+1), V(r):
+        //   phase X: group 0 burst(r)      group 1 softmax(r-1)
+        //   phase Y: group 0 softmax(r)    group 1 burst(r)
+        // K(r) lives in K0 for even r-kt0 and K1 for odd; V(r) likewise.
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();  // previous piece is done with the buffers
         dma(kb, K0, kt0);
-        dma(vb, V0, kt0);
-        if (kt0 + 1 < kt1) dma(kb, K1, kt0 + 1);
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
-        // Score tiles alternate roles: even steps compute S(kt+1) into s_b
-        // while consuming S(kt) from s_a, odd steps the other way round.
-        f32x16 s_a[2][QB], s_b[2][QB];
-        float mx[QB];
-        qk(K0, s_a);
-        row_max(s_a, kt0, ragged_last && kt0 == n_kt - 1, mx);
-        // One step: Kc holds K(kt+1), Kn receives K(kt+2), Vc holds V(kt), Vn receives V(kt+1).
-        auto step = [&](int kt, const __bf16 *Kc, __bf16 *Kn, const __bf16 *Vc, __bf16 *Vn,
-                        f32x16 (&s_cur)[2][QB], f32x16 (&s_nxt)[2][QB]) {
+        auto round = [&](int r, const __bf16 *Kc, __bf16 *Kn, const __bf16 *Vp, __bf16 *Vc) {
+            if (r + 1 < kt1) dma(kb, Kn, r + 1);
+            if (r < kt1) dma(vb, Vc, r);
+            if (grp == 0) burst(r > kt0, Vp, r < kt1, Kc);
+            else if (r > kt0) softmax(r - 1);
+            __builtin_amdgcn_s_barrier();
+            if (grp == 0) { if (r < kt1) softmax(r); }
+            else burst(r > kt0, Vp, r < kt1, Kc);
             __builtin_amdgcn_s_waitcnt(0);
             __builtin_amdgcn_s_barrier();
-            if (kt + 2 < kt1) dma(kb, Kn, kt + 2);
-            rescale(mx);
-            bf16x8 pf[QB][2][2];
-            if (kt + 1 < kt1) {
-                dma(vb, Vn, kt + 1);
-                qk(Kc, s_nxt);
-                probs(s_cur, pf);
-                pv(Vc, pf);
-                row_max(s_nxt, kt + 1, ragged_last && kt + 1 == n_kt - 1, mx);
-            } else {
-                probs(s_cur, pf);
-                pv(Vc, pf);
-            }
         };
-        for (int kt = kt0; kt < kt1; kt += 2) {
-            step(kt, K1, K0, V0, V1, s_a, s_b);
-            if (kt + 1 < kt1) step(kt + 1, K0, K1, V1, V0, s_b, s_a);
+        for (int r = kt0; r <= kt1; r += 2) {
+            round(r, K0, K1, V1, V0);
+            if (r + 1 <= kt1) round(r + 1, K1, K0, V0, V1);
         }
 
-        float l_tot[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) l_tot[qb] = half_pair_sum(l_part[qb]);
-        auto store_out = [&](int qb, float inv_l) {
-            if (!q_valid[qb]) return;
-            __bf16 *op = o + ((size_t)b * N + tok[qb]) * tok_stride + (size_t)h * D;
+        const float l_tot = half_pair_sum(l_part);
+        __bf16 *op = o + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
+        auto store_out = [&](float inv_l) {
+            if (!q_valid) return;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
                     const int d = db * 32 + 8 * i4 + 4 * half;
                     u32x2 wv;
-                    wv[0] = pack_bf16x2(oacc[qb][db][4 * i4 + 0] * inv_l, oacc[qb][db][4 * i4 + 1] * inv_l);
-                    wv[1] = pack_bf16x2(oacc[qb][db][4 * i4 + 2] * inv_l, oacc[qb][db][4 * i4 + 3] * inv_l);
+                    wv[0] = pack_bf16x2(oacc[db][4 * i4 + 0] * inv_l, oacc[db][4 * i4 + 1] * inv_l);
+                    wv[1] = pack_bf16x2(oacc[db][4 * i4 + 2] * inv_l, oacc[db][4 * i4 + 3] * inv_l);
                     *(u32x2 *)(op + d) = wv;
                 }
         };
         if (kt0 == 0 && kt1 == n_kt) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) store_out(qb, 1.0f / l_tot[qb]);
+            store_out(1.0f / l_tot);
             continue;
         }
 
         // ---- a piece of a split unit: publish the partial state.  Each lane
-        // stores its D/2 accumulators per query block contiguously in register
-        // order (the lane that merges reads them back in the same order).
+        // stores its D/2 accumulators contiguously in register order (the
+        // lane that merges reads them back in the same order).
         const size_t slot_elems = (size_t)D * BM;
         const int my_slot = 2 * w + (unit == first_unit ? 0 : 1);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int qi = (wave * QB + qb) * 32 + col;  // query within the unit
+        const int qi = wave * 32 + col;  // query within the unit
+        {
             f32x4 *dst = (f32x4 *)(ws_part + (size_t)my_slot * slot_elems + (size_t)qi * D + (size_t)half * (D / 2));
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4)
-                    dst[db * 4 + i4] = f32x4{oacc[qb][db][4 * i4], oacc[qb][db][4 * i4 + 1],
-                                             oacc[qb][db][4 * i4 + 2], oacc[qb][db][4 * i4 + 3]};
+                    dst[db * 4 + i4] = f32x4{oacc[db][4 * i4], oacc[db][4 * i4 + 1], oacc[db][4 * i4 + 2],
+                                             oacc[db][4 * i4 + 3]};
             float *part_ml = ws_part + (size_t)2 * G * slot_elems + (size_t)my_slot * 2 * BM;
             if (half == 0) {
-                part_ml[qi] = m_ref[qb];
-                part_ml[BM + qi] = l_tot[qb];
+                part_ml[qi] = m_ref;
+                part_ml[BM + qi] = l_tot;
             }
         }
         __threadfence();
@@ -398,45 +349,38 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_bf16_kernel(
         __syncthreads();
         if (!s_flag) continue;
 
-        // ---- last piece to finish: merge every piece of this unit.
+        // ---- last piece to finish: merge every piece of this unit.  Every
+        // piece, this workgroup's own included, is read back from the
+        // workspace and summed in workgroup order, so the result does not
+        // depend on which piece finished last.
         __threadfence();
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int qi = (wave * QB + qb) * 32 + col;
-            // Every piece, this workgroup's own included, is read back from the
-            // workspace and summed in workgroup order, so the result does not
-            // depend on which piece finished last.
-            float m_all = -__builtin_inff();
-            for (int pw = w_first; pw <= w_last; ++pw) {
-                if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
-                const int ps = 2 * pw + (unit == (int)(work_begin(W, G, pw) / n_kt) ? 0 : 1);
-                const float *pml = ws_part + (size_t)2 * G * slot_elems + (size_t)ps * 2 * BM;
-                m_all = fmaxf(m_all, __builtin_nontemporal_load(pml + qi));
-            }
-            f32x16 acc[NDB];
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-            float l_all = 0.0f;
-            for (int pw = w_first; pw <= w_last; ++pw) {
-                if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
-                const int ps = 2 * pw + (unit == (int)(work_begin(W, G, pw) / n_kt) ? 0 : 1);
-                const f32x4 *po = (const f32x4 *)(ws_part + (size_t)ps * slot_elems + (size_t)qi * D + (size_t)half * (D / 2));
-                const float *pml = ws_part + (size_t)2 * G * slot_elems + (size_t)ps * 2 * BM;
-                const float a = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(pml + qi) - m_all);
-                l_all += a * __builtin_nontemporal_load(pml + BM + qi);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4) {
-                        const f32x4 pvv = __builtin_nontemporal_load(po + db * 4 + i4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[db][4 * i4 + e] += a * pvv[e];
-                    }
-            }
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) oacc[qb][db] = acc[db];
-            store_out(qb, 1.0f / l_all);
+        float m_all = -__builtin_inff();
+        for (int pw = w_first; pw <= w_last; ++pw) {
+            if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
+            const int ps = 2 * pw + (unit == (int)(work_begin(W, G, pw) / n_kt) ? 0 : 1);
+            const float *pml = ws_part + (size_t)2 * G * slot_elems + (size_t)ps * 2 * BM;
+            m_all = fmaxf(m_all, __builtin_nontemporal_load(pml + qi));
         }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+        float l_all = 0.0f;
+        for (int pw = w_first; pw <= w_last; ++pw) {
+            if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
+            const int ps = 2 * pw + (unit == (int)(work_begin(W, G, pw) / n_kt) ? 0 : 1);
+            const f32x4 *po = (const f32x4 *)(ws_part + (size_t)ps * slot_elems + (size_t)qi * D + (size_t)half * (D / 2));
+            const float *pml = ws_part + (size_t)2 * G * slot_elems + (size_t)ps * 2 * BM;
+            const float a = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(pml + qi) - m_all);
+            l_all += a * __builtin_nontemporal_load(pml + BM + qi);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x4 pvv = __builtin_nontemporal_load(po + db * 4 + i4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) oacc[db][4 * i4 + e] += a * pvv[e];
+                }
+        }
+        store_out(1.0f / l_all);
         if (tid == 0) ws_count[unit] = 0;  // ready for the next launch
     }
 }
@@ -612,10 +556,10 @@ hipError_t launch_dense(const AttnArgs &a, hipStream_t stream) {
                            units_max);
         const dim3 g1d((G + 7) / 8 * 8);
         if (a.head_dim == 128)
-            hipLaunchKernelGGL(dense_bf16_kernel<128>, g1d, dim3(kDenseThreads), 0, stream, q, k, v, o,
+            hipLaunchKernelGGL(dense_bf16_kernel<128>, g1d, dim3(kDenseThreads16), 0, stream, q, k, v, o,
                                a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, ws_count);
         else
-            hipLaunchKernelGGL(dense_bf16_kernel<64>, g1d, dim3(kDenseThreads), 0, stream, q, k, v, o,
+            hipLaunchKernelGGL(dense_bf16_kernel<64>, g1d, dim3(kDenseThreads16), 0, stream, q, k, v, o,
                                a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, ws_count);
     } else {
         const dim3 grid((a.max_dense + kDenseBM - 1) / kDenseBM, a.heads, a.batch);
