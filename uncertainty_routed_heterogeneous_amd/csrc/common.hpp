@@ -27,6 +27,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define HET_LDS __attribute__((address_space(3)))
+// Kernel-local lambdas must inline: a lambda left as a call makes its
+// by-reference captures addressable, which puts them in scratch memory.
+#define HET_INLINE __attribute__((always_inline))
 
 constexpr float kLog2e = 1.4426950408889634f;
 

@@ -19,6 +19,8 @@
 // previous tile, then S of this tile) with a VALU burst (softmax of this
 // tile), and the two groups run half a round apart, so while one wave of a
 // SIMD computes exponentials the other keeps the matrix unit busy.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -137,6 +139,21 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
     const int v_row_off = 4 * half + (j16 >> 2);
     const int v_chunk_off = 2 * (g16 & 1) + ((j16 & 3) >> 1);
     const int v_elem_off = 4 * (j16 & 1);
+    // Per-lane element offsets inside a tile, shared by every buffer: the
+    // swizzle only sees the low row bits, which the block/step parts of the
+    // row index (multiples of 16) leave alone.
+    //   K, A operand of chunk c:   row col (+32 per key block), chunk 2c+half
+    //   V, slab db, rows +8*lohi:  row v_row_off + 8*lohi (+16*c2 + 32*kbk)
+    int k_off[NC], v_off[NDB][2];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) k_off[c] = col * D + 8 * ((2 * c + half) ^ swz<D>(col));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int lohi = 0; lohi < 2; ++lohi) {
+            const int row = v_row_off + 8 * lohi;
+            v_off[db][lohi] = row * D + 8 * ((4 * db + v_chunk_off) ^ swz<D>(row)) + v_elem_off;
+        }
 
     while (x < x_end) {
         // ---- the unit of item x and the key-tile range of this piece
@@ -167,7 +184,7 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
             for (int c = 0; c < NC; ++c) qf[c] = q_valid ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
         }
 
-        auto dma = [&](const __bf16 *src, __bf16 *dst, int kt) {
+        auto dma = [&](const __bf16 *src, __bf16 *dst, int kt) HET_INLINE {
             const int key0 = kt * BN;
             if (key0 + BN <= N) {
 #pragma unroll
@@ -197,44 +214,63 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         f32x16 sc[2];                     // S^T of the current tile: key block x 32 queries
         bf16x8 pf[2][2];                  // P of the current tile as the B operand
 
-        // MFMA burst of round r: O^T += V(r-1)^T P(r-1)^T, then S(r) = K(r) Q^T.
-        auto burst = [&](bool do_pv, const __bf16 *Vt, bool do_qk, const __bf16 *Kt) {
-            if (do_pv) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-                        for (int c2 = 0; c2 < 2; ++c2) {
-                            const int row = kbk * 32 + 16 * c2 + v_row_off;
-                            const int chunk = 4 * db + v_chunk_off;
-                            const bf16x4 lo = lds_read_tr16((const HET_LDS void *)(Vt + row * D + 8 * (chunk ^ swz<D>(row)) + v_elem_off));
-                            const bf16x4 hi = lds_read_tr16((const HET_LDS void *)(Vt + (row + 8) * D + 8 * (chunk ^ swz<D>(row + 8)) + v_elem_off));
-                            oacc[db] = mfma32_bf16(concat8(lo, hi), pf[kbk][c2], oacc[db]);
-                        }
+        // MFMA burst of round r: O^T += V(r-1)^T P(r-1)^T (steps 0..4*NDB-1),
+        // then S(r) = K(r) Q^T (steps 4*NDB..4*NDB+2*NC-1).  The A operand of
+        // step i is read from LDS kAhead steps before its MFMA, and
+        // sched_barrier keeps the compiler from sinking the reads back.
+        constexpr int kPvSteps = 4 * NDB, kQkSteps = 2 * NC, kAhead = 2;
+        auto a_operand = [&](int i, const __bf16 *Vt, const __bf16 *Kt) HET_INLINE -> bf16x8 {
+            if (i < kPvSteps) {
+                const int db = i >> 2, kbk = (i >> 1) & 1, c2 = i & 1;
+                const __bf16 *base = Vt + (kbk * 32 + 16 * c2) * D;
+                const bf16x4 lo = lds_read_tr16((const HET_LDS void *)(base + v_off[db][0]));
+                const bf16x4 hi = lds_read_tr16((const HET_LDS void *)(base + v_off[db][1]));
+                return concat8(lo, hi);
             }
-            if (do_qk) {
+            const int j = i - kPvSteps, kbk = j / NC, c = j % NC;
+            return *(const HET_LDS bf16x8 *)(Kt + kbk * 32 * D + k_off[c]);
+        };
+        // pv_tag/qk_tag are std::integral_constant<bool, ...>: every index below
+        // is a compile-time constant, so the ring stays in registers.
+        auto burst_ct = [&](auto pv_tag, auto qk_tag, const __bf16 *Vt, const __bf16 *Kt) HET_INLINE {
+            constexpr bool kPv = decltype(pv_tag)::value, kQk = decltype(qk_tag)::value;
+            constexpr int i0 = kPv ? 0 : kPvSteps, i1 = kQk ? kPvSteps + kQkSteps : kPvSteps;
+            if constexpr (i0 < i1) {
+                if constexpr (kQk) {
+                    sc[0] = f32x16{};
+                    sc[1] = f32x16{};
+                }
+                bf16x8 ring[kAhead];
 #pragma unroll
-                for (int kbk = 0; kbk < 2; ++kbk) {
-                    sc[kbk] = f32x16{};
-                    const int row = kbk * 32 + col;
+                for (int a = 0; a < kAhead; ++a)
+                    if (i0 + a < i1) ring[a] = a_operand(i0 + a, Vt, Kt);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int c = 0; c < NC; ++c) {
-                        const bf16x8 a = *(const HET_LDS bf16x8 *)(Kt + row * D + 8 * ((2 * c + half) ^ swz<D>(row)));
+                for (int i = i0; i < i1; ++i) {
+                    const bf16x8 a = ring[(i - i0) % kAhead];
+                    if (i < kPvSteps) {
+                        const int db = i >> 2, kbk = (i >> 1) & 1, c2 = i & 1;
+                        oacc[db] = mfma32_bf16(a, pf[kbk][c2], oacc[db]);
+                    } else {
+                        const int j = i - kPvSteps, kbk = j / NC, c = j % NC;
                         sc[kbk] = mfma32_bf16(a, qf[c], sc[kbk]);
                     }
+                    if (i + kAhead < i1) ring[(i - i0) % kAhead] = a_operand(i + kAhead, Vt, Kt);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
         // VALU burst of round r: softmax of S(r) into P(r) (lazy rescale, base 2).
-        auto softmax = [&](int kt) {
-            if (kt == n_kt - 1 && kt * BN + BN > N) {
+        auto softmax = [&](int kt) HET_INLINE {
+            if (__builtin_expect(kt == n_kt - 1 && kt * BN + BN > N, 0)) {
+                // keys past N in the last tile: branch-free select per element
+                const int lim = N - kt * BN - 4 * half;
 #pragma unroll
                 for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int key = kt * BN + kbk * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-                        if (key >= N) sc[kbk][i] = -__builtin_inff();
+                        const int key_off = kbk * 32 + 8 * (i / 4) + (i % 4);
+                        sc[kbk][i] = key_off < lim ? sc[kbk][i] : -__builtin_inff();
                     }
             }
             float mx = -__builtin_inff();
@@ -244,7 +280,7 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kbk][i]);
             mx = half_pair_max(mx) * scale_log2;
             const bool grow = mx > m_ref + kRescaleSlack;
-            if (__any(grow)) {
+            if (__builtin_expect(__any(grow), 0)) {
                 const float m_new = grow ? mx : m_ref;
                 const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
                 m_ref = m_new;
@@ -275,31 +311,53 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         // V(r-1) in LDS and fetches K(r+1), V(r):
         //   phase X: group 0 burst(r)      group 1 softmax(r-1)
         //   phase Y: group 0 softmax(r)    group 1 burst(r)
-        // K(r) lives in K0 for even r-kt0 and K1 for odd; V(r) likewise.
+        // The first round has no P*V and the last no QK; in between, K(r)
+        // lives in K0 for even r-kt0 and K1 for odd, V(r) likewise.
+        using T_ = std::true_type;
+        using F_ = std::false_type;
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();  // previous piece is done with the buffers
         dma(kb, K0, kt0);
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
-        auto round = [&](int r, const __bf16 *Kc, __bf16 *Kn, const __bf16 *Vp, __bf16 *Vc) {
+        // first round r = kt0
+        if (kt0 + 1 < kt1) dma(kb, K1, kt0 + 1);
+        dma(vb, V0, kt0);
+        if (grp == 0) burst_ct(F_{}, T_{}, V1, K0);
+        __builtin_amdgcn_s_barrier();
+        if (grp == 0) softmax(kt0);
+        else burst_ct(F_{}, T_{}, V1, K0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        // rounds kt0+1 .. kt1-1: full bursts
+        auto round = [&](int r, const __bf16 *Kc, __bf16 *Kn, const __bf16 *Vp, __bf16 *Vc) HET_INLINE {
             if (r + 1 < kt1) dma(kb, Kn, r + 1);
-            if (r < kt1) dma(vb, Vc, r);
-            if (grp == 0) burst(r > kt0, Vp, r < kt1, Kc);
-            else if (r > kt0) softmax(r - 1);
+            dma(vb, Vc, r);
+            if (grp == 0) burst_ct(T_{}, T_{}, Vp, Kc);
+            else softmax(r - 1);
             __builtin_amdgcn_s_barrier();
-            if (grp == 0) { if (r < kt1) softmax(r); }
-            else burst(r > kt0, Vp, r < kt1, Kc);
+            if (grp == 0) softmax(r);
+            else burst_ct(T_{}, T_{}, Vp, Kc);
             __builtin_amdgcn_s_waitcnt(0);
             __builtin_amdgcn_s_barrier();
         };
-        for (int r = kt0; r <= kt1; r += 2) {
-            round(r, K0, K1, V1, V0);
-            if (r + 1 <= kt1) round(r + 1, K1, K0, V0, V1);
+        for (int r = kt0 + 1; r < kt1; r += 2) {
+            round(r, K1, K0, V0, V1);
+            if (r + 1 < kt1) round(r + 1, K0, K1, V1, V0);
+        }
+        // last round r = kt1: P*V of tile kt1-1 only; no DMA is in flight, so
+        // the buffer can be picked at run time.
+        {
+            const __bf16 *Vp = ((kt1 - 1 - kt0) & 1) ? V1 : V0;
+            if (grp == 0) burst_ct(T_{}, F_{}, Vp, K0);
+            else softmax(kt1 - 1);
+            __builtin_amdgcn_s_barrier();
+            if (grp == 1) burst_ct(T_{}, F_{}, Vp, K0);
         }
 
         const float l_tot = half_pair_sum(l_part);
         __bf16 *op = o + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
-        auto store_out = [&](float inv_l) {
+        auto store_out = [&](float inv_l) HET_INLINE {
             if (!q_valid) return;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -439,7 +497,7 @@ __global__ __launch_bounds__(kDenseThreads) void dense_f32_kernel(
 
     u32x4 kreg[Tl::kPasses], vreg[Tl::kPasses];
     const int ld_row = tid / Tl::kChunksPerRow, ld_chunk = tid % Tl::kChunksPerRow;
-    auto fetch = [&](int kt) {
+    auto fetch = [&](int kt) HET_INLINE {
 #pragma unroll
         for (int p = 0; p < Tl::kPasses; ++p) {
             const int key = kt * BN + p * Tl::kRowsPerPass + ld_row;
@@ -452,7 +510,7 @@ __global__ __launch_bounds__(kDenseThreads) void dense_f32_kernel(
             }
         }
     };
-    auto stash = [&]() {
+    auto stash = [&]() HET_INLINE {
 #pragma unroll
         for (int p = 0; p < Tl::kPasses; ++p) {
             const int r = p * Tl::kRowsPerPass + ld_row;

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
 
     // Box row r -> token of its first column (rows past the box clamp to the
     // last row).  r is the same for the whole wave, so this runs on the SALU.
-    auto row_token = [&](int r) -> int {
+    auto row_token = [&](int r) HET_INLINE -> int {
         r = imin(r, rows - 1);
         const int tt = t0 + r / ny, yy = uy0 + r % ny;
         return (tt * g.Hg + yy) * g.Wg + ux0;
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
     bool vok[kStage];
     // Slot s = rr*SR + xo of a block lies in box row rr of the block; slots
     // past the row (xo >= nx) or past the box load a clamped in-box address.
-    auto fetch = [&](int kb, KFrag *kdst) {
+    auto fetch = [&](int kb, KFrag *kdst) HET_INLINE {
         const int rt0 = row_token(kb * rpb), rt1 = row_token(kb * rpb + 1);
         const bool ok0 = kb * rpb < rows, ok1 = rpb > 1 && kb * rpb + 1 < rows;
         const int jk = ((col / SR) ? rt1 : rt0) + imin(col % SR, nx - 1);
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
             vst[it] = *(const u32x4 *)(vbase + (size_t)jv * tok_stride + kVec * (lane % kChunks));
         }
     };
-    auto stage_v = [&]() {
+    auto stage_v = [&]() HET_INLINE {
 #pragma unroll
         for (int it = 0; it < kStage; ++it) {
             const int e = lane + 64 * it, s = e / kChunks, ch = e % kChunks;
