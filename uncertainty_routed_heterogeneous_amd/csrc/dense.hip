@@ -113,13 +113,18 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
     // exact in both threshold modes; every workgroup computes the same list.
     int units = 0;
     for (int bb = 0; bb < B; ++bb) units += H * ((counts[2 * bb] + BM - 1) / BM);
-    const int64_t W = (int64_t)units * n_kt;
+    // Whole units first, round-robin: the G workgroups start their units
+    // together at key tile 0, and the units of one head run on one XCD, so
+    // the K/V stream of a head is fetched once per XCD and shared in its L2.
+    // Only the remaining units_sk = units mod G are split stream-K style.
+    const int units_dp = units / G * G, units_sk = units - units_dp;
+    const int64_t W = (int64_t)units_sk * n_kt;  // stream-K items
     const int w = xcd_remap(blockIdx.x, gridDim.x);
-    if (w >= G || W == 0) return;
-    int64_t x = work_begin(W, G, w);
-    const int64_t x_end = work_begin(W, G, w + 1);
-    if (x >= x_end) return;
-    const int first_unit = (int)(x / n_kt);
+    if (w >= G || units == 0) return;
+    int dp_unit = w;
+    int64_t x = units_sk ? work_begin(W, G, w) : 0;
+    const int64_t x_end = units_sk ? work_begin(W, G, w + 1) : 0;
+    const int first_unit = units_sk ? units_dp + (int)(x / n_kt) : -1;  // first stream-K unit
 
     // DMA geometry: load j of this wave fills tile rows from r0_j on; this
     // lane writes row r0_j + lane/kCpr at chunk position lane%kCpr, so it
@@ -155,12 +160,23 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
             v_off[db][lohi] = row * D + 8 * ((4 * db + v_chunk_off) ^ swz<D>(row)) + v_elem_off;
         }
 
-    while (x < x_end) {
-        // ---- the unit of item x and the key-tile range of this piece
-        const int unit = (int)(x / n_kt);
-        const int kt0 = (int)(x - (int64_t)unit * n_kt);
-        const int kt1 = (int)((x_end - (int64_t)unit * n_kt) < n_kt ? (x_end - (int64_t)unit * n_kt) : n_kt);
-        x = (int64_t)unit * n_kt + kt1;
+    for (;;) {
+        // ---- next task: a whole unit, then pieces of the stream-K units
+        int unit, kt0, kt1;
+        if (dp_unit < units_dp) {
+            unit = dp_unit;
+            kt0 = 0;
+            kt1 = n_kt;
+            dp_unit += G;
+        } else if (x < x_end) {
+            const int sk = (int)(x / n_kt);
+            kt0 = (int)(x - (int64_t)sk * n_kt);
+            kt1 = (int)((x_end - (int64_t)sk * n_kt) < n_kt ? (x_end - (int64_t)sk * n_kt) : n_kt);
+            x = (int64_t)sk * n_kt + kt1;
+            unit = units_dp + sk;
+        } else {
+            break;
+        }
         int b = 0, rem = unit, tiles_b = 0;
         for (;;) {
             tiles_b = (counts[2 * b] + BM - 1) / BM;
@@ -218,7 +234,7 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         // then S(r) = K(r) Q^T (steps 4*NDB..4*NDB+2*NC-1).  The A operand of
         // step i is read from LDS kAhead steps before its MFMA, and
         // sched_barrier keeps the compiler from sinking the reads back.
-        constexpr int kPvSteps = 4 * NDB, kQkSteps = 2 * NC, kAhead = 2;
+        constexpr int kPvSteps = 4 * NDB, kQkSteps = 2 * NC, kAhead = 4;
         auto a_operand = [&](int i, const __bf16 *Vt, const __bf16 *Kt) HET_INLINE -> bf16x8 {
             if (i < kPvSteps) {
                 const int db = i >> 2, kbk = (i >> 1) & 1, c2 = i & 1;
@@ -399,7 +415,7 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         __syncthreads();
         // The pieces of this unit come from the non-empty workgroups owning its
         // items (with fewer items than workgroups some ranges are empty).
-        const int64_t ux0 = (int64_t)unit * n_kt, ux1 = ux0 + n_kt - 1;
+        const int64_t ux0 = (int64_t)(unit - units_dp) * n_kt, ux1 = ux0 + n_kt - 1;
         const int w_first = work_owner(W, G, ux0), w_last = work_owner(W, G, ux1);
         int n_pieces = 0;
         for (int pw = w_first; pw <= w_last; ++pw) n_pieces += work_begin(W, G, pw + 1) > work_begin(W, G, pw);
@@ -415,7 +431,7 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         float m_all = -__builtin_inff();
         for (int pw = w_first; pw <= w_last; ++pw) {
             if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
-            const int ps = 2 * pw + (unit == (int)(work_begin(W, G, pw) / n_kt) ? 0 : 1);
+            const int ps = 2 * pw + (unit == units_dp + (int)(work_begin(W, G, pw) / n_kt) ? 0 : 1);
             const float *pml = ws_part + (size_t)2 * G * slot_elems + (size_t)ps * 2 * BM;
             m_all = fmaxf(m_all, __builtin_nontemporal_load(pml + qi));
         }
@@ -424,7 +440,7 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         float l_all = 0.0f;
         for (int pw = w_first; pw <= w_last; ++pw) {
             if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
-            const int ps = 2 * pw + (unit == (int)(work_begin(W, G, pw) / n_kt) ? 0 : 1);
+            const int ps = 2 * pw + (unit == units_dp + (int)(work_begin(W, G, pw) / n_kt) ? 0 : 1);
             const f32x4 *po = (const f32x4 *)(ws_part + (size_t)ps * slot_elems + (size_t)qi * D + (size_t)half * (D / 2));
             const float *pml = ws_part + (size_t)2 * G * slot_elems + (size_t)ps * 2 * BM;
             const float a = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(pml + qi) - m_all);
