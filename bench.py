@@ -178,6 +178,8 @@ def main():
     ap.add_argument("--no-dense-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=4)
     ap.add_argument("--lib", default=None, help="load this libhetattn.so instead of the in-tree one")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (calibrates HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -189,6 +191,17 @@ def main():
 
     import numpy as np  # noqa: F401
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_calibration} MiB x 5")
+        return
 
     import uncertainty_routed_heterogeneous_amd as het
     import workloads as W
