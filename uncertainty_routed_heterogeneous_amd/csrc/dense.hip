@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         // then S(r) = K(r) Q^T (steps 4*NDB..4*NDB+2*NC-1).  The A operand of
         // step i is read from LDS kAhead steps before its MFMA, and
         // sched_barrier keeps the compiler from sinking the reads back.
-        constexpr int kPvSteps = 4 * NDB, kQkSteps = 2 * NC, kAhead = 4;
+        constexpr int kPvSteps = 4 * NDB, kQkSteps = 2 * NC, kAhead = 6;
         auto a_operand = [&](int i, const __bf16 *Vt, const __bf16 *Kt) HET_INLINE -> bf16x8 {
             if (i < kPvSteps) {
                 const int db = i >> 2, kbk = (i >> 1) & 1, c2 = i & 1;
@@ -325,8 +325,10 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
 
         // ---- rounds kt0 .. kt1 of this piece.  Round r holds K(r) and
         // V(r-1) in LDS and fetches K(r+1), V(r):
-        //   phase X: group 0 burst(r)      group 1 softmax(r-1)
-        //   phase Y: group 0 softmax(r)    group 1 burst(r)
+        //   group 0: burst(r), then softmax(r)
+        //   group 1: softmax(r-1), then burst(r)
+        // so on every SIMD one wave starts on the matrix unit while the other
+        // computes exponentials; only the end of a round is a barrier.
         // The first round has no P*V and the last no QK; in between, K(r)
         // lives in K0 for even r-kt0 and K1 for odd, V(r) likewise.
         using T_ = std::true_type;
@@ -351,7 +353,6 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
             dma(vb, Vc, r);
             if (grp == 0) burst_ct(T_{}, T_{}, Vp, Kc);
             else softmax(r - 1);
-            __builtin_amdgcn_s_barrier();
             if (grp == 0) softmax(r);
             else burst_ct(T_{}, T_{}, Vp, Kc);
             __builtin_amdgcn_s_waitcnt(0);
