@@ -87,16 +87,12 @@ def test_route_mean_std_crafted(oracle_mod):
         assert_route_equal(route_to_numpy(r), oracle_mod.route_mean_std(u, c))
 
 
-@pytest.mark.parametrize("name", ["tiny", "wan13b", "wan5b"])
-def test_route_mean_std_workloads(oracle_mod, name):
+def check_mean_std(oracle_mod, u, grid, c, heads=2, head_dim=64, dtype="f32", window=(3, 3, 3)):
     """The GPU sums in a different (fixed) order than the oracle; a token may
     only differ if its u lies within rounding distance of T."""
-    w = W.WORKLOADS[name]
-    u = W.make_u(w)
-    log(f"[route] mean-std {name} c=0.9")
-    r = gpu_route(u, w.grid, w.window, w.heads, w.head_dim, w.dtype, c=0.9)
+    r = gpu_route(u, grid, window, heads, head_dim, dtype, c=c)
     g = route_to_numpy(r)
-    o = oracle_mod.route_mean_std(u, 0.9)
+    o = oracle_mod.route_mean_std(u, c)
     np.testing.assert_allclose(g["thresh"], o.thresh, rtol=1e-13, atol=0)
     diff = g["mask"] != o.mask
     if diff.any():
@@ -106,6 +102,41 @@ def test_route_mean_std_workloads(oracle_mod, name):
         log(f"  {diff.sum()} tokens at the threshold differ by rounding")
     else:
         assert_route_equal(g, o, exact_thresh=False)
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan13b", "wan5b"])
+def test_route_mean_std_workloads(oracle_mod, name):
+    w = W.WORKLOADS[name]
+    log(f"[route] mean-std {name} c=0.9")
+    check_mean_std(oracle_mod, W.make_u(w), w.grid, 0.9, w.heads, w.head_dim, w.dtype, w.window)
+
+
+@pytest.mark.parametrize("n", [8192, 8193, 16385, 32768, 32769, 65536, 65537, 100003])
+def test_route_chunk_lengths(oracle_mod, n):
+    """Sample lengths at the edges of the per-thread chunk lengths of the
+    route kernel (keys held in registers up to 65536 tokens, re-read from
+    memory beyond).  Sample 0 has both signs (keys differ in the top bit),
+    sample 1 has 51 distinct values (long runs of ties)."""
+    rng = np.random.default_rng(n)
+    u = np.empty((2, n), np.float32)
+    u[0] = rng.standard_normal(n)
+    u[1] = np.round(rng.random(n) * 50) / 50
+    for rho in (0.2, 0.73):
+        log(f"[route] N={n} rho={rho}")
+        run_top_rho(oracle_mod, u, (1, 1, n), rho)
+    log(f"[route] N={n} mean-std c=0.5")
+    check_mean_std(oracle_mod, u, (1, 1, n), 0.5)
+
+
+def test_route_keys_one_ulp_apart(oracle_mod):
+    """All keys share their top 31 bits: the select has a single 1-bit digit."""
+    a = np.float32(1.0)
+    b = np.nextafter(a, np.float32(2.0))
+    rng = np.random.default_rng(5)
+    u = np.where(rng.random((2, 1000)) < 0.5, a, b).astype(np.float32)
+    for rho in (0.1, 0.5, 0.9):
+        log(f"[route] one-ulp keys rho={rho}")
+        run_top_rho(oracle_mod, u, (1, 1, 1000), rho)
 
 
 def test_route_deterministic():

@@ -4,18 +4,26 @@
 // Video Diffusion" (HetA-DiT), §3.2.2 Eqs. 11-12.
 //
 // One 1024-thread workgroup per sample.  The route is computed once per
-// denoising step and shared by every head and every transformer block, so it
-// is latency- rather than bandwidth-bound (u of one sample is at most a few
-// hundred KB and stays in L2 across the passes below).
+// denoising step and shared by every head and every transformer block; u of
+// one sample is at most a few hundred KB, so the kernel is latency-bound and
+// is built to make one coalesced pass over memory in each direction: wave w
+// owns the contiguous range of tokens [w*C, w*C + C), which it reads 64
+// consecutive tokens at a time and keeps in registers (C = 64 * P with
+// P = 8 .. 64, i.e. up to 65536 tokens; larger samples re-read u from memory,
+// where it stays in L2).
 //
-// Top-rho: the K-th largest u is found by a 4-pass MSB-first radix select
-// over order-preserving 32-bit keys (integers only, no rounding).  Tokens
-// with a larger key are dense; of the tokens equal to the K-th key, the first
-// E by index are dense, where E is what the select leaves over.
+// Top-rho: the K-th largest u is found by an MSB-first radix select over
+// order-preserving 32-bit keys (integers only, no rounding).  The bits that
+// every key of the sample shares (the common prefix of the smallest and the
+// largest key) are skipped, so the first histogram already spreads over the
+// sample's range.  Tokens with a larger key are dense; of the tokens equal to
+// the K-th key, the first E by index are dense, where E is what the select
+// leaves over.
 // Mean-std: mu and sigma in fp64 with a fixed reduction order, then
 // dense iff u >= mu + c*sigma.
-// Compaction: tiles of 1024 tokens in index order; a ballot-based block scan
-// gives each token its slot, so both index lists come out ascending.
+// Compaction: ranks inside a wave come from ballots; one exclusive scan of
+// the 16 per-wave counts places the waves, so both index lists come out
+// ascending and every store of a wave goes to consecutive addresses.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,34 +41,11 @@ __device__ __forceinline__ uint32_t rank_key(float x) {
     return (f & 0x80000000u) ? ~f : (f | 0x80000000u);
 }
 
+// Inverse of rank_key on its image: the float a key stands for (NaN was
+// already read as +inf and -0 as +0).
 __device__ __forceinline__ float key_to_float(uint32_t key) {
     uint32_t f = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
     return __uint_as_float(f);
-}
-
-__device__ __forceinline__ double mapped_u(float x) {
-    if (x != x) return __builtin_inf();
-    return (x == 0.0f) ? 0.0 : (double)x;
-}
-
-// Exclusive prefix count of `flag` over the workgroup in thread order; the
-// workgroup total goes to `total`.  Uses s_wave[kRouteWaves].
-__device__ __forceinline__ int block_scan_flag(bool flag, int *s_wave, int &total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint64_t bal = __ballot(flag);
-    const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wave[wave] = __popcll(bal);
-    __syncthreads();
-    int before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < kRouteWaves; ++w) {
-        const int c = s_wave[w];
-        before += (w < wave) ? c : 0;
-        tot += c;
-    }
-    __syncthreads();
-    total = tot;
-    return before + in_wave;
 }
 
 // Sum of one double per thread in a fixed order (butterfly in the wave, then
@@ -78,40 +63,174 @@ __device__ __forceinline__ double block_sum_f64(double x, double *s_part) {
     return t;
 }
 
+// Workgroup min and max of one key per thread.
+__device__ __forceinline__ void block_min_max(uint32_t lo, uint32_t hi, uint32_t *s_w,
+                                              uint32_t &out_lo, uint32_t &out_hi) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+    }
+    if (lane == 0) { s_w[wave] = lo; s_w[kRouteWaves + wave] = hi; }
+    __syncthreads();
+    lo = s_w[0];
+    hi = s_w[kRouteWaves];
+#pragma unroll
+    for (int w = 1; w < kRouteWaves; ++w) {
+        lo = min(lo, s_w[w]);
+        hi = max(hi, s_w[kRouteWaves + w]);
+    }
+    __syncthreads();
+    out_lo = lo;
+    out_hi = hi;
+}
+
+// Calls f(j) for the first `rows` rows of this wave's range, fully unrolled
+// when the range is a compile-time constant (so that keys[j] stays in
+// registers).  `rows` is uniform over the wave.
+template <int kPer, typename F>
+__device__ __forceinline__ void for_rows(int rows, F &&f) {
+    if constexpr (kPer > 0) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (j < rows) f(j);
+    } else {
+        for (int j = 0; j < rows; ++j) f(j);
+    }
+}
+
+// Exclusive prefix sums over the waves of two values per wave (taken from
+// lane 0), in wave order; the workgroup totals go to tx, ty.
+__device__ __forceinline__ void wave_excl_scan2(int x, int y, int *s_wave, int &bx, int &by,
+                                                int &tx, int &ty) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) { s_wave[wave] = x; s_wave[kRouteWaves + wave] = y; }
+    __syncthreads();
+    bx = by = tx = ty = 0;
+#pragma unroll
+    for (int w = 0; w < kRouteWaves; ++w) {
+        const int cx = s_wave[w], cy = s_wave[kRouteWaves + w];
+        bx += (w < wave) ? cx : 0;
+        by += (w < wave) ? cy : 0;
+        tx += cx;
+        ty += cy;
+    }
+    __syncthreads();
+}
+
+// Number of lanes below this one whose bit is set in `bal`.
+__device__ __forceinline__ int lanes_below(uint64_t bal) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
+// Histogram of the radix select: one copy of the 256 bins per lane index, so
+// that the 64 lanes of one atomic never update the same word.  Copy c starts
+// at word 257*c, which puts bin b of copy c in bank (b + c) mod 64: lanes
+// whose keys fall in one bin (neighbouring tokens of a smooth u) also hit 64
+// different banks.
+constexpr int kHistStride = 257;
+constexpr int kHistWords = 64 * kHistStride;
+static_assert(kHistWords % 4 == 0, "the histogram is cleared in 16-byte words");
+
+// kPer > 0: every lane holds kPer keys in registers (N <= 1024 * kPer).
+// kPer == 0: per-wave ranges of ceil(N / 1024) rows of 64, re-read from u.
+template <int kPer>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     const int b = blockIdx.x, tid = threadIdx.x, N = a.n;
+    const int lane = tid & 63, wave = tid >> 6;
     const float *ub = a.u + (size_t)b * N;
-    __shared__ uint32_t hist[256];
-    __shared__ int s_wave[kRouteWaves];
+    __shared__ __attribute__((aligned(16))) uint32_t hcopy[kHistWords];
+    __shared__ uint32_t hpart[4 * 256];
+    __shared__ int s_wave[2 * kRouteWaves];
+    __shared__ uint32_t s_mm[2 * kRouteWaves];
     __shared__ double s_part[kRouteWaves];
     __shared__ int s_sel[2];
 
+    // Row j of this wave is tokens w*C + 64*j + (0..63); `rows` rows hold
+    // tokens below N.  Keys of tokens at or beyond N read as 0, which no
+    // token's key equals (rank_key never returns 0).
+    const int per = kPer > 0 ? kPer : (N + kRouteThreads - 1) / kRouteThreads;
+    const int w0 = wave * per * 64;
+    const int rows = imax(0, imin(per, (N - w0 + 63) >> 6));
+    auto token = [&](int j) HET_INLINE { return w0 + 64 * j + lane; };
+    auto load_key = [&](int j) HET_INLINE -> uint32_t {
+        return (token(j) < N) ? rank_key(ub[token(j)]) : 0u;
+    };
+
     const bool top = (a.mode == 0);
-    uint32_t tkey = 0xffffffffu;  // K = 0: no key is strictly larger, none equal is taken
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    uint32_t keys[kPer > 0 ? kPer : 1];
+    if constexpr (kPer > 0) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            keys[j] = load_key(j);
+            lo = min(lo, keys[j] ? keys[j] : 0xffffffffu);
+            hi = max(hi, keys[j]);
+        }
+    } else if (top) {
+        for (int j = 0; j < rows; ++j) {
+            const uint32_t k = load_key(j);
+            lo = min(lo, k ? k : 0xffffffffu);
+            hi = max(hi, k);
+        }
+    }
+    auto key_at = [&](int j) HET_INLINE -> uint32_t {
+        if constexpr (kPer > 0) return keys[j];
+        else return load_key(j);
+    };
+
+    uint32_t tkey = 0xffffffffu;  // K = 0: no key is larger, none equal is taken
     int take_equal = 0;
     double T = __builtin_inf();
 
     if (top && a.k > 0) {
-        uint32_t prefix = 0, pmask = 0;
+        block_min_max(lo, hi, s_mm, lo, hi);
+        for (int i = tid; i < kHistWords / 4; i += kRouteThreads)
+            reinterpret_cast<u32x4 *>(hcopy)[i] = u32x4{0u, 0u, 0u, 0u};
+        // Bits above `top_bit` are shared by every key of the sample.
+        int top_bit = (lo == hi) ? 0 : 32 - __builtin_clz(lo ^ hi);
+        uint32_t pmask = (top_bit >= 32) ? 0u : ~((1u << top_bit) - 1u);
+        uint32_t prefix = hi & pmask;
         int remaining = a.k;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            if (tid < 256) hist[tid] = 0;
+        uint32_t *my_hist = hcopy + kHistStride * lane;
+        __syncthreads();
+        while (top_bit > 0) {
+            const int width = imin(8, top_bit);
+            const int shift = top_bit - width;
+            const uint32_t dmask = (1u << width) - 1u;
+            for_rows<kPer>(rows, [&](int j) HET_INLINE {
+                const uint32_t k = key_at(j);
+                if (k != 0u && (k & pmask) == prefix) atomicAdd(&my_hist[(k >> shift) & dmask], 1u);
+            });
             __syncthreads();
-            for (int i = tid; i < N; i += kRouteThreads) {
-                const uint32_t key = rank_key(ub[i]);
-                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            {
+                // Thread t sums bin t%256 over copies 16*(t/256) .. +15 and
+                // clears them for the next pass.
+                const int bin = tid & 255, c0 = 16 * (tid >> 8);
+                uint32_t sum = 0;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    sum += hcopy[(c0 + c) * kHistStride + bin];
+                    hcopy[(c0 + c) * kHistStride + bin] = 0u;
+                }
+                hpart[tid] = sum;
             }
             __syncthreads();
             if (tid < 64) {
                 // Wave 0 finds the digit d with count(> d) < remaining <= count(>= d).
                 // Lane l owns digits 255-4l .. 252-4l (descending).
-                int c0 = hist[255 - 4 * tid], c1 = hist[254 - 4 * tid];
-                int c2 = hist[253 - 4 * tid], c3 = hist[252 - 4 * tid];
-                int mine = c0 + c1 + c2 + c3;
-                int incl = mine;  // inclusive scan over lanes (descending digits)
+                auto bin_count = [&](int d) HET_INLINE -> int {
+                    return (int)(hpart[d] + hpart[256 + d] + hpart[512 + d] + hpart[768 + d]);
+                };
+                const int c0 = bin_count(255 - 4 * tid), c1 = bin_count(254 - 4 * tid);
+                const int c2 = bin_count(253 - 4 * tid), c3 = bin_count(252 - 4 * tid);
+                const int mine = c0 + c1 + c2 + c3;
+                int incl = mine;
 #pragma unroll
                 for (int off = 1; off < 64; off <<= 1) {
-                    int y = __shfl_up(incl, off);
+                    const int y = __shfl_up(incl, off);
                     if (tid >= off) incl += y;
                 }
                 const int excl = incl - mine;
@@ -126,54 +245,73 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
             }
             __syncthreads();
             prefix |= (uint32_t)s_sel[0] << shift;
-            pmask |= 255u << shift;
+            pmask |= dmask << shift;
             remaining = s_sel[1];
-            __syncthreads();
+            top_bit = shift;
         }
         tkey = prefix;
         take_equal = remaining;
         T = (double)key_to_float(tkey);
     } else if (!top) {
         double s = 0.0;
-        for (int i = tid; i < N; i += kRouteThreads) s += mapped_u(ub[i]);
+        for_rows<kPer>(rows, [&](int j) HET_INLINE {
+            if (token(j) < N) s += (double)key_to_float(key_at(j));
+        });
         const double mu = block_sum_f64(s, s_part) / (double)N;
         double ss = 0.0;
-        for (int i = tid; i < N; i += kRouteThreads) {
-            const double d = mapped_u(ub[i]) - mu;
-            ss += d * d;
-        }
+        for_rows<kPer>(rows, [&](int j) HET_INLINE {
+            if (token(j) < N) {
+                const double d = (double)key_to_float(key_at(j)) - mu;
+                ss += d * d;
+            }
+        });
         const double sigma = sqrt(block_sum_f64(ss, s_part) / (double)N);
         T = mu + a.c * sigma;
     }
 
+    // Top-rho: token i is dense iff key > tkey, or key == tkey and fewer
+    // than take_equal keys equal to tkey precede it.  Mean-std: iff
+    // !(u < T).  Ballot of the first kind of row j:
+    auto above_row = [&](int j) HET_INLINE -> uint64_t {
+        const uint32_t key = key_at(j);
+        if (top) return __ballot(key > tkey);
+        return __ballot(token(j) < N && !((double)key_to_float(key) < T));
+    };
+    int n_gt = 0, n_eq = 0;
+    for_rows<kPer>(rows, [&](int j) HET_INLINE {
+        n_gt += __popcll(above_row(j));
+        if (top) n_eq += __popcll(__ballot(key_at(j) == tkey));
+    });
+    int gt_before, eq_before, gt_total, eq_total;
+    wave_excl_scan2(n_gt, n_eq, s_wave, gt_before, eq_before, gt_total, eq_total);
+    const int n_dense = gt_total + imin(eq_total, take_equal);
+    int d_seen = gt_before + imin(eq_before, take_equal);
+
     uint8_t *mask = a.mask + (size_t)b * N;
     int32_t *dense_idx = a.dense_idx + (size_t)b * N;
     int32_t *local_idx = a.local_idx + (size_t)b * N;
-    int seen_equal = 0, n_dense = 0;
-    for (int base = 0; base < N; base += kRouteThreads) {
-        const int i = base + tid;
-        const bool in = i < N;
-        const float x = in ? ub[i] : 0.0f;
-        bool dense;
+    int eq_run = eq_before;
+    for_rows<kPer>(rows, [&](int j) HET_INLINE {
+        uint64_t bal = above_row(j);
         if (top) {
-            const uint32_t key = rank_key(x);
-            const bool eq = in && key == tkey;
-            int eq_total;
-            const int eq_rank = seen_equal + block_scan_flag(eq, s_wave, eq_total);
-            seen_equal += eq_total;
-            dense = in && (key > tkey || (eq && eq_rank < take_equal));
-        } else {
-            dense = in && !(mapped_u(x) < T);
+            const uint64_t eq_bal = __ballot(key_at(j) == tkey);
+            if (eq_bal != 0ull) {
+                const bool eq = (eq_bal >> lane) & 1u;
+                bal |= __ballot(eq && eq_run + lanes_below(eq_bal) < take_equal);
+                eq_run += __popcll(eq_bal);
+            }
         }
-        int d_total;
-        const int d_before = n_dense + block_scan_flag(dense, s_wave, d_total);
-        if (in) {
-            mask[i] = dense ? 0 : 1;
-            if (dense) dense_idx[d_before] = i;
-            else local_idx[i - d_before] = i;
+        const int i = token(j);
+        const bool dn = (bal >> lane) & 1u;
+        const int d = d_seen + lanes_below(bal);
+        if (i < N) {
+            mask[i] = dn ? 0 : 1;
+            // One store per row: the dense lanes fill a run of dense_idx, the
+            // others a run of local_idx.
+            *(dn ? dense_idx + d : local_idx + (i - d)) = i;
         }
-        n_dense += d_total;
-    }
+        d_seen += __popcll(bal);
+    });
     for (int i = n_dense + tid; i < N; i += kRouteThreads) dense_idx[i] = -1;
     for (int i = (N - n_dense) + tid; i < N; i += kRouteThreads) local_idx[i] = -1;
     if (tid == 0) {
@@ -184,7 +322,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 }
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(route_kernel, dim3(a.batch), dim3(kRouteThreads), 0, stream, a);
+    const dim3 grid(a.batch), block(kRouteThreads);
+    if (a.n <= 8 * kRouteThreads)
+        hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, stream, a);
+    else if (a.n <= 16 * kRouteThreads)
+        hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, stream, a);
+    else if (a.n <= 32 * kRouteThreads)
+        hipLaunchKernelGGL(route_kernel<32>, grid, block, 0, stream, a);
+    else if (a.n <= 64 * kRouteThreads)
+        hipLaunchKernelGGL(route_kernel<64>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(route_kernel<0>, grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
