@@ -91,7 +91,9 @@ typedef struct {
     int32_t *local_idx;  /* [B, N]: local tokens ascending, then -1 */
     int32_t *counts;     /* [B, 2]: (dense count, local count) per sample */
     double *thresh;      /* [B]: T_b (TOP_RHO: u of the K-th ranked token, +inf if K = 0) */
-    int32_t dense_count_host; /* set by het_attn_route: K in TOP_RHO mode, -1 in MEAN_STD mode */
+    int32_t dense_count_host; /* set by het_attn_route: K in TOP_RHO mode, -1 in MEAN_STD mode;
+                               * when >= 0 the attention calls size their launches by it, so
+                               * it must equal every sample's dense count */
 } het_route;
 
 /* HETATTN_ABI_VERSION of the loaded library. */

@@ -156,6 +156,7 @@ int run_attention(const het_attn_shape *shape, const void *q, const void *k, con
     a.bf16 = shape->dtype == HET_BF16;
     a.scale = scale;
     a.max_dense = route->dense_count_host >= 0 ? route->dense_count_host : (int)d.N;
+    a.dense_exact = route->dense_count_host >= 0;
     a.workspace = workspace;
     a.cu_count = cus;
 

@@ -64,20 +64,22 @@ struct DenseBf16Geom {
 
 // ------------------------------------------------------ stream-K schedule --
 // The dense work is the list of units (sample, head, 256-query tile), each a
-// sequence of n_kt key tiles; flattened unit-major it has W = units * n_kt
-// items.  The grid is persistent (one workgroup per CU) and workgroup w takes
-// items [w*W/G, (w+1)*W/G): every CU gets the same amount of work, so there is
-// no partially filled last wave of tiles.  A unit cut between workgroups is
-// finished in pieces: every piece stores its partial state (unnormalised O,
-// reference max m, row sum l, fp32) in the workspace and bumps the unit's
-// counter; the piece that brings the counter to the number of pieces merges
-// them (O = sum 2^(m_s - m) O_s, l = sum 2^(m_s - m) l_s), writes the output
-// and resets the counter.  No workgroup ever waits for another.
+// sequence of n_kt key tiles.  The grid is persistent (one workgroup per CU,
+// G of them).  Whole units go first, round-robin; the units_sk = units mod G
+// left over are flattened unit-major into W = units_sk * n_kt items and
+// workgroup w takes items [w*W/G, (w+1)*W/G), so every CU gets the same
+// amount of work.  A unit cut between workgroups is finished in pieces: each
+// piece stores its partial state (unnormalised O, reference max m, row sum l,
+// fp32) in the workspace, and a second kernel merges the pieces of every
+// split unit (O = sum 2^(m_s - m) O_s, l = sum 2^(m_s - m) l_s) in workgroup
+// order and writes the output.  The kernel boundary orders the two, so no
+// workgroup waits for another and no device-scope fence (which on this chip
+// writes back a whole L2) is needed inside the persistent kernel.
 //
 // Workspace: [2G slots][kDenseBM16 queries][D] O partials (each lane's
 // accumulators contiguous, in register order), then [2G][2][kDenseBM16]
-// (m, l), then one int counter per unit (zeroed before the launch).  Slot 2w
-// holds the piece of workgroup w's first unit, slot 2w+1 that of its last.
+// (m, l).  Slot 2w holds the piece of workgroup w's first unit, slot 2w+1
+// that of its last.
 __device__ __forceinline__ int64_t work_begin(int64_t W, int G, int w) { return (int64_t)w * W / G; }
 // Workgroup owning item x: the largest w with work_begin(w) <= x.
 __device__ __forceinline__ int work_owner(int64_t W, int G, int64_t x) {
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const int32_t *__restrict__ dense_idx,
     const int32_t *__restrict__ counts, int B, int N, int H, float scale_log2, int G,
-    float *__restrict__ ws_part, int32_t *__restrict__ ws_count) {
+    float *__restrict__ ws_part) {
     using Gm = DenseBf16Geom<D>;
     constexpr int BN = Gm::BN;
     constexpr int BM = kDenseBM16;
@@ -101,7 +103,6 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) __bf16 K1[Gm::kTileElems];
     __shared__ __attribute__((aligned(1024))) __bf16 V0[Gm::kTileElems];
     __shared__ __attribute__((aligned(1024))) __bf16 V1[Gm::kTileElems];
-    __shared__ int s_flag;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = wave >> 2;  // ping-pong group
@@ -412,56 +413,87 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
                 part_ml[BM + qi] = l_tot;
             }
         }
-        __threadfence();
         __syncthreads();
-        // The pieces of this unit come from the non-empty workgroups owning its
-        // items (with fewer items than workgroups some ranges are empty).
-        const int64_t ux0 = (int64_t)(unit - units_dp) * n_kt, ux1 = ux0 + n_kt - 1;
-        const int w_first = work_owner(W, G, ux0), w_last = work_owner(W, G, ux1);
-        int n_pieces = 0;
-        for (int pw = w_first; pw <= w_last; ++pw) n_pieces += work_begin(W, G, pw + 1) > work_begin(W, G, pw);
-        if (tid == 0) s_flag = (atomicAdd(&ws_count[unit], 1) == n_pieces - 1);
-        __syncthreads();
-        if (!s_flag) continue;
-
-        // ---- last piece to finish: merge every piece of this unit.  Every
-        // piece, this workgroup's own included, is read back from the
-        // workspace and summed in workgroup order, so the result does not
-        // depend on which piece finished last.
-        __threadfence();
-        float m_all = -__builtin_inff();
-        for (int pw = w_first; pw <= w_last; ++pw) {
-            if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
-            const int ps = 2 * pw + (unit == units_dp + (int)(work_begin(W, G, pw) / n_kt) ? 0 : 1);
-            const float *pml = ws_part + (size_t)2 * G * slot_elems + (size_t)ps * 2 * BM;
-            m_all = fmaxf(m_all, __builtin_nontemporal_load(pml + qi));
-        }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-        float l_all = 0.0f;
-        for (int pw = w_first; pw <= w_last; ++pw) {
-            if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
-            const int ps = 2 * pw + (unit == units_dp + (int)(work_begin(W, G, pw) / n_kt) ? 0 : 1);
-            const f32x4 *po = (const f32x4 *)(ws_part + (size_t)ps * slot_elems + (size_t)qi * D + (size_t)half * (D / 2));
-            const float *pml = ws_part + (size_t)2 * G * slot_elems + (size_t)ps * 2 * BM;
-            const float a = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(pml + qi) - m_all);
-            l_all += a * __builtin_nontemporal_load(pml + BM + qi);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const f32x4 pvv = __builtin_nontemporal_load(po + db * 4 + i4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) oacc[db][4 * i4 + e] += a * pvv[e];
-                }
-        }
-        store_out(1.0f / l_all);
-        if (tid == 0) ws_count[unit] = 0;  // ready for the next launch
     }
 }
 
-__global__ void zero_i32_kernel(int32_t *p, int n) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+// Partial layout helper shared by the persistent kernel and the merge: the
+// piece slot of workgroup pw for split unit `unit`.
+__device__ __forceinline__ int piece_slot(int64_t W, int G, int n_kt, int units_dp, int unit, int pw) {
+    return 2 * pw + (unit == units_dp + (int)(work_begin(W, G, pw) / n_kt) ? 0 : 1);
+}
+
+// Merge of the split units.  Workgroup = (split unit, kMergeQ queries);
+// thread = (query, 16 consecutive partial floats of it).  Partial float
+// half*(D/2) + 16*db + 4*i4 + e of a query holds output column
+// 32*db + 8*i4 + 4*half + e (the accumulator order of the MFMA C layout).
+template <int D>
+__global__ __launch_bounds__(256) void dense_merge_kernel(
+    __bf16 *__restrict__ o, const int32_t *__restrict__ dense_idx, const int32_t *__restrict__ counts,
+    int B, int N, int H, int G, const float *__restrict__ ws_part) {
+    constexpr int BM = kDenseBM16;
+    constexpr int kSlices = D / 16;
+    constexpr int kMergeQ = 256 / kSlices;
+    constexpr int NDB = D / 32;
+    const int n_kt = (N + DenseBf16Geom<D>::BN - 1) / DenseBf16Geom<D>::BN;
+    int units = 0;
+    for (int bb = 0; bb < B; ++bb) units += H * ((counts[2 * bb] + BM - 1) / BM);
+    const int units_dp = units / G * G, units_sk = units - units_dp;
+    const int sk = blockIdx.x / (BM / kMergeQ);
+    if (sk >= units_sk) return;
+    const int unit = units_dp + sk;
+    int b = 0, rem = unit, tiles_b = 0;
+    for (;;) {
+        tiles_b = (counts[2 * b] + BM - 1) / BM;
+        if (rem < H * tiles_b) break;
+        rem -= H * tiles_b;
+        ++b;
+    }
+    const int h = rem / tiles_b, tile = rem % tiles_b;
+    const int qi = (blockIdx.x % (BM / kMergeQ)) * kMergeQ + (int)threadIdx.x / kSlices;
+    const int slice = (int)threadIdx.x % kSlices;
+    const int qrow = tile * BM + qi;
+    if (qrow >= counts[2 * b]) return;
+
+    const int64_t W = (int64_t)units_sk * n_kt;
+    const int64_t ux0 = (int64_t)sk * n_kt, ux1 = ux0 + n_kt - 1;
+    const int w_first = work_owner(W, G, ux0), w_last = work_owner(W, G, ux1);
+    if (w_first == w_last) return;  // one workgroup ran the whole unit and stored it
+    const size_t slot_elems = (size_t)D * BM;
+    const float *ml = ws_part + (size_t)2 * G * slot_elems;
+    // Pieces come from the non-empty workgroups owning the unit's items.
+    float m_all = -__builtin_inff();
+    for (int pw = w_first; pw <= w_last; ++pw) {
+        if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
+        const int ps = piece_slot(W, G, n_kt, units_dp, unit, pw);
+        m_all = fmaxf(m_all, ml[(size_t)ps * 2 * BM + qi]);
+    }
+    f32x4 acc[4] = {};
+    float l_all = 0.0f;
+    for (int pw = w_first; pw <= w_last; ++pw) {
+        if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
+        const int ps = piece_slot(W, G, n_kt, units_dp, unit, pw);
+        const float a = __builtin_amdgcn_exp2f(ml[(size_t)ps * 2 * BM + qi] - m_all);
+        l_all += a * ml[(size_t)ps * 2 * BM + BM + qi];
+        const f32x4 *po = (const f32x4 *)(ws_part + (size_t)ps * slot_elems + (size_t)qi * D + 16 * slice);
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 pv = po[i4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i4][e] += a * pv[e];
+        }
+    }
+    const float inv_l = 1.0f / l_all;
+    const int half = slice / NDB, db = slice % NDB;
+    const int tok = dense_idx[(size_t)b * N + qrow];
+    __bf16 *op = o + ((size_t)b * N + tok) * ((size_t)H * D) + (size_t)h * D;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+        u32x2 wv;
+        wv[0] = pack_bf16x2(acc[i4][0] * inv_l, acc[i4][1] * inv_l);
+        wv[1] = pack_bf16x2(acc[i4][2] * inv_l, acc[i4][3] * inv_l);
+        *(u32x2 *)(op + 32 * db + 8 * i4 + 4 * half) = wv;
+    }
 }
 
 // The f32 path below uses kDenseBM queries per workgroup and a plain grid.
@@ -612,8 +644,10 @@ int dense_persistent_groups(int cu_count) { return cu_count; }
 size_t dense_workspace_bytes(int batch, int heads, int n, int head_dim, bool bf16, int cu_count) {
     if (!bf16) return 0;
     const size_t G = (size_t)dense_persistent_groups(cu_count);
-    const size_t units = (size_t)batch * heads * ((n + kDenseBM16 - 1) / kDenseBM16);
-    return 2 * G * ((size_t)head_dim * kDenseBM16 + 2 * kDenseBM16) * sizeof(float) + units * sizeof(int32_t);
+    (void)batch;
+    (void)heads;
+    (void)n;
+    return 2 * G * ((size_t)head_dim * kDenseBM16 + 2 * kDenseBM16) * sizeof(float);
 }
 
 hipError_t launch_dense(const AttnArgs &a, hipStream_t stream) {
@@ -624,18 +658,27 @@ hipError_t launch_dense(const AttnArgs &a, hipStream_t stream) {
         auto o = (__bf16 *)a.o;
         const int G = dense_persistent_groups(a.cu_count);
         float *ws_part = (float *)a.workspace;
-        int32_t *ws_count = (int32_t *)((char *)a.workspace +
-                                        2 * (size_t)G * ((size_t)a.head_dim * kDenseBM16 + 2 * kDenseBM16) * sizeof(float));
-        const int units_max = a.batch * a.heads * ((a.n + kDenseBM16 - 1) / kDenseBM16);
-        hipLaunchKernelGGL(zero_i32_kernel, dim3((units_max + 255) / 256), dim3(256), 0, stream, ws_count,
-                           units_max);
         const dim3 g1d((G + 7) / 8 * 8);
-        if (a.head_dim == 128)
+        // Split units: units mod G.  Exact when the host knows the dense count
+        // (top-rho gives every sample the same count), else at most G - 1; the
+        // merge workgroups past the device-side count return at once.
+        const int units_ub = a.batch * a.heads * ((a.max_dense + kDenseBM16 - 1) / kDenseBM16);
+        const int units_sk_ub = a.dense_exact ? units_ub % G : (units_ub < G ? units_ub : G - 1);
+        const int merge_q = 256 / (a.head_dim / 16);
+        const dim3 gm((unsigned)units_sk_ub * (kDenseBM16 / merge_q));
+        if (a.head_dim == 128) {
             hipLaunchKernelGGL(dense_bf16_kernel<128>, g1d, dim3(kDenseThreads16), 0, stream, q, k, v, o,
-                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, ws_count);
-        else
+                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part);
+            if (units_sk_ub > 0)
+                hipLaunchKernelGGL(dense_merge_kernel<128>, gm, dim3(256), 0, stream, o, a.dense_idx, a.counts,
+                                   a.batch, a.n, a.heads, G, (const float *)ws_part);
+        } else {
             hipLaunchKernelGGL(dense_bf16_kernel<64>, g1d, dim3(kDenseThreads16), 0, stream, q, k, v, o,
-                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, ws_count);
+                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part);
+            if (units_sk_ub > 0)
+                hipLaunchKernelGGL(dense_merge_kernel<64>, gm, dim3(256), 0, stream, o, a.dense_idx, a.counts,
+                                   a.batch, a.n, a.heads, G, (const float *)ws_part);
+        }
     } else {
         const dim3 grid((a.max_dense + kDenseBM - 1) / kDenseBM, a.heads, a.batch);
         auto q = (const float *)a.q, k = (const float *)a.k, v = (const float *)a.v;

@@ -29,6 +29,7 @@ struct AttnArgs {
     bool bf16;
     float scale;               // softmax scale (> 0)
     int max_dense;             // upper bound on any sample's dense count
+    bool dense_exact;          // every sample has exactly max_dense dense tokens
     void *workspace;           // dense_workspace_bytes() bytes of device memory
     int cu_count;              // compute units of the device the launch runs on
 };
@@ -36,7 +37,7 @@ struct AttnArgs {
 // Largest effective window along w that the local kernel's key tiling holds.
 constexpr int kLocalMaxWinW = 25;
 
-// Device workspace of the dense kernel's stream-K merge (partials + counters).
+// Device workspace of the dense kernel's stream-K pieces (fp32 partials).
 size_t dense_workspace_bytes(int batch, int heads, int n, int head_dim, bool bf16, int cu_count);
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t stream);
