@@ -37,6 +37,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+    # A kernel whose host-side stub the compiler did not emit leaves an
+    # undefined __device_stub__ symbol, which only fails when the library is
+    # loaded; refuse such a build here.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    if nm.returncode != 0 or missing:
+        os.remove(tmp)
+        raise RuntimeError("kernel stubs missing from the host pass: " + ", ".join(missing or [nm.stderr]))
     os.replace(tmp, LIB)
     return LIB
 

@@ -52,6 +52,20 @@ __device__ __forceinline__ int swz(int row) {
     else return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);              // 8 chunks, 2 rows per 256 B
 }
 
+// Word 3 of a raw buffer descriptor (gfx9 family: 32-bit data format, no
+// swizzle); out-of-range loads return zeros.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// 16 bytes per lane from base + voff (bytes) into LDS (each wave writes one
+// contiguous run from lds, lane l at 16*l).  Bytes at or past `bytes` from
+// base read as zero.  base and bytes must be wave-uniform.
+__device__ __forceinline__ void buffer_load_lds16(const void *base, uint32_t bytes, HET_LDS void *lds,
+                                                  int voff) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferRsrcWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 0, 0);
+}
+
 template <int D>
 struct DenseBf16Geom {
     static constexpr int BN = 64;                  // keys per tile
@@ -129,14 +143,15 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
 
     // DMA geometry: load j of this wave fills tile rows from r0_j on; this
     // lane writes row r0_j + lane/kCpr at chunk position lane%kCpr, so it
-    // fetches the chunk that the swizzle puts there.  Full tiles address as
-    // a wave-uniform row base plus a per-lane 32-bit offset.
+    // fetches the chunk that the swizzle puts there.  The loads go through a
+    // buffer descriptor whose base is the tile's first key row (scalar, per
+    // tile), so each lane's byte offset inside the tile is fixed.
     const int dma_lrow = lane / Gm::kCpr, dma_pos = lane % Gm::kCpr;
-    int dma_lane_off[Gm::kLoadsPerWave];
+    int dma_voff[Gm::kLoadsPerWave];
 #pragma unroll
     for (int j = 0; j < Gm::kLoadsPerWave; ++j) {
         const int r = (wave * Gm::kLoadsPerWave + j) * Gm::kRowsPerLoad + dma_lrow;
-        dma_lane_off[j] = dma_lrow * tok_stride + 8 * (dma_pos ^ swz<D>(r));
+        dma_voff[j] = 2 * (r * tok_stride + 8 * (dma_pos ^ swz<D>(r)));
     }
     // Transposed V read: lane j16 of each 16-lane group points at tile row
     // base + 4*half + j16/4, element column 16*(g16&1) + 4*(j16&3) of a
@@ -201,25 +216,18 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
             for (int c = 0; c < NC; ++c) qf[c] = q_valid ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
         }
 
+        // K or V tile kt -> LDS.  The descriptor covers the rows below N only:
+        // a buffer load past its range returns zeros, so the ragged last tile
+        // needs no special addressing (its extra keys are masked and their V
+        // rows are zero).
         auto dma = [&](const __bf16 *src, __bf16 *dst, int kt) HET_INLINE {
             const int key0 = kt * BN;
-            if (key0 + BN <= N) {
+            const uint32_t bytes = (uint32_t)((N - key0) * tok_stride) * 2u;
+            const __bf16 *base = src + (size_t)key0 * tok_stride;
 #pragma unroll
-                for (int j = 0; j < Gm::kLoadsPerWave; ++j) {
-                    const int r0 = (wave * Gm::kLoadsPerWave + j) * Gm::kRowsPerLoad;
-                    const __bf16 *row_base = src + (size_t)(key0 + r0) * tok_stride;
-                    __builtin_amdgcn_global_load_lds((const void *)(row_base + dma_lane_off[j]),
-                                                     (HET_LDS void *)(dst + r0 * D), 16, 0, 0);
-                }
-            } else {  // last, ragged tile: rows past N repeat key N-1 (their scores are masked)
-#pragma unroll
-                for (int j = 0; j < Gm::kLoadsPerWave; ++j) {
-                    const int r0 = (wave * Gm::kLoadsPerWave + j) * Gm::kRowsPerLoad;
-                    const int r = r0 + dma_lrow;
-                    const int key = imin(key0 + r, N - 1);
-                    const __bf16 *gp = src + (size_t)key * tok_stride + 8 * (dma_pos ^ swz<D>(r));
-                    __builtin_amdgcn_global_load_lds((const void *)gp, (HET_LDS void *)(dst + r0 * D), 16, 0, 0);
-                }
+            for (int j = 0; j < Gm::kLoadsPerWave; ++j) {
+                const int r0 = (wave * Gm::kLoadsPerWave + j) * Gm::kRowsPerLoad;
+                buffer_load_lds16(base, bytes, (HET_LDS void *)(dst + r0 * D), dma_voff[j]);
             }
         };
 
