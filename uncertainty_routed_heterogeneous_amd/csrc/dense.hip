@@ -209,12 +209,27 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         const int qrow = tile * BM + wave * 32 + col;
         const bool q_valid = qrow < n_dense;
         const int tok = q_valid ? dense_idx[(size_t)b * N + qrow] : 0;
+        // The query enters the MFMA pre-multiplied by scale*log2(e) (rounded
+        // to bf16), so that S comes out in the base-2 units of the softmax.
         bf16x8 qf[NC];
         {
             const __bf16 *qp = q + ((size_t)b * N + tok) * tok_stride + (size_t)h * D + 8 * half;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) qf[c] = q_valid ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
+            for (int c = 0; c < NC; ++c) {
+                const bf16x8 raw = q_valid ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = pack_bf16x2((float)raw[2 * e] * scale_log2, (float)raw[2 * e + 1] * scale_log2);
+                qf[c] = __builtin_bit_cast(bf16x8, w);
+            }
         }
+        // One more k-step of the QK product adds -m_ref to every score: A is 1
+        // at k = 0 (every key row), B is -m_ref at k = 0 (this lane's query).
+        // m_ref is kept bf16-representable, so the term is exact; the first
+        // tile of a piece runs against reference 0.
+        bf16x8 ones_a = {}, neg_m_b = {};
+        if (half == 0) ones_a[0] = (__bf16)1.0f;
 
         // K or V tile kt -> LDS.  The descriptor covers the rows below N only:
         // a buffer load past its range returns zeros, so the ragged last tile
@@ -262,8 +277,8 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
             constexpr int i0 = kPv ? 0 : kPvSteps, i1 = kQk ? kPvSteps + kQkSteps : kPvSteps;
             if constexpr (i0 < i1) {
                 if constexpr (kQk) {
-                    sc[0] = f32x16{};
-                    sc[1] = f32x16{};
+                    sc[0] = mfma32_bf16(ones_a, neg_m_b, f32x16{});
+                    sc[1] = mfma32_bf16(ones_a, neg_m_b, f32x16{});
                 }
                 bf16x8 ring[kAhead];
 #pragma unroll
@@ -298,22 +313,29 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
                         sc[kbk][i] = key_off < lim ? sc[kbk][i] : -__builtin_inff();
                     }
             }
+            // Scores are already relative to the reference (base 2).
             float mx = -__builtin_inff();
 #pragma unroll
             for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kbk][i]);
-            mx = half_pair_max(mx) * scale_log2;
-            const bool grow = mx > m_ref + kRescaleSlack;
+            mx = half_pair_max(mx);
+            const bool first = m_ref == -__builtin_inff();  // first tile of the piece
+            const bool grow = first || mx > kRescaleSlack;
             if (__builtin_expect(__any(grow), 0)) {
-                const float m_new = grow ? mx : m_ref;
-                const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+                // The new reference (bf16-representable) and how far it moved.
+                const float m_base = first ? 0.0f : m_ref;
+                const float m_new = grow ? (float)(__bf16)(m_base + mx) : m_base;
+                const float delta = m_new - m_base;
+                const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-delta);
                 m_ref = m_new;
                 l_part *= alpha;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+#pragma unroll
+                for (int kbk = 0; kbk < 2; ++kbk) sc[kbk] -= delta;
+                if (half == 0) neg_m_b[0] = (__bf16)(-m_ref);
             }
-            const float neg_m = -m_ref;
             // chunk c2 of key block kb = registers 8*c2 .. 8*c2+7, i.e. keys
             // 16*c2 + 8(j/4) + 4*half + j%4 (j < 8) of the block.
 #pragma unroll
@@ -323,8 +345,8 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
                     u32x4 wv;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][8 * c2 + 2 * j], scale_log2, neg_m));
-                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][8 * c2 + 2 * j + 1], scale_log2, neg_m));
+                        const float p0 = __builtin_amdgcn_exp2f(sc[kbk][8 * c2 + 2 * j]);
+                        const float p1 = __builtin_amdgcn_exp2f(sc[kbk][8 * c2 + 2 * j + 1]);
                         l_part += p0 + p1;
                         wv[j] = pack_bf16x2(p0, p1);
                     }
