@@ -93,6 +93,31 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
     return (bid & 7) * per_xcd + (bid >> 3);
 }
 
+// Word 3 of a raw buffer descriptor (gfx9 family: 32-bit data format, no
+// swizzle); out-of-range loads return zeros.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// 16 bytes per lane from base + voff (bytes) into LDS (each wave writes one
+// contiguous 1 KB run from lds, lane l at 16*l).  Bytes at or past `bytes`
+// from base read as zero.  base, bytes and lds must be wave-uniform.
+__device__ __forceinline__ void buffer_load_lds16(const void *base, uint32_t bytes, HET_LDS void *lds,
+                                                  int voff) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferRsrcWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 0, 0);
+}
+
+// XOR swizzle of the 16-byte chunks of a bf16 row of D elements held in LDS
+// (rows unpadded): chunk c of row r is stored at chunk c ^ swz<D>(r).  The
+// LDS has 64 banks of 4 bytes; with this swizzle a 16-lane ds_read_b128 of 16
+// consecutive rows at one chunk, and a 32-lane transposed read of 4
+// consecutive rows x 4 consecutive chunks, both touch every bank once.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);  // 16 chunks per row
+    else return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);              // 8 chunks, 2 rows per 256 B
+}
+
 // Window start along one axis (shifted inside the grid), see hetattn.h.
 __device__ __forceinline__ int window_start(int pos, int k, int len, int S) {
     int s = pos - (k - 1) / 2;

@@ -32,40 +32,17 @@ constexpr int kDenseThreads16 = 512;  // bf16 path: 8 waves
 constexpr int kDenseBM16 = 256;       // bf16 path: queries per workgroup
 
 // ---------------------------------------------------------------- bf16 ----
-// K and V tiles move global -> LDS by DMA (global_load_lds_dwordx4: each wave
-// writes one contiguous 1 KB run, lane l at byte 16*l), double-buffered in
-// four separate LDS arrays so that reads of one buffer never wait on DMA into
-// another.  Rows are unpadded; the 16-byte chunk c of key row r is stored at
-// chunk c ^ swz<D>(r).  The LDS has 64 banks of 4 bytes (256 B per cycle):
-// a 16-lane ds_read_b128 of 16 consecutive rows at one chunk (K, A operand)
-// and a 32-lane transposed read of 4 consecutive rows x 4 consecutive chunks
-// (V) then both touch every bank exactly once.
+// K and V tiles move global -> LDS by DMA (buffer_load_dwordx4 ... lds: each
+// wave writes one contiguous 1 KB run, lane l at byte 16*l), double-buffered
+// in four separate LDS arrays so that reads of one buffer never wait on DMA
+// into another.  Rows are unpadded and chunk-swizzled (swz<D>), so the K
+// reads (A operand) and the transposed V reads are free of bank conflicts.
 //
 // Per iteration kt (one barrier):
 //   wait for own DMA, barrier      K(kt+1), V(kt) now in LDS; previous reads done
 //   DMA K(kt+2), V(kt+1)           into the buffers freed by the barrier
 //   S(kt+1) = K(kt+1) Q^T  ||  P(kt) = exp2(S(kt) - m)
 //   O^T += V(kt)^T P^T     ||  row max of S(kt+1)
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-    if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);  // 16 chunks per row
-    else return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);              // 8 chunks, 2 rows per 256 B
-}
-
-// Word 3 of a raw buffer descriptor (gfx9 family: 32-bit data format, no
-// swizzle); out-of-range loads return zeros.
-constexpr int kBufferRsrcWord3 = 0x00020000;
-
-// 16 bytes per lane from base + voff (bytes) into LDS (each wave writes one
-// contiguous run from lds, lane l at 16*l).  Bytes at or past `bytes` from
-// base read as zero.  base and bytes must be wave-uniform.
-__device__ __forceinline__ void buffer_load_lds16(const void *base, uint32_t bytes, HET_LDS void *lds,
-                                                  int voff) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferRsrcWord3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 0, 0);
-}
-
 template <int D>
 struct DenseBf16Geom {
     static constexpr int BN = 64;                  // keys per tile
@@ -261,13 +238,13 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         constexpr int kPvSteps = 4 * NDB, kQkSteps = 2 * NC, kAhead = 6;
         auto a_operand = [&](int i, const __bf16 *Vt, const __bf16 *Kt) HET_INLINE -> bf16x8 {
             if (i < kPvSteps) {
-                const int db = i >> 2, kbk = (i >> 1) & 1, c2 = i & 1;
+                const int db = i % NDB, kbk = (i / NDB) >> 1, c2 = (i / NDB) & 1;
                 const __bf16 *base = Vt + (kbk * 32 + 16 * c2) * D;
                 const bf16x4 lo = lds_read_tr16((const HET_LDS void *)(base + v_off[db][0]));
                 const bf16x4 hi = lds_read_tr16((const HET_LDS void *)(base + v_off[db][1]));
                 return concat8(lo, hi);
             }
-            const int j = i - kPvSteps, kbk = j / NC, c = j % NC;
+            const int j = i - kPvSteps, kbk = j & 1, c = j >> 1;
             return *(const HET_LDS bf16x8 *)(Kt + kbk * 32 * D + k_off[c]);
         };
         // pv_tag/qk_tag are std::integral_constant<bool, ...>: every index below
@@ -289,10 +266,10 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
                 for (int i = i0; i < i1; ++i) {
                     const bf16x8 a = ring[(i - i0) % kAhead];
                     if (i < kPvSteps) {
-                        const int db = i >> 2, kbk = (i >> 1) & 1, c2 = i & 1;
+                        const int db = i % NDB, kbk = (i / NDB) >> 1, c2 = (i / NDB) & 1;
                         oacc[db] = mfma32_bf16(a, pf[kbk][c2], oacc[db]);
                     } else {
-                        const int j = i - kPvSteps, kbk = j / NC, c = j % NC;
+                        const int j = i - kPvSteps, kbk = j & 1, c = j >> 1;
                         sc[kbk] = mfma32_bf16(a, qf[c], sc[kbk]);
                     }
                     if (i + kAhead < i1) ring[(i - i0) % kAhead] = a_operand(i + kAhead, Vt, Kt);

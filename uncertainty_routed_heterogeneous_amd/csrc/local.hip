@@ -277,6 +277,272 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
     }
 }
 
+// ------------------------------------------------------------ bf16 path ----
+// One workgroup = kBandWaves waves = 2 query frames (t, t+1) x kBandNW
+// x-tiles of 4 (h) x 8 (w) queries, all on the rows ybase .. ybase+3.  The
+// tiles of a workgroup share one key box: the frames [F0, F1) that the two
+// frames' windows cover x ny rows x C columns (the union of the tiles' column
+// windows).  The box goes through LDS in bands of rpb = 32/SR rows of one
+// frame (one MFMA key block per wave and band), double-buffered: the DMA of
+// band i+1 runs while the waves work on band i.  Every K/V row of the box is
+// read from L2 once per workgroup instead of once per tile.  A wave takes
+// from each band the SR columns of its own tile's box (clamped at the edge of
+// the workgroup box; such slots are masked) and skips bands outside its
+// frame's window.
+constexpr int kBandNW = 4;
+constexpr int kBandWaves = 2 * kBandNW;
+
+template <int D, int SR>
+struct BandGeom {
+    static constexpr int rpb = 32 / SR;                          // box rows per band
+    static constexpr int kCpr = D / 8;                           // 16-byte chunks per token row
+    static constexpr int kTokPerLoad = 64 / kCpr;                // token rows per wave DMA (1 KB)
+    static constexpr int kMaxLw = SR == 16 ? 16 - kLocalQX + 1 : kLocalMaxWinW;
+    // LDS rows per box row: the widest workgroup box, in whole DMA loads.
+    static constexpr int kCb = (kBandNW * kLocalQX + kMaxLw - 1 + kTokPerLoad - 1) / kTokPerLoad * kTokPerLoad;
+    static constexpr int kBandRows = rpb * kCb;
+    static constexpr int kLoads = kBandRows / kTokPerLoad;      // DMA loads per tensor and band
+    static constexpr int kLoadsPerWave = (kLoads + kBandWaves - 1) / kBandWaves;
+    static constexpr int kBufElems = kBandRows * D;              // one tensor, one buffer
+};
+
+
+template <int D, int SR>
+__global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    __bf16 *__restrict__ o, const uint8_t *__restrict__ mask, int N, int H, float scale_log2, LocalGeom g,
+    int n_units, int x_blocks, int t_pairs) {
+    using Bg = BandGeom<D, SR>;
+    constexpr int rpb = Bg::rpb, NC = D / 16, NDB = D / 32;
+    __shared__ __attribute__((aligned(1024))) __bf16 Kb0[Bg::kBufElems];
+    __shared__ __attribute__((aligned(1024))) __bf16 Kb1[Bg::kBufElems];
+    __shared__ __attribute__((aligned(1024))) __bf16 Vb0[Bg::kBufElems];
+    __shared__ __attribute__((aligned(1024))) __bf16 Vb1[Bg::kBufElems];
+
+    const int unit = xcd_remap(blockIdx.x, gridDim.x);
+    if (unit >= n_units) return;  // the whole workgroup
+    int rest = unit;
+    const int xb = rest % x_blocks;
+    rest /= x_blocks;
+    const int ty = rest % g.tiles_y;
+    rest /= g.tiles_y;
+    const int tp = rest % t_pairs;
+    rest /= t_pairs;
+    const int h = rest % H, b = rest / H;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int half = lane >> 5, col = lane & 31;
+    const int gq = lane >> 4, j16 = lane & 15;
+
+    // Workgroup box (uniform).
+    const int ybase = ty * kLocalQY;
+    const int uy0 = window_start(ybase, g.wh, g.lh, g.Hg);
+    const int ny = window_start(imin(ybase + kLocalQY - 1, g.Hg - 1), g.wh, g.lh, g.Hg) + g.lh - uy0;
+    const int xt0 = xb * kBandNW, xt1 = imin(xt0 + kBandNW, g.tiles_x) - 1;
+    const int ux0 = window_start(xt0 * kLocalQX, g.ww, g.lw, g.Wg);
+    const int C = window_start(imin(xt1 * kLocalQX + kLocalQX - 1, g.Wg - 1), g.ww, g.lw, g.Wg) + g.lw - ux0;
+    const int tA = 2 * tp, tB = imin(tA + 1, g.T - 1);
+    const int F0 = window_start(tA, g.wt, g.lt, g.T);
+    const int F1 = window_start(tB, g.wt, g.lt, g.T) + g.lt;
+    const int nb_f = (ny + rpb - 1) / rpb;
+    const int n_bands = (F1 - F0) * nb_f;
+
+    // This wave's tile and this lane's query.
+    const int xt = xt0 + wave % kBandNW;
+    const int t = tA + wave / kBandNW;
+    const bool wave_on = t < g.T && xt < g.tiles_x;
+    const int xbase = xt * kLocalQX;
+    const int y = ybase + col / kLocalQX, x = xbase + col % kLocalQX;
+    const bool in_grid = wave_on && y < g.Hg && x < g.Wg;
+    const int tok = in_grid ? (t * g.Hg + y) * g.Wg + x : 0;
+    const bool is_local = in_grid && mask[(size_t)b * N + tok] != 0;
+    const bool active = __any(is_local);
+    const int t0 = window_start(imin(t, g.T - 1), g.wt, g.lt, g.T);
+    const int qy0 = window_start(imin(y, g.Hg - 1), g.wh, g.lh, g.Hg);
+    const int qx0 = window_start(imin(x, g.Wg - 1), g.ww, g.lw, g.Wg);
+    const int uxw = window_start(imin(xbase, g.Wg - 1), g.ww, g.lw, g.Wg);
+    const int nxw = window_start(imin(xbase + kLocalQX - 1, g.Wg - 1), g.ww, g.lw, g.Wg) + g.lw - uxw;
+    const int cw = uxw - ux0;  // this tile's box inside the workgroup box
+
+    const size_t tok_stride = (size_t)H * D;
+    bf16x8 qf[NC];
+    {
+        const __bf16 *qp = q + ((size_t)b * N + tok) * tok_stride + (size_t)h * D + 8 * half;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qf[c] = is_local ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
+    }
+
+    // LDS row of key slot s (0..31) of this wave's block: box row s/SR of the
+    // band, column cw + s%SR, clamped to the box.
+    auto band_row = [&](int s) HET_INLINE -> int {
+        const int rr = s / SR, cc = s % SR;
+        return rr * Bg::kCb + imin(cw + cc, C - 1);
+    };
+    int k_off[NC];  // K, A operand: slot col, chunk 2c+half
+    {
+        const int row = band_row(col);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) k_off[c] = row * D + 8 * ((2 * c + half) ^ swz<D>(row));
+    }
+    // V, transposed read of key chunk c2 (slots 16*c2 ..), rows +8*lohi, 32-column slab db.
+    int v_off[2][2][NDB];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int lohi = 0; lohi < 2; ++lohi) {
+            const int row = band_row(16 * c2 + 4 * half + (j16 >> 2) + 8 * lohi);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                v_off[c2][lohi][db] =
+                    row * D + 8 * ((4 * db + 2 * (gq & 1) + ((j16 & 3) >> 1)) ^ swz<D>(row)) + 4 * (j16 & 1);
+        }
+    // DMA: load i (i = wave + kBandWaves*j) fills LDS rows [i*kTokPerLoad, ..);
+    // this lane writes row R = i*kTokPerLoad + lane/kCpr at chunk position
+    // lane%kCpr.  Row R = rr*kCb + c holds column c of band row rr; the byte
+    // offset from the band's first token is fixed per lane.  Columns past
+    // the box get an offset beyond any descriptor's range: they read as
+    // zeros and cost no memory traffic (no read ever reaches them).
+    int dma_voff[Bg::kLoadsPerWave];
+#pragma unroll
+    for (int j = 0; j < Bg::kLoadsPerWave; ++j) {
+        const int i = wave + kBandWaves * j;
+        const int R = i * Bg::kTokPerLoad + lane / Bg::kCpr;
+        const int rr = R / Bg::kCb, c = R % Bg::kCb;
+        dma_voff[j] = c < C ? 2 * ((rr * g.Wg + c) * (int)tok_stride + 8 * ((lane % Bg::kCpr) ^ swz<D>(R)))
+                            : 0x7ffffff0;
+    }
+    const __bf16 *kbase = k + (size_t)b * N * tok_stride + (size_t)h * D;
+    const __bf16 *vbase = v + (size_t)b * N * tok_stride + (size_t)h * D;
+    // Band bi -> LDS.  The descriptors end at token N of this sample, so a
+    // second band row past the grid reads zeros (its slots are masked).
+    auto dma_band = [&](int bi, __bf16 *Kd, __bf16 *Vd) HET_INLINE {
+        const int f = F0 + bi / nb_f, yy0 = uy0 + (bi % nb_f) * rpb;
+        const int tok0 = (f * g.Hg + yy0) * g.Wg + ux0;
+        const uint32_t bytes = (uint32_t)((N - tok0) * (int)tok_stride) * 2u;
+        const __bf16 *kp = kbase + (size_t)tok0 * tok_stride, *vp = vbase + (size_t)tok0 * tok_stride;
+#pragma unroll
+        for (int j = 0; j < Bg::kLoadsPerWave; ++j) {
+            const int i = wave + kBandWaves * j;
+            if (i < Bg::kLoads) {
+                buffer_load_lds16(kp, bytes, (HET_LDS void *)(Kd + i * Bg::kTokPerLoad * D), dma_voff[j]);
+                buffer_load_lds16(vp, bytes, (HET_LDS void *)(Vd + i * Bg::kTokPerLoad * D), dma_voff[j]);
+            }
+        }
+    };
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    float m_run = -__builtin_inff();
+    float l_part = 0.0f;
+    // Columns of this query's window relative to the tile box, inside the box.
+    const int xlo = qx0 - uxw, xhi = imin(qx0 - uxw + g.lw, nxw);
+
+    // Band bi is read from (Kc, Vc) while the DMA of band bi+1 goes to
+    // (Kn, Vn).  The buffers are fixed at each call site (the loop is
+    // unrolled by two), so the compiler can see that the reads of one buffer
+    // do not wait on the DMA into the other.
+    auto step = [&](int bi, const __bf16 *Kc, const __bf16 *Vc, __bf16 *Kn, __bf16 *Vn) HET_INLINE {
+        // Band bi has landed for every wave, and every wave is done with
+        // band bi-1, whose buffers the next DMA refills.
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        if (bi + 1 < n_bands) dma_band(bi + 1, Kn, Vn);
+        const int f = F0 + bi / nb_f, yy0 = uy0 + (bi % nb_f) * rpb;
+        if (!active || f < t0 || f >= t0 + g.lt) return;
+
+        // All LDS operands of the block are requested up front: the K reads
+        // feed the QK product, the V reads land while the softmax runs.
+        bf16x8 ka[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) ka[c] = *(const HET_LDS bf16x8 *)(Kc + k_off[c]);
+        bf16x4 vr[2][2][NDB];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+            for (int lohi = 0; lohi < 2; ++lohi)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    vr[c2][lohi][db] = lds_read_tr16((const HET_LDS void *)(Vc + v_off[c2][lohi][db]));
+        __builtin_amdgcn_sched_barrier(0);
+        // S^T = K Q^T for this wave's key block.
+        f32x16 s = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) s = mfma32_bf16(ka[c], qf[c], s);
+
+        // Keep only keys inside this query's window.  Register i holds slot
+        // 8(i/4) + 4*half + i%4 of the block: box row (i/4 >= 2 && SR == 16),
+        // column 8*((i/4) % (SR/8)) + 4*half + i%4.
+        const bool y_in0 = yy0 < uy0 + ny && yy0 >= qy0 && yy0 < qy0 + g.lh;
+        const bool y_in1 = rpb > 1 && yy0 + 1 < uy0 + ny && yy0 + 1 >= qy0 && yy0 + 1 < qy0 + g.lh;
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int xo = 8 * ((i / 4) % (SR / 8)) + 4 * half + (i % 4);
+            const bool y_in = (SR == 16 && i >= 8) ? y_in1 : y_in0;
+            const bool ok = y_in && xo >= xlo && xo < xhi;
+            const float xv = ok ? s[i] : -__builtin_inff();
+            s[i] = xv;
+            mx = fmaxf(mx, xv);
+        }
+        // Online softmax in base 2 with a lazily moved reference max; a block
+        // may hold none of this query's keys (mx = -inf), the reference then
+        // stays put.
+        mx = half_pair_max(mx) * scale_log2;
+        const bool grow = mx > m_run + kRescaleSlack;
+        // Rare after the first blocks; kept a branch (not a select) so that
+        // the accumulators are not rescaled on every band.
+        if (__builtin_expect(__any(grow), 0)) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            m_run = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        }
+        const float neg_m = -((m_run == -__builtin_inff()) ? 0.0f : m_run);
+        bf16x8 pf[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            u32x4 w;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c2 + 2 * jj], scale_log2, neg_m));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c2 + 2 * jj + 1], scale_log2, neg_m));
+                l_part += p0 + p1;
+                w[jj] = pack_bf16x2(p0, p1);
+            }
+            pf[c2] = __builtin_bit_cast(bf16x8, w);
+        }
+        // O^T += V^T P^T.
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+                oacc[db] = mfma32_bf16(concat8(vr[c2][0][db], vr[c2][1][db]), pf[c2], oacc[db]);
+    };
+
+    dma_band(0, Kb0, Vb0);
+    for (int bi = 0; bi < n_bands; bi += 2) {
+        step(bi, Kb0, Vb0, Kb1, Vb1);
+        if (bi + 1 < n_bands) step(bi + 1, Kb1, Vb1, Kb0, Vb0);
+    }
+
+    if (!is_local) return;
+    const float inv_l = 1.0f / half_pair_sum(l_part);
+    __bf16 *op = o + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int d = db * 32 + 8 * i4 + 4 * half;
+            u32x2 w;
+            w[0] = pack_bf16x2(oacc[db][4 * i4 + 0] * inv_l, oacc[db][4 * i4 + 1] * inv_l);
+            w[1] = pack_bf16x2(oacc[db][4 * i4 + 2] * inv_l, oacc[db][4 * i4 + 3] * inv_l);
+            *(u32x2 *)(op + d) = w;
+        }
+}
+
 hipError_t launch_local(const AttnArgs &a, hipStream_t stream) {
     LocalGeom g;
     g.T = a.grid_t; g.Hg = a.grid_h; g.Wg = a.grid_w;
@@ -297,11 +563,19 @@ hipError_t launch_local(const AttnArgs &a, hipStream_t stream) {
                        (const T_ *)a.k, (const T_ *)a.v, (T_ *)a.o, a.mask, a.n, a.heads, sl2, g, units)
     const bool sr16 = g.slot_row == 16;
     if (a.bf16) {
+        const int x_blocks = (g.tiles_x + kBandNW - 1) / kBandNW, t_pairs = (g.T + 1) / 2;
+        const int band_units = a.batch * a.heads * t_pairs * g.tiles_y * x_blocks;
+        const dim3 bgrid((band_units + 7) / 8 * 8), bblock(64 * kBandWaves);
+#define HET_BAND_LAUNCH(D_, SR_)                                                                       \
+    hipLaunchKernelGGL((local_band_kernel<D_, SR_>), bgrid, bblock, 0, stream, (const __bf16 *)a.q,    \
+                       (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, a.mask, a.n, a.heads, sl2, g, \
+                       band_units, x_blocks, t_pairs)
         if (a.head_dim == 128) {
-            if (sr16) HET_LOCAL_LAUNCH(__bf16, 128, 16); else HET_LOCAL_LAUNCH(__bf16, 128, 32);
+            if (sr16) HET_BAND_LAUNCH(128, 16); else HET_BAND_LAUNCH(128, 32);
         } else {
-            if (sr16) HET_LOCAL_LAUNCH(__bf16, 64, 16); else HET_LOCAL_LAUNCH(__bf16, 64, 32);
+            if (sr16) HET_BAND_LAUNCH(64, 16); else HET_BAND_LAUNCH(64, 32);
         }
+#undef HET_BAND_LAUNCH
     } else {
         if (a.head_dim == 128) {
             if (sr16) HET_LOCAL_LAUNCH(float, 128, 16); else HET_LOCAL_LAUNCH(float, 128, 32);
