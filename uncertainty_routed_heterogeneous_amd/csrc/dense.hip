@@ -434,6 +434,8 @@ __device__ __forceinline__ int piece_slot(int64_t W, int G, int n_kt, int units_
 // thread = (query, 16 consecutive partial floats of it).  Partial float
 // half*(D/2) + 16*db + 4*i4 + e of a query holds output column
 // 32*db + 8*i4 + 4*half + e (the accumulator order of the MFMA C layout).
+// The piece list of the unit (64-bit schedule arithmetic) is worked out by a
+// few threads per batch and shared through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void dense_merge_kernel(
     __bf16 *__restrict__ o, const int32_t *__restrict__ dense_idx, const int32_t *__restrict__ counts,
@@ -442,12 +444,15 @@ __global__ __launch_bounds__(256) void dense_merge_kernel(
     constexpr int kSlices = D / 16;
     constexpr int kMergeQ = 256 / kSlices;
     constexpr int NDB = D / 32;
+    constexpr int kMergeBatch = 8;
+    __shared__ int s_range[2];
+    __shared__ int s_slot[kMergeBatch];
     const int n_kt = (N + DenseBf16Geom<D>::BN - 1) / DenseBf16Geom<D>::BN;
     int units = 0;
     for (int bb = 0; bb < B; ++bb) units += H * ((counts[2 * bb] + BM - 1) / BM);
     const int units_dp = units / G * G, units_sk = units - units_dp;
     const int sk = blockIdx.x / (BM / kMergeQ);
-    if (sk >= units_sk) return;
+    if (sk >= units_sk) return;  // the whole workgroup
     const int unit = units_dp + sk;
     int b = 0, rem = unit, tiles_b = 0;
     for (;;) {
@@ -457,39 +462,68 @@ __global__ __launch_bounds__(256) void dense_merge_kernel(
         ++b;
     }
     const int h = rem / tiles_b, tile = rem % tiles_b;
-    const int qi = (blockIdx.x % (BM / kMergeQ)) * kMergeQ + (int)threadIdx.x / kSlices;
-    const int slice = (int)threadIdx.x % kSlices;
+    const int tid = (int)threadIdx.x;
+    const int qi = (blockIdx.x % (BM / kMergeQ)) * kMergeQ + tid / kSlices;
+    const int slice = tid % kSlices;
     const int qrow = tile * BM + qi;
-    if (qrow >= counts[2 * b]) return;
+    const bool q_valid = qrow < counts[2 * b];
 
     const int64_t W = (int64_t)units_sk * n_kt;
-    const int64_t ux0 = (int64_t)sk * n_kt, ux1 = ux0 + n_kt - 1;
-    const int w_first = work_owner(W, G, ux0), w_last = work_owner(W, G, ux1);
+    if (tid == 0) {
+        const int64_t ux0 = (int64_t)sk * n_kt;
+        s_range[0] = work_owner(W, G, ux0);
+        s_range[1] = work_owner(W, G, ux0 + n_kt - 1);
+    }
+    __syncthreads();
+    const int w_first = s_range[0], w_last = s_range[1];
     if (w_first == w_last) return;  // one workgroup ran the whole unit and stored it
     const size_t slot_elems = (size_t)D * BM;
     const float *ml = ws_part + (size_t)2 * G * slot_elems;
-    // Pieces come from the non-empty workgroups owning the unit's items.
+    // Pieces come from the non-empty workgroups owning the unit's items,
+    // taken kMergeBatch at a time with all their loads in flight (the running
+    // max and the sums are rescaled between batches).
     float m_all = -__builtin_inff();
-    for (int pw = w_first; pw <= w_last; ++pw) {
-        if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
-        const int ps = piece_slot(W, G, n_kt, units_dp, unit, pw);
-        m_all = fmaxf(m_all, ml[(size_t)ps * 2 * BM + qi]);
-    }
     f32x4 acc[4] = {};
     float l_all = 0.0f;
-    for (int pw = w_first; pw <= w_last; ++pw) {
-        if (work_begin(W, G, pw + 1) == work_begin(W, G, pw)) continue;
-        const int ps = piece_slot(W, G, n_kt, units_dp, unit, pw);
-        const float a = __builtin_amdgcn_exp2f(ml[(size_t)ps * 2 * BM + qi] - m_all);
-        l_all += a * ml[(size_t)ps * 2 * BM + BM + qi];
-        const f32x4 *po = (const f32x4 *)(ws_part + (size_t)ps * slot_elems + (size_t)qi * D + 16 * slice);
+    for (int pw0 = w_first; pw0 <= w_last; pw0 += kMergeBatch) {
+        if (tid < kMergeBatch) {
+            const int pw = pw0 + tid;
+            const bool ok = pw <= w_last && work_begin(W, G, pw + 1) > work_begin(W, G, pw);
+            s_slot[tid] = ok ? piece_slot(W, G, n_kt, units_dp, unit, pw) : -1;
+        }
+        __syncthreads();
+        float mp[kMergeBatch], lp[kMergeBatch];
+        f32x4 pv[kMergeBatch][4];
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            const f32x4 pv = po[i4];
+        for (int j = 0; j < kMergeBatch; ++j) {
+            const int ps = s_slot[j];
+            const bool ok = ps >= 0 && q_valid;
+            const f32x4 *po = (const f32x4 *)(ws_part + (size_t)(ok ? ps : 0) * slot_elems + (size_t)qi * D + 16 * slice);
+            mp[j] = ok ? ml[(size_t)ps * 2 * BM + qi] : -__builtin_inff();
+            lp[j] = ok ? ml[(size_t)ps * 2 * BM + BM + qi] : 0.0f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i4][e] += a * pv[e];
+            for (int i4 = 0; i4 < 4; ++i4) pv[j][i4] = ok ? po[i4] : f32x4{};
+        }
+        __syncthreads();  // s_slot is rewritten by the next batch
+        float m_new = m_all;
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) m_new = fmaxf(m_new, mp[j]);
+        const float r = (m_all == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_all - m_new);
+        l_all *= r;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) acc[i4] *= r;
+        m_all = m_new;
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+            const float a = (mp[j] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mp[j] - m_all);
+            l_all += a * lp[j];
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i4][e] += a * pv[j][i4][e];
         }
     }
+    if (!q_valid) return;
     const float inv_l = 1.0f / l_all;
     const int half = slice / NDB, db = slice % NDB;
     const int tok = dense_idx[(size_t)b * N + qrow];

@@ -357,6 +357,8 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     const int tok = in_grid ? (t * g.Hg + y) * g.Wg + x : 0;
     const bool is_local = in_grid && mask[(size_t)b * N + tok] != 0;
     const bool active = __any(is_local);
+    // A workgroup whose queries are all dense has nothing to do.
+    if (!__syncthreads_or(is_local)) return;
     const int t0 = window_start(imin(t, g.T - 1), g.wt, g.lt, g.T);
     const int qy0 = window_start(imin(y, g.Hg - 1), g.wh, g.lh, g.Hg);
     const int qx0 = window_start(imin(x, g.Wg - 1), g.ww, g.lw, g.Wg);
