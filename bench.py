@@ -106,9 +106,12 @@ class Layer:
             raise self.het.HetAttnError(st, "het_attn_dense")
 
 
-def time_layer(layer, steps: int, warmup: int):
+def time_layer(layer, steps: int, warmup: int, scrub=None):
     """Warm up, then time exactly `steps` steps; per-kernel times come from
-    events recorded between the launches on the same stream."""
+    events recorded between the launches on the same stream.  With `scrub`
+    (a device tensor), every step is preceded, outside the events, by a write
+    of the whole tensor, which evicts L2 and the last-level cache (cold
+    timing)."""
     import torch
     for _ in range(warmup):
         layer.route(); layer.local(); layer.dense()
@@ -120,6 +123,8 @@ def time_layer(layer, steps: int, warmup: int):
     t0 = time.perf_counter()
     start.record()
     for s in range(steps):
+        if scrub is not None:
+            scrub.fill_(s)
         ev[s][0].record(); layer.route()
         ev[s][1].record(); layer.local()
         ev[s][2].record(); layer.dense()
@@ -130,9 +135,13 @@ def time_layer(layer, steps: int, warmup: int):
     total_ms = start.elapsed_time(end)
     per = [[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in ev]
     mean = lambda xs: sum(xs) / len(xs)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    step = [sum(p) for p in per]
     return dict(ms_per_step=total_ms / steps, wall_ms_per_step=1e3 * wall / steps,
                 route_ms=mean([p[0] for p in per]), local_ms=mean([p[1] for p in per]),
-                dense_ms=mean([p[2] for p in per]))
+                dense_ms=mean([p[2] for p in per]),
+                step_ms_median=med(step), route_ms_median=med([p[0] for p in per]),
+                local_ms_median=med([p[1] for p in per]), dense_ms_median=med([p[2] for p in per]))
 
 
 def cpu_baseline(w, q, k, v, u, rho, stride: int):
@@ -167,6 +176,63 @@ def cpu_baseline(w, q, k, v, u, rho, stride: int):
                        f"for the whole layer")}
 
 
+def run_sweep(het, W, torch, rho_main):
+    """Warm timings of the rho sweep on the Wan-1.3B shape and of the other
+    workloads at their own rho (medians of 20 steps after 5 warm-ups)."""
+    cases = [("wan13b", r) for r in W.RHO_SWEEP] + [("wan5b", None), ("long", None)]
+    rows = []
+    for name, r in cases:
+        w = W.WORKLOADS[name]
+        rho = w.rho if r is None else r
+        qn, kn, vn = W.make_qkv(w)
+        un = W.make_u(w)
+        to_bf16 = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+        q, k, v = to_bf16(qn), to_bf16(kn), to_bf16(vn)
+        u = torch.from_numpy(un).cuda()
+        layer = Layer(het, w, q, k, v, u, rho)
+        res = time_layer(layer, 20, 5)
+        n_dense = [W.dense_count(w.n_tokens, rho)] * w.batch
+        eff = W.effective_flops(w, n_dense)
+        ms = res["step_ms_median"]
+        row = {"workload": name, "rho": rho, "tokens": w.n_tokens, "batch": w.batch, "heads": w.heads,
+               "ms_per_layer": round(ms, 5), "route_ms": round(res["route_ms_median"], 5),
+               "local_ms": round(res["local_ms_median"], 5), "dense_ms": round(res["dense_ms_median"], 5),
+               "effective_TFLOPs": round(eff / (ms * 1e-3) / 1e12, 2),
+               "pct_mfma_peak": round(100.0 * eff / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        log(f"[bench] sweep {row}")
+        rows.append(row)
+        del layer, q, k, v, u
+        torch.cuda.synchronize()
+    return rows
+
+
+def run_oracle_full(W):
+    """The fp64 oracle on whole layers (route + every dense and local row),
+    timed on the host cores."""
+    import numpy as np
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    cases = [("tiny", None)] + [("wan13b", r) for r in W.RHO_SWEEP] + [("wan5b", None), ("long", None)]
+    rows = []
+    for name, r in cases:
+        w = W.WORKLOADS[name]
+        rho = w.rho if r is None else r
+        qn, kn, vn = W.make_qkv(w)
+        un = W.make_u(w)
+        t0 = time.perf_counter()
+        rt = oracle.route_top_rho(un, rho)
+        t1 = time.perf_counter()
+        all_rows = np.arange(w.batch * w.n_tokens, dtype=np.int64)
+        oracle.attend_rows(qn, kn, vn, w.grid, w.window, w.softmax_scale, rt.mask, all_rows, nthreads=threads)
+        t2 = time.perf_counter()
+        eff = W.effective_flops(w.with_(rho=rho))
+        row = {"workload": name, "rho": rho, "route_s": round(t1 - t0, 3), "forward_s": round(t2 - t1, 2),
+               "effective_TFLOPs": round(eff / (t2 - t0) / 1e12, 5), "threads": threads}
+        log(f"[bench] oracle {row}")
+        rows.append(row)
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +246,11 @@ def main():
     ap.add_argument("--lib", default=None, help="load this libhetattn.so instead of the in-tree one")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (calibrates HBM counters)")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the rho sweep on the Wan-1.3B shape and the other workloads")
+    ap.add_argument("--oracle-full", action="store_true",
+                    help="also time the fp64 oracle on whole layers (minutes of host time)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -240,6 +311,17 @@ def main():
         f"local={res['local_ms']:.4f} dense={res['dense_ms']:.4f} -> {value:.1f} TFLOP/s effective, "
         f"dense kernel {dense_tflops:.1f} TFLOP/s")
 
+    cold = None
+    if not args.no_cold:
+        # 512 MiB write between steps evicts L2 (4 MiB per XCD) and the 256 MiB last-level cache.
+        scrub = torch.empty(512 * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+        rc = time_layer(layer, max(10, args.steps // 2), 2, scrub=scrub)
+        del scrub
+        cold = {"scrub_MiB": 512, "steps": max(10, args.steps // 2), "ms_per_step_median": round(rc["step_ms_median"], 5),
+                "route_ms_median": round(rc["route_ms_median"], 5), "local_ms_median": round(rc["local_ms_median"], 5),
+                "dense_ms_median": round(rc["dense_ms_median"], 5)}
+        log(f"[bench] cold: {cold}")
+
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5),
@@ -263,8 +345,17 @@ def main():
             "local_GBps": round(local_bytes / (res["local_ms"] * 1e-3) / 1e9, 1),
             "local_frac_hbm": round(local_bytes / (res["local_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "dense_ms": round(res["dense_ms"], 5),
+            "route_ms_median": round(res["route_ms_median"], 5),
+            "local_ms_median": round(res["local_ms_median"], 5),
+            "dense_ms_median": round(res["dense_ms_median"], 5),
+            "ms_per_step_median": round(res["step_ms_median"], 5),
+            # the route is computed once per denoising step and shared by every block
+            "ms_per_layer_route_amortized_30": round(res["route_ms_median"] / 30 + res["local_ms_median"] +
+                                                     res["dense_ms_median"], 5),
         },
     }
+    if cold is not None:
+        out["cold"] = cold
 
     if not args.no_dense_baseline and rho < 1.0:
         dl = Layer(het, w, q, k, v, u, 1.0)
@@ -276,6 +367,12 @@ def main():
         log(f"[bench] rho=1 dense path: {rd['ms_per_step']:.4f} ms/step "
             f"({out['dense_rho1']['speedup_vs_rho1']}x slower than rho={rho})")
         del dl
+
+    if args.sweep:
+        out["sweep"] = run_sweep(het, W, torch, rho)
+
+    if args.oracle_full:
+        out["oracle_full"] = run_oracle_full(W)
 
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 CPU oracle on a sample ...")
