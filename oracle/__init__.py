@@ -69,8 +69,12 @@ def _load():
                                            ctypes.c_double, P, P, ctypes.c_long, P, i]
         lib.oracle_attention_weights.argtypes = [P, P, i, i, i, i, i, i, i, i, i,
                                                  ctypes.c_double, P, ctypes.c_long, i, P]
+        lib.oracle_philox4x32_10.argtypes = [P, P, P]
+        lib.oracle_philox4x32_10.restype = None
+        lib.oracle_route_swap.argtypes = [P, i, i, ctypes.c_double, ctypes.c_ulonglong, ctypes.c_uint,
+                                          ctypes.c_uint, P, P, P, P]
         for fn in (lib.oracle_route_top_rho, lib.oracle_route_mean_std, lib.oracle_window_axis,
-                   lib.oracle_attend_rows, lib.oracle_attention_weights):
+                   lib.oracle_attend_rows, lib.oracle_attention_weights, lib.oracle_route_swap):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -112,6 +116,34 @@ def route_top_rho(u: np.ndarray, rho: float) -> Route:
 
 def route_mean_std(u: np.ndarray, c: float) -> Route:
     return _route("oracle_route_mean_std", u, c)
+
+
+def philox4x32_10(ctr, key) -> tuple:
+    """Philox4x32-10 (Salmon et al., SC'11) of a 4-word counter and a 2-word key."""
+    c = np.array(ctr, dtype=np.uint32)
+    kk = np.array(key, dtype=np.uint32)
+    out = np.empty(4, np.uint32)
+    _load().oracle_philox4x32_10(_ptr(c), _ptr(kk), _ptr(out))
+    return tuple(int(x) for x in out)
+
+
+def route_swap(mask_in: np.ndarray, r: float, seed: int, step: int, block: int) -> Route:
+    """Per-block random swap of a route ([HetA §3.2.2 after Eq. 12; App. B,
+    Table 8]); see oracle_route_swap.  thresh is not defined by the swap and
+    is returned as NaN."""
+    m = np.ascontiguousarray(mask_in, dtype=np.uint8)
+    if m.ndim != 2:
+        raise ValueError("mask must be [B, N]")
+    B, N = m.shape
+    mask = np.empty((B, N), np.uint8)
+    di = np.empty((B, N), np.int32)
+    li = np.empty((B, N), np.int32)
+    counts = np.empty((B, 2), np.int32)
+    rc = _load().oracle_route_swap(_ptr(m), B, N, float(r), int(seed), int(step), int(block),
+                                   _ptr(mask), _ptr(di), _ptr(li), _ptr(counts))
+    if rc != 0:
+        raise ValueError(f"oracle_route_swap rejected its arguments (rc={rc})")
+    return Route(mask, di, li, counts, np.full(B, np.nan))
 
 
 def window_axis(S: int, k: int, pos: int) -> tuple[int, int]:

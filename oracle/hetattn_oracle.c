@@ -133,6 +133,109 @@ int oracle_route_mean_std(const float *u, int B, int N, double c,
     return 0;
 }
 
+/* Philox4x32 (Salmon et al., SC'11): one round multiplies two of the four
+ * words by the Philox constants, takes the high and low halves of the 64-bit
+ * products and mixes the high halves with the other two words and the key;
+ * the key is advanced by the two Weyl increments between rounds. */
+void oracle_philox4x32_10(const unsigned int ctr[4], const unsigned int key[2], unsigned int out[4])
+{
+    const unsigned long long M0 = 0xD2511F53ull, M1 = 0xCD9E8D57ull;
+    const unsigned int W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    unsigned int x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+    unsigned int k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; round++) {
+        if (round > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        unsigned long long p0 = M0 * (unsigned long long)x0;
+        unsigned long long p1 = M1 * (unsigned long long)x2;
+        unsigned int hi0 = (unsigned int)(p0 >> 32), lo0 = (unsigned int)p0;
+        unsigned int hi1 = (unsigned int)(p1 >> 32), lo1 = (unsigned int)p1;
+        unsigned int y0 = hi1 ^ x1 ^ k0;
+        unsigned int y2 = hi0 ^ x3 ^ k1;
+        x0 = y0;
+        x1 = lo1;
+        x2 = y2;
+        x3 = lo0;
+    }
+    out[0] = x0;
+    out[1] = x1;
+    out[2] = x2;
+    out[3] = x3;
+}
+
+typedef struct {
+    unsigned int key;
+    int idx;
+} keyed_token;
+
+/* Smaller key first; equal keys -> smaller token index first. */
+static int key_cmp(const void *pa, const void *pb)
+{
+    const keyed_token *a = (const keyed_token *)pa;
+    const keyed_token *b = (const keyed_token *)pb;
+    if (a->key < b->key) return -1;
+    if (a->key > b->key) return 1;
+    if (a->idx == b->idx) return 0;
+    return (a->idx < b->idx) ? -1 : 1;
+}
+
+int oracle_route_swap(const unsigned char *mask_in, int B, int N, double r,
+                      unsigned long long seed, unsigned int step, unsigned int block,
+                      unsigned char *mask, int *dense_idx, int *local_idx, int *counts)
+{
+    if (!mask_in || !mask || !dense_idx || !local_idx || !counts) return -1;
+    if (B <= 0 || N <= 0) return -1;
+    if (!(r >= 0.0 && r <= 1.0)) return -1;
+    const long S0 = (long)floor(r * (double)N + 0.5);
+    const unsigned int key[2] = {(unsigned int)(seed & 0xffffffffull), (unsigned int)(seed >> 32)};
+
+    keyed_token *dset = (keyed_token *)malloc(sizeof(keyed_token) * (size_t)N);
+    keyed_token *lset = (keyed_token *)malloc(sizeof(keyed_token) * (size_t)N);
+    unsigned char *dense = (unsigned char *)malloc((size_t)N);
+    if (!dset || !lset || !dense) {
+        free(dset);
+        free(lset);
+        free(dense);
+        return -2;
+    }
+    for (int b = 0; b < B; b++) {
+        const unsigned char *mb = mask_in + (size_t)b * N;
+        int nd = 0, nl = 0;
+        for (int i = 0; i < N; i++) {
+            const unsigned int ctr[4] = {(unsigned int)i, (unsigned int)b, block, step};
+            unsigned int out[4];
+            oracle_philox4x32_10(ctr, key, out);
+            if (mb[i] == 0) {
+                dset[nd].key = out[0];
+                dset[nd].idx = i;
+                nd++;
+            } else {
+                lset[nl].key = out[0];
+                lset[nl].idx = i;
+                nl++;
+            }
+        }
+        long S = S0;
+        if (S > nd) S = nd;
+        if (S > nl) S = nl;
+        qsort(dset, (size_t)nd, sizeof(keyed_token), key_cmp);
+        qsort(lset, (size_t)nl, sizeof(keyed_token), key_cmp);
+        for (int i = 0; i < N; i++) dense[i] = (mb[i] == 0);
+        for (long s = 0; s < S; s++) {
+            dense[dset[s].idx] = 0;
+            dense[lset[s].idx] = 1;
+        }
+        write_route(dense, N, mask + (size_t)b * N, dense_idx + (size_t)b * N,
+                    local_idx + (size_t)b * N, counts + 2 * b);
+    }
+    free(dset);
+    free(lset);
+    free(dense);
+    return 0;
+}
+
 int oracle_window_axis(int S, int k, int pos, int *start, int *len)
 {
     if (S <= 0 || k <= 0 || (k % 2) == 0 || pos < 0 || pos >= S || !start || !len)

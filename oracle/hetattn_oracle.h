@@ -46,6 +46,26 @@ int oracle_route_mean_std(const float *u, int B, int N, double c,
                           unsigned char *mask, int *dense_idx, int *local_idx,
                           int *counts, double *thresh);
 
+/* Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
+ * Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11): ten rounds of
+ * the 4x32 Philox S-box on the counter ctr[4], with the key key[2] bumped by
+ * the Weyl constants between rounds; the result goes to out[4]. */
+void oracle_philox4x32_10(const unsigned int ctr[4], const unsigned int key[2], unsigned int out[4]);
+
+/* Per-block random swap ([HetA §3.2.2, the text after Eq. 12: at each block
+ * a subset of uncertain tokens is swapped with randomly selected certain
+ * ones; App. B, Random Token Percentage and Table 8: the swap ratio r).
+ * Reading: per sample b with K_b dense tokens in mask_in, S_b =
+ * min(floor(r*N + 1/2), K_b, N - K_b) dense tokens become local and S_b local
+ * tokens become dense, so K_b is unchanged.  Token i of sample b draws the
+ * key philox4x32_10(ctr = {i, b, block, step}, key = {seed low 32 bits,
+ * seed high 32 bits})[0]; in each of the two sets the S_b tokens with the
+ * smallest key (equal keys: smaller token index first) are the ones swapped.
+ * Writes the swapped route like oracle_route_top_rho (no thresh). */
+int oracle_route_swap(const unsigned char *mask_in, int B, int N, double r,
+                      unsigned long long seed, unsigned int step, unsigned int block,
+                      unsigned char *mask, int *dense_idx, int *local_idx, int *counts);
+
 /* The local neighbourhood of [HetA §3.1.1 Eq. 3] along one axis of extent S
  * for an odd window k at coordinate pos: length min(k, S), start shifted so
  * the box stays inside [0, S). */

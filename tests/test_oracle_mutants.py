@@ -31,6 +31,15 @@ MUTANTS = {
     "value_from_query_row": ("const float *vr = vbase + (long)keys[j] * key_stride;",
                              "const float *vr = vbase;"),
     "local_mask_inverted": ("if (!is_local) {", "if (is_local) {"),
+    # per-block random swap and its generator
+    "philox_weyl_constant": ("W1 = 0xBB67AE85u", "W1 = 0xBB67AE86u"),
+    "philox_key_not_bumped_first_round_too": ("if (round > 0) {", "if (round >= 0) {"),
+    "swap_largest_keys": ("if (a->key < b->key) return -1;\n    if (a->key > b->key) return 1;",
+                          "if (a->key < b->key) return 1;\n    if (a->key > b->key) return -1;"),
+    "swap_ratio_truncated": ("floor(r * (double)N + 0.5)", "floor(r * (double)N)"),
+    "swap_counter_words_swapped": ("{(unsigned int)i, (unsigned int)b, block, step}",
+                                   "{(unsigned int)i, (unsigned int)b, step, block}"),
+    "swap_not_capped_by_local_set": ("if (S > nl) S = nl;", ""),
 }
 
 
@@ -48,6 +57,7 @@ def test_planted_mistake_is_caught(name, tmp_path):
     env = dict(os.environ, HETATTN_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_route.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_attention.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_attention.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_swap.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"planted mistake {name!r} passed every pin:\n{r.stdout[-2000:]}"
