@@ -71,6 +71,9 @@ def _load():
                                                  ctypes.c_double, P, ctypes.c_long, i, P]
         lib.oracle_philox4x32_10.argtypes = [P, P, P]
         lib.oracle_philox4x32_10.restype = None
+        lib.oracle_swap_draws.argtypes = [i, ctypes.c_uint, ctypes.c_ulonglong, ctypes.c_uint,
+                                          ctypes.c_uint, P]
+        lib.oracle_swap_draws.restype = None
         lib.oracle_route_swap.argtypes = [P, i, i, ctypes.c_double, ctypes.c_ulonglong, ctypes.c_uint,
                                           ctypes.c_uint, P, P, P, P]
         for fn in (lib.oracle_route_top_rho, lib.oracle_route_mean_std, lib.oracle_window_axis,
@@ -144,6 +147,13 @@ def route_swap(mask_in: np.ndarray, r: float, seed: int, step: int, block: int) 
     if rc != 0:
         raise ValueError(f"oracle_route_swap rejected its arguments (rc={rc})")
     return Route(mask, di, li, counts, np.full(B, np.nan))
+
+
+def swap_draws(N: int, b: int, seed: int, step: int, block: int) -> np.ndarray:
+    """The per-token draws route_swap ranks, for sample b: uint32 [N]."""
+    out = np.empty(N, np.uint32)
+    _load().oracle_swap_draws(int(N), int(b), int(seed), int(step), int(block), _ptr(out))
+    return out
 
 
 def window_axis(S: int, k: int, pos: int) -> tuple[int, int]:

@@ -236,6 +236,18 @@ int oracle_route_swap(const unsigned char *mask_in, int B, int N, double r,
     return 0;
 }
 
+void oracle_swap_draws(int N, unsigned int b, unsigned long long seed, unsigned int step,
+                       unsigned int block, unsigned int *out)
+{
+    const unsigned int key[2] = {(unsigned int)(seed & 0xffffffffull), (unsigned int)(seed >> 32)};
+    for (int i = 0; i < N; i++) {
+        const unsigned int ctr[4] = {(unsigned int)i, b, block, step};
+        unsigned int w[4];
+        oracle_philox4x32_10(ctr, key, w);
+        out[i] = w[0];
+    }
+}
+
 int oracle_window_axis(int S, int k, int pos, int *start, int *len)
 {
     if (S <= 0 || k <= 0 || (k % 2) == 0 || pos < 0 || pos >= S || !start || !len)

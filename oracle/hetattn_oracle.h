@@ -66,6 +66,11 @@ int oracle_route_swap(const unsigned char *mask_in, int B, int N, double r,
                       unsigned long long seed, unsigned int step, unsigned int block,
                       unsigned char *mask, int *dense_idx, int *local_idx, int *counts);
 
+/* The draws of oracle_route_swap for one sample: out[i] =
+ * philox4x32_10({i, b, block, step}, {seed low, seed high})[0], i < N. */
+void oracle_swap_draws(int N, unsigned int b, unsigned long long seed, unsigned int step,
+                       unsigned int block, unsigned int *out);
+
 /* The local neighbourhood of [HetA §3.1.1 Eq. 3] along one axis of extent S
  * for an odd window k at coordinate pos: length min(k, S), start shifted so
  * the box stays inside [0, S). */

@@ -40,6 +40,8 @@ MUTANTS = {
     "swap_counter_words_swapped": ("{(unsigned int)i, (unsigned int)b, block, step}",
                                    "{(unsigned int)i, (unsigned int)b, step, block}"),
     "swap_not_capped_by_local_set": ("if (S > nl) S = nl;", ""),
+    "swap_ties_higher_index_first": ("return (a->idx < b->idx) ? -1 : 1;",
+                                     "return (a->idx < b->idx) ? 1 : -1;"),
 }
 
 

@@ -151,3 +151,22 @@ def test_uniform_coverage_over_blocks(oracle_mod):
     mean = hits[local0].mean()
     assert abs(mean - blocks * p) < 0.02
     assert abs(hits[local0].var() - blocks * p * (1 - p)) < 0.1
+
+
+def test_equal_draws_split_by_index(oracle_mod):
+    """Two tokens with the same draw at the selection boundary: only the one
+    with the lower index moves; one more swap slot moves both."""
+    from swap_cases import tie_cases, tie_mask
+    for case in tie_cases():
+        m = tie_mask(oracle_mod, case)
+        x = oracle_mod.swap_draws(case["N"], case["b"], case["seed"], case["step"], case["block"])
+        i, j = case["i"], case["j"]
+        assert i < j and x[i] == x[j] == case["draw"]
+        assert int(np.count_nonzero(x < x[i])) == case["c"]
+        side_before = m[0, i]
+        r = oracle_mod.route_swap(m, case["r"], case["seed"], case["step"], case["block"])
+        assert r.mask[0, i] != side_before and r.mask[0, j] == side_before
+        assert r.counts[0, 0] == int(np.count_nonzero(m == 0))
+        r2 = oracle_mod.route_swap(m, (case["c"] + 2) / case["N"], case["seed"], case["step"],
+                                   case["block"])
+        assert r2.mask[0, i] != side_before and r2.mask[0, j] != side_before
