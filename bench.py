@@ -144,6 +144,39 @@ def time_layer(layer, steps: int, warmup: int, scrub=None):
                 local_ms_median=med([p[1] for p in per]), dense_ms_median=med([p[2] for p in per]))
 
 
+def time_swap(layer, ratio: float, n_blocks: int, iters: int, warmup: int = 3):
+    """Median time of one het_attn_swap launch that makes the routes of
+    n_blocks blocks from the layer's route (already computed)."""
+    import torch
+    het, w = layer.het, layer.w
+    B, N = w.batch, w.n_tokens
+    dev = layer.mask.device
+    bufs = [torch.empty((n_blocks, B, N), dtype=torch.uint8, device=dev),
+            torch.empty((n_blocks, B, N), dtype=torch.int32, device=dev),
+            torch.empty((n_blocks, B, N), dtype=torch.int32, device=dev),
+            torch.empty((n_blocks, B, 2), dtype=torch.int32, device=dev),
+            torch.empty((n_blocks, B), dtype=torch.float64, device=dev)]
+    out = het.RouteStruct(*[b.data_ptr() for b in bufs], -1)
+
+    def launch(step):
+        st = layer.lib.het_attn_swap(ctypes.byref(layer.shape), ctypes.byref(layer.rs), ratio, 12345,
+                                     step, 0, n_blocks, ctypes.byref(out), layer.stream)
+        if st != 0:
+            raise het.HetAttnError(st, "het_attn_swap")
+
+    layer.route()
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [(E(), E()) for _ in range(iters)]
+    for i, (a, b) in enumerate(ev):
+        a.record(); launch(i); b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    return ts[len(ts) // 2]
+
+
 def cpu_baseline(w, q, k, v, u, rho, stride: int):
     """The fp64 oracle on the host cores, on a bounded sample of the same
     layer: the full route plus every `stride`-th dense and local row."""
@@ -249,6 +282,8 @@ def main():
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the rho sweep on the Wan-1.3B shape and the other workloads")
+    ap.add_argument("--swap-ratio", type=float, default=0.07,
+                    help="ratio r of the per-block random swap timed beside the step (0 skips it)")
     ap.add_argument("--oracle-full", action="store_true",
                     help="also time the fp64 oracle on whole layers (minutes of host time)")
     args = ap.parse_args()
@@ -356,6 +391,16 @@ def main():
     }
     if cold is not None:
         out["cold"] = cold
+
+    if args.swap_ratio > 0:
+        # Per-block random swap: one launch makes the routes of all 30 blocks
+        # of a Wan step; it depends only on the step's route.
+        s30 = time_swap(layer, args.swap_ratio, 30, max(10, args.steps // 2))
+        s1 = time_swap(layer, args.swap_ratio, 1, max(10, args.steps // 2))
+        out["swap"] = {"ratio": args.swap_ratio, "blocks": 30, "ms_30_blocks_median": round(s30, 5),
+                       "ms_1_block_median": round(s1, 5), "ms_per_block_amortized": round(s30 / 30, 5),
+                       "GBps_30_blocks": round(30 * 10 * w.batch * w.n_tokens / (s30 * 1e-3) / 1e9, 1)}
+        log(f"[bench] swap: {out['swap']}")
 
     if not args.no_dense_baseline and rho < 1.0:
         dl = Layer(het, w, q, k, v, u, 1.0)

@@ -115,6 +115,35 @@ size_t het_attn_workspace_bytes(const het_attn_shape *shape);
 int het_attn_route(const het_attn_shape *shape, const float *u, int mode, double param,
                    het_route *out, void *stream);
 
+/* Per-block random swap of a route ([HetA §3.2.2], the remark after Eq. 12:
+ * at every block some uncertain tokens trade places with randomly chosen
+ * certain ones; [HetA App. B], "Random Token Percentage", and Table 8 give
+ * the swap ratio r).  For each block l in block .. block + n_blocks - 1 and
+ * each sample b, with K_b the dense count of `in` and
+ * S_b = min(floor(r*N + 1/2), K_b, N - K_b), the S_b dense tokens and the
+ * S_b local tokens with the smallest draw x_i change sides (equal draws:
+ * lower token index first), so the counts stay those of `in`.
+ * x_i = output word 0 of Philox4x32-10 (Salmon et al., "Parallel Random
+ * Numbers: As Easy as 1, 2, 3", SC 2011) at counter words (i, b, l, step)
+ * under key words (seed & 0xffffffff, seed >> 32).
+ *   in     host struct; in->mask [B, N] is read (0 = dense, else local);
+ *          in->thresh, when it and out->thresh are set, is copied into every
+ *          route; the other buffers of `in` are not read.
+ *   r      in [0, 1]; r = 0 copies the route.
+ *   n_blocks  1 .. 65535 routes, made by one launch.
+ *   out    host struct of device buffers with n_blocks routes back to back:
+ *          mask, dense_idx, local_idx [n_blocks, B, N], counts [n_blocks, B, 2],
+ *          thresh [n_blocks, B] or NULL (NaN when in->thresh is NULL).  Route l
+ *          starts at each pointer plus l times its per-route size.
+ *          out->dense_count_host is set to in->dense_count_host.
+ *          out must not overlap in->mask or in->thresh, except that with
+ *          n_blocks = 1 out may be `in` itself (out->mask == in->mask, and
+ *          out->thresh == in->thresh or either NULL): the swap in place.
+ * Deterministic: the same in->mask, r, seed, step and block give bit-identical
+ * routes. */
+int het_attn_swap(const het_attn_shape *shape, const het_route *in, double r, uint64_t seed,
+                  uint32_t step, uint32_t block, int32_t n_blocks, het_route *out, void *stream);
+
 /* Heterogeneous attention ([HetA §3.2.2 Eq. 13]) with the route of
  * het_attn_route for the same shape.
  *   q, k, v  device, [B, N, heads, head_dim] of shape->dtype, read only.

@@ -133,3 +133,59 @@ def test_binding_rejects_bad_tensors():
         het.route(u, (4, 8, 8), (3, 3, 3), 2, 64, torch.float32, rho=0.2)  # not on a GPU
     with pytest.raises(ValueError):
         het.route(u, (4, 8, 8), (3, 3, 3), 2, 64, torch.float32)  # neither rho nor c
+
+
+def call_swap(lib, shape, src=None, dst=None, r=0.07, n_blocks=1):
+    s_in = src if src is not None else fake_route()
+    s_out = dst if dst is not None else het.RouteStruct(0x100000, 0x200000, 0x300000, 0x400000,
+                                                         0x500000, -1)
+    return lib.het_attn_swap(ctypes.byref(shape) if shape is not None else None,
+                             ctypes.byref(s_in) if s_in is not False else None, r, 7, 0, 0,
+                             n_blocks, ctypes.byref(s_out) if s_out is not False else None, None)
+
+
+def test_swap_argument_errors(lib):
+    s = good_shape()  # N = 256
+    assert call_swap(lib, None) == het.HET_ERR_INVALID_ARG
+    assert call_swap(lib, s, src=False) == het.HET_ERR_INVALID_ARG
+    assert call_swap(lib, s, dst=False) == het.HET_ERR_INVALID_ARG
+    assert call_swap(lib, good_shape(head_dim=96)) == het.HET_ERR_UNSUPPORTED
+    r = fake_route()
+    r.mask = None
+    assert call_swap(lib, s, src=r) == het.HET_ERR_INVALID_ARG
+    for field in ("mask", "dense_idx", "local_idx", "counts"):
+        d = het.RouteStruct(0x100000, 0x200000, 0x300000, 0x400000, 0x500000, -1)
+        setattr(d, field, None)
+        assert call_swap(lib, s, dst=d) == het.HET_ERR_INVALID_ARG, field
+    for ratio in (-0.01, 1.01, float("nan"), float("inf")):
+        assert call_swap(lib, s, r=ratio) == het.HET_ERR_INVALID_ARG
+    for nb in (0, -1, 65536):
+        assert call_swap(lib, s, n_blocks=nb) == het.HET_ERR_INVALID_ARG
+    r = fake_route()
+    r.dense_count_host = 257
+    assert call_swap(lib, s, src=r) == het.HET_ERR_INVALID_ARG
+
+
+def test_swap_overlap_errors(lib):
+    """Outputs may not overlap the input mask or thresholds, except for the
+    in-place form (one route, the very same buffers)."""
+    s = good_shape()  # B = 1, N = 256
+    src = het.RouteStruct(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, -1)
+
+    def dst(**kw):
+        d = het.RouteStruct(0x100000, 0x200000, 0x300000, 0x400000, 0x500000, -1)
+        for k, v in kw.items():
+            setattr(d, k, v)
+        return d
+
+    # The same mask with two routes: route 1 would overwrite what route 0 reads.
+    assert call_swap(lib, s, src, dst(mask=0x10000), n_blocks=2) == het.HET_ERR_INVALID_ARG
+    # Index lists, counts or thresholds on top of the input mask.
+    assert call_swap(lib, s, src, dst(dense_idx=0x10000 - 512)) == het.HET_ERR_INVALID_ARG
+    assert call_swap(lib, s, src, dst(local_idx=0x10000 + 255)) == het.HET_ERR_INVALID_ARG
+    assert call_swap(lib, s, src, dst(counts=0x10000 + 100)) == het.HET_ERR_INVALID_ARG
+    assert call_swap(lib, s, src, dst(thresh=0x10000 + 8)) == het.HET_ERR_INVALID_ARG
+    # A mask shifted into the input mask, and thresholds shared by two routes.
+    assert call_swap(lib, s, src, dst(mask=0x10000 + 1)) == het.HET_ERR_INVALID_ARG
+    assert call_swap(lib, s, src, dst(thresh=0x50000), n_blocks=2) == het.HET_ERR_INVALID_ARG
+    assert call_swap(lib, s, src, dst(mask=0x50000 + 4)) == het.HET_ERR_INVALID_ARG

@@ -8,7 +8,8 @@ kernels of ``csrc/``.  PyTorch supplies device memory and the current stream.
 Diffusion" (HetA-DiT, arXiv 2609.31050).
 
     r = route(u, grid, window, q.shape, rho=0.2)   # §3.2.2 Eqs. 11-12
-    o = forward(q, k, v, r)                        # §3.2.2 Eq. 13
+    rb = swap(r, 0.07, seed, step, n_blocks=30)    # §3.2.2, per-block swap
+    o = forward(q, k, v, rb[block])                # §3.2.2 Eq. 13
 
 The library is loaded on first use; if it is missing the call raises -- there
 is no fallback implementation.
@@ -56,6 +57,10 @@ SIGNATURES = {
     "het_attn_route": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_int,
                                       ctypes.c_double, ctypes.POINTER(RouteStruct), ctypes.c_void_p]),
 }
+SIGNATURES["het_attn_swap"] = (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(RouteStruct),
+                                              ctypes.c_double, ctypes.c_uint64, ctypes.c_uint32,
+                                              ctypes.c_uint32, ctypes.c_int32,
+                                              ctypes.POINTER(RouteStruct), ctypes.c_void_p])
 _ATTN_ARGS = [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
               ctypes.POINTER(RouteStruct), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
               ctypes.c_void_p]
@@ -150,6 +155,45 @@ def route(u, grid, window, heads: int, head_dim: int, dtype, rho: float | None =
         raise HetAttnError(st, "het_attn_route")
     r.dense_count_host = rs.dense_count_host
     return r
+
+
+def swap(r: Route, ratio: float, seed: int, step: int, block: int = 0, n_blocks: int = 1,
+         in_place: bool = False, stream=None):
+    """Per-block random swap of a route (het_attn_swap).
+
+    Returns the routes of blocks block .. block + n_blocks - 1 as a list of
+    Route objects viewing one allocation ([n_blocks, B, N] tensors); with
+    in_place=True (n_blocks = 1 only) `r` itself is rewritten and returned."""
+    import torch
+    B, N = r.mask.shape
+    dev = r.mask.device
+    if in_place:
+        if n_blocks != 1:
+            raise ValueError("in_place needs n_blocks == 1")
+        outs = [r]
+        rs_out = r.as_struct()
+    else:
+        nb = int(n_blocks)
+        mask = torch.empty((nb, B, N), dtype=torch.uint8, device=dev)
+        di = torch.empty((nb, B, N), dtype=torch.int32, device=dev)
+        li = torch.empty((nb, B, N), dtype=torch.int32, device=dev)
+        cnt = torch.empty((nb, B, 2), dtype=torch.int32, device=dev)
+        th = torch.empty((nb, B), dtype=torch.float64, device=dev)
+        outs = [Route(mask[l], di[l], li[l], cnt[l], th[l], r.dense_count_host, r.grid, r.window)
+                for l in range(nb)]
+        rs_out = RouteStruct(mask.data_ptr(), di.data_ptr(), li.data_ptr(), cnt.data_ptr(),
+                             th.data_ptr(), -1)
+    shape = make_shape(B, 1, 64, r.grid, r.window, HET_F32)
+    rs_in = r.as_struct()
+    st = load_library().het_attn_swap(ctypes.byref(shape), ctypes.byref(rs_in), float(ratio),
+                                      int(seed) & (2**64 - 1), int(step) & 0xffffffff,
+                                      int(block) & 0xffffffff, int(n_blocks), ctypes.byref(rs_out),
+                                      _stream_handle(stream))
+    if st != HET_OK:
+        raise HetAttnError(st, "het_attn_swap")
+    for o in outs:
+        o.dense_count_host = rs_out.dense_count_host
+    return outs
 
 
 def workspace_bytes(shape: Shape) -> int:

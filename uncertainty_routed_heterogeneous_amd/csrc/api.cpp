@@ -13,6 +13,7 @@ namespace {
 
 using hetattn::AttnArgs;
 using hetattn::RouteArgs;
+using hetattn::SwapArgs;
 
 struct Dims {
     int64_t B, N, H, D;
@@ -38,6 +39,12 @@ het_status check_shape(const het_attn_shape *s, Dims &d, float &scale) {
     if (lw > hetattn::kLocalMaxWinW) return HET_ERR_UNSUPPORTED;
     scale = s->scale > 0.0f ? s->scale : 1.0f / std::sqrt((float)s->head_dim);
     return HET_OK;
+}
+
+// True when the byte ranges [p, p + n) and [q, q + m) share a byte.
+bool overlaps(const void *p, size_t n, const void *q, size_t m) {
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + m && b < a + n;
 }
 
 // Compute units of the current device (0 if it cannot be queried).
@@ -109,6 +116,51 @@ int het_attn_route(const het_attn_shape *shape, const float *u, int mode, double
     }
     if (hetattn::launch_route(a, (hipStream_t)stream) != hipSuccess) return HET_ERR_HIP;
     out->dense_count_host = (a.mode == 0) ? a.k : -1;
+    return HET_OK;
+}
+
+int het_attn_swap(const het_attn_shape *shape, const het_route *in, double r, uint64_t seed,
+                  uint32_t step, uint32_t block, int32_t n_blocks, het_route *out, void *stream) {
+    Dims d;
+    float scale;
+    const het_status st = check_shape(shape, d, scale);
+    if (st != HET_OK) return st;
+    if (!in || !in->mask || !out || !out->mask || !out->dense_idx || !out->local_idx || !out->counts)
+        return HET_ERR_INVALID_ARG;
+    if (!(r >= 0.0 && r <= 1.0) || n_blocks <= 0 || n_blocks > 65535) return HET_ERR_INVALID_ARG;
+    if (in->dense_count_host < -1 || in->dense_count_host > d.N) return HET_ERR_INVALID_ARG;
+    // The buffers read (in->mask, in->thresh) may be written only in place,
+    // by a single route at the very same address.
+    const size_t routes = (size_t)n_blocks * (size_t)d.B;
+    const size_t in_mask = (size_t)(d.B * d.N), in_th = (size_t)d.B * sizeof(double);
+    auto hits_input = [&](const void *p, size_t bytes, bool may_be_mask, bool may_be_thresh) {
+        if (!(may_be_mask && p == in->mask) && overlaps(p, bytes, in->mask, in_mask)) return true;
+        return in->thresh && !(may_be_thresh && p == in->thresh) && overlaps(p, bytes, in->thresh, in_th);
+    };
+    const bool single = n_blocks == 1;
+    if (hits_input(out->mask, routes * d.N, single, false) ||
+        hits_input(out->dense_idx, routes * d.N * 4, false, false) ||
+        hits_input(out->local_idx, routes * d.N * 4, false, false) ||
+        hits_input(out->counts, routes * 8, false, false) ||
+        (out->thresh && hits_input(out->thresh, routes * sizeof(double), false, single)))
+        return HET_ERR_INVALID_ARG;
+    SwapArgs a;
+    a.mask_in = in->mask;
+    a.thresh_in = in->thresh;
+    a.batch = (int)d.B;
+    a.n = (int)d.N;
+    a.s0 = (int)std::floor(r * (double)d.N + 0.5);
+    a.key0 = (uint32_t)(seed & 0xffffffffu);
+    a.key1 = (uint32_t)(seed >> 32);
+    a.step = step;
+    a.block0 = block;
+    a.mask = out->mask;
+    a.dense_idx = out->dense_idx;
+    a.local_idx = out->local_idx;
+    a.counts = out->counts;
+    a.thresh = out->thresh;
+    if (hetattn::launch_swap(a, n_blocks, (hipStream_t)stream) != hipSuccess) return HET_ERR_HIP;
+    out->dense_count_host = in->dense_count_host;
     return HET_OK;
 }
 

@@ -18,6 +18,20 @@ struct RouteArgs {
     double *thresh;
 };
 
+// Per-block random swap: routes of blocks block0 .. block0 + n_blocks - 1,
+// each [batch, n] (counts [batch, 2], thresh [batch]), back to back.
+struct SwapArgs {
+    const uint8_t *mask_in;
+    const double *thresh_in;  // copied into thresh when both are set
+    int batch, n;
+    int s0;                   // floor(r * n + 1/2), before the clamp to the set sizes
+    uint32_t key0, key1;      // Philox key: seed low and high words
+    uint32_t step, block0;
+    uint8_t *mask;
+    int32_t *dense_idx, *local_idx, *counts;
+    double *thresh;           // may be null
+};
+
 struct AttnArgs {
     const void *q, *k, *v;
     void *o;
@@ -41,6 +55,7 @@ constexpr int kLocalMaxWinW = 25;
 size_t dense_workspace_bytes(int batch, int heads, int n, int head_dim, bool bf16, int cu_count);
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t stream);
+hipError_t launch_swap(const SwapArgs &a, int n_blocks, hipStream_t stream);
 hipError_t launch_dense(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_local(const AttnArgs &a, hipStream_t stream);
 

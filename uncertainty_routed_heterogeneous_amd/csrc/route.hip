@@ -134,6 +134,83 @@ constexpr int kHistStride = 257;
 constexpr int kHistWords = 64 * kHistStride;
 static_assert(kHistWords % 4 == 0, "the histogram is cleared in 16-byte words");
 
+// MSB-first radix select over the keys of the members of one sample.
+// Precondition: 1 <= k <= the number of members, and [lo, hi] is the range of
+// the members' keys (workgroup-uniform).  Returns in tkey the k-th largest
+// member key and in take_equal the number of members equal to tkey that the
+// k largest hold, i.e. k minus the number of members above tkey.  The bits
+// above the highest bit in which lo and hi differ are shared by every member
+// and are skipped.  hcopy must be all zero on entry and is all zero on exit;
+// member(j) and key_at(j) describe row j of this wave's range as in
+// route_kernel.
+template <int kPer, typename KeyAt, typename Member>
+__device__ __forceinline__ void radix_select_largest(int k, uint32_t lo, uint32_t hi, int rows,
+                                                     KeyAt &&key_at, Member &&member,
+                                                     uint32_t *hcopy, uint32_t *hpart, int *s_sel,
+                                                     uint32_t &tkey, int &take_equal) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    int top_bit = (lo == hi) ? 0 : 32 - __builtin_clz(lo ^ hi);
+    uint32_t pmask = (top_bit >= 32) ? 0u : ~((1u << top_bit) - 1u);
+    uint32_t prefix = hi & pmask;
+    int remaining = k;
+    uint32_t *my_hist = hcopy + kHistStride * lane;
+    while (top_bit > 0) {
+        const int width = imin(8, top_bit);
+        const int shift = top_bit - width;
+        const uint32_t dmask = (1u << width) - 1u;
+        for_rows<kPer>(rows, [&](int j) HET_INLINE {
+            const uint32_t x = key_at(j);
+            if (member(j) && (x & pmask) == prefix) atomicAdd(&my_hist[(x >> shift) & dmask], 1u);
+        });
+        __syncthreads();
+        {
+            // Thread t sums bin t%256 over copies 16*(t/256) .. +15 and
+            // clears them for the next pass.
+            const int bin = tid & 255, c0 = 16 * (tid >> 8);
+            uint32_t sum = 0;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                sum += hcopy[(c0 + c) * kHistStride + bin];
+                hcopy[(c0 + c) * kHistStride + bin] = 0u;
+            }
+            hpart[tid] = sum;
+        }
+        __syncthreads();
+        if (tid < 64) {
+            // Wave 0 finds the digit d with count(> d) < remaining <= count(>= d).
+            // Lane l owns digits 255-4l .. 252-4l (descending).
+            auto bin_count = [&](int d) HET_INLINE -> int {
+                return (int)(hpart[d] + hpart[256 + d] + hpart[512 + d] + hpart[768 + d]);
+            };
+            const int c0 = bin_count(255 - 4 * tid), c1 = bin_count(254 - 4 * tid);
+            const int c2 = bin_count(253 - 4 * tid), c3 = bin_count(252 - 4 * tid);
+            const int mine = c0 + c1 + c2 + c3;
+            int incl = mine;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(incl, off);
+                if (tid >= off) incl += y;
+            }
+            const int excl = incl - mine;
+            if (excl < remaining && remaining <= incl) {
+                int d = 255 - 4 * tid, before = excl;
+                if (before + c0 < remaining) { before += c0; d--;
+                    if (before + c1 < remaining) { before += c1; d--;
+                        if (before + c2 < remaining) { before += c2; d--; } } }
+                s_sel[0] = d;
+                s_sel[1] = remaining - before;
+            }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)s_sel[0] << shift;
+        pmask |= dmask << shift;
+        remaining = s_sel[1];
+        top_bit = shift;
+    }
+    tkey = prefix;
+    take_equal = remaining;
+}
+
 // kPer > 0: every lane holds kPer keys in registers (N <= 1024 * kPer).
 // kPer == 0: per-wave ranges of ceil(N / 1024) rows of 64, re-read from u.
 template <int kPer>
@@ -189,68 +266,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         block_min_max(lo, hi, s_mm, lo, hi);
         for (int i = tid; i < kHistWords / 4; i += kRouteThreads)
             reinterpret_cast<u32x4 *>(hcopy)[i] = u32x4{0u, 0u, 0u, 0u};
-        // Bits above `top_bit` are shared by every key of the sample.
-        int top_bit = (lo == hi) ? 0 : 32 - __builtin_clz(lo ^ hi);
-        uint32_t pmask = (top_bit >= 32) ? 0u : ~((1u << top_bit) - 1u);
-        uint32_t prefix = hi & pmask;
-        int remaining = a.k;
-        uint32_t *my_hist = hcopy + kHistStride * lane;
         __syncthreads();
-        while (top_bit > 0) {
-            const int width = imin(8, top_bit);
-            const int shift = top_bit - width;
-            const uint32_t dmask = (1u << width) - 1u;
-            for_rows<kPer>(rows, [&](int j) HET_INLINE {
-                const uint32_t k = key_at(j);
-                if (k != 0u && (k & pmask) == prefix) atomicAdd(&my_hist[(k >> shift) & dmask], 1u);
-            });
-            __syncthreads();
-            {
-                // Thread t sums bin t%256 over copies 16*(t/256) .. +15 and
-                // clears them for the next pass.
-                const int bin = tid & 255, c0 = 16 * (tid >> 8);
-                uint32_t sum = 0;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    sum += hcopy[(c0 + c) * kHistStride + bin];
-                    hcopy[(c0 + c) * kHistStride + bin] = 0u;
-                }
-                hpart[tid] = sum;
-            }
-            __syncthreads();
-            if (tid < 64) {
-                // Wave 0 finds the digit d with count(> d) < remaining <= count(>= d).
-                // Lane l owns digits 255-4l .. 252-4l (descending).
-                auto bin_count = [&](int d) HET_INLINE -> int {
-                    return (int)(hpart[d] + hpart[256 + d] + hpart[512 + d] + hpart[768 + d]);
-                };
-                const int c0 = bin_count(255 - 4 * tid), c1 = bin_count(254 - 4 * tid);
-                const int c2 = bin_count(253 - 4 * tid), c3 = bin_count(252 - 4 * tid);
-                const int mine = c0 + c1 + c2 + c3;
-                int incl = mine;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const int y = __shfl_up(incl, off);
-                    if (tid >= off) incl += y;
-                }
-                const int excl = incl - mine;
-                if (excl < remaining && remaining <= incl) {
-                    int d = 255 - 4 * tid, before = excl;
-                    if (before + c0 < remaining) { before += c0; d--;
-                        if (before + c1 < remaining) { before += c1; d--;
-                            if (before + c2 < remaining) { before += c2; d--; } } }
-                    s_sel[0] = d;
-                    s_sel[1] = remaining - before;
-                }
-            }
-            __syncthreads();
-            prefix |= (uint32_t)s_sel[0] << shift;
-            pmask |= dmask << shift;
-            remaining = s_sel[1];
-            top_bit = shift;
-        }
-        tkey = prefix;
-        take_equal = remaining;
+        radix_select_largest<kPer>(
+            a.k, lo, hi, rows, key_at, [&](int j) HET_INLINE { return key_at(j) != 0u; }, hcopy,
+            hpart, s_sel, tkey, take_equal);
         T = (double)key_to_float(tkey);
     } else if (!top) {
         double s = 0.0;
@@ -321,6 +340,209 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Per-block random swap ([HetA §3.2.2], the remark after Eq. 12; App. B,
+// "Random Token Percentage", Table 8).  Starting from a route, S of the dense
+// tokens become local and S of the local tokens become dense, with
+// S = min(s0, K_b, N - K_b), so the counts do not change.  Token i of sample b
+// draws x_i = word 0 of Philox4x32-10 at counter (i, b, block, step) under the
+// 64-bit seed; in each set the S tokens with the smallest x (equal x: lower
+// index first) are the ones that move.  Selecting the S smallest x is the
+// radix select of the S largest ~x, whose tie rule (lower index first) is the
+// route's, so the swap reuses the route's select and compaction unchanged.
+// Grid (batch, n_blocks): workgroup (b, l) writes the route of block
+// block0 + l for sample b; one launch makes the routes of every block of a
+// step, which depend only on the step's route and the block index.
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC 2011): ten rounds; in each, the words 0 and 2 are
+// multiplied by two fixed odd constants into 64-bit products, the high halves
+// are mixed with words 1 and 3 and the round key, and the key advances by two
+// Weyl constants (the fractional parts of the golden ratio and of sqrt(3)).
+// Only output word 0 is used, so the compiler drops the rest of the last round.
+__device__ __forceinline__ uint32_t philox4x32_10_word0(uint32_t x0, uint32_t x1, uint32_t x2,
+                                                        uint32_t x3, uint32_t k0, uint32_t k1) {
+    constexpr uint32_t kMul0 = 0xD2511F53u, kMul1 = 0xCD9E8D57u;
+    constexpr uint32_t kWeyl0 = 0x9E3779B9u, kWeyl1 = 0xBB67AE85u;
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint32_t hi0 = __umulhi(kMul0, x0), lo0 = kMul0 * x0;
+        const uint32_t hi1 = __umulhi(kMul1, x2), lo1 = kMul1 * x2;
+        x0 = hi1 ^ x1 ^ k0;
+        x1 = lo1;
+        x2 = hi0 ^ x3 ^ k1;
+        x3 = lo0;
+        k0 += kWeyl0;
+        k1 += kWeyl1;
+    }
+    return x0;
+}
+
+// Exclusive prefix sums over the waves of kNV wave-uniform values, in wave
+// order; the workgroup totals go to total[].
+template <int kNV>
+__device__ __forceinline__ void wave_excl_scan(const int (&x)[kNV], int *s_wave, int (&before)[kNV],
+                                               int (&total)[kNV]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+#pragma unroll
+        for (int v = 0; v < kNV; ++v) s_wave[v * kRouteWaves + wave] = x[v];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < kNV; ++v) {
+        int bv = 0, tv = 0;
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) {
+            const int c = s_wave[v * kRouteWaves + w];
+            bv += (w < wave) ? c : 0;
+            tv += c;
+        }
+        before[v] = bv;
+        total[v] = tv;
+    }
+    __syncthreads();
+}
+
+// kPer as in route_kernel: > 0 keeps kPer draws and the set bits in
+// registers, 0 draws again and re-reads mask_in in every pass.
+template <int kPer>
+__global__ __launch_bounds__(kRouteThreads) void swap_kernel(SwapArgs a) {
+    const int b = blockIdx.x, l = blockIdx.y, tid = threadIdx.x, N = a.n;
+    const int lane = tid & 63, wave = tid >> 6;
+    const uint32_t blk = a.block0 + (uint32_t)l;
+    const uint8_t *min_b = a.mask_in + (size_t)b * N;
+    const size_t r = (size_t)l * a.batch + b;  // index of the route written
+    __shared__ __attribute__((aligned(16))) uint32_t hcopy[kHistWords];
+    __shared__ uint32_t hpart[4 * 256];
+    __shared__ int s_wave[5 * kRouteWaves];
+    __shared__ uint32_t s_mm[2 * kRouteWaves];
+    __shared__ int s_sel[2];
+
+    const int per = kPer > 0 ? kPer : (N + kRouteThreads - 1) / kRouteThreads;
+    const int w0 = wave * per * 64;
+    const int rows = imax(0, imin(per, (N - w0 + 63) >> 6));
+    auto token = [&](int j) HET_INLINE { return w0 + 64 * j + lane; };
+    // Selection key of token i: ~x_i, so that the largest keys are the
+    // smallest draws.
+    auto draw_key = [&](int j) HET_INLINE -> uint32_t {
+        return ~philox4x32_10_word0((uint32_t)token(j), (uint32_t)b, blk, a.step, a.key0, a.key1);
+    };
+    auto read_dense = [&](int j) HET_INLINE -> bool {
+        return token(j) < N && min_b[token(j)] == 0;
+    };
+
+    uint32_t keys[kPer > 0 ? kPer : 1];
+    uint64_t dbits = 0;  // bit j: token(j) is in the dense set of the input route
+    if constexpr (kPer > 0) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            if (j < rows) {
+                keys[j] = draw_key(j);
+                if (read_dense(j)) dbits |= 1ull << j;
+            } else {
+                keys[j] = 0u;
+            }
+        }
+    }
+    auto key_at = [&](int j) HET_INLINE -> uint32_t {
+        if constexpr (kPer > 0) return keys[j];
+        else return draw_key(j);
+    };
+    auto in_dense = [&](int j) HET_INLINE -> bool {
+        if constexpr (kPer > 0) return (dbits >> j) & 1u;
+        else return read_dense(j);
+    };
+    auto in_local = [&](int j) HET_INLINE -> bool { return token(j) < N && !in_dense(j); };
+
+    // Set sizes and the key range of each set.
+    int nd_w = 0;
+    uint32_t dlo = 0xffffffffu, dhi = 0u, llo = 0xffffffffu, lhi = 0u;
+    for_rows<kPer>(rows, [&](int j) HET_INLINE {
+        const uint32_t x = key_at(j);
+        const bool dn = in_dense(j), lc = in_local(j);
+        nd_w += __popcll(__ballot(dn));
+        if (dn) { dlo = min(dlo, x); dhi = max(dhi, x); }
+        if (lc) { llo = min(llo, x); lhi = max(lhi, x); }
+    });
+    block_min_max(dlo, dhi, s_mm, dlo, dhi);
+    block_min_max(llo, lhi, s_mm, llo, lhi);
+    int nd_total;
+    {
+        int x[1] = {nd_w}, bf[1], tt[1];
+        wave_excl_scan<1>(x, s_wave, bf, tt);
+        nd_total = tt[0];
+    }
+    const int S = imin(a.s0, imin(nd_total, N - nd_total));
+
+    // S = 0 leaves tkey = ~0 with nothing equal taken: no token moves.
+    uint32_t tkd = 0xffffffffu, tkl = 0xffffffffu;
+    int ted = 0, tel = 0;
+    if (S > 0) {
+        for (int i = tid; i < kHistWords / 4; i += kRouteThreads)
+            reinterpret_cast<u32x4 *>(hcopy)[i] = u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();
+        radix_select_largest<kPer>(S, dlo, dhi, rows, key_at, in_dense, hcopy, hpart, s_sel, tkd,
+                                   ted);
+        radix_select_largest<kPer>(S, llo, lhi, rows, key_at, in_local, hcopy, hpart, s_sel, tkl,
+                                   tel);
+    }
+
+    // Per wave: dense-set size, and in each set the tokens above the select
+    // key and those equal to it.
+    int cnt[5] = {nd_w, 0, 0, 0, 0};
+    for_rows<kPer>(rows, [&](int j) HET_INLINE {
+        const uint32_t x = key_at(j);
+        const bool dn = in_dense(j), lc = in_local(j);
+        cnt[1] += __popcll(__ballot(dn && x > tkd));
+        cnt[2] += __popcll(__ballot(dn && x == tkd));
+        cnt[3] += __popcll(__ballot(lc && x > tkl));
+        cnt[4] += __popcll(__ballot(lc && x == tkl));
+    });
+    int bef[5], tot[5];
+    wave_excl_scan<5>(cnt, s_wave, bef, tot);
+    // Dense tokens of the output before this wave: the input's, less those
+    // that left, plus those that came.
+    int d_seen = bef[0] - (bef[1] + imin(bef[2], ted)) + (bef[3] + imin(bef[4], tel));
+    const int n_dense = nd_total;
+
+    uint8_t *mask = a.mask + r * N;
+    int32_t *dense_idx = a.dense_idx + r * N;
+    int32_t *local_idx = a.local_idx + r * N;
+    int eqd_run = bef[2], eql_run = bef[4];
+    for_rows<kPer>(rows, [&](int j) HET_INLINE {
+        const uint32_t x = key_at(j);
+        const bool dn = in_dense(j), lc = in_local(j);
+        uint64_t out_d = __ballot(dn && x > tkd);  // dense tokens that move
+        uint64_t in_l = __ballot(lc && x > tkl);   // local tokens that move
+        const uint64_t eqd = __ballot(dn && x == tkd), eql = __ballot(lc && x == tkl);
+        if (eqd != 0ull) {
+            out_d |= __ballot(((eqd >> lane) & 1u) && eqd_run + lanes_below(eqd) < ted);
+            eqd_run += __popcll(eqd);
+        }
+        if (eql != 0ull) {
+            in_l |= __ballot(((eql >> lane) & 1u) && eql_run + lanes_below(eql) < tel);
+            eql_run += __popcll(eql);
+        }
+        const uint64_t bal = (__ballot(dn) & ~out_d) | in_l;
+        const int i = token(j);
+        const bool now_dense = (bal >> lane) & 1u;
+        const int d = d_seen + lanes_below(bal);
+        if (i < N) {
+            mask[i] = now_dense ? 0 : 1;
+            *(now_dense ? dense_idx + d : local_idx + (i - d)) = i;
+        }
+        d_seen += __popcll(bal);
+    });
+    for (int i = n_dense + tid; i < N; i += kRouteThreads) dense_idx[i] = -1;
+    for (int i = (N - n_dense) + tid; i < N; i += kRouteThreads) local_idx[i] = -1;
+    if (tid == 0) {
+        a.counts[2 * r] = n_dense;
+        a.counts[2 * r + 1] = N - n_dense;
+        if (a.thresh) a.thresh[r] = a.thresh_in ? a.thresh_in[b] : __builtin_nan("");
+    }
+}
+
 hipError_t launch_route(const RouteArgs &a, hipStream_t stream) {
     const dim3 grid(a.batch), block(kRouteThreads);
     if (a.n <= 8 * kRouteThreads)
@@ -333,6 +555,21 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL(route_kernel<64>, grid, block, 0, stream, a);
     else
         hipLaunchKernelGGL(route_kernel<0>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_swap(const SwapArgs &a, int n_blocks, hipStream_t stream) {
+    const dim3 grid(a.batch, n_blocks), block(kRouteThreads);
+    if (a.n <= 8 * kRouteThreads)
+        hipLaunchKernelGGL(swap_kernel<8>, grid, block, 0, stream, a);
+    else if (a.n <= 16 * kRouteThreads)
+        hipLaunchKernelGGL(swap_kernel<16>, grid, block, 0, stream, a);
+    else if (a.n <= 32 * kRouteThreads)
+        hipLaunchKernelGGL(swap_kernel<32>, grid, block, 0, stream, a);
+    else if (a.n <= 64 * kRouteThreads)
+        hipLaunchKernelGGL(swap_kernel<64>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(swap_kernel<0>, grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
