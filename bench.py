@@ -212,10 +212,13 @@ def cpu_baseline(w, q, k, v, u, rho, stride: int):
 def run_sweep(het, W, torch, rho_main):
     """Warm timings of the rho sweep on the Wan-1.3B shape and of the other
     workloads at their own rho (medians of 20 steps after 5 warm-ups)."""
-    cases = [("wan13b", r) for r in W.RHO_SWEEP] + [("wan5b", None), ("long", None)]
+    cases = ([("wan13b", r, None) for r in W.RHO_SWEEP] + [("wan5b", None, None), ("long", None, None)] +
+             [("wan13b", None, win) for win in W.WINDOW_SWEEP] + [("wan5b", None, (11, 11, 11))])
     rows = []
-    for name, r in cases:
+    for name, r, win in cases:
         w = W.WORKLOADS[name]
+        if win is not None:
+            w = w.with_(window=win)
         rho = w.rho if r is None else r
         qn, kn, vn = W.make_qkv(w)
         un = W.make_u(w)
@@ -227,7 +230,8 @@ def run_sweep(het, W, torch, rho_main):
         n_dense = [W.dense_count(w.n_tokens, rho)] * w.batch
         eff = W.effective_flops(w, n_dense)
         ms = res["step_ms_median"]
-        row = {"workload": name, "rho": rho, "tokens": w.n_tokens, "batch": w.batch, "heads": w.heads,
+        row = {"workload": name, "rho": rho, "window": list(w.window), "tokens": w.n_tokens,
+               "batch": w.batch, "heads": w.heads,
                "ms_per_layer": round(ms, 5), "route_ms": round(res["route_ms_median"], 5),
                "local_ms": round(res["local_ms_median"], 5), "dense_ms": round(res["dense_ms_median"], 5),
                "effective_TFLOPs": round(eff / (ms * 1e-3) / 1e12, 2),
@@ -271,7 +275,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="wan13b", choices=["wan13b", "wan5b", "long", "tiny"])
+    ap.add_argument("--workload", default="wan13b",
+                    choices=["wan13b", "wan5b", "long", "tiny", "wan13b_w11", "wan5b_w11"])
+    ap.add_argument("--window", default=None, help="override the workload's window, e.g. 11,11,11")
     ap.add_argument("--rho", type=float, default=None, help="override the workload's rho")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-baseline", action="store_true")
@@ -320,6 +326,8 @@ def main():
     if w.dtype != "bf16":
         w = w.with_(dtype="bf16")
     rho = w.rho if args.rho is None else args.rho
+    if args.window:
+        w = w.with_(window=tuple(int(x) for x in args.window.split(",")))
     log(f"[bench] workload={w.name} grid={w.grid} B={w.batch} heads={w.heads} D={w.head_dim} "
         f"rho={rho} window={w.window}")
     qn, kn, vn = W.make_qkv(w)

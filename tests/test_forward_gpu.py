@@ -59,6 +59,16 @@ def test_window_shapes(oracle_mod, window):
     full_parity(oracle_mod, w, q, k, v, u, rho=0.2, what=f"window {window}")
 
 
+@pytest.mark.parametrize("window", [(9, 9, 9), (11, 11, 11), (13, 13, 13)])
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("f32", 64)])
+def test_cubic_windows_all_rows(oracle_mod, window, dtype, head_dim):
+    """The window ablation's neighbourhoods ([HetA] Table 7; 11^3 is the
+    default): every row of a ragged grid larger than the window in each axis."""
+    w, q, k, v, u = small_case((15, 18, 29), 2, head_dim, dtype, batch=1, seed=20 + window[0],
+                               window=window)
+    full_parity(oracle_mod, w, q, k, v, u, rho=0.2, what=f"window {window}")
+
+
 def test_window_covering_grid_equals_dense(oracle_mod):
     w, q, k, v, u = small_case((3, 4, 5), 2, 128, "f32", batch=1, seed=8, window=(5, 9, 11))
     got_local, ref, _ = full_parity(oracle_mod, w, q, k, v, u, rho=0.0, what="cover-local")
@@ -121,7 +131,8 @@ def sampled_rows(mask_b: np.ndarray, n_each: int, rng) -> np.ndarray:
 
 
 @pytest.mark.parametrize("name,rho", [("wan13b", 0.2), ("wan5b", 0.2), ("long", 0.2),
-                                      ("wan13b", 1.0), ("wan13b", 0.05)])
+                                      ("wan13b", 1.0), ("wan13b", 0.05), ("wan13b_w11", 0.2),
+                                      ("wan5b_w11", 0.2), ("wan13b_w11", 0.0)])
 def test_full_size_sampled_rows(oracle_mod, name, rho):
     w = W.WORKLOADS[name]
     q, k, v = W.make_qkv(w)

@@ -279,7 +279,9 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
 
 // ------------------------------------------------------------ bf16 path ----
 // One workgroup = kBandWaves waves = 2 query frames (t, t+1) x kBandNW
-// x-tiles of 4 (h) x 8 (w) queries, all on the rows ybase .. ybase+3.  The
+// x-tiles of QY (h) x QX (w) = 32 queries, all on the rows ybase ..
+// ybase+QY-1 (QY = 4 or 8, chosen per window: the tile whose key box takes
+// the fewest 32-key blocks per frame).  The
 // tiles of a workgroup share one key box: the frames [F0, F1) that the two
 // frames' windows cover x ny rows x C columns (the union of the tiles' column
 // windows).  The box goes through LDS in bands of rpb = 32/SR rows of one
@@ -292,14 +294,14 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
 constexpr int kBandNW = 4;
 constexpr int kBandWaves = 2 * kBandNW;
 
-template <int D, int SR>
+template <int D, int SR, int QX>
 struct BandGeom {
     static constexpr int rpb = 32 / SR;                          // box rows per band
     static constexpr int kCpr = D / 8;                           // 16-byte chunks per token row
     static constexpr int kTokPerLoad = 64 / kCpr;                // token rows per wave DMA (1 KB)
-    static constexpr int kMaxLw = SR == 16 ? 16 - kLocalQX + 1 : kLocalMaxWinW;
+    static constexpr int kMaxLw = SR == 16 ? 16 - QX + 1 : kLocalMaxWinW;
     // LDS rows per box row: the widest workgroup box, in whole DMA loads.
-    static constexpr int kCb = (kBandNW * kLocalQX + kMaxLw - 1 + kTokPerLoad - 1) / kTokPerLoad * kTokPerLoad;
+    static constexpr int kCb = (kBandNW * QX + kMaxLw - 1 + kTokPerLoad - 1) / kTokPerLoad * kTokPerLoad;
     static constexpr int kBandRows = rpb * kCb;
     static constexpr int kLoads = kBandRows / kTokPerLoad;      // DMA loads per tensor and band
     static constexpr int kLoadsPerWave = (kLoads + kBandWaves - 1) / kBandWaves;
@@ -307,12 +309,13 @@ struct BandGeom {
 };
 
 
-template <int D, int SR>
+template <int D, int SR, int QY>
 __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const uint8_t *__restrict__ mask, int N, int H, float scale_log2, LocalGeom g,
     int n_units, int x_blocks, int t_pairs) {
-    using Bg = BandGeom<D, SR>;
+    constexpr int QX = 32 / QY;
+    using Bg = BandGeom<D, SR, QX>;
     constexpr int rpb = Bg::rpb, NC = D / 16, NDB = D / 32;
     __shared__ __attribute__((aligned(1024))) __bf16 Kb0[Bg::kBufElems];
     __shared__ __attribute__((aligned(1024))) __bf16 Kb1[Bg::kBufElems];
@@ -335,12 +338,12 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     const int gq = lane >> 4, j16 = lane & 15;
 
     // Workgroup box (uniform).
-    const int ybase = ty * kLocalQY;
+    const int ybase = ty * QY;
     const int uy0 = window_start(ybase, g.wh, g.lh, g.Hg);
-    const int ny = window_start(imin(ybase + kLocalQY - 1, g.Hg - 1), g.wh, g.lh, g.Hg) + g.lh - uy0;
+    const int ny = window_start(imin(ybase + QY - 1, g.Hg - 1), g.wh, g.lh, g.Hg) + g.lh - uy0;
     const int xt0 = xb * kBandNW, xt1 = imin(xt0 + kBandNW, g.tiles_x) - 1;
-    const int ux0 = window_start(xt0 * kLocalQX, g.ww, g.lw, g.Wg);
-    const int C = window_start(imin(xt1 * kLocalQX + kLocalQX - 1, g.Wg - 1), g.ww, g.lw, g.Wg) + g.lw - ux0;
+    const int ux0 = window_start(xt0 * QX, g.ww, g.lw, g.Wg);
+    const int C = window_start(imin(xt1 * QX + QX - 1, g.Wg - 1), g.ww, g.lw, g.Wg) + g.lw - ux0;
     const int tA = 2 * tp, tB = imin(tA + 1, g.T - 1);
     const int F0 = window_start(tA, g.wt, g.lt, g.T);
     const int F1 = window_start(tB, g.wt, g.lt, g.T) + g.lt;
@@ -351,8 +354,8 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     const int xt = xt0 + wave % kBandNW;
     const int t = tA + wave / kBandNW;
     const bool wave_on = t < g.T && xt < g.tiles_x;
-    const int xbase = xt * kLocalQX;
-    const int y = ybase + col / kLocalQX, x = xbase + col % kLocalQX;
+    const int xbase = xt * QX;
+    const int y = ybase + col / QX, x = xbase + col % QX;
     const bool in_grid = wave_on && y < g.Hg && x < g.Wg;
     const int tok = in_grid ? (t * g.Hg + y) * g.Wg + x : 0;
     const bool is_local = in_grid && mask[(size_t)b * N + tok] != 0;
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     const int qy0 = window_start(imin(y, g.Hg - 1), g.wh, g.lh, g.Hg);
     const int qx0 = window_start(imin(x, g.Wg - 1), g.ww, g.lw, g.Wg);
     const int uxw = window_start(imin(xbase, g.Wg - 1), g.ww, g.lw, g.Wg);
-    const int nxw = window_start(imin(xbase + kLocalQX - 1, g.Wg - 1), g.ww, g.lw, g.Wg) + g.lw - uxw;
+    const int nxw = window_start(imin(xbase + QX - 1, g.Wg - 1), g.ww, g.lw, g.Wg) + g.lw - uxw;
     const int cw = uxw - ux0;  // this tile's box inside the workgroup box
 
     const size_t tok_stride = (size_t)H * D;
@@ -565,17 +568,37 @@ hipError_t launch_local(const AttnArgs &a, hipStream_t stream) {
                        (const T_ *)a.k, (const T_ *)a.v, (T_ *)a.o, a.mask, a.n, a.heads, sl2, g, units)
     const bool sr16 = g.slot_row == 16;
     if (a.bf16) {
-        const int x_blocks = (g.tiles_x + kBandNW - 1) / kBandNW, t_pairs = (g.T + 1) / 2;
-        const int band_units = a.batch * a.heads * t_pairs * g.tiles_y * x_blocks;
+        // Tile shape: 4x8 or 8x4 queries, whichever needs fewer 32-key blocks
+        // per key frame (box rows / rows per block).
+        auto blocks_per_frame = [&](int qy) {
+            const int qx = 32 / qy, nx = qx + g.lw - 1, rows = qy + g.lh - 1;
+            const int rpb = nx <= 16 ? 2 : 1;
+            return nx > 32 ? 1 << 30 : (rows + rpb - 1) / rpb;
+        };
+        const int qy = blocks_per_frame(8) < blocks_per_frame(4) ? 8 : 4, qx = 32 / qy;
+        LocalGeom gb = g;
+        gb.tiles_y = (a.grid_h + qy - 1) / qy;
+        gb.tiles_x = (a.grid_w + qx - 1) / qx;
+        const bool b16 = qx + g.lw - 1 <= 16;
+        const int x_blocks = (gb.tiles_x + kBandNW - 1) / kBandNW, t_pairs = (g.T + 1) / 2;
+        const int band_units = a.batch * a.heads * t_pairs * gb.tiles_y * x_blocks;
         const dim3 bgrid((band_units + 7) / 8 * 8), bblock(64 * kBandWaves);
-#define HET_BAND_LAUNCH(D_, SR_)                                                                       \
-    hipLaunchKernelGGL((local_band_kernel<D_, SR_>), bgrid, bblock, 0, stream, (const __bf16 *)a.q,    \
-                       (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, a.mask, a.n, a.heads, sl2, g, \
+#define HET_BAND_LAUNCH(D_, SR_, QY_)                                                                  \
+    hipLaunchKernelGGL((local_band_kernel<D_, SR_, QY_>), bgrid, bblock, 0, stream, (const __bf16 *)a.q, \
+                       (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, a.mask, a.n, a.heads, sl2, gb, \
                        band_units, x_blocks, t_pairs)
         if (a.head_dim == 128) {
-            if (sr16) HET_BAND_LAUNCH(128, 16); else HET_BAND_LAUNCH(128, 32);
+            if (qy == 4) {
+                if (b16) HET_BAND_LAUNCH(128, 16, 4); else HET_BAND_LAUNCH(128, 32, 4);
+            } else {
+                if (b16) HET_BAND_LAUNCH(128, 16, 8); else HET_BAND_LAUNCH(128, 32, 8);
+            }
         } else {
-            if (sr16) HET_BAND_LAUNCH(64, 16); else HET_BAND_LAUNCH(64, 32);
+            if (qy == 4) {
+                if (b16) HET_BAND_LAUNCH(64, 16, 4); else HET_BAND_LAUNCH(64, 32, 4);
+            } else {
+                if (b16) HET_BAND_LAUNCH(64, 16, 8); else HET_BAND_LAUNCH(64, 32, 8);
+            }
         }
 #undef HET_BAND_LAUNCH
     } else {

@@ -69,6 +69,12 @@ WORKLOADS = {
 # rho sweep on the Wan2.1-1.3B layer shape, same seeded inputs as "wan13b".
 RHO_SWEEP = (0.05, 0.1, 0.2, 0.4, 1.0)
 
+# Local neighbourhoods of the paper's window ablation (Table 7; 11x11x11 is
+# its default), on the same seeded inputs as the 3x7x7 workloads.
+WINDOW_SWEEP = ((9, 9, 9), (11, 11, 11), (13, 13, 13))
+WORKLOADS["wan13b_w11"] = WORKLOADS["wan13b"].with_(name="wan13b_w11", window=(11, 11, 11))
+WORKLOADS["wan5b_w11"] = WORKLOADS["wan5b"].with_(name="wan5b_w11", window=(11, 11, 11))
+
 
 def _rng(config_id: int, tensor_id: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(1000 * config_id + tensor_id))
