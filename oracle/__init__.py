@@ -65,10 +65,14 @@ def _load():
         lib.oracle_route_top_rho.argtypes = [P, i, i, ctypes.c_double, P, P, P, P, P]
         lib.oracle_route_mean_std.argtypes = [P, i, i, ctypes.c_double, P, P, P, P, P]
         lib.oracle_window_axis.argtypes = [i, i, i, P, P]
-        lib.oracle_attend_rows.argtypes = [P, P, P, i, i, i, i, i, i, i, i, i,
+        lib.oracle_window_axis_cut.argtypes = [i, i, i, P, P]
+        lib.oracle_attend_rows.argtypes = [P, P, P, i, i, i, i, i, i, i, i, i, i,
                                            ctypes.c_double, P, P, ctypes.c_long, P, i]
-        lib.oracle_attention_weights.argtypes = [P, P, i, i, i, i, i, i, i, i, i,
+        lib.oracle_attention_weights.argtypes = [P, P, i, i, i, i, i, i, i, i, i, i,
                                                  ctypes.c_double, P, ctypes.c_long, i, P]
+        lib.oracle_route_uniform.argtypes = [i, i, ctypes.c_double, P, P, P, P]
+        lib.oracle_route_random.argtypes = [i, i, ctypes.c_double, ctypes.c_ulonglong, ctypes.c_uint,
+                                            ctypes.c_uint, P, P, P, P]
         lib.oracle_philox4x32_10.argtypes = [P, P, P]
         lib.oracle_philox4x32_10.restype = None
         lib.oracle_swap_draws.argtypes = [i, ctypes.c_uint, ctypes.c_ulonglong, ctypes.c_uint,
@@ -77,7 +81,8 @@ def _load():
         lib.oracle_route_swap.argtypes = [P, i, i, ctypes.c_double, ctypes.c_ulonglong, ctypes.c_uint,
                                           ctypes.c_uint, P, P, P, P]
         for fn in (lib.oracle_route_top_rho, lib.oracle_route_mean_std, lib.oracle_window_axis,
-                   lib.oracle_attend_rows, lib.oracle_attention_weights, lib.oracle_route_swap):
+                   lib.oracle_attend_rows, lib.oracle_attention_weights, lib.oracle_route_swap,
+                   lib.oracle_window_axis_cut, lib.oracle_route_uniform, lib.oracle_route_random):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -156,10 +161,41 @@ def swap_draws(N: int, b: int, seed: int, step: int, block: int) -> np.ndarray:
     return out
 
 
-def window_axis(S: int, k: int, pos: int) -> tuple[int, int]:
+def _routes_out(B: int, N: int):
+    return (np.empty((B, N), np.uint8), np.empty((B, N), np.int32), np.empty((B, N), np.int32),
+            np.empty((B, 2), np.int32))
+
+
+def route_uniform(B: int, N: int, rho: float) -> Route:
+    """Fixed uniform routing ([HetA §5.1, Table 6]; see oracle_route_uniform).
+    thresh is not defined and is returned as NaN."""
+    mask, di, li, counts = _routes_out(B, N)
+    rc = _load().oracle_route_uniform(int(B), int(N), float(rho), _ptr(mask), _ptr(di), _ptr(li),
+                                      _ptr(counts))
+    if rc != 0:
+        raise ValueError(f"oracle_route_uniform rejected its arguments (rc={rc})")
+    return Route(mask, di, li, counts, np.full(B, np.nan))
+
+
+def route_random(B: int, N: int, rho: float, seed: int, step: int, block: int) -> Route:
+    """Random routing per block ([HetA §5.1, Table 6]; see oracle_route_random).
+    thresh is not defined and is returned as NaN."""
+    mask, di, li, counts = _routes_out(B, N)
+    rc = _load().oracle_route_random(int(B), int(N), float(rho), int(seed), int(step), int(block),
+                                     _ptr(mask), _ptr(di), _ptr(li), _ptr(counts))
+    if rc != 0:
+        raise ValueError(f"oracle_route_random rejected its arguments (rc={rc})")
+    return Route(mask, di, li, counts, np.full(B, np.nan))
+
+
+_BORDER = {"shift": 0, "truncate": 1}
+
+
+def window_axis(S: int, k: int, pos: int, border: str = "shift") -> tuple[int, int]:
     start = ctypes.c_int()
     length = ctypes.c_int()
-    rc = _load().oracle_window_axis(S, k, pos, ctypes.addressof(start), ctypes.addressof(length))
+    fn = _load().oracle_window_axis if _BORDER[border] == 0 else _load().oracle_window_axis_cut
+    rc = fn(S, k, pos, ctypes.addressof(start), ctypes.addressof(length))
     if rc != 0:
         raise ValueError("bad window arguments")
     return start.value, length.value
@@ -169,7 +205,8 @@ def _as_f32(x: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(x, dtype=np.float32)
 
 
-def attend_rows(q, k, v, grid, window, scale, mask, rows, nthreads: int = 0) -> np.ndarray:
+def attend_rows(q, k, v, grid, window, scale, mask, rows, nthreads: int = 0,
+                border: str = "shift") -> np.ndarray:
     """Outputs [len(rows), heads, D] (float64) for rows = b*N + n."""
     q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
     B, N, H, D = q.shape
@@ -181,21 +218,24 @@ def attend_rows(q, k, v, grid, window, scale, mask, rows, nthreads: int = 0) -> 
     out = np.empty((rows.size, H, D), np.float64)
     wt, wh, ww = window
     rc = _load().oracle_attend_rows(_ptr(q), _ptr(k), _ptr(v), B, H, D, T, Hg, Wg, wt, wh, ww,
-                                    float(scale), _ptr(mask), _ptr(rows), rows.size, _ptr(out),
+                                    _BORDER[border], float(scale), _ptr(mask), _ptr(rows), rows.size, _ptr(out),
                                     int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_attend_rows rejected its arguments (rc={rc})")
     return out
 
 
-def forward(q, k, v, grid, window, scale, mask, nthreads: int = 0) -> np.ndarray:
+def forward(q, k, v, grid, window, scale, mask, nthreads: int = 0,
+            border: str = "shift") -> np.ndarray:
     """Outputs [B, N, heads, D] (float64) for every token."""
     B, N, H, D = q.shape
     rows = np.arange(B * N, dtype=np.int64)
-    return attend_rows(q, k, v, grid, window, scale, mask, rows, nthreads).reshape(B, N, H, D)
+    return attend_rows(q, k, v, grid, window, scale, mask, rows, nthreads,
+                       border).reshape(B, N, H, D)
 
 
-def attention_weights(q, k, grid, window, scale, mask, row: int, head: int) -> np.ndarray:
+def attention_weights(q, k, grid, window, scale, mask, row: int, head: int,
+                      border: str = "shift") -> np.ndarray:
     q, k = _as_f32(q), _as_f32(k)
     B, N, H, D = q.shape
     T, Hg, Wg = grid
@@ -203,7 +243,7 @@ def attention_weights(q, k, grid, window, scale, mask, row: int, head: int) -> n
     w = np.empty(N, np.float64)
     wt, wh, ww = window
     rc = _load().oracle_attention_weights(_ptr(q), _ptr(k), B, H, D, T, Hg, Wg, wt, wh, ww,
-                                          float(scale), _ptr(mask), int(row), int(head), _ptr(w))
+                                          _BORDER[border], float(scale), _ptr(mask), int(row), int(head), _ptr(w))
     if rc != 0:
         raise ValueError("oracle_attention_weights rejected its arguments")
     return w

@@ -248,6 +248,66 @@ void oracle_swap_draws(int N, unsigned int b, unsigned long long seed, unsigned 
     }
 }
 
+/* Dense count of the rho-based routers: floor(rho*N + 1/2), clamped. */
+static long rho_count(double rho, int N)
+{
+    double k = floor((double)N * rho + 0.5);
+    if (k < 0.0) k = 0.0;
+    if (k > (double)N) k = (double)N;
+    return (long)k;
+}
+
+int oracle_route_uniform(int B, int N, double rho, unsigned char *mask, int *dense_idx,
+                         int *local_idx, int *counts)
+{
+    if (!mask || !dense_idx || !local_idx || !counts || B <= 0 || N <= 0) return -1;
+    if (!(rho >= 0.0 && rho <= 1.0)) return -1;
+    const long K = rho_count(rho, N);
+    unsigned char *dense = (unsigned char *)calloc((size_t)N, 1);
+    if (!dense) return -2;
+    /* K lattice points over the flattened volume, starting at token 0. */
+    for (long j = 0; j < K; j++) dense[j * (long)N / K] = 1;
+    for (int b = 0; b < B; b++)
+        write_route(dense, N, mask + (size_t)b * N, dense_idx + (size_t)b * N,
+                    local_idx + (size_t)b * N, counts + 2 * b);
+    free(dense);
+    return 0;
+}
+
+int oracle_route_random(int B, int N, double rho, unsigned long long seed, unsigned int step,
+                        unsigned int block, unsigned char *mask, int *dense_idx, int *local_idx,
+                        int *counts)
+{
+    if (!mask || !dense_idx || !local_idx || !counts || B <= 0 || N <= 0) return -1;
+    if (!(rho >= 0.0 && rho <= 1.0)) return -1;
+    const long K = rho_count(rho, N);
+    keyed_token *tok = (keyed_token *)malloc(sizeof(keyed_token) * (size_t)N);
+    unsigned int *x = (unsigned int *)malloc(sizeof(unsigned int) * (size_t)N);
+    unsigned char *dense = (unsigned char *)malloc((size_t)N);
+    if (!tok || !x || !dense) {
+        free(tok);
+        free(x);
+        free(dense);
+        return -2;
+    }
+    for (int b = 0; b < B; b++) {
+        oracle_swap_draws(N, (unsigned int)b, seed, step, block, x);
+        for (int i = 0; i < N; i++) {
+            tok[i].key = x[i];
+            tok[i].idx = i;
+            dense[i] = 0;
+        }
+        qsort(tok, (size_t)N, sizeof(keyed_token), key_cmp);
+        for (long j = 0; j < K; j++) dense[tok[j].idx] = 1;
+        write_route(dense, N, mask + (size_t)b * N, dense_idx + (size_t)b * N,
+                    local_idx + (size_t)b * N, counts + 2 * b);
+    }
+    free(tok);
+    free(x);
+    free(dense);
+    return 0;
+}
+
 int oracle_window_axis(int S, int k, int pos, int *start, int *len)
 {
     if (S <= 0 || k <= 0 || (k % 2) == 0 || pos < 0 || pos >= S || !start || !len)
@@ -258,6 +318,19 @@ int oracle_window_axis(int S, int k, int pos, int *start, int *len)
     if (s < 0) s = 0;
     *start = s;
     *len = L;
+    return 0;
+}
+
+int oracle_window_axis_cut(int S, int k, int pos, int *start, int *len)
+{
+    if (S <= 0 || k <= 0 || (k % 2) == 0 || pos < 0 || pos >= S || !start || !len)
+        return -1;
+    const int h = (k - 1) / 2;
+    int lo = pos - h, hi = pos + h + 1; /* centred on pos ... */
+    if (lo < 0) lo = 0;                 /* ... and cut at the grid border */
+    if (hi > S) hi = S;
+    *start = lo;
+    *len = hi - lo;
     return 0;
 }
 
@@ -294,9 +367,10 @@ static void attend_one(const float *qrow, const float *kbase, const float *vbase
 }
 
 /* The key set of token n: every token of the sample when dense (mask 0),
- * else the 3D box of [HetA §3.1.1 Eq. 3] in t-major order. */
+ * else the 3D box of [HetA §3.1.1 Eq. 3] in t-major order, shifted inside
+ * the grid (border 0) or cut at its border (border 1). */
 static int key_set(int n, unsigned char is_local, int T, int Hg, int Wg,
-                   int wt, int wh, int ww, int *keys)
+                   int wt, int wh, int ww, int border, int *keys)
 {
     int N = T * Hg * Wg;
     if (!is_local) {
@@ -305,9 +379,15 @@ static int key_set(int n, unsigned char is_local, int T, int Hg, int Wg,
     }
     int t = n / (Hg * Wg), y = (n / Wg) % Hg, x = n % Wg;
     int t0, lt, y0, ly, x0, lx;
-    oracle_window_axis(T, wt, t, &t0, &lt);
-    oracle_window_axis(Hg, wh, y, &y0, &ly);
-    oracle_window_axis(Wg, ww, x, &x0, &lx);
+    if (border == 0) {
+        oracle_window_axis(T, wt, t, &t0, &lt);
+        oracle_window_axis(Hg, wh, y, &y0, &ly);
+        oracle_window_axis(Wg, ww, x, &x0, &lx);
+    } else {
+        oracle_window_axis_cut(T, wt, t, &t0, &lt);
+        oracle_window_axis_cut(Hg, wh, y, &y0, &ly);
+        oracle_window_axis_cut(Wg, ww, x, &x0, &lx);
+    }
     int m = 0;
     for (int a = t0; a < t0 + lt; a++)
         for (int bb = y0; bb < y0 + ly; bb++)
@@ -316,8 +396,9 @@ static int key_set(int n, unsigned char is_local, int T, int Hg, int Wg,
 }
 
 static int check_shape(int B, int heads, int D, int T, int Hg, int Wg, int wt,
-                       int wh, int ww)
+                       int wh, int ww, int border)
 {
+    if (border != 0 && border != 1) return -1;
     if (B <= 0 || heads <= 0 || D <= 0 || T <= 0 || Hg <= 0 || Wg <= 0) return -1;
     if (wt <= 0 || wh <= 0 || ww <= 0) return -1;
     if (wt % 2 == 0 || wh % 2 == 0 || ww % 2 == 0) return -1;
@@ -326,12 +407,12 @@ static int check_shape(int B, int heads, int D, int T, int Hg, int Wg, int wt,
 
 int oracle_attend_rows(const float *q, const float *k, const float *v,
                        int B, int heads, int D,
-                       int T, int Hg, int Wg, int wt, int wh, int ww,
+                       int T, int Hg, int Wg, int wt, int wh, int ww, int border,
                        double scale, const unsigned char *mask,
                        const long *rows, long nrows, double *out, int nthreads)
 {
     if (!q || !k || !v || !mask || !rows || !out) return -1;
-    if (check_shape(B, heads, D, T, Hg, Wg, wt, wh, ww)) return -1;
+    if (check_shape(B, heads, D, T, Hg, Wg, wt, wh, ww, border)) return -1;
     const long N = (long)T * Hg * Wg;
     for (long r = 0; r < nrows; r++)
         if (rows[r] < 0 || rows[r] >= (long)B * N) return -1;
@@ -353,7 +434,7 @@ int oracle_attend_rows(const float *q, const float *k, const float *v,
 #pragma omp for schedule(dynamic, 1)
             for (long r = 0; r < nrows; r++) {
                 long b = rows[r] / N, n = rows[r] % N;
-                int nk = key_set((int)n, mask[b * N + n], T, Hg, Wg, wt, wh, ww, keys);
+                int nk = key_set((int)n, mask[b * N + n], T, Hg, Wg, wt, wh, ww, border, keys);
                 for (int h = 0; h < heads; h++) {
                     const float *qrow = q + (b * N + n) * tok_stride + (long)h * D;
                     const float *kb = k + b * N * tok_stride + (long)h * D;
@@ -371,12 +452,12 @@ int oracle_attend_rows(const float *q, const float *k, const float *v,
 
 int oracle_attention_weights(const float *q, const float *k,
                              int B, int heads, int D,
-                             int T, int Hg, int Wg, int wt, int wh, int ww,
+                             int T, int Hg, int Wg, int wt, int wh, int ww, int border,
                              double scale, const unsigned char *mask,
                              long row, int head, double *weights)
 {
     if (!q || !k || !mask || !weights) return -1;
-    if (check_shape(B, heads, D, T, Hg, Wg, wt, wh, ww)) return -1;
+    if (check_shape(B, heads, D, T, Hg, Wg, wt, wh, ww, border)) return -1;
     const long N = (long)T * Hg * Wg;
     if (row < 0 || row >= (long)B * N || head < 0 || head >= heads) return -1;
     const long tok_stride = (long)heads * D;
@@ -389,7 +470,7 @@ int oracle_attention_weights(const float *q, const float *k,
         free(keys); free(s); free(w); free(o);
         return -2;
     }
-    int nk = key_set((int)n, mask[b * N + n], T, Hg, Wg, wt, wh, ww, keys);
+    int nk = key_set((int)n, mask[b * N + n], T, Hg, Wg, wt, wh, ww, border, keys);
     const float *qrow = q + (b * N + n) * tok_stride + (long)head * D;
     const float *kb = k + b * N * tok_stride + (long)head * D;
     attend_one(qrow, kb, NULL, tok_stride, D, keys, nk, scale, s, o, w);

@@ -71,20 +71,46 @@ int oracle_route_swap(const unsigned char *mask_in, int B, int N, double r,
 void oracle_swap_draws(int N, unsigned int b, unsigned long long seed, unsigned int step,
                        unsigned int block, unsigned int *out);
 
+/* Fixed uniform routing, the ablation router of [HetA §5.1, Routing
+ * Strategy, Table 6], which picks tokens evenly over the token volume with a
+ * fixed pattern.  The pattern is not given; reading: K = floor(rho*N + 1/2)
+ * lattice points over the flattened (t-major) volume, the j-th dense token
+ * being floor(j*N/K), j = 0 .. K-1; the same for every sample, step and
+ * block.  Writes the route like oracle_route_top_rho (no thresh). */
+int oracle_route_uniform(int B, int N, double rho, unsigned char *mask, int *dense_idx,
+                         int *local_idx, int *counts);
+
+/* Random routing, the ablation router of [HetA §5.1, Routing Strategy,
+ * Table 6]: at every block an independent random subset of K =
+ * floor(rho*N + 1/2) tokens is dense.  Reading: the K tokens with the smallest
+ * draw of oracle_swap_draws(N, b, seed, step, block) (equal draws: smaller
+ * index first).  Writes the route like oracle_route_top_rho (no thresh). */
+int oracle_route_random(int B, int N, double rho, unsigned long long seed, unsigned int step,
+                        unsigned int block, unsigned char *mask, int *dense_idx, int *local_idx,
+                        int *counts);
+
 /* The local neighbourhood of [HetA §3.1.1 Eq. 3] along one axis of extent S
  * for an odd window k at coordinate pos: length min(k, S), start shifted so
  * the box stays inside [0, S). */
 int oracle_window_axis(int S, int k, int pos, int *start, int *len);
 
+/* The other reading of the window border: the window of odd size k centred
+ * on pos, cut at the border of [0, S): start = max(pos - (k-1)/2, 0),
+ * end = min(pos + (k-1)/2 + 1, S), len = end - start (fewer keys near the
+ * border). */
+int oracle_window_axis_cut(int S, int k, int pos, int *start, int *len);
+
 /* Heterogeneous attention [HetA §3.2.2 Eq. 13] for a list of rows.
  * rows[r] = b*N + n selects the token; out[r*heads*D + h*D + d] receives the
  * output of every head.  A token with mask 0 attends to all N tokens of its
  * sample ([HetA §3.1.1 Eq. 2]); a token with mask 1 attends to its 3D window
- * ([HetA §3.1.1 Eq. 3]).  Softmax is taken over the key set with the given
- * scale.  nthreads <= 0 uses the OpenMP default. */
+ * ([HetA §3.1.1 Eq. 3]), shifted inside the grid (border 0, oracle_window_axis)
+ * or cut at its border (border 1, oracle_window_axis_cut).  Softmax is taken
+ * over the key set with the given scale.  nthreads <= 0 uses the OpenMP
+ * default. */
 int oracle_attend_rows(const float *q, const float *k, const float *v,
                        int B, int heads, int D,
-                       int T, int Hg, int Wg, int wt, int wh, int ww,
+                       int T, int Hg, int Wg, int wt, int wh, int ww, int border,
                        double scale, const unsigned char *mask,
                        const long *rows, long nrows, double *out, int nthreads);
 
@@ -93,7 +119,7 @@ int oracle_attend_rows(const float *q, const float *k, const float *v,
  * key set).  Used to check support and normalisation. */
 int oracle_attention_weights(const float *q, const float *k,
                              int B, int heads, int D,
-                             int T, int Hg, int Wg, int wt, int wh, int ww,
+                             int T, int Hg, int Wg, int wt, int wh, int ww, int border,
                              double scale, const unsigned char *mask,
                              long row, int head, double *weights);
 

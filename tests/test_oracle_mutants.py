@@ -42,6 +42,15 @@ MUTANTS = {
     "swap_not_capped_by_local_set": ("if (S > nl) S = nl;", ""),
     "swap_ties_higher_index_first": ("return (a->idx < b->idx) ? -1 : 1;",
                                      "return (a->idx < b->idx) ? 1 : -1;"),
+    # ablation routers and the cut window border
+    "uniform_lattice_ends_segments": ("dense[j * (long)N / K] = 1;",
+                                      "dense[(j * (long)N + K - 1) / K] = 1;"),
+    "router_count_truncated": ("floor((double)N * rho + 0.5)", "floor((double)N * rho)"),
+    "random_largest_draws": ("for (long j = 0; j < K; j++) dense[tok[j].idx] = 1;",
+                             "for (long j = 0; j < K; j++) dense[tok[N - 1 - j].idx] = 1;"),
+    "cut_window_short_high_side": ("int lo = pos - h, hi = pos + h + 1;", "int lo = pos - h, hi = pos + h;"),
+    "cut_border_uses_shifted_window": ("    if (border == 0) {\n        oracle_window_axis(T,",
+                                       "    if (border >= 0) {\n        oracle_window_axis(T,"),
 }
 
 
@@ -60,6 +69,7 @@ def test_planted_mistake_is_caught(name, tmp_path):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_route.py"),
                         os.path.join(ROOT, "tests", "test_oracle_attention.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_swap.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_swap.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_variants.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"planted mistake {name!r} passed every pin:\n{r.stdout[-2000:]}"
