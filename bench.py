@@ -66,7 +66,7 @@ class Layer:
     """Pre-built ctypes arguments for one workload, so the timed loop issues
     three library calls per step and nothing else."""
 
-    def __init__(self, het, w, q, k, v, u, rho):
+    def __init__(self, het, w, q, k, v, u, rho, router="top_rho", border="shift"):
         import torch
         self.het, self.lib, self.w = het, het.load_library(), w
         B, N = w.batch, w.n_tokens
@@ -78,7 +78,8 @@ class Layer:
         self.lidx = torch.empty((B, N), dtype=torch.int32, device=dev)
         self.counts = torch.empty((B, 2), dtype=torch.int32, device=dev)
         self.thresh = torch.empty((B,), dtype=torch.float64, device=dev)
-        self.shape = het.make_shape(B, w.heads, w.head_dim, w.grid, w.window, het.HET_BF16)
+        self.shape = het.make_shape(B, w.heads, w.head_dim, w.grid, w.window, het.HET_BF16, border=border)
+        self.router = router
         self.rs = het.RouteStruct(self.mask.data_ptr(), self.didx.data_ptr(), self.lidx.data_ptr(),
                                   self.counts.data_ptr(), self.thresh.data_ptr(), -1)
         self.rho = float(rho)
@@ -90,10 +91,15 @@ class Layer:
                      ctypes.byref(self.rs), self.o.data_ptr(), self.ws.data_ptr(), ws, self.stream)
 
     def route(self):
-        st = self.lib.het_attn_route(ctypes.byref(self.shape), self.u.data_ptr(), self.het.HET_TOP_RHO,
-                                     self.rho, ctypes.byref(self.rs), self.stream)
+        if self.router == "random":
+            st = self.lib.het_attn_route_random(ctypes.byref(self.shape), self.rho, 12345, 0, 0, 1,
+                                                ctypes.byref(self.rs), self.stream)
+        else:
+            mode = self.het.HET_UNIFORM if self.router == "uniform" else self.het.HET_TOP_RHO
+            st = self.lib.het_attn_route(ctypes.byref(self.shape), self.u.data_ptr(), mode, self.rho,
+                                         ctypes.byref(self.rs), self.stream)
         if st != 0:
-            raise self.het.HetAttnError(st, "het_attn_route")
+            raise self.het.HetAttnError(st, "route (" + self.router + ")")
 
     def local(self):
         st = self.lib.het_attn_local(*self.args)
@@ -104,6 +110,33 @@ class Layer:
         st = self.lib.het_attn_dense(*self.args)
         if st != 0:
             raise self.het.HetAttnError(st, "het_attn_dense")
+
+
+def window_lengths(S: int, k: int, cut: bool):
+    """Keys of the window along one axis for every position (shifted windows
+    hold min(k, S); cut windows lose the positions past the border)."""
+    import numpy as np
+    pos = np.arange(S)
+    if not cut:
+        return np.full(S, min(k, S))
+    h = (k - 1) // 2
+    return np.minimum(pos + h + 1, S) - np.maximum(pos - h, 0)
+
+
+def effective_flops_routed(w, mask, border: str) -> float:
+    """4*D*heads*(sum of dense keys + sum of local window keys) for the route
+    `mask` ([B, N], 1 = local): Eq. 14's terms, with the window size of each
+    local token (constant M for shifted windows)."""
+    import numpy as np
+    T, H, Wd = w.grid
+    cut = border == "cut"
+    M = (window_lengths(T, w.window[0], cut)[:, None, None] * window_lengths(H, w.window[1], cut)[None, :, None]
+         * window_lengths(Wd, w.window[2], cut)[None, None, :]).reshape(-1).astype(np.float64)
+    total = 0.0
+    for b in range(mask.shape[0]):
+        local = mask[b] != 0
+        total += float((~local).sum()) * w.n_tokens + float(M[local].sum())
+    return 4.0 * w.head_dim * w.heads * total
 
 
 def time_layer(layer, steps: int, warmup: int, scrub=None):
@@ -288,6 +321,10 @@ def main():
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the rho sweep on the Wan-1.3B shape and the other workloads")
+    ap.add_argument("--router", default="top_rho", choices=["top_rho", "uniform", "random"],
+                    help="routing of the timed layer (the ablation routers of the routing study)")
+    ap.add_argument("--border", default="shift", choices=["shift", "cut"],
+                    help="local window border: shifted inside the grid, or cut at it")
     ap.add_argument("--swap-ratio", type=float, default=0.07,
                     help="ratio r of the per-block random swap timed beside the step (0 skips it)")
     ap.add_argument("--oracle-full", action="store_true",
@@ -337,10 +374,10 @@ def main():
     u = torch.from_numpy(un).cuda()
     torch.cuda.synchronize()
 
-    layer = Layer(het, w, q, k, v, u, rho)
+    layer = Layer(het, w, q, k, v, u, rho, router=args.router, border=args.border)
     res = time_layer(layer, args.steps, args.warmup)
     n_dense = [W.dense_count(w.n_tokens, rho)] * w.batch
-    eff_flop = W.effective_flops(w, n_dense)
+    eff_flop = effective_flops_routed(w, layer.mask.cpu().numpy(), args.border)
     dense_flop = 4.0 * w.head_dim * w.heads * sum(kd * w.n_tokens for kd in n_dense)
     bytes_el = 2
     BNHD = w.batch * w.n_tokens * w.heads * w.head_dim
@@ -374,7 +411,8 @@ def main():
                                f"head_dim {w.head_dim}, grid {w.grid[0]}x{w.grid[1]}x{w.grid[2]}",
                    "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim, "grid": list(w.grid),
                    "tokens": w.n_tokens, "rho": rho, "dense_tokens": n_dense,
-                   "window": list(w.window), "u": w.u_kind, "effective_flop": eff_flop},
+                   "window": list(w.window), "u": w.u_kind, "effective_flop": eff_flop,
+                   "router": args.router, "border": args.border},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "kernel": "dense_bf16_kernel<128>",
                      "achieved": round(dense_tflops, 2), "peak": PEAK_BF16_TFLOPS,

@@ -30,12 +30,18 @@
  * HET_MEAN_STD is [HetA §3.2.2 Eq. 11] as printed: T = mu + c*sigma with the
  * mean and population standard deviation of the sample's u (fp64), dense iff
  * u_i >= T.  In both forms a NaN u counts as +inf and -0 as +0.
+ * HET_UNIFORM is the fixed uniform router of the routing ablation ([HetA §5.1,
+ * Routing Strategy, Table 6]), whose pattern the paper does not give: the K
+ * dense tokens are the lattice floor(j*N/K), j = 0 .. K-1, over the flattened
+ * volume, the same for every sample (u is not used; thresh is NaN).
  *
  * Window.  Along each axis of extent S, an odd window k covers min(k, S)
  * positions starting at clamp(pos - (k-1)/2, 0, S - min(k, S)): it is shifted,
  * not cut, at the grid border, so every local token sees the same number of
  * keys M (the constant M of [HetA §3.2.2 Eq. 14]).  A window at least as large
- * as the grid covers the whole axis.
+ * as the grid covers the whole axis.  shape->border = HET_BORDER_CUT selects
+ * the other reading of the border: positions within (k-1)/2 of pos, cut to
+ * [0, S), so tokens near the border see fewer keys.
  *
  * Memory.  All tensor arguments are device pointers owned by the caller; the
  * library allocates and frees nothing and keeps no state between calls.
@@ -58,7 +64,7 @@
 extern "C" {
 #endif
 
-#define HETATTN_ABI_VERSION 1
+#define HETATTN_ABI_VERSION 2
 
 typedef enum {
     HET_OK = 0,
@@ -72,8 +78,14 @@ typedef enum { HET_BF16 = 0, HET_F32 = 1 } het_dtype;
 
 typedef enum {
     HET_TOP_RHO = 0,  /* param = rho in [0, 1] */
-    HET_MEAN_STD = 1  /* param = c, finite */
+    HET_MEAN_STD = 1, /* param = c, finite */
+    HET_UNIFORM = 2   /* param = rho in [0, 1]; u is not read (may be NULL) */
 } het_thresh_mode;
+
+typedef enum {
+    HET_BORDER_SHIFT = 0, /* window shifted to stay inside the grid: M keys for every token */
+    HET_BORDER_CUT = 1    /* window centred on the token and cut at the grid border */
+} het_border;
 
 typedef struct {
     int32_t batch;     /* B >= 1 */
@@ -83,6 +95,7 @@ typedef struct {
     int32_t win_t, win_h, win_w;     /* odd, >= 1 */
     int32_t dtype;     /* het_dtype of Q, K, V and O */
     float scale;       /* softmax scale; <= 0 selects 1/sqrt(head_dim) ([HetA §3.1.1 Eq. 2]) */
+    int32_t border;    /* het_border of the local window (0 = HET_BORDER_SHIFT) */
 } het_attn_shape;
 
 typedef struct {
@@ -91,7 +104,8 @@ typedef struct {
     int32_t *local_idx;  /* [B, N]: local tokens ascending, then -1 */
     int32_t *counts;     /* [B, 2]: (dense count, local count) per sample */
     double *thresh;      /* [B]: T_b (TOP_RHO: u of the K-th ranked token, +inf if K = 0) */
-    int32_t dense_count_host; /* set by het_attn_route: K in TOP_RHO mode, -1 in MEAN_STD mode;
+    int32_t dense_count_host; /* set by het_attn_route: K in TOP_RHO and UNIFORM modes, -1 in
+                               * MEAN_STD mode;
                                * when >= 0 the attention calls size their launches by it, so
                                * it must equal every sample's dense count */
 } het_route;
@@ -107,13 +121,28 @@ const char *het_status_string(int status);
 size_t het_attn_workspace_bytes(const het_attn_shape *shape);
 
 /* Threshold selection, mask and stable compaction ([HetA §3.2.2 Eqs. 11-12]).
- *   u      device, float32 [B, N], read only.
+ *   u      device, float32 [B, N], read only (not read, and may be NULL, for
+ *          HET_UNIFORM).
  *   mode   het_thresh_mode; param = rho (TOP_RHO) or c (MEAN_STD).
  *   out    host struct of caller-owned device buffers, all written;
  *          out->dense_count_host is written on the host.
  * Deterministic: the same u gives bit-identical outputs. */
 int het_attn_route(const het_attn_shape *shape, const float *u, int mode, double param,
                    het_route *out, void *stream);
+
+/* Random routing per block, the other router of the routing ablation
+ * ([HetA §5.1, Routing Strategy, Table 6]): for each block l in
+ * block .. block + n_blocks - 1 and sample b, the K = floor(rho*N + 1/2)
+ * tokens with the smallest draw x_i are dense (equal draws: lower index
+ * first), with x_i drawn as in het_attn_swap (Philox4x32-10 word 0 at counter
+ * (i, b, l, step) under the 64-bit seed).
+ *   rho       in [0, 1].
+ *   n_blocks  1 .. 65535 routes, made by one launch.
+ *   out       as in het_attn_swap: n_blocks routes back to back; thresh
+ *             [n_blocks, B] is NaN (or NULL); out->dense_count_host = K.
+ * Deterministic in (rho, seed, step, block). */
+int het_attn_route_random(const het_attn_shape *shape, double rho, uint64_t seed, uint32_t step,
+                          uint32_t block, int32_t n_blocks, het_route *out, void *stream);
 
 /* Per-block random swap of a route ([HetA §3.2.2], the remark after Eq. 12:
  * at every block some uncertain tokens trade places with randomly chosen

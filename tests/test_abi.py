@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.het_attn_abi_version() == het.ABI_VERSION == 1
+    assert lib.het_attn_abi_version() == het.ABI_VERSION == 2
     for st in range(5):
         assert het.status_string(st)
     assert het.status_string(99) == "unknown status"
@@ -44,8 +44,12 @@ def test_version_and_status_strings(lib):
 
 def good_shape(**kw):
     d = dict(batch=1, heads=2, head_dim=64, grid=(4, 8, 8), window=(3, 3, 3), dtype=het.HET_F32)
+    border = kw.pop("border", None)
     d.update(kw)
-    return het.make_shape(d["batch"], d["heads"], d["head_dim"], d["grid"], d["window"], d["dtype"])
+    s = het.make_shape(d["batch"], d["heads"], d["head_dim"], d["grid"], d["window"], d["dtype"])
+    if border is not None:
+        s.border = border
+    return s
 
 
 def fake_route():
@@ -71,6 +75,8 @@ def call_forward(lib, shape, route=None, q=FAKE, o=FAKE, ws=None, ws_bytes=0):
     (dict(window=(2, 3, 3)), het.HET_ERR_INVALID_ARG),
     (dict(window=(3, 3, 0)), het.HET_ERR_INVALID_ARG),
     (dict(dtype=7), het.HET_ERR_INVALID_ARG),
+    (dict(border=2), het.HET_ERR_INVALID_ARG),
+    (dict(border=-1), het.HET_ERR_INVALID_ARG),
     (dict(head_dim=96), het.HET_ERR_UNSUPPORTED),
     (dict(head_dim=256), het.HET_ERR_UNSUPPORTED),
     (dict(grid=(64, 64, 64), heads=64, head_dim=128, batch=8), het.HET_ERR_UNSUPPORTED),
@@ -105,6 +111,14 @@ def test_route_argument_errors(lib):
     for c in (float("nan"), float("inf"), float("-inf")):
         assert call_route(lib, s, het.HET_MEAN_STD, c) == het.HET_ERR_INVALID_ARG
     assert call_route(lib, s, mode=5) == het.HET_ERR_INVALID_ARG
+    # u may be NULL only for the uniform lattice, which still checks rho
+    for mode in (het.HET_TOP_RHO, het.HET_MEAN_STD):
+        assert call_route(lib, s, mode, 0.2, u=None) == het.HET_ERR_INVALID_ARG
+    for rho in (-0.5, 1.5, float("nan")):
+        assert call_route(lib, s, het.HET_UNIFORM, rho, u=None) == het.HET_ERR_INVALID_ARG
+    r = fake_route()
+    r.local_idx = None
+    assert call_route(lib, s, het.HET_UNIFORM, 0.2, u=None, route=r) == het.HET_ERR_INVALID_ARG
 
 
 def test_forward_argument_errors(lib):
@@ -189,3 +203,24 @@ def test_swap_overlap_errors(lib):
     assert call_swap(lib, s, src, dst(mask=0x10000 + 1)) == het.HET_ERR_INVALID_ARG
     assert call_swap(lib, s, src, dst(thresh=0x50000), n_blocks=2) == het.HET_ERR_INVALID_ARG
     assert call_swap(lib, s, src, dst(mask=0x50000 + 4)) == het.HET_ERR_INVALID_ARG
+
+
+def test_route_random_argument_errors(lib):
+    s = good_shape()
+
+    def call(shape=s, rho=0.2, n_blocks=1, out=None):
+        o = out if out is not None else het.RouteStruct(0x100000, 0x200000, 0x300000, 0x400000, 0, -1)
+        return lib.het_attn_route_random(ctypes.byref(shape) if shape is not None else None, rho, 1, 0, 0,
+                                         n_blocks, ctypes.byref(o) if o is not False else None, None)
+
+    assert call(shape=None) == het.HET_ERR_INVALID_ARG
+    assert call(shape=good_shape(window=(4, 3, 3))) == het.HET_ERR_INVALID_ARG
+    assert call(out=False) == het.HET_ERR_INVALID_ARG
+    for rho in (-0.01, 1.01, float("nan")):
+        assert call(rho=rho) == het.HET_ERR_INVALID_ARG
+    for nb in (0, -3, 65536):
+        assert call(n_blocks=nb) == het.HET_ERR_INVALID_ARG
+    for field in ("mask", "dense_idx", "local_idx", "counts"):
+        o = het.RouteStruct(0x100000, 0x200000, 0x300000, 0x400000, 0, -1)
+        setattr(o, field, None)
+        assert call(out=o) == het.HET_ERR_INVALID_ARG, field

@@ -26,8 +26,10 @@ LIB_PATH = os.path.join(_HERE, "libhetattn.so")
 
 HET_OK, HET_ERR_INVALID_ARG, HET_ERR_UNSUPPORTED, HET_ERR_WORKSPACE, HET_ERR_HIP = range(5)
 HET_BF16, HET_F32 = 0, 1
-HET_TOP_RHO, HET_MEAN_STD = 0, 1
-ABI_VERSION = 1
+HET_TOP_RHO, HET_MEAN_STD, HET_UNIFORM = 0, 1, 2
+HET_BORDER_SHIFT, HET_BORDER_CUT = 0, 1
+ABI_VERSION = 2
+_BORDERS = {"shift": HET_BORDER_SHIFT, "cut": HET_BORDER_CUT}
 
 
 class HetAttnError(RuntimeError):
@@ -40,7 +42,7 @@ class Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("grid_t", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
                 ("win_t", ctypes.c_int32), ("win_h", ctypes.c_int32), ("win_w", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("border", ctypes.c_int32)]
 
 
 class RouteStruct(ctypes.Structure):
@@ -57,6 +59,9 @@ SIGNATURES = {
     "het_attn_route": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_int,
                                       ctypes.c_double, ctypes.POINTER(RouteStruct), ctypes.c_void_p]),
 }
+SIGNATURES["het_attn_route_random"] = (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_double, ctypes.c_uint64,
+                                                      ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int32,
+                                                      ctypes.POINTER(RouteStruct), ctypes.c_void_p])
 SIGNATURES["het_attn_swap"] = (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(RouteStruct),
                                               ctypes.c_double, ctypes.c_uint64, ctypes.c_uint32,
                                               ctypes.c_uint32, ctypes.c_int32,
@@ -92,9 +97,9 @@ def status_string(status: int) -> str:
     return load_library().het_status_string(int(status)).decode()
 
 
-def make_shape(batch, heads, head_dim, grid, window, dtype, scale=0.0) -> Shape:
+def make_shape(batch, heads, head_dim, grid, window, dtype, scale=0.0, border="shift") -> Shape:
     return Shape(int(batch), int(heads), int(head_dim), *[int(g) for g in grid],
-                 *[int(w) for w in window], int(dtype), float(scale))
+                 *[int(w) for w in window], int(dtype), float(scale), _BORDERS[border])
 
 
 def _stream_handle(stream=None) -> int:
@@ -157,6 +162,49 @@ def route(u, grid, window, heads: int, head_dim: int, dtype, rho: float | None =
     return r
 
 
+def _new_routes(n_blocks: int, B: int, N: int, device):
+    import torch
+    return (torch.empty((n_blocks, B, N), dtype=torch.uint8, device=device),
+            torch.empty((n_blocks, B, N), dtype=torch.int32, device=device),
+            torch.empty((n_blocks, B, N), dtype=torch.int32, device=device),
+            torch.empty((n_blocks, B, 2), dtype=torch.int32, device=device),
+            torch.empty((n_blocks, B), dtype=torch.float64, device=device))
+
+
+def route_uniform(batch: int, grid, window, rho: float, device=None, stream=None) -> Route:
+    """Fixed uniform routing (HET_UNIFORM): the lattice floor(j*N/K), j < K."""
+    import torch
+    N = math.prod(grid)
+    bufs = [b[0] for b in _new_routes(1, batch, N, device or torch.device("cuda"))]
+    r = Route(*bufs, -1, tuple(grid), tuple(window))
+    shape = make_shape(batch, 1, 64, grid, window, HET_F32)
+    rs = r.as_struct()
+    st = load_library().het_attn_route(ctypes.byref(shape), None, HET_UNIFORM, float(rho),
+                                       ctypes.byref(rs), _stream_handle(stream))
+    if st != HET_OK:
+        raise HetAttnError(st, "het_attn_route")
+    r.dense_count_host = rs.dense_count_host
+    return r
+
+
+def route_random(batch: int, grid, window, rho: float, seed: int, step: int, block: int = 0,
+                 n_blocks: int = 1, device=None, stream=None):
+    """Random routing per block (het_attn_route_random): a list of n_blocks
+    Route objects viewing one allocation, route l for block `block + l`."""
+    import torch
+    N = math.prod(grid)
+    bufs = _new_routes(int(n_blocks), batch, N, device or torch.device("cuda"))
+    rs = RouteStruct(*[b.data_ptr() for b in bufs], -1)
+    shape = make_shape(batch, 1, 64, grid, window, HET_F32)
+    st = load_library().het_attn_route_random(ctypes.byref(shape), float(rho), int(seed) & (2**64 - 1),
+                                              int(step) & 0xffffffff, int(block) & 0xffffffff,
+                                              int(n_blocks), ctypes.byref(rs), _stream_handle(stream))
+    if st != HET_OK:
+        raise HetAttnError(st, "het_attn_route_random")
+    return [Route(*[b[l] for b in bufs], rs.dense_count_host, tuple(grid), tuple(window))
+            for l in range(int(n_blocks))]
+
+
 def swap(r: Route, ratio: float, seed: int, step: int, block: int = 0, n_blocks: int = 1,
          in_place: bool = False, stream=None):
     """Per-block random swap of a route (het_attn_swap).
@@ -174,11 +222,7 @@ def swap(r: Route, ratio: float, seed: int, step: int, block: int = 0, n_blocks:
         rs_out = r.as_struct()
     else:
         nb = int(n_blocks)
-        mask = torch.empty((nb, B, N), dtype=torch.uint8, device=dev)
-        di = torch.empty((nb, B, N), dtype=torch.int32, device=dev)
-        li = torch.empty((nb, B, N), dtype=torch.int32, device=dev)
-        cnt = torch.empty((nb, B, 2), dtype=torch.int32, device=dev)
-        th = torch.empty((nb, B), dtype=torch.float64, device=dev)
+        mask, di, li, cnt, th = _new_routes(nb, B, N, dev)
         outs = [Route(mask[l], di[l], li[l], cnt[l], th[l], r.dense_count_host, r.grid, r.window)
                 for l in range(nb)]
         rs_out = RouteStruct(mask.data_ptr(), di.data_ptr(), li.data_ptr(), cnt.data_ptr(),
@@ -201,11 +245,12 @@ def workspace_bytes(shape: Shape) -> int:
 
 
 def forward(q, k, v, r: Route, scale: float | None = None, out=None, stream=None,
-            part: str = "both"):
+            part: str = "both", border: str = "shift"):
     """Heterogeneous attention for contiguous [B, N, heads, D] CUDA tensors.
 
     part = "both" (het_attn_forward), "dense" (het_attn_dense: rows with
-    m_i = 0 only) or "local" (het_attn_local: rows with m_i = 1 only)."""
+    m_i = 0 only) or "local" (het_attn_local: rows with m_i = 1 only).
+    border = "shift" (window shifted inside the grid) or "cut" (cut at it)."""
     import torch
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
@@ -213,7 +258,7 @@ def forward(q, k, v, r: Route, scale: float | None = None, out=None, stream=None
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape and dtype")
     B, N, H, D = q.shape
-    shape = make_shape(B, H, D, r.grid, r.window, _dtype_code(q.dtype), scale or 0.0)
+    shape = make_shape(B, H, D, r.grid, r.window, _dtype_code(q.dtype), scale or 0.0, border)
     if out is None:
         out = torch.empty_like(q)
     ws_n = workspace_bytes(shape)

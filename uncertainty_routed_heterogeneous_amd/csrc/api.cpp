@@ -28,6 +28,7 @@ het_status check_shape(const het_attn_shape *s, Dims &d, float &scale) {
     if (s->win_t % 2 == 0 || s->win_h % 2 == 0 || s->win_w % 2 == 0) return HET_ERR_INVALID_ARG;
     if (s->dtype != HET_BF16 && s->dtype != HET_F32) return HET_ERR_INVALID_ARG;
     if (std::isnan(s->scale) || std::isinf(s->scale)) return HET_ERR_INVALID_ARG;
+    if (s->border != HET_BORDER_SHIFT && s->border != HET_BORDER_CUT) return HET_ERR_INVALID_ARG;
     if (s->head_dim != 64 && s->head_dim != 128) return HET_ERR_UNSUPPORTED;
     d.B = s->batch;
     d.H = s->heads;
@@ -45,6 +46,39 @@ het_status check_shape(const het_attn_shape *s, Dims &d, float &scale) {
 bool overlaps(const void *p, size_t n, const void *q, size_t m) {
     const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
     return a < b + m && b < a + n;
+}
+
+// Dense count floor(rho*N + 1/2), clamped to [0, N] (rho in [0, 1]).
+int rho_count(double rho, int64_t N) {
+    double k = std::floor(rho * (double)N + 0.5);
+    if (k < 0.0) k = 0.0;
+    if (k > (double)N) k = (double)N;
+    return (int)k;
+}
+
+// Checks the output routes of het_attn_swap / het_attn_route_random: n_blocks
+// routes back to back, none overlapping the buffers the launch reads (the
+// input mask and thresholds, NULL when absent); with n_blocks = 1 the output
+// may be the input route itself.
+het_status check_routes_out(const Dims &d, int32_t n_blocks, const het_route *out,
+                            const uint8_t *in_mask, const double *in_thresh) {
+    if (!out || !out->mask || !out->dense_idx || !out->local_idx || !out->counts) return HET_ERR_INVALID_ARG;
+    if (n_blocks <= 0 || n_blocks > 65535) return HET_ERR_INVALID_ARG;
+    const size_t routes = (size_t)n_blocks * (size_t)d.B;
+    const size_t in_mask_bytes = (size_t)(d.B * d.N), in_th = (size_t)d.B * sizeof(double);
+    auto hits_input = [&](const void *p, size_t bytes, bool may_be_mask, bool may_be_thresh) {
+        if (in_mask && !(may_be_mask && p == in_mask) && overlaps(p, bytes, in_mask, in_mask_bytes))
+            return true;
+        return in_thresh && !(may_be_thresh && p == in_thresh) && overlaps(p, bytes, in_thresh, in_th);
+    };
+    const bool single = n_blocks == 1;
+    if (hits_input(out->mask, routes * d.N, single, false) ||
+        hits_input(out->dense_idx, routes * d.N * 4, false, false) ||
+        hits_input(out->local_idx, routes * d.N * 4, false, false) ||
+        hits_input(out->counts, routes * 8, false, false) ||
+        (out->thresh && hits_input(out->thresh, routes * sizeof(double), false, single)))
+        return HET_ERR_INVALID_ARG;
+    return HET_OK;
 }
 
 // Compute units of the current device (0 if it cannot be queried).
@@ -87,7 +121,8 @@ int het_attn_route(const het_attn_shape *shape, const float *u, int mode, double
     float scale;
     const het_status st = check_shape(shape, d, scale);
     if (st != HET_OK) return st;
-    if (!u || !out || !out->mask || !out->dense_idx || !out->local_idx || !out->counts || !out->thresh)
+    if ((!u && mode != HET_UNIFORM) || !out || !out->mask || !out->dense_idx || !out->local_idx ||
+        !out->counts || !out->thresh)
         return HET_ERR_INVALID_ARG;
     RouteArgs a;
     a.u = u;
@@ -100,13 +135,10 @@ int het_attn_route(const het_attn_shape *shape, const float *u, int mode, double
     a.thresh = out->thresh;
     a.c = 0.0;
     a.k = 0;
-    if (mode == HET_TOP_RHO) {
+    if (mode == HET_TOP_RHO || mode == HET_UNIFORM) {
         if (!(param >= 0.0 && param <= 1.0)) return HET_ERR_INVALID_ARG;
-        double kk = std::floor(param * (double)d.N + 0.5);
-        if (kk < 0.0) kk = 0.0;
-        if (kk > (double)d.N) kk = (double)d.N;
-        a.mode = 0;
-        a.k = (int)kk;
+        a.mode = mode == HET_TOP_RHO ? 0 : 2;
+        a.k = rho_count(param, d.N);
     } else if (mode == HET_MEAN_STD) {
         if (!std::isfinite(param)) return HET_ERR_INVALID_ARG;
         a.mode = 1;
@@ -115,7 +147,7 @@ int het_attn_route(const het_attn_shape *shape, const float *u, int mode, double
         return HET_ERR_INVALID_ARG;
     }
     if (hetattn::launch_route(a, (hipStream_t)stream) != hipSuccess) return HET_ERR_HIP;
-    out->dense_count_host = (a.mode == 0) ? a.k : -1;
+    out->dense_count_host = (a.mode == 1) ? -1 : a.k;
     return HET_OK;
 }
 
@@ -125,26 +157,13 @@ int het_attn_swap(const het_attn_shape *shape, const het_route *in, double r, ui
     float scale;
     const het_status st = check_shape(shape, d, scale);
     if (st != HET_OK) return st;
-    if (!in || !in->mask || !out || !out->mask || !out->dense_idx || !out->local_idx || !out->counts)
-        return HET_ERR_INVALID_ARG;
-    if (!(r >= 0.0 && r <= 1.0) || n_blocks <= 0 || n_blocks > 65535) return HET_ERR_INVALID_ARG;
+    if (!in || !in->mask) return HET_ERR_INVALID_ARG;
+    if (!(r >= 0.0 && r <= 1.0)) return HET_ERR_INVALID_ARG;
     if (in->dense_count_host < -1 || in->dense_count_host > d.N) return HET_ERR_INVALID_ARG;
-    // The buffers read (in->mask, in->thresh) may be written only in place,
-    // by a single route at the very same address.
-    const size_t routes = (size_t)n_blocks * (size_t)d.B;
-    const size_t in_mask = (size_t)(d.B * d.N), in_th = (size_t)d.B * sizeof(double);
-    auto hits_input = [&](const void *p, size_t bytes, bool may_be_mask, bool may_be_thresh) {
-        if (!(may_be_mask && p == in->mask) && overlaps(p, bytes, in->mask, in_mask)) return true;
-        return in->thresh && !(may_be_thresh && p == in->thresh) && overlaps(p, bytes, in->thresh, in_th);
-    };
-    const bool single = n_blocks == 1;
-    if (hits_input(out->mask, routes * d.N, single, false) ||
-        hits_input(out->dense_idx, routes * d.N * 4, false, false) ||
-        hits_input(out->local_idx, routes * d.N * 4, false, false) ||
-        hits_input(out->counts, routes * 8, false, false) ||
-        (out->thresh && hits_input(out->thresh, routes * sizeof(double), false, single)))
-        return HET_ERR_INVALID_ARG;
+    const het_status so = check_routes_out(d, n_blocks, out, in->mask, in->thresh);
+    if (so != HET_OK) return so;
     SwapArgs a;
+    a.random = 0;
     a.mask_in = in->mask;
     a.thresh_in = in->thresh;
     a.batch = (int)d.B;
@@ -161,6 +180,36 @@ int het_attn_swap(const het_attn_shape *shape, const het_route *in, double r, ui
     a.thresh = out->thresh;
     if (hetattn::launch_swap(a, n_blocks, (hipStream_t)stream) != hipSuccess) return HET_ERR_HIP;
     out->dense_count_host = in->dense_count_host;
+    return HET_OK;
+}
+
+int het_attn_route_random(const het_attn_shape *shape, double rho, uint64_t seed, uint32_t step,
+                          uint32_t block, int32_t n_blocks, het_route *out, void *stream) {
+    Dims d;
+    float scale;
+    const het_status st = check_shape(shape, d, scale);
+    if (st != HET_OK) return st;
+    if (!(rho >= 0.0 && rho <= 1.0)) return HET_ERR_INVALID_ARG;
+    const het_status so = check_routes_out(d, n_blocks, out, nullptr, nullptr);
+    if (so != HET_OK) return so;
+    SwapArgs a;
+    a.random = 1;
+    a.mask_in = nullptr;
+    a.thresh_in = nullptr;
+    a.batch = (int)d.B;
+    a.n = (int)d.N;
+    a.s0 = rho_count(rho, d.N);
+    a.key0 = (uint32_t)(seed & 0xffffffffu);
+    a.key1 = (uint32_t)(seed >> 32);
+    a.step = step;
+    a.block0 = block;
+    a.mask = out->mask;
+    a.dense_idx = out->dense_idx;
+    a.local_idx = out->local_idx;
+    a.counts = out->counts;
+    a.thresh = out->thresh;
+    if (hetattn::launch_swap(a, n_blocks, (hipStream_t)stream) != hipSuccess) return HET_ERR_HIP;
+    out->dense_count_host = a.s0;
     return HET_OK;
 }
 
@@ -205,6 +254,7 @@ int run_attention(const het_attn_shape *shape, const void *q, const void *k, con
     a.win_t = shape->win_t;
     a.win_h = shape->win_h;
     a.win_w = shape->win_w;
+    a.cut = shape->border == HET_BORDER_CUT ? 1 : 0;
     a.bf16 = shape->dtype == HET_BF16;
     a.scale = scale;
     a.max_dense = route->dense_count_host >= 0 ? route->dense_count_host : (int)d.N;

@@ -10,17 +10,20 @@ namespace hetattn {
 struct RouteArgs {
     const float *u;
     int batch, n;
-    int mode;       // 0 = top-rho, 1 = mean-std
-    int k;          // dense count (top-rho)
+    int mode;       // 0 = top-rho, 1 = mean-std, 2 = fixed uniform lattice (u not read)
+    int k;          // dense count (top-rho, uniform)
     double c;       // mean-std coefficient
     uint8_t *mask;
     int32_t *dense_idx, *local_idx, *counts;
     double *thresh;
 };
 
-// Per-block random swap: routes of blocks block0 .. block0 + n_blocks - 1,
-// each [batch, n] (counts [batch, 2], thresh [batch]), back to back.
+// Per-block random swap (random = 0), or per-block random routing (random =
+// 1: the s0 tokens with the smallest draws are dense, mask_in not read):
+// routes of blocks block0 .. block0 + n_blocks - 1, each [batch, n] (counts
+// [batch, 2], thresh [batch]), back to back.
 struct SwapArgs {
+    int random;
     const uint8_t *mask_in;
     const double *thresh_in;  // copied into thresh when both are set
     int batch, n;
@@ -40,6 +43,7 @@ struct AttnArgs {
     int batch, n, heads, head_dim;
     int grid_t, grid_h, grid_w;
     int win_t, win_h, win_w;   // odd, requested
+    int cut;                   // window border: 0 = shifted inside the grid, 1 = cut at it
     bool bf16;
     float scale;               // softmax scale (> 0)
     int max_dense;             // upper bound on any sample's dense count

@@ -37,7 +37,21 @@ struct LocalGeom {
     int lt, lh, lw;    // effective window lengths, min(w, extent)
     int tiles_y, tiles_x;
     int slot_row;      // SR: 16 or 32 column slots per box row
+    int cut;           // window border: 0 = shifted inside the grid, 1 = cut at it
 };
+
+// Window [lo, hi) of position pos along an axis of extent S, for the odd
+// window k of effective length len = min(k, S): shifted to stay inside
+// [0, S) (cut = 0), or centred on pos and cut at the border (cut = 1).  Both
+// ends are non-decreasing in pos, so the union of the windows of the
+// positions p0 <= p <= p1 is [lo(p0), hi(p1)), and it is never wider than
+// p1 - p0 + len.
+__device__ __forceinline__ int win_lo(int pos, int k, int len, int S, int cut) {
+    return cut ? imax(pos - (k - 1) / 2, 0) : window_start(pos, k, len, S);
+}
+__device__ __forceinline__ int win_hi(int pos, int k, int len, int S, int cut) {
+    return cut ? imin(pos + (k - 1) / 2 + 1, S) : window_start(pos, k, len, S) + len;
+}
 
 template <typename T, int D, int SR>
 __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
@@ -72,15 +86,18 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
     if (!__any(is_local)) return;
 
     // Window of this query, and the union box of the tile.
-    const int t0 = window_start(t, g.wt, g.lt, g.T);
-    const int qy0 = window_start(imin(y, g.Hg - 1), g.wh, g.lh, g.Hg);
-    const int qx0 = window_start(imin(x, g.Wg - 1), g.ww, g.lw, g.Wg);
+    const int t0 = win_lo(t, g.wt, g.lt, g.T, g.cut);
+    const int nt = win_hi(t, g.wt, g.lt, g.T, g.cut) - t0;
+    const int ylo = win_lo(imin(y, g.Hg - 1), g.wh, g.lh, g.Hg, g.cut);
+    const int yhi = win_hi(imin(y, g.Hg - 1), g.wh, g.lh, g.Hg, g.cut);
+    const int qxlo = win_lo(imin(x, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut);
+    const int qxhi = win_hi(imin(x, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut);
     const int ylast = imin(ybase + kLocalQY - 1, g.Hg - 1), xlast = imin(xbase + kLocalQX - 1, g.Wg - 1);
-    const int uy0 = window_start(ybase, g.wh, g.lh, g.Hg);
-    const int ux0 = window_start(xbase, g.ww, g.lw, g.Wg);
-    const int ny = window_start(ylast, g.wh, g.lh, g.Hg) + g.lh - uy0;
-    const int nx = window_start(xlast, g.ww, g.lw, g.Wg) + g.lw - ux0;
-    const int rows = g.lt * ny;
+    const int uy0 = win_lo(ybase, g.wh, g.lh, g.Hg, g.cut);
+    const int ux0 = win_lo(xbase, g.ww, g.lw, g.Wg, g.cut);
+    const int ny = win_hi(ylast, g.wh, g.lh, g.Hg, g.cut) - uy0;
+    const int nx = win_hi(xlast, g.ww, g.lw, g.Wg, g.cut) - ux0;
+    const int rows = nt * ny;
     const int n_blocks = (rows + rpb - 1) / rpb;
 
     const size_t tok_stride = (size_t)H * D;
@@ -181,10 +198,10 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
         // column 8*((i/4) % (SR/8)) + 4*half + i%4.
         const int r0 = kb * rpb;
         const int yy0 = uy0 + imin(r0, rows - 1) % ny, yy1 = uy0 + imin(r0 + 1, rows - 1) % ny;
-        const bool y_in0 = r0 < rows && yy0 >= qy0 && yy0 < qy0 + g.lh;
-        const bool y_in1 = rpb > 1 && r0 + 1 < rows && yy1 >= qy0 && yy1 < qy0 + g.lh;
+        const bool y_in0 = r0 < rows && yy0 >= ylo && yy0 < yhi;
+        const bool y_in1 = rpb > 1 && r0 + 1 < rows && yy1 >= ylo && yy1 < yhi;
         // Columns of the query's window relative to the box, intersected with the box.
-        const int xlo = qx0 - ux0, xhi = imin(qx0 - ux0 + g.lw, nx);
+        const int xlo = qxlo - ux0, xhi = imin(qxhi - ux0, nx);
         float mx = -__builtin_inff();
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -339,14 +356,14 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
 
     // Workgroup box (uniform).
     const int ybase = ty * QY;
-    const int uy0 = window_start(ybase, g.wh, g.lh, g.Hg);
-    const int ny = window_start(imin(ybase + QY - 1, g.Hg - 1), g.wh, g.lh, g.Hg) + g.lh - uy0;
+    const int uy0 = win_lo(ybase, g.wh, g.lh, g.Hg, g.cut);
+    const int ny = win_hi(imin(ybase + QY - 1, g.Hg - 1), g.wh, g.lh, g.Hg, g.cut) - uy0;
     const int xt0 = xb * kBandNW, xt1 = imin(xt0 + kBandNW, g.tiles_x) - 1;
-    const int ux0 = window_start(xt0 * QX, g.ww, g.lw, g.Wg);
-    const int C = window_start(imin(xt1 * QX + QX - 1, g.Wg - 1), g.ww, g.lw, g.Wg) + g.lw - ux0;
+    const int ux0 = win_lo(xt0 * QX, g.ww, g.lw, g.Wg, g.cut);
+    const int C = win_hi(imin(xt1 * QX + QX - 1, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut) - ux0;
     const int tA = 2 * tp, tB = imin(tA + 1, g.T - 1);
-    const int F0 = window_start(tA, g.wt, g.lt, g.T);
-    const int F1 = window_start(tB, g.wt, g.lt, g.T) + g.lt;
+    const int F0 = win_lo(tA, g.wt, g.lt, g.T, g.cut);
+    const int F1 = win_hi(tB, g.wt, g.lt, g.T, g.cut);
     const int nb_f = (ny + rpb - 1) / rpb;
     const int n_bands = (F1 - F0) * nb_f;
 
@@ -362,11 +379,14 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     const bool active = __any(is_local);
     // A workgroup whose queries are all dense has nothing to do.
     if (!__syncthreads_or(is_local)) return;
-    const int t0 = window_start(imin(t, g.T - 1), g.wt, g.lt, g.T);
-    const int qy0 = window_start(imin(y, g.Hg - 1), g.wh, g.lh, g.Hg);
-    const int qx0 = window_start(imin(x, g.Wg - 1), g.ww, g.lw, g.Wg);
-    const int uxw = window_start(imin(xbase, g.Wg - 1), g.ww, g.lw, g.Wg);
-    const int nxw = window_start(imin(xbase + QX - 1, g.Wg - 1), g.ww, g.lw, g.Wg) + g.lw - uxw;
+    const int t0 = win_lo(imin(t, g.T - 1), g.wt, g.lt, g.T, g.cut);
+    const int t1 = win_hi(imin(t, g.T - 1), g.wt, g.lt, g.T, g.cut);
+    const int ylo = win_lo(imin(y, g.Hg - 1), g.wh, g.lh, g.Hg, g.cut);
+    const int yhi = win_hi(imin(y, g.Hg - 1), g.wh, g.lh, g.Hg, g.cut);
+    const int qxlo = win_lo(imin(x, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut);
+    const int qxhi = win_hi(imin(x, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut);
+    const int uxw = win_lo(imin(xbase, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut);
+    const int nxw = win_hi(imin(xbase + QX - 1, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut) - uxw;
     const int cw = uxw - ux0;  // this tile's box inside the workgroup box
 
     const size_t tok_stride = (size_t)H * D;
@@ -441,7 +461,7 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     float m_run = -__builtin_inff();
     float l_part = 0.0f;
     // Columns of this query's window relative to the tile box, inside the box.
-    const int xlo = qx0 - uxw, xhi = imin(qx0 - uxw + g.lw, nxw);
+    const int xlo = qxlo - uxw, xhi = imin(qxhi - uxw, nxw);
 
     // Band bi is read from (Kc, Vc) while the DMA of band bi+1 goes to
     // (Kn, Vn).  The buffers are fixed at each call site (the loop is
@@ -454,7 +474,7 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
         __builtin_amdgcn_s_barrier();
         if (bi + 1 < n_bands) dma_band(bi + 1, Kn, Vn);
         const int f = F0 + bi / nb_f, yy0 = uy0 + (bi % nb_f) * rpb;
-        if (!active || f < t0 || f >= t0 + g.lt) return;
+        if (!active || f < t0 || f >= t1) return;
 
         // All LDS operands of the block are requested up front: the K reads
         // feed the QK product, the V reads land while the softmax runs.
@@ -478,8 +498,8 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
         // Keep only keys inside this query's window.  Register i holds slot
         // 8(i/4) + 4*half + i%4 of the block: box row (i/4 >= 2 && SR == 16),
         // column 8*((i/4) % (SR/8)) + 4*half + i%4.
-        const bool y_in0 = yy0 < uy0 + ny && yy0 >= qy0 && yy0 < qy0 + g.lh;
-        const bool y_in1 = rpb > 1 && yy0 + 1 < uy0 + ny && yy0 + 1 >= qy0 && yy0 + 1 < qy0 + g.lh;
+        const bool y_in0 = yy0 < uy0 + ny && yy0 >= ylo && yy0 < yhi;
+        const bool y_in1 = rpb > 1 && yy0 + 1 < uy0 + ny && yy0 + 1 >= ylo && yy0 + 1 < yhi;
         float mx = -__builtin_inff();
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -555,6 +575,7 @@ hipError_t launch_local(const AttnArgs &a, hipStream_t stream) {
     g.lt = a.win_t < a.grid_t ? a.win_t : a.grid_t;
     g.lh = a.win_h < a.grid_h ? a.win_h : a.grid_h;
     g.lw = a.win_w < a.grid_w ? a.win_w : a.grid_w;
+    g.cut = a.cut;
     g.tiles_y = (a.grid_h + kLocalQY - 1) / kLocalQY;
     g.tiles_x = (a.grid_w + kLocalQX - 1) / kLocalQX;
     const int nx_max = kLocalQX + g.lw - 1;

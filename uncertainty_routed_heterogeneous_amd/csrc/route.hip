@@ -213,11 +213,13 @@ __device__ __forceinline__ void radix_select_largest(int k, uint32_t lo, uint32_
 
 // kPer > 0: every lane holds kPer keys in registers (N <= 1024 * kPer).
 // kPer == 0: per-wave ranges of ceil(N / 1024) rows of 64, re-read from u.
-template <int kPer>
+// kUniform: the fixed uniform lattice (mode 2), a separate instantiation so
+// that its index arithmetic stays out of the threshold modes' code.
+template <int kPer, bool kUniform>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     const int b = blockIdx.x, tid = threadIdx.x, N = a.n;
     const int lane = tid & 63, wave = tid >> 6;
-    const float *ub = a.u + (size_t)b * N;
+    const float *ub = a.u ? a.u + (size_t)b * N : nullptr;  // not read in the uniform mode
     __shared__ __attribute__((aligned(16))) uint32_t hcopy[kHistWords];
     __shared__ uint32_t hpart[4 * 256];
     __shared__ int s_wave[2 * kRouteWaves];
@@ -232,11 +234,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     const int w0 = wave * per * 64;
     const int rows = imax(0, imin(per, (N - w0 + 63) >> 6));
     auto token = [&](int j) HET_INLINE { return w0 + 64 * j + lane; };
+    constexpr bool uniform = kUniform;
+    const bool top = !kUniform && a.mode == 0;
     auto load_key = [&](int j) HET_INLINE -> uint32_t {
-        return (token(j) < N) ? rank_key(ub[token(j)]) : 0u;
+        return (!uniform && token(j) < N) ? rank_key(ub[token(j)]) : 0u;
     };
-
-    const bool top = (a.mode == 0);
     uint32_t lo = 0xffffffffu, hi = 0u;
     uint32_t keys[kPer > 0 ? kPer : 1];
     if constexpr (kPer > 0) {
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
             a.k, lo, hi, rows, key_at, [&](int j) HET_INLINE { return key_at(j) != 0u; }, hcopy,
             hpart, s_sel, tkey, take_equal);
         T = (double)key_to_float(tkey);
-    } else if (!top) {
+    } else if (!kUniform && a.mode == 1) {
         double s = 0.0;
         for_rows<kPer>(rows, [&](int j) HET_INLINE {
             if (token(j) < N) s += (double)key_to_float(key_at(j));
@@ -290,8 +292,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 
     // Top-rho: token i is dense iff key > tkey, or key == tkey and fewer
     // than take_equal keys equal to tkey precede it.  Mean-std: iff
-    // !(u < T).  Ballot of the first kind of row j:
+    // !(u < T).  Uniform lattice (dense tokens floor(j*N/K), j < K): token i
+    // is dense iff the first lattice index at or after it, ceil(i*K/N), lands
+    // on i, i.e. ceil(i*K/N)*N < (i+1)*K.  Ballot of the first kind of row j:
     auto above_row = [&](int j) HET_INLINE -> uint64_t {
+        if constexpr (kUniform) {
+            const uint64_t i = (uint64_t)token(j), K = (uint64_t)a.k, n = (uint64_t)N;
+            return __ballot(token(j) < N && (i * K + n - 1) / n * n < (i + 1) * K);
+        }
         const uint32_t key = key_at(j);
         if (top) return __ballot(key > tkey);
         return __ballot(token(j) < N && !((double)key_to_float(key) < T));
@@ -336,7 +344,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     if (tid == 0) {
         a.counts[2 * b] = n_dense;
         a.counts[2 * b + 1] = N - n_dense;
-        a.thresh[b] = T;
+        a.thresh[b] = uniform ? __builtin_nan("") : T;
     }
 }
 
@@ -411,7 +419,7 @@ __global__ __launch_bounds__(kRouteThreads) void swap_kernel(SwapArgs a) {
     const int b = blockIdx.x, l = blockIdx.y, tid = threadIdx.x, N = a.n;
     const int lane = tid & 63, wave = tid >> 6;
     const uint32_t blk = a.block0 + (uint32_t)l;
-    const uint8_t *min_b = a.mask_in + (size_t)b * N;
+    const uint8_t *min_b = a.random ? nullptr : a.mask_in + (size_t)b * N;
     const size_t r = (size_t)l * a.batch + b;  // index of the route written
     __shared__ __attribute__((aligned(16))) uint32_t hcopy[kHistWords];
     __shared__ uint32_t hpart[4 * 256];
@@ -428,8 +436,9 @@ __global__ __launch_bounds__(kRouteThreads) void swap_kernel(SwapArgs a) {
     auto draw_key = [&](int j) HET_INLINE -> uint32_t {
         return ~philox4x32_10_word0((uint32_t)token(j), (uint32_t)b, blk, a.step, a.key0, a.key1);
     };
+    // Random routing starts from an all-local route.
     auto read_dense = [&](int j) HET_INLINE -> bool {
-        return token(j) < N && min_b[token(j)] == 0;
+        return !a.random && token(j) < N && min_b[token(j)] == 0;
     };
 
     uint32_t keys[kPer > 0 ? kPer : 1];
@@ -473,20 +482,26 @@ __global__ __launch_bounds__(kRouteThreads) void swap_kernel(SwapArgs a) {
         wave_excl_scan<1>(x, s_wave, bf, tt);
         nd_total = tt[0];
     }
+    // Tokens that leave the dense set (s_out) and the local set (s_in): S
+    // each way for the swap; for random routing none leave the (empty) dense
+    // set and the s0 smallest draws of all tokens come in.
     const int S = imin(a.s0, imin(nd_total, N - nd_total));
+    const int s_out = a.random ? 0 : S, s_in = a.random ? imin(a.s0, N) : S;
 
-    // S = 0 leaves tkey = ~0 with nothing equal taken: no token moves.
+    // A count of 0 leaves tkey = ~0 with nothing equal taken: no token moves.
     uint32_t tkd = 0xffffffffu, tkl = 0xffffffffu;
     int ted = 0, tel = 0;
-    if (S > 0) {
+    if (s_out > 0 || s_in > 0) {
         for (int i = tid; i < kHistWords / 4; i += kRouteThreads)
             reinterpret_cast<u32x4 *>(hcopy)[i] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
-        radix_select_largest<kPer>(S, dlo, dhi, rows, key_at, in_dense, hcopy, hpart, s_sel, tkd,
-                                   ted);
-        radix_select_largest<kPer>(S, llo, lhi, rows, key_at, in_local, hcopy, hpart, s_sel, tkl,
-                                   tel);
     }
+    if (s_out > 0)
+        radix_select_largest<kPer>(s_out, dlo, dhi, rows, key_at, in_dense, hcopy, hpart, s_sel, tkd,
+                                   ted);
+    if (s_in > 0)
+        radix_select_largest<kPer>(s_in, llo, lhi, rows, key_at, in_local, hcopy, hpart, s_sel, tkl,
+                                   tel);
 
     // Per wave: dense-set size, and in each set the tokens above the select
     // key and those equal to it.
@@ -504,7 +519,7 @@ __global__ __launch_bounds__(kRouteThreads) void swap_kernel(SwapArgs a) {
     // Dense tokens of the output before this wave: the input's, less those
     // that left, plus those that came.
     int d_seen = bef[0] - (bef[1] + imin(bef[2], ted)) + (bef[3] + imin(bef[4], tel));
-    const int n_dense = nd_total;
+    const int n_dense = nd_total - s_out + s_in;
 
     uint8_t *mask = a.mask + r * N;
     int32_t *dense_idx = a.dense_idx + r * N;
@@ -539,22 +554,28 @@ __global__ __launch_bounds__(kRouteThreads) void swap_kernel(SwapArgs a) {
     if (tid == 0) {
         a.counts[2 * r] = n_dense;
         a.counts[2 * r + 1] = N - n_dense;
-        if (a.thresh) a.thresh[r] = a.thresh_in ? a.thresh_in[b] : __builtin_nan("");
+        if (a.thresh) a.thresh[r] = (!a.random && a.thresh_in) ? a.thresh_in[b] : __builtin_nan("");
     }
 }
 
-hipError_t launch_route(const RouteArgs &a, hipStream_t stream) {
+template <bool kUniform>
+static void launch_route_kind(const RouteArgs &a, hipStream_t stream) {
     const dim3 grid(a.batch), block(kRouteThreads);
     if (a.n <= 8 * kRouteThreads)
-        hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((route_kernel<8, kUniform>), grid, block, 0, stream, a);
     else if (a.n <= 16 * kRouteThreads)
-        hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((route_kernel<16, kUniform>), grid, block, 0, stream, a);
     else if (a.n <= 32 * kRouteThreads)
-        hipLaunchKernelGGL(route_kernel<32>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((route_kernel<32, kUniform>), grid, block, 0, stream, a);
     else if (a.n <= 64 * kRouteThreads)
-        hipLaunchKernelGGL(route_kernel<64>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((route_kernel<64, kUniform>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL(route_kernel<0>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((route_kernel<0, kUniform>), grid, block, 0, stream, a);
+}
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t stream) {
+    if (a.mode == 2) launch_route_kind<true>(a, stream);
+    else launch_route_kind<false>(a, stream);
     return hipGetLastError();
 }
 
