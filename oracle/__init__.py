@@ -71,6 +71,10 @@ def _load():
         lib.oracle_attention_weights.argtypes = [P, P, i, i, i, i, i, i, i, i, i, i,
                                                  ctypes.c_double, P, ctypes.c_long, i, P]
         lib.oracle_route_uniform.argtypes = [i, i, ctypes.c_double, P, P, P, P]
+        lib.oracle_attend_backward.argtypes = [P, P, P, P, i, i, i, i, i, i, i, i, i, i,
+                                               ctypes.c_double, P, P, P, P, i]
+        lib.oracle_attend_backward_dq_rows.argtypes = [P, P, P, P, i, i, i, i, i, i, i, i, i, i,
+                                                       ctypes.c_double, P, P, ctypes.c_long, P, i]
         lib.oracle_route_random.argtypes = [i, i, ctypes.c_double, ctypes.c_ulonglong, ctypes.c_uint,
                                             ctypes.c_uint, P, P, P, P]
         lib.oracle_philox4x32_10.argtypes = [P, P, P]
@@ -82,7 +86,8 @@ def _load():
                                           ctypes.c_uint, P, P, P, P]
         for fn in (lib.oracle_route_top_rho, lib.oracle_route_mean_std, lib.oracle_window_axis,
                    lib.oracle_attend_rows, lib.oracle_attention_weights, lib.oracle_route_swap,
-                   lib.oracle_window_axis_cut, lib.oracle_route_uniform, lib.oracle_route_random):
+                   lib.oracle_window_axis_cut, lib.oracle_route_uniform, lib.oracle_route_random,
+                   lib.oracle_attend_backward, lib.oracle_attend_backward_dq_rows):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -188,7 +193,7 @@ def route_random(B: int, N: int, rho: float, seed: int, step: int, block: int) -
     return Route(mask, di, li, counts, np.full(B, np.nan))
 
 
-_BORDER = {"shift": 0, "truncate": 1}
+_BORDER = {"shift": 0, "cut": 1, "truncate": 1}  # "truncate" = "cut"
 
 
 def window_axis(S: int, k: int, pos: int, border: str = "shift") -> tuple[int, int]:
@@ -247,3 +252,40 @@ def attention_weights(q, k, grid, window, scale, mask, row: int, head: int,
     if rc != 0:
         raise ValueError("oracle_attention_weights rejected its arguments")
     return w
+
+
+def backward(q, k, v, dout, grid, window, scale, mask, nthreads: int = 0, border: str = "shift"):
+    """(dQ, dK, dV) as float64 [B, N, heads, D] arrays (oracle_attend_backward)."""
+    q, k, v, dout = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
+    B, N, H, D = q.shape
+    T, Hg, Wg = grid
+    if T * Hg * Wg != N or any(x.shape != q.shape for x in (k, v, dout)):
+        raise ValueError("shape mismatch")
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    dq, dk, dv = (np.empty((B, N, H, D), np.float64) for _ in range(3))
+    wt, wh, ww = window
+    rc = _load().oracle_attend_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, D, T, Hg, Wg,
+                                        wt, wh, ww, _BORDER[border], float(scale), _ptr(mask),
+                                        _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_attend_backward rejected its arguments (rc={rc})")
+    return dq, dk, dv
+
+
+def backward_dq_rows(q, k, v, dout, grid, window, scale, mask, rows, nthreads: int = 0,
+                     border: str = "shift") -> np.ndarray:
+    """dL/dQ of the listed rows: [len(rows), heads, D] float64."""
+    q, k, v, dout = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
+    B, N, H, D = q.shape
+    T, Hg, Wg = grid
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, H, D), np.float64)
+    wt, wh, ww = window
+    rc = _load().oracle_attend_backward_dq_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, D, T, Hg,
+                                                Wg, wt, wh, ww, _BORDER[border], float(scale),
+                                                _ptr(mask), _ptr(rows), rows.size, _ptr(out),
+                                                int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_attend_backward_dq_rows rejected its arguments (rc={rc})")
+    return out

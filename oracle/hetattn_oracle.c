@@ -479,3 +479,145 @@ int oracle_attention_weights(const float *q, const float *k,
     free(keys); free(s); free(w); free(o);
     return 0;
 }
+
+/* Backward of one query row over its key list, in double ([HetA §3.1.1
+ * Eqs. 2-3] differentiated): with p the softmax weights, dP_j = dO.v_j,
+ * D = sum_j p_j dP_j and dS_j = p_j (dP_j - D), the row adds
+ * scale * sum_j dS_j k_j to dq, scale * dS_j q to dk_j and p_j dO to dv_j
+ * (dk, dv may be NULL).  s and w are scratch of nkeys doubles. */
+static void backward_one(const float *qrow, const float *dorow, const float *kbase,
+                         const float *vbase, long key_stride, int D, const int *keys, int nkeys,
+                         double scale, double *s, double *w, double *dq, double *dkbase,
+                         double *dvbase)
+{
+    double smax = -INFINITY;
+    for (int j = 0; j < nkeys; j++) {
+        const float *krow = kbase + keys[j] * key_stride;
+        double qk = 0.0;
+        for (int d = 0; d < D; d++) qk += (double)qrow[d] * (double)krow[d];
+        s[j] = qk * scale;
+        if (s[j] > smax) smax = s[j];
+    }
+    double denom = 0.0;
+    for (int j = 0; j < nkeys; j++) {
+        s[j] = exp(s[j] - smax);
+        denom += s[j];
+    }
+    double Dsum = 0.0;
+    for (int j = 0; j < nkeys; j++) {
+        s[j] /= denom; /* p_j */
+        const float *vrow = vbase + keys[j] * key_stride;
+        double dp = 0.0;
+        for (int d = 0; d < D; d++) dp += (double)dorow[d] * (double)vrow[d];
+        w[j] = dp; /* dP_j */
+        Dsum += s[j] * dp;
+    }
+    for (int d = 0; d < D; d++) dq[d] = 0.0;
+    for (int j = 0; j < nkeys; j++) {
+        const double ds = s[j] * (w[j] - Dsum);
+        const float *krow = kbase + keys[j] * key_stride;
+        for (int d = 0; d < D; d++) dq[d] += scale * ds * (double)krow[d];
+        if (dkbase) {
+            double *dkr = dkbase + (long)keys[j] * key_stride;
+            double *dvr = dvbase + (long)keys[j] * key_stride;
+            for (int d = 0; d < D; d++) {
+                dkr[d] += scale * ds * (double)qrow[d];
+                dvr[d] += s[j] * (double)dorow[d];
+            }
+        }
+    }
+}
+
+int oracle_attend_backward(const float *q, const float *k, const float *v, const float *dout,
+                           int B, int heads, int D,
+                           int T, int Hg, int Wg, int wt, int wh, int ww, int border,
+                           double scale, const unsigned char *mask,
+                           double *dq, double *dk, double *dv, int nthreads)
+{
+    if (!q || !k || !v || !dout || !mask || !dq || !dk || !dv) return -1;
+    if (check_shape(B, heads, D, T, Hg, Wg, wt, wh, ww, border)) return -1;
+    const long N = (long)T * Hg * Wg;
+    const long tok_stride = (long)heads * D;
+    for (long e = 0; e < (long)B * N * tok_stride; e++) {
+        dk[e] = 0.0;
+        dv[e] = 0.0;
+    }
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    /* One (sample, head) per task: the dk, dv rows it adds to are its own. */
+#pragma omp parallel reduction(| : err)
+    {
+        int *keys = (int *)malloc(sizeof(int) * (size_t)N);
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        double *w = (double *)malloc(sizeof(double) * (size_t)N);
+        if (!keys || !s || !w) {
+            err = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long bh = 0; bh < (long)B * heads; bh++) {
+                const long b = bh / heads, h = bh % heads;
+                const long base = b * N * tok_stride + h * D;
+                for (long n = 0; n < N; n++) {
+                    int nk = key_set((int)n, mask[b * N + n], T, Hg, Wg, wt, wh, ww, border, keys);
+                    backward_one(q + base + n * tok_stride, dout + base + n * tok_stride, k + base,
+                                 v + base, tok_stride, D, keys, nk, scale, s, w,
+                                 dq + base + n * tok_stride, dk + base, dv + base);
+                }
+            }
+        }
+        free(keys);
+        free(s);
+        free(w);
+    }
+    return err ? -2 : 0;
+}
+
+int oracle_attend_backward_dq_rows(const float *q, const float *k, const float *v,
+                                   const float *dout, int B, int heads, int D,
+                                   int T, int Hg, int Wg, int wt, int wh, int ww, int border,
+                                   double scale, const unsigned char *mask,
+                                   const long *rows, long nrows, double *dq, int nthreads)
+{
+    if (!q || !k || !v || !dout || !mask || !rows || !dq) return -1;
+    if (check_shape(B, heads, D, T, Hg, Wg, wt, wh, ww, border)) return -1;
+    const long N = (long)T * Hg * Wg;
+    for (long r = 0; r < nrows; r++)
+        if (rows[r] < 0 || rows[r] >= (long)B * N) return -1;
+    const long tok_stride = (long)heads * D;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel reduction(| : err)
+    {
+        int *keys = (int *)malloc(sizeof(int) * (size_t)N);
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        double *w = (double *)malloc(sizeof(double) * (size_t)N);
+        if (!keys || !s || !w) {
+            err = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long r = 0; r < nrows; r++) {
+                const long b = rows[r] / N, n = rows[r] % N;
+                int nk = key_set((int)n, mask[b * N + n], T, Hg, Wg, wt, wh, ww, border, keys);
+                for (int h = 0; h < heads; h++) {
+                    const long base = b * N * tok_stride + (long)h * D;
+                    backward_one(q + base + n * tok_stride, dout + base + n * tok_stride, k + base,
+                                 v + base, tok_stride, D, keys, nk, scale, s, w,
+                                 dq + (r * heads + h) * (long)D, NULL, NULL);
+                }
+            }
+        }
+        free(keys);
+        free(s);
+        free(w);
+    }
+    return err ? -2 : 0;
+}
+

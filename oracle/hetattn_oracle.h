@@ -123,6 +123,26 @@ int oracle_attention_weights(const float *q, const float *k,
                              double scale, const unsigned char *mask,
                              long row, int head, double *weights);
 
+/* Backward of heterogeneous attention: given dout = dL/dO ([B, N, heads, D]),
+ * the gradients dL/dQ, dL/dK, dL/dV (double, same layout) of the outputs of
+ * oracle_attend_rows over all rows, with each row's key set and softmax as
+ * there ([HetA §3.1.1 Eqs. 2-3, §3.2.2 Eq. 13] differentiated; the route is
+ * a constant).  Per row: p = softmax(scale*q.k_j), dP_j = dout.v_j,
+ * D = sum_j p_j dP_j, dS_j = p_j (dP_j - D); dQ = scale * sum_j dS_j k_j,
+ * dK_j += scale * dS_j q, dV_j += p_j dout. */
+int oracle_attend_backward(const float *q, const float *k, const float *v, const float *dout,
+                           int B, int heads, int D,
+                           int T, int Hg, int Wg, int wt, int wh, int ww, int border,
+                           double scale, const unsigned char *mask,
+                           double *dq, double *dk, double *dv, int nthreads);
+
+/* dL/dQ of the listed rows only (rows[r] = b*N + n), into dq[r*heads*D + h*D + d]. */
+int oracle_attend_backward_dq_rows(const float *q, const float *k, const float *v,
+                                   const float *dout, int B, int heads, int D,
+                                   int T, int Hg, int Wg, int wt, int wh, int ww, int border,
+                                   double scale, const unsigned char *mask,
+                                   const long *rows, long nrows, double *dq, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

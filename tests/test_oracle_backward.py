@@ -1,0 +1,133 @@
+"""Pins of the oracle's backward pass (dQ, dK, dV of heterogeneous attention).
+
+[HetA] = "Where Compute Matters: Heterogeneous Attention for Efficient Video
+Diffusion" (HetA-DiT): the dense (Eq. 2) and local (Eq. 3) softmax attention
+merged by Eq. 13, differentiated with the route held fixed.  The paper's
+second training stage fine-tunes through this layer (§4, Training Setting).
+
+Pins: central finite differences of the (separately pinned) oracle forward;
+torch autograd in float64 through a brute-force masked softmax built from an
+independent characterisation of each key set; sum identities that hold at
+any size (sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per sample and head);
+equal keys give dQ = 0.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+
+def quantised(rng, shape, step=2.0 ** -6):
+    """float32 values on a grid of `step`, so that x +- 2^-12 is exact."""
+    return (np.round(rng.standard_normal(shape) / step) * step).astype(np.float32)
+
+
+def allowed_matrix(grid, window, mask_row, border):
+    """[N, N] key sets: all keys for dense rows; for local rows the window,
+    described per axis by distance (cut) or as the nearest in-grid interval of
+    length min(k, S) containing the position (shifted)."""
+    T, H, W = grid
+    N = T * H * W
+    coords = np.array(list(itertools.product(range(T), range(H), range(W))))
+    ext = np.array(grid)
+    allowed = np.zeros((N, N), bool)
+    for n in range(N):
+        if mask_row[n] == 0:
+            allowed[n] = True
+            continue
+        ok = np.ones(N, bool)
+        for ax in range(3):
+            S, k, p = ext[ax], window[ax], coords[n, ax]
+            if border == "cut":
+                ok &= np.abs(coords[:, ax] - p) <= (k - 1) // 2
+            else:
+                L = min(k, S)
+                best = min((abs(s + (L - 1) / 2.0 - p), s) for s in range(S - L + 1) if s <= p < s + L)[1]
+                ok &= (coords[:, ax] >= best) & (coords[:, ax] < best + L)
+        allowed[n] = ok
+    return allowed
+
+
+def torch_grads(q, k, v, dout, grid, window, scale, mask, border):
+    B, N, H, D = q.shape
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    outs = []
+    for b in range(B):
+        allowed = torch.from_numpy(allowed_matrix(grid, window, mask[b], border))
+        for h in range(H):
+            s = scale * tq[b, :, h, :] @ tk[b, :, h, :].T
+            s = s.masked_fill(~allowed, float("-inf"))
+            outs.append((torch.softmax(s, dim=1) @ tv[b, :, h, :], b, h))
+    loss = sum((o * torch.from_numpy(dout[b, :, h, :].astype(np.float64))).sum() for o, b, h in outs)
+    loss.backward()
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("border", ["shift", "cut"])
+@pytest.mark.parametrize("grid,window", [((3, 4, 5), (3, 3, 3)), ((2, 5, 6), (1, 3, 5))])
+def test_backward_matches_torch_autograd(oracle_mod, border, grid, window):
+    rng = np.random.default_rng(sum(grid) + (border == "cut"))
+    N = int(np.prod(grid))
+    q, k, v, do = (rng.standard_normal((2, N, 2, 8)).astype(np.float32) for _ in range(4))
+    mask = (rng.random((2, N)) < 0.7).astype(np.uint8)
+    dq, dk, dv = oracle_mod.backward(q, k, v, do, grid, window, 0.4, mask, border=border)
+    rq, rk, rv = torch_grads(q, k, v, do, grid, window, 0.4, mask, border)
+    for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("border", ["shift", "cut"])
+def test_backward_matches_finite_differences(oracle_mod, border):
+    """dL/dx for L = sum(dO * O) by central differences of the oracle forward."""
+    grid, window, scale = (2, 3, 4), (1, 3, 3), 0.5
+    rng = np.random.default_rng(11)
+    N = 24
+    q, k, v, do = (quantised(rng, (1, N, 2, 4)) for _ in range(4))
+    mask = (rng.random((1, N)) < 0.6).astype(np.uint8)
+    dq, dk, dv = oracle_mod.backward(q, k, v, do, grid, window, scale, mask, border=border)
+
+    def loss(qq, kk, vv):
+        o = oracle_mod.forward(qq, kk, vv, grid, window, scale, mask, border=border)
+        return float((o * do.astype(np.float64)).sum())
+
+    h = 2.0 ** -12
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for idx in itertools.product(range(N), range(2), range(4)):
+            if (idx[0] * 8 + idx[1] * 4 + idx[2]) % 5:
+                continue  # a fifth of the elements, spread over tokens, heads and dims
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][(0,) + idx] += np.float32(h)
+            up = loss(*args)
+            args[which][(0,) + idx] -= np.float32(2 * h)
+            down = loss(*args)
+            fd = (up - down) / (2 * h)
+            assert abs(fd - grad[(0,) + idx]) < 1e-6, (which, idx, fd, grad[(0,) + idx])
+
+
+def test_backward_sum_identities_and_rows(oracle_mod):
+    grid, window = (6, 10, 20), (3, 7, 7)
+    N = 1200
+    rng = np.random.default_rng(5)
+    q, k, v, do = (rng.standard_normal((2, N, 2, 32)).astype(np.float32) for _ in range(4))
+    mask = (rng.random((2, N)) < 0.8).astype(np.uint8)
+    dq, dk, dv = oracle_mod.backward(q, k, v, do, grid, window, 0.17, mask)
+    # each row's dS sums to zero, so the key gradients of a (sample, head) do
+    scale_k = np.abs(dk).sum(axis=1).max()
+    assert np.abs(dk.sum(axis=1)).max() < 1e-12 * scale_k * N
+    # each row's weights sum to one, so dV sums to dO
+    np.testing.assert_allclose(dv.sum(axis=1), do.astype(np.float64).sum(axis=1), rtol=1e-11, atol=1e-10)
+    rows = np.array([0, 17, 599, 1199, 1200, 2399], dtype=np.int64)
+    got = oracle_mod.backward_dq_rows(q, k, v, do, grid, window, 0.17, mask, rows)
+    np.testing.assert_array_equal(got, dq.reshape(2 * N, 2, 32)[rows])
+
+
+def test_equal_keys_give_zero_dq(oracle_mod):
+    grid, window = (2, 4, 4), (1, 3, 3)
+    N = 32
+    rng = np.random.default_rng(2)
+    q, v, do = (rng.standard_normal((1, N, 1, 8)).astype(np.float32) for _ in range(3))
+    k = np.broadcast_to(rng.standard_normal((1, 1, 1, 8)).astype(np.float32), (1, N, 1, 8)).copy()
+    mask = (rng.random((1, N)) < 0.5).astype(np.uint8)
+    dq, _, _ = oracle_mod.backward(q, k, v, do, grid, window, 1.0, mask)
+    assert np.abs(dq).max() < 1e-14

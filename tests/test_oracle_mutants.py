@@ -45,6 +45,10 @@ MUTANTS = {
     # ablation routers and the cut window border
     "uniform_lattice_ends_segments": ("dense[j * (long)N / K] = 1;",
                                       "dense[(j * (long)N + K - 1) / K] = 1;"),
+    # backward pass
+    "backward_drops_row_term": ("const double ds = s[j] * (w[j] - Dsum);", "const double ds = s[j] * w[j];"),
+    "backward_dk_without_scale": ("dkr[d] += scale * ds * (double)qrow[d];", "dkr[d] += ds * (double)qrow[d];"),
+    "backward_dv_uses_ds": ("dvr[d] += s[j] * (double)dorow[d];", "dvr[d] += ds * (double)dorow[d];"),
     "router_count_truncated": ("floor((double)N * rho + 0.5)", "floor((double)N * rho)"),
     "random_largest_draws": ("for (long j = 0; j < K; j++) dense[tok[j].idx] = 1;",
                              "for (long j = 0; j < K; j++) dense[tok[N - 1 - j].idx] = 1;"),
@@ -70,6 +74,7 @@ def test_planted_mistake_is_caught(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_route.py"),
                         os.path.join(ROOT, "tests", "test_oracle_attention.py"),
                         os.path.join(ROOT, "tests", "test_oracle_swap.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_variants.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_variants.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_backward.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"planted mistake {name!r} passed every pin:\n{r.stdout[-2000:]}"
