@@ -210,6 +210,39 @@ def time_swap(layer, ratio: float, n_blocks: int, iters: int, warmup: int = 3):
     return ts[len(ts) // 2]
 
 
+def time_backward(layer, iters: int, warmup: int = 2):
+    """Median time of one het_attn_backward call on the layer's route and
+    output, with a seeded dO; per-kernel split from events is not possible
+    inside one call, so only the whole call is timed here."""
+    import torch
+    het, w = layer.het, layer.w
+    g = torch.Generator(device="cuda").manual_seed(77)
+    dout = torch.randn(layer.q.shape, generator=g, device="cuda", dtype=torch.float32).to(layer.q.dtype)
+    dq, dk, dv = (torch.empty_like(layer.q) for _ in range(3))
+    ws_n = int(layer.lib.het_attn_backward_workspace_bytes(ctypes.byref(layer.shape)))
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    layer.route(); layer.local(); layer.dense()
+
+    def call():
+        st = layer.lib.het_attn_backward(ctypes.byref(layer.shape), layer.q.data_ptr(), layer.k.data_ptr(),
+                                         layer.v.data_ptr(), ctypes.byref(layer.rs), layer.o.data_ptr(),
+                                         dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                         ws.data_ptr(), ws_n, layer.stream)
+        if st != 0:
+            raise het.HetAttnError(st, "het_attn_backward")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [(E(), E()) for _ in range(iters)]
+    for a, b in ev:
+        a.record(); call(); b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    return ts[len(ts) // 2]
+
+
 def cpu_baseline(w, q, k, v, u, rho, stride: int):
     """The fp64 oracle on the host cores, on a bounded sample of the same
     layer: the full route plus every `stride`-th dense and local row."""
@@ -325,6 +358,8 @@ def main():
                     help="routing of the timed layer (the ablation routers of the routing study)")
     ap.add_argument("--border", default="shift", choices=["shift", "cut"],
                     help="local window border: shifted inside the grid, or cut at it")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time het_attn_backward (dQ, dK, dV) on the same layer")
     ap.add_argument("--swap-ratio", type=float, default=0.07,
                     help="ratio r of the per-block random swap timed beside the step (0 skips it)")
     ap.add_argument("--oracle-full", action="store_true",
@@ -437,6 +472,14 @@ def main():
     }
     if cold is not None:
         out["cold"] = cold
+
+    if args.backward:
+        bms = time_backward(layer, max(5, args.steps // 5))
+        bflop = 2.5 * eff_flop  # five products (S, dP, dV, dQ, dK) against the forward's two
+        out["backward"] = {"ms_median": round(bms, 4), "algorithmic_flop": bflop,
+                           "TFLOPs": round(bflop / (bms * 1e-3) / 1e12, 2),
+                           "frac_bf16_peak": round(bflop / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench] backward: {out['backward']}")
 
     if args.swap_ratio > 0:
         # Per-block random swap: one launch makes the routes of all 30 blocks

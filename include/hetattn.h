@@ -200,6 +200,29 @@ int het_attn_local(const het_attn_shape *shape, const void *q, const void *k, co
                    const het_route *route, void *o, void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/* Device workspace het_attn_backward needs for this shape, in bytes
+ * (2 * B * heads * N fp32 values); 0 for an invalid shape. */
+size_t het_attn_backward_workspace_bytes(const het_attn_shape *shape);
+
+/* Backward pass of het_attn_forward with the route held fixed: the layer is
+ * softmax attention over each row's key set ([HetA §3.1.1 Eqs. 2-3, §3.2.2
+ * Eq. 13]), so for dout = dL/dO and P the softmax weights of a row,
+ *   dP_j = dout.v_j, D = dout.o = sum_j P_j dP_j, dS_j = P_j (dP_j - D),
+ *   dQ = scale * sum_j dS_j k_j, dK_j += scale * dS_j q, dV_j += P_j dout,
+ * summed over every row whose key set holds key j.  The paper's second
+ * training stage fine-tunes through this layer ([HetA §4, Training Setting]).
+ *   q, k, v, route  as given to het_attn_forward (same shape).
+ *   o        the output het_attn_forward wrote for them.
+ *   dout     dL/dO, same layout and type.
+ *   dq, dk, dv  device, same layout and type; every row is written once.
+ *            Must not overlap the inputs or each other.
+ *   workspace, workspace_bytes: at least het_attn_backward_workspace_bytes(shape).
+ * Accumulation in fp32; with bf16 inputs P and dS are rounded to bf16 as
+ * operands of the products. */
+int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                      const het_route *route, const void *o, const void *dout, void *dq, void *dk,
+                      void *dv, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -224,3 +224,37 @@ def test_route_random_argument_errors(lib):
         o = het.RouteStruct(0x100000, 0x200000, 0x300000, 0x400000, 0, -1)
         setattr(o, field, None)
         assert call(out=o) == het.HET_ERR_INVALID_ARG, field
+
+
+def test_backward_argument_errors(lib):
+    s = good_shape()  # B=1, N=256, heads=2, D=64, f32: 128 KiB per tensor
+    ws_n = lib.het_attn_backward_workspace_bytes(ctypes.byref(s))
+    assert ws_n == 2 * 1 * 2 * 256 * 4
+    assert lib.het_attn_backward_workspace_bytes(ctypes.byref(good_shape(head_dim=96))) == 0
+    span = 1 << 20
+    base = {n: (i + 1) * span for i, n in enumerate(("q", "k", "v", "o", "dout", "dq", "dk", "dv", "ws"))}
+
+    def call(shape=s, route=None, ws_bytes=ws_n, **kw):
+        p = dict(base, **kw)
+        r = route if route is not None else fake_route()
+        return lib.het_attn_backward(ctypes.byref(shape) if shape is not None else None, p["q"], p["k"],
+                                     p["v"], ctypes.byref(r), p["o"], p["dout"], p["dq"], p["dk"], p["dv"],
+                                     p["ws"], ws_bytes, None)
+
+    assert call(shape=None) == het.HET_ERR_INVALID_ARG
+    assert call(shape=good_shape(head_dim=96)) == het.HET_ERR_UNSUPPORTED
+    for name in ("q", "k", "v", "o", "dout", "dq", "dk", "dv"):
+        assert call(**{name: None}) == het.HET_ERR_INVALID_ARG, name
+    r = fake_route()
+    r.counts = None
+    assert call(route=r) == het.HET_ERR_INVALID_ARG
+    r = fake_route()
+    r.dense_count_host = 300
+    assert call(route=r) == het.HET_ERR_INVALID_ARG
+    # outputs overlapping an input or each other
+    assert call(dq=base["v"] + 64) == het.HET_ERR_INVALID_ARG
+    assert call(dk=base["dq"] + 4096) == het.HET_ERR_INVALID_ARG
+    assert call(dv=base["dout"]) == het.HET_ERR_INVALID_ARG
+    # workspace
+    assert call(ws_bytes=ws_n - 1) == het.HET_ERR_WORKSPACE
+    assert call(ws=None) == het.HET_ERR_WORKSPACE

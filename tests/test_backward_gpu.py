@@ -1,0 +1,142 @@
+"""GPU backward pass (het_attn_backward) against the fp64 oracle.
+
+[HetA] = "Where Compute Matters: Heterogeneous Attention for Efficient Video
+Diffusion" (HetA-DiT): the routed layer (§3.2.2 Eq. 13 over §3.1.1 Eqs. 2-3)
+differentiated with the route held fixed, as the second training stage needs
+(§4, Training Setting).
+
+Errors are taken relative to the largest magnitude of each reference
+gradient tensor G: max |got - ref| / max |G| and mean |got - ref| / max |G|.
+Bounds: bf16 2e-2 / 2e-3 (inputs exact, P and dS rounded to bf16 as MFMA
+operands, outputs rounded to bf16: a few 2^-9 relative per term), fp32
+1e-5 / 1e-6.  Small cases compare every element of dQ, dK and dV; the full
+Wan-1.3B shape compares sampled dQ rows (the oracle computes them row by
+row) and, for dK and dV, identities that hold at any size: the key
+gradients of a (sample, head) sum to zero and the value gradients sum to
+the sum of dO.
+"""
+import numpy as np
+import pytest
+
+import uncertainty_routed_heterogeneous_amd as het
+import workloads as W
+from gpu_util import gpu_route, log, to_gpu, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-5, 1e-6)}
+
+
+def rel_check(got, ref, dtype, what):
+    scale = float(np.abs(ref).max()) or 1.0
+    err = np.abs(got.astype(np.float64) - ref) / scale
+    mx, mean = float(err.max()), float(err.mean())
+    tmax, tmean = TOL[dtype]
+    log(f"  {what}: max {mx:.2e} mean {mean:.2e} of max|ref| {scale:.3e} (tol {tmax:.0e}/{tmean:.0e})")
+    assert np.isfinite(got).all(), what
+    assert mx <= tmax and mean <= tmean, what
+
+
+def make_case(grid, heads, head_dim, dtype, batch=2, seed=0, window=(3, 7, 7), u_kind="iid"):
+    w = W.Workload(f"bwd{seed}", 970 + seed, batch, heads, head_dim, tuple(grid), tuple(window), 0.3,
+                   dtype, u_kind)
+    q, k, v = W.make_qkv(w)
+    rng = np.random.default_rng(4000 + seed)
+    dout = rng.standard_normal(q.shape).astype(np.float32)
+    if dtype == "bf16":
+        dout = W.round_to_bf16(dout)
+    return w, q, k, v, dout, W.make_u(w)
+
+
+def gpu_backward(w, q, k, v, dout, r, border="shift"):
+    import torch
+    t = lambda x: to_gpu(x, w.dtype)
+    qg, kg, vg, dg = t(q), t(k), t(v), t(dout)
+    o = het.forward(qg, kg, vg, r, border=border)
+    dq, dk, dv = het.backward(qg, kg, vg, r, o, dg, border=border)
+    torch.cuda.synchronize()
+    return tuple(x.float().cpu().numpy() for x in (dq, dk, dv))
+
+
+def full_check(oracle_mod, w, q, k, v, dout, r, what, border="shift"):
+    log(f"[backward] {what} grid={w.grid} win={w.window} B={w.batch} H={w.heads} D={w.head_dim} "
+        f"{w.dtype} border={border}")
+    got = gpu_backward(w, q, k, v, dout, r, border)
+    mask = r.mask.cpu().numpy()
+    ref = oracle_mod.backward(q, k, v, dout, w.grid, w.window, w.softmax_scale, mask, border=border)
+    for name, g, rf in zip(("dQ", "dK", "dV"), got, ref):
+        rel_check(g, rf, w.dtype, f"{what} {name}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("rho", [0.0, 0.3, 1.0])
+def test_backward_small_grid(oracle_mod, dtype, head_dim, rho):
+    # N = 1200: ragged query and key tiles in every axis, 38 dense blocks of 32.
+    w, q, k, v, dout, u = make_case((6, 10, 20), 2, head_dim, dtype, seed=head_dim + int(10 * rho))
+    r = gpu_route(u, w.grid, w.window, w.heads, w.head_dim, dtype, rho=rho)
+    full_check(oracle_mod, w, q, k, v, dout, r, f"rho={rho}")
+
+
+@pytest.mark.parametrize("window", [(1, 3, 3), (5, 9, 13), (3, 9, 25), (11, 11, 11)])
+def test_backward_windows(oracle_mod, window):
+    w, q, k, v, dout, u = make_case((15, 18, 29), 1, 128, "bf16", batch=1, seed=window[2], window=window)
+    r = gpu_route(u, w.grid, w.window, w.heads, w.head_dim, "bf16", rho=0.2)
+    full_check(oracle_mod, w, q, k, v, dout, r, f"window {window}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_cut_border(oracle_mod, dtype):
+    w, q, k, v, dout, u = make_case((6, 10, 20), 2, 64, dtype, seed=31, window=(3, 7, 9))
+    r = gpu_route(u, w.grid, w.window, w.heads, w.head_dim, dtype, rho=0.2)
+    full_check(oracle_mod, w, q, k, v, dout, r, "cut border", border="cut")
+
+
+def test_backward_mean_std_and_swapped_routes(oracle_mod):
+    import torch
+    w, q, k, v, dout, u = make_case((6, 10, 20), 2, 128, "bf16", seed=41, u_kind="lognormal")
+    r = gpu_route(u, w.grid, w.window, w.heads, w.head_dim, "bf16", c=0.9)
+    full_check(oracle_mod, w, q, k, v, dout, r, "mean-std route")
+    (rs,) = het.swap(r, 0.1, 5, 0, 3)
+    torch.cuda.synchronize()
+    full_check(oracle_mod, w, q, k, v, dout, rs, "swapped route")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_single_token(oracle_mod, dtype):
+    w, q, k, v, dout, u = make_case((1, 1, 1), 1, 64, dtype, batch=1, seed=51, window=(3, 3, 3))
+    for rho in (0.0, 1.0):
+        r = gpu_route(u, w.grid, w.window, w.heads, w.head_dim, dtype, rho=rho)
+        dq, dk, dv = gpu_backward(w, q, k, v, dout, r)
+        # one key: P = 1, so dV = dO, and dS = P (dP - D) = 0 up to the two
+        # fp32 sums for dP and D, so dQ = dK = 0 to that rounding
+        np.testing.assert_allclose(dv, dout, rtol=0, atol=1e-6)
+        tol = 1e-4 if dtype == "bf16" else 1e-5
+        assert np.abs(dq).max() < tol and np.abs(dk).max() < tol
+
+
+def test_backward_full_size_sampled(oracle_mod):
+    w = W.WORKLOADS["wan13b"]
+    q, k, v = W.make_qkv(w)
+    u = W.make_u(w)
+    dout = W.round_to_bf16(np.random.default_rng(77).standard_normal(q.shape).astype(np.float32))
+    log(f"[backward] full size {w.name} rho={w.rho}")
+    r = gpu_route(u, w.grid, w.window, w.heads, w.head_dim, "bf16", rho=w.rho)
+    dq, dk, dv = gpu_backward(w, q, k, v, dout, r)
+    mask = r.mask.cpu().numpy()
+    rng = np.random.default_rng(8)
+    dense = np.nonzero(mask[0] == 0)[0]
+    local = np.nonzero(mask[0] == 1)[0]
+    rows = np.unique(np.concatenate([rng.choice(dense, 24, replace=False), rng.choice(local, 40, replace=False),
+                                     [dense[0], dense[-1], local[0], local[-1]]])).astype(np.int64)
+    ref = oracle_mod.backward_dq_rows(q, k, v, dout, w.grid, w.window, w.softmax_scale, mask, rows)
+    rel_check(dq.reshape(w.n_tokens, w.heads, w.head_dim)[rows], ref, "bf16", "wan13b dQ sampled rows")
+    # sum identities over all keys of each head (float64 sums of the bf16 results)
+    sk = dk.astype(np.float64).sum(axis=1)          # [B, heads, D]
+    ak = np.abs(dk.astype(np.float64)).sum(axis=1)
+    assert np.all(np.abs(sk) <= 4e-3 * ak + 1e-6), float((np.abs(sk) / ak).max())
+    sv = dv.astype(np.float64).sum(axis=1)
+    so = dout.astype(np.float64).sum(axis=1)
+    av = np.abs(dv.astype(np.float64)).sum(axis=1)
+    assert np.all(np.abs(sv - so) <= 4e-3 * av + 1e-3), float((np.abs(sv - so) / av).max())
+    assert np.isfinite(dk).all() and np.isfinite(dv).all()

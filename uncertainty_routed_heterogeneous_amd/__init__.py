@@ -59,6 +59,12 @@ SIGNATURES = {
     "het_attn_route": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_int,
                                       ctypes.c_double, ctypes.POINTER(RouteStruct), ctypes.c_void_p]),
 }
+SIGNATURES["het_attn_backward_workspace_bytes"] = (ctypes.c_size_t, [ctypes.POINTER(Shape)])
+SIGNATURES["het_attn_backward"] = (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.POINTER(RouteStruct),
+                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_size_t, ctypes.c_void_p])
 SIGNATURES["het_attn_route_random"] = (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_double, ctypes.c_uint64,
                                                       ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int32,
                                                       ctypes.POINTER(RouteStruct), ctypes.c_void_p])
@@ -272,3 +278,24 @@ def forward(q, k, v, r: Route, scale: float | None = None, out=None, stream=None
     if st != HET_OK:
         raise HetAttnError(st, name)
     return out
+
+
+def backward(q, k, v, r: Route, o, dout, scale: float | None = None, stream=None, border: str = "shift"):
+    """(dQ, dK, dV) of forward(q, k, v, r) = o for dL/dO = dout (het_attn_backward)."""
+    import torch
+    for t in (q, k, v, o, dout):
+        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, dout must be contiguous CUDA tensors of one shape and dtype")
+    B, N, H, D = q.shape
+    shape = make_shape(B, H, D, r.grid, r.window, _dtype_code(q.dtype), scale or 0.0, border)
+    lib = load_library()
+    ws_n = int(lib.het_attn_backward_workspace_bytes(ctypes.byref(shape)))
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    rs = r.as_struct()
+    st = lib.het_attn_backward(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(rs),
+                               o.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                               ws.data_ptr(), ws_n, _stream_handle(stream))
+    if st != HET_OK:
+        raise HetAttnError(st, "het_attn_backward")
+    return dq, dk, dv

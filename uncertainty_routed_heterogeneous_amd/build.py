@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhetattn.so")
-SOURCES = ["api.cpp", "route.hip", "dense.hip", "local.hip"]
+SOURCES = ["api.cpp", "route.hip", "dense.hip", "local.hip", "backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU ops stay disabled: plain fp32 code must not be turned into

@@ -292,3 +292,69 @@ int het_attn_local(const het_attn_shape *shape, const void *q, const void *k, co
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t het_attn_backward_workspace_bytes(const het_attn_shape *shape) {
+    Dims d;
+    float scale;
+    if (check_shape(shape, d, scale) != HET_OK) return 0;
+    return hetattn::backward_workspace_bytes((int)d.B, (int)d.H, (int)d.N);
+}
+
+int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                      const het_route *route, const void *o, const void *dout, void *dq, void *dk,
+                      void *dv, void *workspace, size_t workspace_bytes, void *stream) {
+    Dims d;
+    float scale;
+    const het_status st = check_shape(shape, d, scale);
+    if (st != HET_OK) return st;
+    if (!q || !k || !v || !o || !dout || !dq || !dk || !dv || !route || !route->mask ||
+        !route->dense_idx || !route->counts)
+        return HET_ERR_INVALID_ARG;
+    if (route->dense_count_host < -1 || route->dense_count_host > d.N) return HET_ERR_INVALID_ARG;
+    const size_t elem = shape->dtype == HET_BF16 ? 2 : 4;
+    const size_t bytes = (size_t)(d.B * d.N * d.H * d.D) * elem;
+    const void *ins[5] = {q, k, v, o, dout};
+    void *outs[3] = {dq, dk, dv};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(outs[i], bytes, ins[j], bytes)) return HET_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], bytes, outs[j], bytes)) return HET_ERR_INVALID_ARG;
+    }
+    const size_t need = hetattn::backward_workspace_bytes((int)d.B, (int)d.H, (int)d.N);
+    if (!workspace || workspace_bytes < need) return HET_ERR_WORKSPACE;
+    hetattn::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.mask = route->mask;
+    a.dense_idx = route->dense_idx;
+    a.counts = route->counts;
+    a.lse = (float *)workspace;
+    a.dsum = (float *)workspace + (size_t)(d.B * d.H * d.N);
+    a.batch = (int)d.B;
+    a.n = (int)d.N;
+    a.heads = (int)d.H;
+    a.head_dim = (int)d.D;
+    a.grid_t = shape->grid_t;
+    a.grid_h = shape->grid_h;
+    a.grid_w = shape->grid_w;
+    a.win_t = shape->win_t;
+    a.win_h = shape->win_h;
+    a.win_w = shape->win_w;
+    a.cut = shape->border == HET_BORDER_CUT ? 1 : 0;
+    a.bf16 = shape->dtype == HET_BF16;
+    a.scale = scale;
+    a.max_dense = route->dense_count_host >= 0 ? route->dense_count_host : (int)d.N;
+    if (hetattn::launch_backward(a, (hipStream_t)stream) != hipSuccess) return HET_ERR_HIP;
+    return HET_OK;
+}
+
+}  // extern "C"

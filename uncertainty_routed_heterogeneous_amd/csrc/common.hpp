@@ -125,4 +125,17 @@ __device__ __forceinline__ int window_start(int pos, int k, int len, int S) {
     return imax(s, 0);
 }
 
+// Window [lo, hi) of position pos along an axis of extent S, for the odd
+// window k of effective length len = min(k, S): shifted to stay inside
+// [0, S) (cut = 0), or centred on pos and cut at the border (cut = 1).  Both
+// ends are non-decreasing in pos, so the union of the windows of the
+// positions p0 <= p <= p1 is [lo(p0), hi(p1)), and it is never wider than
+// p1 - p0 + len.
+__device__ __forceinline__ int win_lo(int pos, int k, int len, int S, int cut) {
+    return cut ? imax(pos - (k - 1) / 2, 0) : window_start(pos, k, len, S);
+}
+__device__ __forceinline__ int win_hi(int pos, int k, int len, int S, int cut) {
+    return cut ? imin(pos + (k - 1) / 2 + 1, S) : window_start(pos, k, len, S) + len;
+}
+
 }  // namespace hetattn

@@ -52,6 +52,34 @@ struct AttnArgs {
     int cu_count;              // compute units of the device the launch runs on
 };
 
+// Grid and window of the local kernels and the backward pass (query tiles of
+// tiles_y x tiles_x per frame).
+struct LocalGeom {
+    int T, Hg, Wg;     // grid
+    int wt, wh, ww;    // requested (odd) window
+    int lt, lh, lw;    // effective window lengths, min(w, extent)
+    int tiles_y, tiles_x;
+    int slot_row;      // SR: 16 or 32 column slots per box row
+    int cut;           // window border: 0 = shifted inside the grid, 1 = cut at it
+};
+
+// Backward pass: gradients of the layer for dout = dL/dO, with the route held
+// fixed.  lse and dsum are [batch, heads, n] fp32 workspace arrays.
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    void *dq, *dk, *dv;
+    const uint8_t *mask;
+    const int32_t *dense_idx, *counts;
+    float *lse, *dsum;
+    int batch, n, heads, head_dim;
+    int grid_t, grid_h, grid_w;
+    int win_t, win_h, win_w;
+    int cut;
+    bool bf16;
+    float scale;
+    int max_dense;  // upper bound on any sample's dense count
+};
+
 // Largest effective window along w that the local kernel's key tiling holds.
 constexpr int kLocalMaxWinW = 25;
 
@@ -62,5 +90,7 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t stream);
 hipError_t launch_swap(const SwapArgs &a, int n_blocks, hipStream_t stream);
 hipError_t launch_dense(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_local(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
+size_t backward_workspace_bytes(int batch, int heads, int n);
 
 }  // namespace hetattn

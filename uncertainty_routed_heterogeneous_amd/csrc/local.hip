@@ -31,27 +31,7 @@ namespace hetattn {
 constexpr int kLocalQY = 4;
 constexpr int kLocalQX = 8;
 
-struct LocalGeom {
-    int T, Hg, Wg;     // grid
-    int wt, wh, ww;    // requested (odd) window
-    int lt, lh, lw;    // effective window lengths, min(w, extent)
-    int tiles_y, tiles_x;
-    int slot_row;      // SR: 16 or 32 column slots per box row
-    int cut;           // window border: 0 = shifted inside the grid, 1 = cut at it
-};
 
-// Window [lo, hi) of position pos along an axis of extent S, for the odd
-// window k of effective length len = min(k, S): shifted to stay inside
-// [0, S) (cut = 0), or centred on pos and cut at the border (cut = 1).  Both
-// ends are non-decreasing in pos, so the union of the windows of the
-// positions p0 <= p <= p1 is [lo(p0), hi(p1)), and it is never wider than
-// p1 - p0 + len.
-__device__ __forceinline__ int win_lo(int pos, int k, int len, int S, int cut) {
-    return cut ? imax(pos - (k - 1) / 2, 0) : window_start(pos, k, len, S);
-}
-__device__ __forceinline__ int win_hi(int pos, int k, int len, int S, int cut) {
-    return cut ? imin(pos + (k - 1) / 2 + 1, S) : window_start(pos, k, len, S) + len;
-}
 
 template <typename T, int D, int SR>
 __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
