@@ -11,22 +11,26 @@
 //   dQ_i = scale * sum_j dS_ij k_j,  dK_j = scale * sum_i dS_ij q_i,
 //   dV_j = sum_i P_ij dO_i.
 //
-// Three kernels, each workgroup one wave that owns 32 output rows (no
-// atomics; every row of dQ, dK, dV is written once):
-//   bwd_prep_kernel   D_i for every (token, head);
-//   bwd_dq_kernel     32 query rows: a first pass over their key blocks for
-//                     LSE_i (written to the workspace for the next kernel),
-//                     then S, P, dP, dS per block and dQ += dS K;
-//   bwd_dkdv_kernel   32 keys (a 4x8 tile of one frame, K and V rows kept in
-//                     registers): every dense query of the sample, then the
-//                     local queries whose windows may hold these keys (per
-//                     axis an interval of positions), dV += P^T dO and
-//                     dK += dS^T Q.
+// Four kernels; every workgroup owns its output rows (no atomics; every row
+// of dQ, dK, dV is written once):
+//   bwd_prep_kernel      D_i for every (token, head);
+//   bwd_dq_dense_kernel  128 dense rows, 32 per wave: a first pass over the
+//                        key blocks for LSE_i (written to the workspace for
+//                        the dK/dV kernel), then S, P, dP, dS per block and
+//                        dQ += dS K; the four waves share each 32-key block
+//                        of K and V staged in LDS;
+//   bwd_dq_kernel        the same for a 4x8 tile of local rows of one frame
+//                        over its window box (one wave);
+//   bwd_dkdv_kernel      128 keys (four 4x8 tiles of one frame, a wave each,
+//                        K and V rows in registers): every dense query of the
+//                        sample, then the local queries whose windows may
+//                        hold these keys (per axis an interval of positions);
+//                        the waves share each staged 32-query block;
+//                        dV += P^T dO and dK += dS^T Q.
 // Products run on the 32x32 MFMA of the element type (bf16 with fp32
 // accumulation: P and dS are rounded to bf16 as operands; fp32: fp32 MFMA).
-// Operands whose rows must be read transposed (K for dQ, Q and dO for dK and
-// dV) go through LDS; the others are loaded from global memory straight into
-// the lane layout of the MFMA.
+// Operands whose rows are read transposed (K for dQ, Q and dO for dK and dV)
+// go through LDS.
 #include <type_traits>
 
 #include "common.hpp"
@@ -77,17 +81,29 @@ struct Slab {
 };
 
 // Copies row `row_of(s)` (or zeros when !ok_of(s)) of each slot s < 32 into
-// the slab; every lane moves kStage 16-byte chunks.
-template <typename T, int D, typename RowOf, typename OkOf>
+// the slab; the first kThreads threads of the workgroup move the 16-byte
+// chunks between them.
+template <typename T, int D, int kThreads = 64, typename RowOf, typename OkOf>
 __device__ __forceinline__ void stage_rows(T *slab, RowOf &&row_of, OkOf &&ok_of) {
     using S = Slab<T, D>;
-    const int lane = threadIdx.x & 63;
+    constexpr int kTotal = 32 * S::kChunks;
+    static_assert(kTotal % kThreads == 0, "chunks per thread");
+    const int tid = threadIdx.x % kThreads;
 #pragma unroll
-    for (int it = 0; it < S::kStage; ++it) {
-        const int e = lane + 64 * it, s = e / S::kChunks, ch = e % S::kChunks;
+    for (int it = 0; it < kTotal / kThreads; ++it) {
+        const int e = tid + kThreads * it, s = e / S::kChunks, ch = e % S::kChunks;
         const u32x4 val = ok_of(s) ? *(const u32x4 *)(row_of(s) + S::kVec * ch) : u32x4{0, 0, 0, 0};
         *(u32x4 *)(slab + s * S::kPitch + S::kVec * ch) = val;
     }
+}
+
+// Fragment c of slab row l%32 as a 32x32 MFMA operand (as load_frag).
+template <typename T, int D>
+__device__ __forceinline__ typename Frag<T>::type lds_frag(const T *slab, int c) {
+    using S = Slab<T, D>;
+    const int lane = threadIdx.x & 63, half = lane >> 5, row = lane & 31;
+    if constexpr (Frag<T>::kBf16) return *(const bf16x8 *)(slab + row * S::kPitch + 16 * c + 8 * half);
+    else return slab[row * S::kPitch + 2 * c + half];
 }
 
 // acc[db] += X^T B, X = the slab (32 slots x D, slot order of the B
@@ -189,8 +205,110 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T *__restrict__ o, 
     }
 }
 
+constexpr int kBwdWaves = 4;  // waves of the dense-dQ and dK/dV workgroups
+
+// dQ and LSE of 128 dense rows (consecutive entries of the dense index list):
+// wave w takes 32 of them; the four waves share every 32-key block of K and
+// V, staged once into LDS (row reads for S and dP, transposed reads of K for
+// dQ += dS K).
+template <typename T, int D>
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_dq_dense_kernel(BwdArgs a, int n_units) {
+    using F = Frag<T>;
+    using S = Slab<T, D>;
+    constexpr int kSteps = F::template steps<D>();
+    __shared__ __attribute__((aligned(16))) T Ks[32 * S::kPitch];
+    __shared__ __attribute__((aligned(16))) T Vs[32 * S::kPitch];
+
+    const int unit = blockIdx.x;
+    if (unit >= n_units) return;
+    const int N = a.n, H = a.heads;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, col = lane & 31;
+    const T *q = (const T *)a.q, *k = (const T *)a.k, *v = (const T *)a.v, *dout = (const T *)a.dout;
+    const size_t tok_stride = (size_t)H * D;
+    const int groups = (a.max_dense + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
+    const int grp = unit % groups, h = (unit / groups) % H, b = unit / groups / H;
+    const int cnt = a.counts[2 * b];
+    if (32 * kBwdWaves * grp >= cnt) return;  // the whole workgroup
+    const int slot = 32 * kBwdWaves * grp + 32 * wave + col;
+    const bool valid = slot < cnt;
+    const int tok = valid ? a.dense_idx[(size_t)b * N + slot] : 0;
+    const size_t sample = (size_t)b * N * tok_stride + (size_t)h * D;
+    const size_t row_bh = ((size_t)b * H + h) * N;
+    const float sl2 = a.scale * kLog2e;
+
+    typename F::type qf[kSteps], df[kSteps];
+#pragma unroll
+    for (int c = 0; c < kSteps; ++c) {
+        qf[c] = load_frag(q + sample + (size_t)tok * tok_stride, c, valid);
+        df[c] = load_frag(dout + sample + (size_t)tok * tok_stride, c, valid);
+    }
+    const float dq_i = valid ? a.dsum[row_bh + tok] : 0.0f;
+    const int n_blocks = (N + 31) / 32;
+    auto key_row = [&](const T *base, int kb) HET_INLINE {
+        return [=](int s) HET_INLINE { return base + sample + (size_t)imin(32 * kb + s, N - 1) * tok_stride; };
+    };
+    auto key_ok = [&](int kb) HET_INLINE { return [=](int s) HET_INLINE { return 32 * kb + s < N; }; };
+    auto in_block = [&](int kb, int i) HET_INLINE {
+        return valid && 32 * kb + 8 * (i / 4) + 4 * half + (i % 4) < N;
+    };
+
+    // Pass 1: LSE of every row (log2 units of scale * q.k).
+    float m_run = -__builtin_inff(), l_run = 0.0f;
+    for (int kb = 0; kb < n_blocks; ++kb) {
+        __syncthreads();  // every wave is done with the previous block
+        stage_rows<T, D, 64 * kBwdWaves>(Ks, key_row(k, kb), key_ok(kb));
+        __syncthreads();
+        f32x16 sc = f32x16{};
+#pragma unroll
+        for (int c = 0; c < kSteps; ++c) sc = mma<T>(lds_frag<T, D>(Ks, c), qf[c], sc);
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (in_block(kb, i)) mx = fmaxf(mx, sc[i] * sl2);
+        mx = half_pair_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        float part = 0.0f;
+        if (m_new != -__builtin_inff()) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (in_block(kb, i)) part += __builtin_amdgcn_exp2f(sc[i] * sl2 - m_new);
+            l_run = l_run * (m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new));
+        }
+        l_run += part;
+        m_run = m_new;
+    }
+    const float lse2 = valid ? m_run + __builtin_log2f(half_pair_sum(l_run)) : 0.0f;
+    if (valid && half == 0) a.lse[row_bh + tok] = lse2;
+
+    // Pass 2: dQ^T += K^T dS^T.
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+    for (int kb = 0; kb < n_blocks; ++kb) {
+        __syncthreads();
+        stage_rows<T, D, 64 * kBwdWaves>(Ks, key_row(k, kb), key_ok(kb));
+        stage_rows<T, D, 64 * kBwdWaves>(Vs, key_row(v, kb), key_ok(kb));
+        __syncthreads();
+        f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int c = 0; c < kSteps; ++c) {
+            sc = mma<T>(lds_frag<T, D>(Ks, c), qf[c], sc);
+            dp = mma<T>(lds_frag<T, D>(Vs, c), df[c], dp);
+        }
+        float ds[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = in_block(kb, i) ? __builtin_amdgcn_exp2f(sc[i] * sl2 - lse2) : 0.0f;
+            ds[i] = p * (dp[i] - dq_i);
+        }
+        mma_slab_t<T, D>(Ks, ds, acc);
+    }
+    if (valid) store_row_t<T, D>((T *)a.dq + sample + (size_t)tok * tok_stride, acc, a.scale);
+}
+
 // dQ of 32 query rows (kDense: 32 consecutive entries of the dense index
-// list; else a 4x8 tile of local rows of one frame), and LSE of those rows.
+// list -- the one-wave form; the dense rows use bwd_dq_dense_kernel -- else
+// a 4x8 tile of local rows of one frame), and LSE of those rows.
 template <typename T, int D, bool kDense, int SR>
 __global__ __launch_bounds__(64) void bwd_dq_kernel(BwdArgs a, LocalGeom g, int n_units) {
     using F = Frag<T>;
@@ -351,12 +469,18 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BwdArgs a, LocalGeom g, int 
     if (valid) store_row_t<T, D>((T *)a.dq + sample + (size_t)tok * tok_stride, acc, a.scale);
 }
 
-// dK and dV of 32 keys: the 4x8 tile (ty, tx) of frame t.
+// dK and dV of 128 keys: the 4x8 tiles (ty, 4*xg + w) of frame t, wave w
+// taking one tile with its K and V rows in registers.  The four waves share
+// every 32-query block: Q and dO rows, LSE, D and the window of each query,
+// staged once into LDS (row reads for S and dP, transposed reads for dK and
+// dV).
 template <typename T, int D>
-__global__ __launch_bounds__(64) void bwd_dkdv_kernel(BwdArgs a, LocalGeom g, int n_units) {
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_dkdv_kernel(BwdArgs a, LocalGeom g, int x_groups,
+                                                                  int n_units) {
     using F = Frag<T>;
     using S = Slab<T, D>;
     constexpr int kSteps = F::template steps<D>();
+    constexpr int kThreads = 64 * kBwdWaves;
     __shared__ __attribute__((aligned(16))) T Qs[32 * S::kPitch];
     __shared__ __attribute__((aligned(16))) T Ds[32 * S::kPitch];
     __shared__ float s_lse[32], s_d[32];
@@ -365,19 +489,20 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(BwdArgs a, LocalGeom g, in
     const int unit = blockIdx.x;
     if (unit >= n_units) return;
     const int N = a.n, H = a.heads;
-    const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
     const T *q = (const T *)a.q, *k = (const T *)a.k, *v = (const T *)a.v, *dout = (const T *)a.dout;
     const size_t tok_stride = (size_t)H * D;
 
-    const int tx = unit % g.tiles_x;
-    int rest = unit / g.tiles_x;
+    const int xg = unit % x_groups;
+    int rest = unit / x_groups;
     const int ty = rest % g.tiles_y;
     rest /= g.tiles_y;
     const int t = rest % g.T;
     rest /= g.T;
     const int h = rest % H, b = rest / H;
+    const int tx = kBwdWaves * xg + wave;
     const int ky = ty * kBwdQY + col / kBwdQX, kx = tx * kBwdQX + col % kBwdQX;
-    const bool key_ok = ky < g.Hg && kx < g.Wg;
+    const bool key_ok = tx < g.tiles_x && ky < g.Hg && kx < g.Wg;
     const int ktok = key_ok ? (t * g.Hg + ky) * g.Wg + kx : 0;
     const size_t sample = (size_t)b * N * tok_stride + (size_t)h * D;
     const size_t row_bh = ((size_t)b * H + h) * N;
@@ -394,55 +519,55 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(BwdArgs a, LocalGeom g, in
     for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = f32x16{};
 
     // One block of 32 query slots: tok_of(s) is slot s's token (any in-range
-    // token when !ok_of(s)); in_set(s) says whether this lane's key is in
-    // the key set of slot s's query, given its staged window.
+    // token when !ok_of(s)); `windowed` queries see their window, the others
+    // every key.
     auto block = [&](auto &&tok_of, auto &&ok_of, bool windowed) HET_INLINE {
-        stage_rows<T, D>(Qs, [&](int s) HET_INLINE { return q + sample + (size_t)tok_of(s) * tok_stride; }, ok_of);
-        stage_rows<T, D>(Ds, [&](int s) HET_INLINE { return dout + sample + (size_t)tok_of(s) * tok_stride; }, ok_of);
-        if (lane < 32) {
-            const bool ok = ok_of(lane);
-            const int qt = tok_of(lane);
-            s_lse[lane] = ok ? a.lse[row_bh + qt] : 0.0f;
-            s_d[lane] = ok ? a.dsum[row_bh + qt] : 0.0f;
+        __syncthreads();  // every wave is done with the previous block
+        stage_rows<T, D, kThreads>(Qs, [&](int s) HET_INLINE { return q + sample + (size_t)tok_of(s) * tok_stride; },
+                                   ok_of);
+        stage_rows<T, D, kThreads>(Ds, [&](int s) HET_INLINE { return dout + sample + (size_t)tok_of(s) * tok_stride; },
+                                   ok_of);
+        if (tid < 32) {
+            const bool ok = ok_of(tid);
+            const int qt = tok_of(tid);
+            s_lse[tid] = ok ? a.lse[row_bh + qt] : 0.0f;
+            s_d[tid] = ok ? a.dsum[row_bh + qt] : 0.0f;
             if (windowed && ok) {
                 const int qtt = qt / (g.Hg * g.Wg), qy = (qt / g.Wg) % g.Hg, qx = qt % g.Wg;
-                s_win[lane][0] = win_lo(qtt, g.wt, g.lt, g.T, g.cut);
-                s_win[lane][1] = win_hi(qtt, g.wt, g.lt, g.T, g.cut);
-                s_win[lane][2] = win_lo(qy, g.wh, g.lh, g.Hg, g.cut);
-                s_win[lane][3] = win_hi(qy, g.wh, g.lh, g.Hg, g.cut);
-                s_win[lane][4] = win_lo(qx, g.ww, g.lw, g.Wg, g.cut);
-                s_win[lane][5] = win_hi(qx, g.ww, g.lw, g.Wg, g.cut);
+                s_win[tid][0] = win_lo(qtt, g.wt, g.lt, g.T, g.cut);
+                s_win[tid][1] = win_hi(qtt, g.wt, g.lt, g.T, g.cut);
+                s_win[tid][2] = win_lo(qy, g.wh, g.lh, g.Hg, g.cut);
+                s_win[tid][3] = win_hi(qy, g.wh, g.lh, g.Hg, g.cut);
+                s_win[tid][4] = win_lo(qx, g.ww, g.lw, g.Wg, g.cut);
+                s_win[tid][5] = win_hi(qx, g.ww, g.lw, g.Wg, g.cut);
             } else {
-                s_win[lane][0] = ok ? 0 : 0x7fffffff;  // dense query: every key; none: no key
-                s_win[lane][1] = 0x7fffffff;
-                s_win[lane][2] = 0;
-                s_win[lane][3] = 0x7fffffff;
-                s_win[lane][4] = 0;
-                s_win[lane][5] = 0x7fffffff;
+                s_win[tid][0] = ok ? 0 : 0x7fffffff;  // dense query: every key; none: no key
+                s_win[tid][1] = 0x7fffffff;
+                s_win[tid][2] = 0;
+                s_win[tid][3] = 0x7fffffff;
+                s_win[tid][4] = 0;
+                s_win[tid][5] = 0x7fffffff;
             }
         }
-        // S and dP of the block: rows = query slots (A from global rows), columns = keys.
-        const int qt_l = tok_of(col);
-        const bool ok_l = ok_of(col);
-        f32x16 s = f32x16{}, dp = f32x16{};
+        __syncthreads();  // slabs and per-query data visible
+        // S and dP of the block: rows = query slots, columns = this wave's keys.
+        f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int c = 0; c < kSteps; ++c) {
-            s = mma<T>(load_frag(q + sample + (size_t)qt_l * tok_stride, c, ok_l), kf[c], s);
-            dp = mma<T>(load_frag(dout + sample + (size_t)qt_l * tok_stride, c, ok_l), vf[c], dp);
+            sc = mma<T>(lds_frag<T, D>(Qs, c), kf[c], sc);
+            dp = mma<T>(lds_frag<T, D>(Ds, c), vf[c], dp);
         }
-        __syncthreads();  // slabs and per-query data visible
         float p[16], ds[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int qs = 8 * (i / 4) + 4 * half + (i % 4);
             const int *w = s_win[qs];
             const bool in = key_ok && t >= w[0] && t < w[1] && ky >= w[2] && ky < w[3] && kx >= w[4] && kx < w[5];
-            p[i] = in ? __builtin_amdgcn_exp2f(s[i] * sl2 - s_lse[qs]) : 0.0f;
+            p[i] = in ? __builtin_amdgcn_exp2f(sc[i] * sl2 - s_lse[qs]) : 0.0f;
             ds[i] = p[i] * (dp[i] - s_d[qs]);
         }
         mma_slab_t<T, D>(Ds, p, dv);   // dV^T += dO^T P
         mma_slab_t<T, D>(Qs, ds, dk);  // dK^T += Q^T dS
-        __syncthreads();  // slabs free for the next block
     };
 
     // Every dense query of the sample sees every key.
@@ -452,11 +577,12 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(BwdArgs a, LocalGeom g, in
         block([&](int s) HET_INLINE { return didx[imin(32 * qb + s, cnt - 1)]; },
               [&](int s) HET_INLINE { return 32 * qb + s < cnt; }, false);
     }
-    // Local queries whose window may hold a key of this tile.
+    // Local queries whose window may hold a key of the workgroup's tiles.
+    const int tx0 = kBwdWaves * xg, tx1 = imin(tx0 + kBwdWaves, g.tiles_x) - 1;
     int pt0, pt1, py0, py1, px0, px1;
     inverse_window(t, t, g.wt, g.lt, g.T, g.cut, pt0, pt1);
     inverse_window(ty * kBwdQY, imin(ty * kBwdQY + kBwdQY - 1, g.Hg - 1), g.wh, g.lh, g.Hg, g.cut, py0, py1);
-    inverse_window(tx * kBwdQX, imin(tx * kBwdQX + kBwdQX - 1, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut, px0, px1);
+    inverse_window(tx0 * kBwdQX, imin(tx1 * kBwdQX + kBwdQX - 1, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut, px0, px1);
     const int nby = py1 - py0 + 1, nbx = px1 - px0 + 1;
     const int total = (pt1 - pt0 + 1) * nby * nbx;
     const uint8_t *mb = a.mask + (size_t)b * N;
@@ -493,8 +619,10 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
     if (kBwdQX + g.lw - 1 > 32) return hipErrorInvalidValue;  // rejected earlier by the ABI layer
 
     const long rows = (long)a.batch * a.n * a.heads;
-    const int dense_units = a.batch * a.heads * ((a.max_dense + 31) / 32);
+    const int dense_units = a.batch * a.heads * ((a.max_dense + 32 * kBwdWaves - 1) / (32 * kBwdWaves));
     const int tile_units = a.batch * a.heads * g.T * g.tiles_y * g.tiles_x;
+    const int x_groups = (g.tiles_x + kBwdWaves - 1) / kBwdWaves;
+    const int key_units = a.batch * a.heads * g.T * g.tiles_y * x_groups;
     const bool sr16 = g.slot_row == 16;
 #define HET_BWD(T_, D_)                                                                                        \
     do {                                                                                                       \
@@ -502,15 +630,16 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((bwd_prep_kernel<T_, D_>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), \
                            dim3(256), 0, stream, (const T_ *)a.o, (const T_ *)a.dout, a.dsum, rows, a.n, a.heads); \
         if (dense_units > 0)                                                                                   \
-            hipLaunchKernelGGL((bwd_dq_kernel<T_, D_, true, 32>), dim3(dense_units), dim3(64), 0, stream, a, g,  \
-                               dense_units);                                                                   \
+            hipLaunchKernelGGL((bwd_dq_dense_kernel<T_, D_>), dim3(dense_units), dim3(64 * kBwdWaves), 0, stream, \
+                               a, dense_units);                                                                \
         if (sr16)                                                                                              \
             hipLaunchKernelGGL((bwd_dq_kernel<T_, D_, false, 16>), dim3(tile_units), dim3(64), 0, stream, a, g,  \
                                tile_units);                                                                    \
         else                                                                                                   \
             hipLaunchKernelGGL((bwd_dq_kernel<T_, D_, false, 32>), dim3(tile_units), dim3(64), 0, stream, a, g,  \
                                tile_units);                                                                    \
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T_, D_>), dim3(tile_units), dim3(64), 0, stream, a, g, tile_units); \
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T_, D_>), dim3(key_units), dim3(64 * kBwdWaves), 0, stream, a, g,   \
+                           x_groups, key_units);                                                               \
     } while (0)
     if (a.bf16) {
         if (a.head_dim == 128) HET_BWD(__bf16, 128);
