@@ -218,7 +218,8 @@ size_t het_attn_backward_workspace_bytes(const het_attn_shape *shape);
  *            Must not overlap the inputs or each other.
  *   workspace, workspace_bytes: at least het_attn_backward_workspace_bytes(shape).
  * Accumulation in fp32; with bf16 inputs P and dS are rounded to bf16 as
- * operands of the products. */
+ * operands of the products.  Grid axes longer than 32767 are
+ * HET_ERR_UNSUPPORTED. */
 int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k, const void *v,
                       const het_route *route, const void *o, const void *dout, void *dq, void *dk,
                       void *dv, void *workspace, size_t workspace_bytes, void *stream);

@@ -243,6 +243,7 @@ def test_backward_argument_errors(lib):
 
     assert call(shape=None) == het.HET_ERR_INVALID_ARG
     assert call(shape=good_shape(head_dim=96)) == het.HET_ERR_UNSUPPORTED
+    assert call(shape=good_shape(grid=(1, 1, 40000), window=(1, 1, 1))) == het.HET_ERR_UNSUPPORTED
     for name in ("q", "k", "v", "o", "dout", "dq", "dk", "dv"):
         assert call(**{name: None}) == het.HET_ERR_INVALID_ARG, name
     r = fake_route()

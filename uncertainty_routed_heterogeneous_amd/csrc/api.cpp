@@ -313,6 +313,8 @@ int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k,
         !route->dense_idx || !route->counts)
         return HET_ERR_INVALID_ARG;
     if (route->dense_count_host < -1 || route->dense_count_host > d.N) return HET_ERR_INVALID_ARG;
+    // The dK/dV kernel packs window ends of an axis into 16 bits.
+    if (shape->grid_t > 32767 || shape->grid_h > 32767 || shape->grid_w > 32767) return HET_ERR_UNSUPPORTED;
     const size_t elem = shape->dtype == HET_BF16 ? 2 : 4;
     const size_t bytes = (size_t)(d.B * d.N * d.H * d.D) * elem;
     const void *ins[5] = {q, k, v, o, dout};

@@ -244,20 +244,41 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dq_dense_kernel(BwdArgs a,
     }
     const float dq_i = valid ? a.dsum[row_bh + tok] : 0.0f;
     const int n_blocks = (N + 31) / 32;
-    auto key_row = [&](const T *base, int kb) HET_INLINE {
-        return [=](int s) HET_INLINE { return base + sample + (size_t)imin(32 * kb + s, N - 1) * tok_stride; };
-    };
-    auto key_ok = [&](int kb) HET_INLINE { return [=](int s) HET_INLINE { return 32 * kb + s < N; }; };
     auto in_block = [&](int kb, int i) HET_INLINE {
         return valid && 32 * kb + 8 * (i / 4) + 4 * half + (i % 4) < N;
+    };
+    // Staging of key block kb, software-pipelined: the rows of block kb+1
+    // are loaded into registers while block kb is computed.
+    constexpr int kThreads = 64 * kBwdWaves;
+    constexpr int kPer = 32 * S::kChunks / kThreads;
+    const int tid = threadIdx.x;
+    u32x4 rk[kPer], rv[kPer];
+    auto fetch = [&](int kb, bool with_v) HET_INLINE {
+#pragma unroll
+        for (int it = 0; it < kPer; ++it) {
+            const int e = tid + kThreads * it, key = 32 * kb + e / S::kChunks;
+            const size_t off = sample + (size_t)imin(key, N - 1) * tok_stride + (e % S::kChunks) * S::kVec;
+            rk[it] = key < N ? *(const u32x4 *)(k + off) : u32x4{0, 0, 0, 0};
+            if (with_v) rv[it] = key < N ? *(const u32x4 *)(v + off) : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto store = [&](bool with_v) HET_INLINE {
+#pragma unroll
+        for (int it = 0; it < kPer; ++it) {
+            const int e = tid + kThreads * it, o = (e / S::kChunks) * S::kPitch + (e % S::kChunks) * S::kVec;
+            *(u32x4 *)(Ks + o) = rk[it];
+            if (with_v) *(u32x4 *)(Vs + o) = rv[it];
+        }
     };
 
     // Pass 1: LSE of every row (log2 units of scale * q.k).
     float m_run = -__builtin_inff(), l_run = 0.0f;
+    fetch(0, false);
     for (int kb = 0; kb < n_blocks; ++kb) {
         __syncthreads();  // every wave is done with the previous block
-        stage_rows<T, D, 64 * kBwdWaves>(Ks, key_row(k, kb), key_ok(kb));
+        store(false);
         __syncthreads();
+        if (kb + 1 < n_blocks) fetch(kb + 1, false);
         f32x16 sc = f32x16{};
 #pragma unroll
         for (int c = 0; c < kSteps; ++c) sc = mma<T>(lds_frag<T, D>(Ks, c), qf[c], sc);
@@ -284,11 +305,12 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dq_dense_kernel(BwdArgs a,
     f32x16 acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+    fetch(0, true);
     for (int kb = 0; kb < n_blocks; ++kb) {
         __syncthreads();
-        stage_rows<T, D, 64 * kBwdWaves>(Ks, key_row(k, kb), key_ok(kb));
-        stage_rows<T, D, 64 * kBwdWaves>(Vs, key_row(v, kb), key_ok(kb));
+        store(true);
         __syncthreads();
+        if (kb + 1 < n_blocks) fetch(kb + 1, true);
         f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int c = 0; c < kSteps; ++c) {
@@ -483,8 +505,11 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dkdv_kernel(BwdArgs a, Loc
     constexpr int kThreads = 64 * kBwdWaves;
     __shared__ __attribute__((aligned(16))) T Qs[32 * S::kPitch];
     __shared__ __attribute__((aligned(16))) T Ds[32 * S::kPitch];
-    __shared__ float s_lse[32], s_d[32];
-    __shared__ int s_win[32][6];  // query window [t0, t1), [y0, y1), [x0, x1); t0 = INT_MAX: no query
+    // Per query slot: LSE (+inf for a slot without a query, so that P = 0)
+    // and the window [lo, hi) per axis packed as lo | hi << 16 (t, y, x);
+    // D apart.  One 16-byte record per slot is one LDS read per register.
+    __shared__ __attribute__((aligned(16))) int4 s_rec[32];
+    __shared__ float s_d[32];
 
     const int unit = blockIdx.x;
     if (unit >= n_units) return;
@@ -518,65 +543,104 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dkdv_kernel(BwdArgs a, Loc
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = f32x16{};
 
-    // One block of 32 query slots: tok_of(s) is slot s's token (any in-range
-    // token when !ok_of(s)); `windowed` queries see their window, the others
-    // every key.
-    auto block = [&](auto &&tok_of, auto &&ok_of, bool windowed) HET_INLINE {
-        __syncthreads();  // every wave is done with the previous block
-        stage_rows<T, D, kThreads>(Qs, [&](int s) HET_INLINE { return q + sample + (size_t)tok_of(s) * tok_stride; },
-                                   ok_of);
-        stage_rows<T, D, kThreads>(Ds, [&](int s) HET_INLINE { return dout + sample + (size_t)tok_of(s) * tok_stride; },
-                                   ok_of);
-        if (tid < 32) {
-            const bool ok = ok_of(tid);
-            const int qt = tok_of(tid);
-            s_lse[tid] = ok ? a.lse[row_bh + qt] : 0.0f;
-            s_d[tid] = ok ? a.dsum[row_bh + qt] : 0.0f;
-            if (windowed && ok) {
-                const int qtt = qt / (g.Hg * g.Wg), qy = (qt / g.Wg) % g.Hg, qx = qt % g.Wg;
-                s_win[tid][0] = win_lo(qtt, g.wt, g.lt, g.T, g.cut);
-                s_win[tid][1] = win_hi(qtt, g.wt, g.lt, g.T, g.cut);
-                s_win[tid][2] = win_lo(qy, g.wh, g.lh, g.Hg, g.cut);
-                s_win[tid][3] = win_hi(qy, g.wh, g.lh, g.Hg, g.cut);
-                s_win[tid][4] = win_lo(qx, g.ww, g.lw, g.Wg, g.cut);
-                s_win[tid][5] = win_hi(qx, g.ww, g.lw, g.Wg, g.cut);
-            } else {
-                s_win[tid][0] = ok ? 0 : 0x7fffffff;  // dense query: every key; none: no key
-                s_win[tid][1] = 0x7fffffff;
-                s_win[tid][2] = 0;
-                s_win[tid][3] = 0x7fffffff;
-                s_win[tid][4] = 0;
-                s_win[tid][5] = 0x7fffffff;
+    // Blocks of 32 query slots, software-pipelined: while block qb is
+    // computed, the Q and dO rows (and LSE, D) of block qb+1 are in flight,
+    // and the slot metadata of block qb+2 (its token, and whether it holds a
+    // query) -- itself a global load for both query sources.  meta(qb, s,
+    // tok, ok) gives slot s's token (any in-range token when it holds no
+    // query); `windowed` queries see their window, the others every key.
+    constexpr int kPer = 32 * S::kChunks / kThreads;  // staged chunks per thread and tensor
+    auto chunk_slot = [&](int it) HET_INLINE { return (tid + kThreads * it) / S::kChunks; };
+    auto chunk_off = [&](int it) HET_INLINE { return ((tid + kThreads * it) % S::kChunks) * S::kVec; };
+    auto run = [&](int n_blocks, auto &&meta, auto windowed_tag) HET_INLINE {
+        constexpr bool windowed = decltype(windowed_tag)::value;
+        if (n_blocks <= 0) return;
+        int mtok[kPer + 1];  // slots of this thread's chunks, then slot tid % 32
+        bool mok[kPer + 1];
+        u32x4 rq[kPer], rd[kPer];
+        float r_lse = 0.0f, r_d = 0.0f;
+        int own_tok = 0;
+        bool own_ok = false;
+        auto fetch_meta = [&](int qb) HET_INLINE {
+#pragma unroll
+            for (int it = 0; it < kPer; ++it) meta(qb, chunk_slot(it), mtok[it], mok[it]);
+            meta(qb, tid & 31, mtok[kPer], mok[kPer]);
+        };
+        auto fetch_rows = [&]() HET_INLINE {
+#pragma unroll
+            for (int it = 0; it < kPer; ++it) {
+                const size_t off = sample + (size_t)mtok[it] * tok_stride + chunk_off(it);
+                rq[it] = mok[it] ? *(const u32x4 *)(q + off) : u32x4{0, 0, 0, 0};
+                rd[it] = mok[it] ? *(const u32x4 *)(dout + off) : u32x4{0, 0, 0, 0};
             }
-        }
-        __syncthreads();  // slabs and per-query data visible
-        // S and dP of the block: rows = query slots, columns = this wave's keys.
-        f32x16 sc = f32x16{}, dp = f32x16{};
+            own_tok = mtok[kPer];
+            own_ok = mok[kPer];
+            if (tid < 32) {
+                r_lse = own_ok ? a.lse[row_bh + own_tok] : 0.0f;
+                r_d = own_ok ? a.dsum[row_bh + own_tok] : 0.0f;
+            }
+        };
+        fetch_meta(0);
+        fetch_rows();
+        if (n_blocks > 1) fetch_meta(1);
+        for (int qb = 0; qb < n_blocks; ++qb) {
+            __syncthreads();  // every wave is done with the previous block
 #pragma unroll
-        for (int c = 0; c < kSteps; ++c) {
-            sc = mma<T>(lds_frag<T, D>(Qs, c), kf[c], sc);
-            dp = mma<T>(lds_frag<T, D>(Ds, c), vf[c], dp);
-        }
-        float p[16], ds[16];
+            for (int it = 0; it < kPer; ++it) {
+                const int sl = chunk_slot(it), o = chunk_off(it);
+                *(u32x4 *)(Qs + sl * S::kPitch + o) = rq[it];
+                *(u32x4 *)(Ds + sl * S::kPitch + o) = rd[it];
+            }
+            if (tid < 32) {
+                int4 rec = {0, 0, 0, __float_as_int(own_ok ? r_lse : __builtin_inff())};
+                if (windowed && own_ok) {
+                    const int qtt = own_tok / (g.Hg * g.Wg), qy = (own_tok / g.Wg) % g.Hg, qx = own_tok % g.Wg;
+                    rec.x = win_lo(qtt, g.wt, g.lt, g.T, g.cut) | (win_hi(qtt, g.wt, g.lt, g.T, g.cut) << 16);
+                    rec.y = win_lo(qy, g.wh, g.lh, g.Hg, g.cut) | (win_hi(qy, g.wh, g.lh, g.Hg, g.cut) << 16);
+                    rec.z = win_lo(qx, g.ww, g.lw, g.Wg, g.cut) | (win_hi(qx, g.ww, g.lw, g.Wg, g.cut) << 16);
+                }
+                s_rec[tid] = rec;
+                s_d[tid] = r_d;
+            }
+            __syncthreads();  // slabs and per-query data visible
+            if (qb + 1 < n_blocks) {
+                fetch_rows();
+                if (qb + 2 < n_blocks) fetch_meta(qb + 2);
+            }
+            // S and dP of the block: rows = query slots, columns = this wave's keys.
+            f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int qs = 8 * (i / 4) + 4 * half + (i % 4);
-            const int *w = s_win[qs];
-            const bool in = key_ok && t >= w[0] && t < w[1] && ky >= w[2] && ky < w[3] && kx >= w[4] && kx < w[5];
-            p[i] = in ? __builtin_amdgcn_exp2f(sc[i] * sl2 - s_lse[qs]) : 0.0f;
-            ds[i] = p[i] * (dp[i] - s_d[qs]);
+            for (int c = 0; c < kSteps; ++c) {
+                sc = mma<T>(lds_frag<T, D>(Qs, c), kf[c], sc);
+                dp = mma<T>(lds_frag<T, D>(Ds, c), vf[c], dp);
+            }
+            float p[16], ds[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int qs = 8 * (i / 4) + 4 * half + (i % 4);
+                const int4 rec = s_rec[qs];
+                bool in = key_ok;
+                if constexpr (windowed) {
+                    auto inside = [](int c, int w) HET_INLINE { return c >= (w & 0xffff) && c < (w >> 16); };
+                    in = in && inside(t, rec.x) && inside(ky, rec.y) && inside(kx, rec.z);
+                }
+                p[i] = in ? __builtin_amdgcn_exp2f(sc[i] * sl2 - __int_as_float(rec.w)) : 0.0f;
+                ds[i] = p[i] * (dp[i] - s_d[qs]);
+            }
+            mma_slab_t<T, D>(Ds, p, dv);   // dV^T += dO^T P
+            mma_slab_t<T, D>(Qs, ds, dk);  // dK^T += Q^T dS
         }
-        mma_slab_t<T, D>(Ds, p, dv);   // dV^T += dO^T P
-        mma_slab_t<T, D>(Qs, ds, dk);  // dK^T += Q^T dS
     };
 
     // Every dense query of the sample sees every key.
     const int cnt = a.counts[2 * b];
     const int32_t *didx = a.dense_idx + (size_t)b * N;
-    for (int qb = 0; qb < (cnt + 31) / 32; ++qb) {
-        block([&](int s) HET_INLINE { return didx[imin(32 * qb + s, cnt - 1)]; },
-              [&](int s) HET_INLINE { return 32 * qb + s < cnt; }, false);
-    }
+    run((cnt + 31) / 32,
+        [&](int qb, int s, int &tk, bool &ok) HET_INLINE {
+            ok = 32 * qb + s < cnt;
+            tk = didx[imin(32 * qb + s, cnt - 1)];
+        },
+        std::false_type{});
     // Local queries whose window may hold a key of the workgroup's tiles.
     const int tx0 = kBwdWaves * xg, tx1 = imin(tx0 + kBwdWaves, g.tiles_x) - 1;
     int pt0, pt1, py0, py1, px0, px1;
@@ -586,14 +650,13 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dkdv_kernel(BwdArgs a, Loc
     const int nby = py1 - py0 + 1, nbx = px1 - px0 + 1;
     const int total = (pt1 - pt0 + 1) * nby * nbx;
     const uint8_t *mb = a.mask + (size_t)b * N;
-    auto box_tok = [&](int e) HET_INLINE {
-        e = imin(e, total - 1);
-        return ((pt0 + e / (nby * nbx)) * g.Hg + py0 + (e / nbx) % nby) * g.Wg + px0 + e % nbx;
-    };
-    for (int qb = 0; qb < (total + 31) / 32; ++qb) {
-        block([&](int s) HET_INLINE { return box_tok(32 * qb + s); },
-              [&](int s) HET_INLINE { return 32 * qb + s < total && mb[box_tok(32 * qb + s)] != 0; }, true);
-    }
+    run((total + 31) / 32,
+        [&](int qb, int s, int &tk, bool &ok) HET_INLINE {
+            const int e = imin(32 * qb + s, total - 1);
+            tk = ((pt0 + e / (nby * nbx)) * g.Hg + py0 + (e / nbx) % nby) * g.Wg + px0 + e % nbx;
+            ok = 32 * qb + s < total && mb[tk] != 0;
+        },
+        std::true_type{});
 
     if (key_ok) {
         store_row_t<T, D>((T *)a.dk + sample + (size_t)ktok * tok_stride, dk, a.scale);
