@@ -358,8 +358,8 @@ def main():
                     help="routing of the timed layer (the ablation routers of the routing study)")
     ap.add_argument("--border", default="shift", choices=["shift", "cut"],
                     help="local window border: shifted inside the grid, or cut at it")
-    ap.add_argument("--backward", action="store_true",
-                    help="also time het_attn_backward (dQ, dK, dV) on the same layer")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing het_attn_backward (dQ, dK, dV) on the same layer")
     ap.add_argument("--swap-ratio", type=float, default=0.07,
                     help="ratio r of the per-block random swap timed beside the step (0 skips it)")
     ap.add_argument("--oracle-full", action="store_true",
@@ -473,7 +473,7 @@ def main():
     if cold is not None:
         out["cold"] = cold
 
-    if args.backward:
+    if not args.no_backward:
         bms = time_backward(layer, max(5, args.steps // 5))
         bflop = 2.5 * eff_flop  # five products (S, dP, dV, dQ, dK) against the forward's two
         out["backward"] = {"ms_median": round(bms, 4), "algorithmic_flop": bflop,
