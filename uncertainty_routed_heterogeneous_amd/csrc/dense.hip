@@ -290,45 +290,67 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
                         sc[kbk][i] = key_off < lim ? sc[kbk][i] : -__builtin_inff();
                     }
             }
-            // Scores are already relative to the reference (base 2).
-            float mx = -__builtin_inff();
+            // Scores are already relative to the reference (base 2).  The
+            // reference moves (exactly as a running max would) only on the
+            // first tile of a piece and when a tile's exponentials ran
+            // large: with every score <= kRescaleSlack a lane's 32
+            // exponentials sum to at most 32 * 2^kRescaleSlack, so a larger
+            // sum (or a non-finite one) sends the tile through the exact max
+            // and its exponentials are taken again.  Without the max on
+            // every tile a score may exceed the reference by up to
+            // log2(32) + kRescaleSlack, well inside fp32 and bf16 range.
+            auto rescale = [&]() HET_INLINE {
+                float mx = -__builtin_inff();
 #pragma unroll
-            for (int kbk = 0; kbk < 2; ++kbk)
+                for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kbk][i]);
-            mx = half_pair_max(mx);
-            const bool first = m_ref == -__builtin_inff();  // first tile of the piece
-            const bool grow = first || mx > kRescaleSlack;
-            if (__builtin_expect(__any(grow), 0)) {
-                // The new reference (bf16-representable) and how far it moved.
-                const float m_base = first ? 0.0f : m_ref;
-                const float m_new = grow ? (float)(__bf16)(m_base + mx) : m_base;
-                const float delta = m_new - m_base;
-                const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-delta);
-                m_ref = m_new;
-                l_part *= alpha;
+                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kbk][i]);
+                mx = half_pair_max(mx);
+                const bool first = m_ref == -__builtin_inff();  // first tile of the piece
+                const bool grow = first || mx > kRescaleSlack;
+                if (__builtin_expect(__any(grow), 0)) {
+                    // The new reference (bf16-representable) and how far it moved.
+                    const float m_base = first ? 0.0f : m_ref;
+                    const float m_new = grow ? (float)(__bf16)(m_base + mx) : m_base;
+                    const float delta = m_new - m_base;
+                    const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-delta);
+                    m_ref = m_new;
+                    l_part *= alpha;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+                    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
 #pragma unroll
-                for (int kbk = 0; kbk < 2; ++kbk) sc[kbk] -= delta;
-                if (half == 0) neg_m_b[0] = (__bf16)(-m_ref);
-            }
+                    for (int kbk = 0; kbk < 2; ++kbk) sc[kbk] -= delta;
+                    if (half == 0) neg_m_b[0] = (__bf16)(-m_ref);
+                }
+            };
             // chunk c2 of key block kb = registers 8*c2 .. 8*c2+7, i.e. keys
             // 16*c2 + 8(j/4) + 4*half + j%4 (j < 8) of the block.
+            auto exps = [&]() HET_INLINE -> float {
+                float tsum = 0.0f;
 #pragma unroll
-            for (int kbk = 0; kbk < 2; ++kbk)
+                for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    u32x4 wv;
+                    for (int c2 = 0; c2 < 2; ++c2) {
+                        u32x4 wv;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float p0 = __builtin_amdgcn_exp2f(sc[kbk][8 * c2 + 2 * j]);
-                        const float p1 = __builtin_amdgcn_exp2f(sc[kbk][8 * c2 + 2 * j + 1]);
-                        l_part += p0 + p1;
-                        wv[j] = pack_bf16x2(p0, p1);
+                        for (int j = 0; j < 4; ++j) {
+                            const float p0 = __builtin_amdgcn_exp2f(sc[kbk][8 * c2 + 2 * j]);
+                            const float p1 = __builtin_amdgcn_exp2f(sc[kbk][8 * c2 + 2 * j + 1]);
+                            tsum += p0 + p1;
+                            wv[j] = pack_bf16x2(p0, p1);
+                        }
+                        pf[kbk][c2] = __builtin_bit_cast(bf16x8, wv);
                     }
-                    pf[kbk][c2] = __builtin_bit_cast(bf16x8, wv);
-                }
+                return tsum;
+            };
+            constexpr float kTileSumLimit = 32.0f * (float)(1 << (int)kRescaleSlack);
+            if (__builtin_expect(__any(m_ref == -__builtin_inff()), 0)) rescale();
+            float tsum = exps();
+            if (__builtin_expect(__any(!(tsum <= kTileSumLimit)), 0)) {
+                rescale();
+                tsum = exps();
+            }
+            l_part += tsum;
         };
 
         // ---- rounds kt0 .. kt1 of this piece.  Round r holds K(r) and

@@ -480,45 +480,61 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
         // column 8*((i/4) % (SR/8)) + 4*half + i%4.
         const bool y_in0 = yy0 < uy0 + ny && yy0 >= ylo && yy0 < yhi;
         const bool y_in1 = rpb > 1 && yy0 + 1 < uy0 + ny && yy0 + 1 >= ylo && yy0 + 1 < yhi;
-        float mx = -__builtin_inff();
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int xo = 8 * ((i / 4) % (SR / 8)) + 4 * half + (i % 4);
             const bool y_in = (SR == 16 && i >= 8) ? y_in1 : y_in0;
             const bool ok = y_in && xo >= xlo && xo < xhi;
-            const float xv = ok ? s[i] : -__builtin_inff();
-            s[i] = xv;
-            mx = fmaxf(mx, xv);
+            s[i] = ok ? s[i] : -__builtin_inff();
         }
-        // Online softmax in base 2 with a lazily moved reference max; a block
-        // may hold none of this query's keys (mx = -inf), the reference then
-        // stays put.
-        mx = half_pair_max(mx) * scale_log2;
-        const bool grow = mx > m_run + kRescaleSlack;
-        // Rare after the first blocks; kept a branch (not a select) so that
-        // the accumulators are not rescaled on every band.
-        if (__builtin_expect(__any(grow), 0)) {
-            const float m_new = grow ? mx : m_run;
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-            m_run = m_new;
-            l_part *= alpha;
+        // Online softmax in base 2 with a lazily moved reference max (see the
+        // dense kernel): the reference is set on a query's first block with
+        // keys and moves only when a block's exponentials ran large -- with
+        // every score <= reference + kRescaleSlack a lane's 16 exponentials
+        // sum to at most 16 * 2^kRescaleSlack, so a larger (or non-finite) sum
+        // sends the block through the exact max and its exponentials are
+        // taken again.  A block may hold none of this query's keys.
+        auto rescale = [&]() HET_INLINE {
+            float mx = -__builtin_inff();
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-        }
-        const float neg_m = -((m_run == -__builtin_inff()) ? 0.0f : m_run);
-        bf16x8 pf[2];
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+            mx = half_pair_max(mx) * scale_log2;
+            const bool grow = mx > m_run + kRescaleSlack;
+            if (__builtin_expect(__any(grow), 0)) {
+                const float m_new = grow ? mx : m_run;
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+                m_run = m_new;
+                l_part *= alpha;
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-            u32x4 w;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c2 + 2 * jj], scale_log2, neg_m));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c2 + 2 * jj + 1], scale_log2, neg_m));
-                l_part += p0 + p1;
-                w[jj] = pack_bf16x2(p0, p1);
+                for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
             }
-            pf[c2] = __builtin_bit_cast(bf16x8, w);
+        };
+        bf16x8 pf[2];
+        auto exps = [&]() HET_INLINE -> float {
+            const float neg_m = -((m_run == -__builtin_inff()) ? 0.0f : m_run);
+            float tsum = 0.0f;
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                u32x4 w;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c2 + 2 * jj], scale_log2, neg_m));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c2 + 2 * jj + 1], scale_log2, neg_m));
+                    tsum += p0 + p1;
+                    w[jj] = pack_bf16x2(p0, p1);
+                }
+                pf[c2] = __builtin_bit_cast(bf16x8, w);
+            }
+            return tsum;
+        };
+        constexpr float kBlockSumLimit = 16.0f * (float)(1 << (int)kRescaleSlack);
+        if (__builtin_expect(__any(m_run == -__builtin_inff()), 0)) rescale();
+        float tsum = exps();
+        if (__builtin_expect(__any(!(tsum <= kBlockSumLimit)), 0)) {
+            rescale();
+            tsum = exps();
         }
+        l_part += tsum;
         // O^T += V^T P^T.
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
