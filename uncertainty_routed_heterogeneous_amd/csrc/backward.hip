@@ -21,12 +21,14 @@
 //                        of K and V staged in LDS;
 //   bwd_dq_kernel        the same for a 4x8 tile of local rows of one frame
 //                        over its window box (one wave);
-//   bwd_dkdv_kernel      128 keys (four 4x8 tiles of one frame, a wave each,
-//                        K and V rows in registers): every dense query of the
-//                        sample, then the local queries whose windows may
-//                        hold these keys (per axis an interval of positions);
-//                        the waves share each staged 32-query block;
-//                        dV += P^T dO and dK += dS^T Q.
+//   bwd_dkdv_bf16_kernel 128 consecutive keys, two waves per 32 keys (one
+//                        with K: S, P, dV; one with V: dP, dS, dK): every
+//                        dense query of the sample, then the local queries
+//                        whose windows may hold these keys, in tiles of 64
+//                        gathered into LDS by DMA;
+//   bwd_dkdv_kernel      the fp32 form: 128 keys (four 4x8 tiles of one frame,
+//                        a wave each, K and V rows in registers), the waves
+//                        sharing each staged 32-query block.
 // Products run on the 32x32 MFMA of the element type (bf16 with fp32
 // accumulation: P and dS are rounded to bf16 as operands; fp32: fp32 MFMA).
 // Operands whose rows are read transposed (K for dQ, Q and dO for dK and dV)
@@ -664,6 +666,337 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dkdv_kernel(BwdArgs a, Loc
     }
 }
 
+// dK and dV of 128 consecutive tokens of one (sample, head), bf16.  The
+// block's keys come in four groups of 32, and each group has two waves on
+// one SIMD (waves g and g + 4), so that the exponentials of one overlap the
+// products of the other:
+//   wave g      K rows in registers: S = Q K^T, P = exp2(S - LSE) (window
+//               mask for local queries), dV^T += dO^T P;
+//   wave g + 4  V rows in registers: dP = dO V^T, dS = P (dP - D),
+//               dK^T += Q^T dS, one tile behind, with P taken from LDS.
+// Every product keeps the key in the lane (B operand: a K or V row, or P or
+// dS of the C layout; A operand: 32 query rows read from LDS, row-wise or
+// transposed).  Queries come in tiles of 64 slots: every dense query of the
+// sample, then, for each frame the block touches, the local queries of the
+// box of positions whose windows can reach the block's keys in that frame.
+// A key takes only the pairs of the box of its own frame, so no pair is
+// counted twice.  The Q and dO rows of a tile are gathered global -> LDS by
+// DMA (each lane fetches one 16-byte chunk of a row at its own offset, so a
+// slot's row comes from wherever its token sits), chunk-swizzled as in the
+// forward dense kernel, in three buffers (tile r+1 in flight while tiles r
+// and r-1 are read); a slot without a query reads zeros (its offset is past
+// the buffer's range) and has LSE = +inf, so its P and dS are 0.  Slot tokens
+// run two tiles ahead; one barrier per tile.
+template <int D>
+__global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdArgs a, LocalGeom g, int n_kblocks, int n_units) {
+    constexpr int kTile = 64;                         // query slots per tile
+    constexpr int kCpr = D / 8;                       // 16-byte chunks per row
+    constexpr int kRowsPerLoad = 64 / kCpr;           // rows per wave DMA (1 KB)
+    constexpr int kLoads = kTile / kRowsPerLoad / 8;  // DMAs per wave and tensor
+    constexpr int NC = D / 16, NDB = D / 32;
+    static_assert(kLoads >= 1, "tile shape");
+    // LDS, in bytes: Q tiles [3][kTile][D] and dO tiles likewise (rows
+    // chunk-swizzled), P as B-operand chunks [2 buffers][4 groups][2 halves of
+    // 32 slots][2 chunks of 16 slots][64 lanes] x 16 B, then the per-slot LSE,
+    // D and window records [3][kTile].  Every read below is a per-lane offset
+    // fixed for the tile plus a constant.
+    constexpr uint32_t kTileB = kTile * D * 2, kHalfB = 32 * D * 2, kChunkB = 16 * D * 2;
+    constexpr uint32_t kQ = 0, kG = 3 * kTileB, kP = 6 * kTileB, kPBuf = 4 * 2 * 2 * 64 * 16;
+    constexpr uint32_t kLse = kP + 2 * kPBuf, kDd = kLse + 3 * kTile * 4, kWin = kDd + 3 * kTile * 4;
+    constexpr uint32_t kLdsBytes = kWin + 3 * kTile * 16;
+    static_assert(kG + kTileB <= 65536, "dO reads take the Q offset plus an immediate");
+    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+    HET_LDS char *lds = (HET_LDS char *)smem;
+
+    const int unit = blockIdx.x;
+    if (unit >= n_units) return;
+    const int N = a.n, H = a.heads, HW = g.Hg * g.Wg;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+    const int grp = wave & 3;
+    const bool role_p = wave < 4;  // S, P, dV (else dP, dS, dK)
+    const int kblk = unit % n_kblocks, h = (unit / n_kblocks) % H, b = unit / n_kblocks / H;
+    const int key0 = 128 * kblk, key1 = imin(key0 + 128, N);
+    const int key = key0 + 32 * grp + col;
+    const bool key_ok = key < N;
+    const int kt = key / HW, ky = (key / g.Wg) % g.Hg, kx = key % g.Wg;
+    const int tok_stride = H * D;
+    const size_t sample = (size_t)b * N * tok_stride + (size_t)h * D;
+    const __bf16 *qsrc = (const __bf16 *)a.q + sample, *gsrc = (const __bf16 *)a.dout + sample;
+    // Bytes from the (sample, head) base to the end of the sample's last row;
+    // below 2^32 because every tensor holds fewer than 2^31 elements.
+    const uint32_t range = (uint32_t)N * (uint32_t)tok_stride * 2u;
+    const size_t row_bh = ((size_t)b * H + h) * N;
+    const float sl2 = a.scale * kLog2e;
+
+    // This wave's key operand: K rows (role P) or V rows.
+    bf16x8 kv[NC];
+    {
+        const __bf16 *src = (const __bf16 *)(role_p ? a.k : a.v) + sample + (size_t)(key_ok ? key : 0) * tok_stride +
+                            8 * half;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kv[c] = key_ok ? *(const bf16x8 *)(src + 16 * c) : bf16x8{};
+    }
+    f32x16 acc[NDB];  // dV^T (role P) or dK^T
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+    // DMA j of this wave fills slots from (wave*kLoads + j)*kRowsPerLoad on;
+    // this lane writes slot dma_slot[j] at chunk position lane%kCpr and so
+    // fetches the chunk the swizzle puts there.
+    int dma_slot[kLoads], dma_byte[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int s = (wave * kLoads + j) * kRowsPerLoad + lane / kCpr;
+        dma_slot[j] = s;
+        dma_byte[j] = 16 * ((lane % kCpr) ^ swz<D>(s));
+    }
+    // A operands (byte offsets in a tile): slot rows (S, dP) at chunk 2c + half
+    // of row col, and the transposed reads (dV, dK) with the forward dense
+    // kernel's V offsets; the 32-slot half and the 16-slot chunk only move
+    // whole swizzle periods, so they are constants.
+    const int g16 = lane >> 4, j16 = lane & 15;
+    uint32_t r_off[NC], t_off[NDB][2];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) r_off[c] = 2 * (col * D + 8 * ((2 * c + half) ^ swz<D>(col)));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int lohi = 0; lohi < 2; ++lohi) {
+            const int row = 4 * half + (j16 >> 2) + 8 * lohi;
+            t_off[db][lohi] =
+                2 * (row * D + 8 * ((4 * db + 2 * (g16 & 1) + ((j16 & 3) >> 1)) ^ swz<D>(row)) + 4 * (j16 & 1));
+        }
+    const uint32_t p_lane = kP + grp * 4096 + lane * 16;  // + buffer, half, chunk
+    const uint32_t rec_lane = 16 * half;                  // 4 slots of 4 bytes per half
+
+    auto ld128 = [&](uint32_t off) HET_INLINE -> bf16x8 { return *(const HET_LDS bf16x8 *)(lds + off); };
+    auto ldtr8 = [&](uint32_t lo, uint32_t hi) HET_INLINE -> bf16x8 {
+        return concat8(lds_read_tr16((const HET_LDS void *)(lds + lo)), lds_read_tr16((const HET_LDS void *)(lds + hi)));
+    };
+    constexpr int kA = 4;  // A operands read ahead of their MFMA
+
+    // One wave's products on the tile in buffer cur (both roles): the row
+    // product of both 32-slot halves (independent accumulators, A = Q rows
+    // for S or dO rows for dP), the element-wise step, then the transposed
+    // product of both halves into acc (A = dO^T for dV or Q^T for dK).
+    // `elem` turns the two row products into the four B-operand chunks.
+    auto tile_products = [&](uint32_t row_base, uint32_t tr_base, auto &&elem) HET_INLINE {
+        uint32_t ra[NC], ta[NDB][2];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) ra[c] = row_base + r_off[c];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            ta[db][0] = tr_base + t_off[db][0];
+            ta[db][1] = tr_base + t_off[db][1];
+        }
+        f32x16 rp[2] = {f32x16{}, f32x16{}};
+        bf16x8 ring[kA];
+        constexpr int n1 = 2 * NC;  // step i: half i&1, k-chunk i>>1
+        auto op1 = [&](int i) HET_INLINE -> bf16x8 { return ld128(ra[i >> 1] + (i & 1) * kHalfB); };
+#pragma unroll
+        for (int x = 0; x < kA; ++x) ring[x] = op1(x);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < n1; ++i) {
+            rp[i & 1] = mfma32_bf16(ring[i % kA], kv[i >> 1], rp[i & 1]);
+            if (i + kA < n1) ring[i % kA] = op1(i + kA);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        constexpr int n3 = 4 * NDB;  // step i: dim block i%NDB, chunk (i/NDB)&1, half i/(2 NDB)
+        auto op3 = [&](int i) HET_INLINE -> bf16x8 {
+            const int db = i % NDB, c2 = (i / NDB) & 1, qb2 = i / (2 * NDB);
+            const uint32_t o = c2 * kChunkB + qb2 * kHalfB;
+            return ldtr8(ta[db][0] + o, ta[db][1] + o);
+        };
+#pragma unroll
+        for (int x = 0; x < kA; ++x) ring[x] = op3(x);
+        bf16x8 bf[2][2];
+        elem(rp, bf);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < n3; ++i) {
+            const int db = i % NDB, c2 = (i / NDB) & 1, qb2 = i / (2 * NDB);
+            acc[db] = mfma32_bf16(ring[i % kA], bf[qb2][c2], acc[db]);
+            if (i + kA < n3) ring[i % kA] = op3(i + kA);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // meta(r, s): token of slot s of tile r, or -1 for a slot without a query.
+    auto run = [&](int n_tiles, auto &&meta, auto windowed_tag, bool key_in_part) HET_INLINE {
+        constexpr bool windowed = decltype(windowed_tag)::value;
+        if (n_tiles <= 0) return;
+        int tk_next[kLoads + 1], tk_ahead[kLoads + 1];  // DMA slots, then record slot tid
+        auto fetch_meta = [&](int r, int(&dst)[kLoads + 1]) HET_INLINE {
+#pragma unroll
+            for (int j = 0; j < kLoads; ++j) dst[j] = meta(r, dma_slot[j]);
+            dst[kLoads] = tid < kTile ? meta(r, tid) : -1;
+        };
+        auto issue_dma = [&](int buf, const int(&tk)[kLoads + 1]) HET_INLINE {
+#pragma unroll
+            for (int j = 0; j < kLoads; ++j) {
+                // unsigned: a row offset can pass 2^31 bytes (it stays below range)
+                const uint32_t voff =
+                    tk[j] >= 0 ? (uint32_t)tk[j] * (uint32_t)tok_stride * 2u + (uint32_t)dma_byte[j] : range;
+                const uint32_t dst = buf * kTileB + (wave * kLoads + j) * kRowsPerLoad * D * 2;
+                buffer_load_lds16(qsrc, range, (HET_LDS void *)(lds + kQ + dst), (int)voff);
+                buffer_load_lds16(gsrc, range, (HET_LDS void *)(lds + kG + dst), (int)voff);
+            }
+        };
+        float r_lse = 0.0f, r_d = 0.0f;
+        i32x4 r_win = {0, 0, 0, 0};
+        auto load_rec = [&](const int(&tk)[kLoads + 1]) HET_INLINE {
+            if (tid < kTile) {
+                const int t = tk[kLoads];
+                r_lse = t >= 0 ? a.lse[row_bh + t] : __builtin_inff();
+                r_d = t >= 0 ? a.dsum[row_bh + t] : 0.0f;
+                if (windowed && t >= 0) {
+                    const int qt = t / HW, qy = (t / g.Wg) % g.Hg, qx = t % g.Wg;
+                    r_win[0] = win_lo(qt, g.wt, g.lt, g.T, g.cut) | (win_hi(qt, g.wt, g.lt, g.T, g.cut) << 16);
+                    r_win[1] = win_lo(qy, g.wh, g.lh, g.Hg, g.cut) | (win_hi(qy, g.wh, g.lh, g.Hg, g.cut) << 16);
+                    r_win[2] = win_lo(qx, g.ww, g.lw, g.Wg, g.cut) | (win_hi(qx, g.ww, g.lw, g.Wg, g.cut) << 16);
+                }
+            }
+        };
+        auto store_rec = [&](int buf) HET_INLINE {
+            if (tid < kTile) {
+                *(HET_LDS float *)(lds + kLse + buf * kTile * 4 + tid * 4) = r_lse;
+                *(HET_LDS float *)(lds + kDd + buf * kTile * 4 + tid * 4) = r_d;
+                if (windowed) *(HET_LDS i32x4 *)(lds + kWin + buf * kTile * 16 + tid * 16) = r_win;
+            }
+        };
+        // Role P: P = exp2(S - LSE) (0 outside the window), published for
+        // the partner wave, and dV^T += dO^T P.
+        auto compute_p = [&](int cur, int pb) HET_INLINE {
+            tile_products(kQ + cur * kTileB, kG + cur * kTileB, [&](const f32x16(&sc)[2], bf16x8(&pf)[2][2]) HET_INLINE {
+#pragma unroll
+                for (int qb2 = 0; qb2 < 2; ++qb2)
+#pragma unroll
+                    for (int c2 = 0; c2 < 2; ++c2) {
+                        u32x4 wp;
+#pragma unroll
+                        for (int g2 = 0; g2 < 2; ++g2) {
+                            // register 4*g4 + e: slot 32*qb2 + 8*g4 + 4*half + e
+                            const int g4 = 2 * c2 + g2;
+                            const f32x4 l4 =
+                                *(const HET_LDS f32x4 *)(lds + kLse + cur * kTile * 4 + rec_lane + 4 * (32 * qb2 + 8 * g4));
+                            float p[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb2][4 * g4 + e], sl2, -l4[e]));
+                                if constexpr (windowed) {
+                                    const i32x4 w = *(const HET_LDS i32x4 *)(lds + kWin + cur * kTile * 16 +
+                                                                            16 * (32 * qb2 + 8 * g4 + 4 * half + e));
+                                    auto inside = [](int cc, int ww) HET_INLINE {
+                                        return cc >= (ww & 0xffff) && cc < (ww >> 16);
+                                    };
+                                    const bool in =
+                                        key_in_part && inside(kt, w[0]) && inside(ky, w[1]) && inside(kx, w[2]);
+                                    p[e] = in ? p[e] : 0.0f;
+                                }
+                            }
+                            wp[2 * g2] = pack_bf16x2(p[0], p[1]);
+                            wp[2 * g2 + 1] = pack_bf16x2(p[2], p[3]);
+                        }
+                        pf[qb2][c2] = __builtin_bit_cast(bf16x8, wp);
+                        *(HET_LDS bf16x8 *)(lds + p_lane + pb * kPBuf + qb2 * 2048 + c2 * 1024) = pf[qb2][c2];
+                    }
+            });
+        };
+        // Role dS: dS = P (dP - D) with the partner's P, and dK^T += Q^T dS.
+        auto compute_ds = [&](int cur, int pb) HET_INLINE {
+            tile_products(kG + cur * kTileB, kQ + cur * kTileB, [&](const f32x16(&dp)[2], bf16x8(&sf)[2][2]) HET_INLINE {
+#pragma unroll
+                for (int qb2 = 0; qb2 < 2; ++qb2)
+#pragma unroll
+                    for (int c2 = 0; c2 < 2; ++c2) {
+                        const bf16x8 pf = ld128(p_lane + pb * kPBuf + qb2 * 2048 + c2 * 1024);
+                        u32x4 ws;
+#pragma unroll
+                        for (int g2 = 0; g2 < 2; ++g2) {
+                            const int g4 = 2 * c2 + g2;
+                            const f32x4 d4 =
+                                *(const HET_LDS f32x4 *)(lds + kDd + cur * kTile * 4 + rec_lane + 4 * (32 * qb2 + 8 * g4));
+                            float s[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) s[e] = (float)pf[4 * g2 + e] * (dp[qb2][4 * g4 + e] - d4[e]);
+                            ws[2 * g2] = pack_bf16x2(s[0], s[1]);
+                            ws[2 * g2 + 1] = pack_bf16x2(s[2], s[3]);
+                        }
+                        sf[qb2][c2] = __builtin_bit_cast(bf16x8, ws);
+                    }
+            });
+        };
+
+        fetch_meta(0, tk_next);
+        if (n_tiles > 1) fetch_meta(1, tk_ahead);
+        __syncthreads();  // the previous run is done with the buffers
+        issue_dma(0, tk_next);
+        load_rec(tk_next);
+        store_rec(0);
+        // Iteration r: role P on tile r (buffer r % 3, P buffer r % 2), role
+        // dS on tile r - 1.
+        int cur = 0;
+        for (int r = 0; r <= n_tiles; ++r) {
+            const int nxt = cur == 2 ? 0 : cur + 1, prv = cur == 0 ? 2 : cur - 1;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();  // tile r, its records and P of tile r-1 in LDS; tile r-2 done
+            if (r + 1 < n_tiles) {
+#pragma unroll
+                for (int j = 0; j <= kLoads; ++j) tk_next[j] = tk_ahead[j];
+                issue_dma(nxt, tk_next);
+                load_rec(tk_next);
+                if (r + 2 < n_tiles) fetch_meta(r + 2, tk_ahead);
+            }
+            if (role_p) {
+                if (r < n_tiles) compute_p(cur, r & 1);
+            } else if (r > 0) {
+                compute_ds(prv, (r - 1) & 1);
+            }
+            if (r + 1 < n_tiles) store_rec(nxt);
+            cur = nxt;
+        }
+    };
+
+    // Every dense query of the sample sees every key.
+    const int cnt = a.counts[2 * b];
+    const int32_t *didx = a.dense_idx + (size_t)b * N;
+    run((cnt + kTile - 1) / kTile,
+        [&](int r, int s) HET_INLINE -> int {
+            const int i = kTile * r + s;
+            return i < cnt ? didx[i] : -1;
+        },
+        std::false_type{}, true);
+    // Local queries, per frame the block touches: the box of positions whose
+    // windows can hold a key of the block in that frame (rows y0..y1 of the
+    // frame; columns x0..x1 when the block stays in one row, else all).
+    const uint8_t *mb = a.mask + (size_t)b * N;
+    for (int f = key0 / HW; f <= (key1 - 1) / HW; ++f) {
+        const int lo = imax(key0, f * HW) - f * HW, hi = imin(key1, (f + 1) * HW) - 1 - f * HW;
+        const int y0 = lo / g.Wg, y1 = hi / g.Wg;
+        const int x0 = y0 == y1 ? lo % g.Wg : 0, x1 = y0 == y1 ? hi % g.Wg : g.Wg - 1;
+        int pt0, pt1, py0, py1, px0, px1;
+        inverse_window(f, f, g.wt, g.lt, g.T, g.cut, pt0, pt1);
+        inverse_window(y0, y1, g.wh, g.lh, g.Hg, g.cut, py0, py1);
+        inverse_window(x0, x1, g.ww, g.lw, g.Wg, g.cut, px0, px1);
+        const int nby = py1 - py0 + 1, nbx = px1 - px0 + 1;
+        const int total = (pt1 - pt0 + 1) * nby * nbx;
+        run((total + kTile - 1) / kTile,
+            [&](int r, int s) HET_INLINE -> int {
+                const int e = kTile * r + s;
+                if (e >= total) return -1;
+                const int tk = ((pt0 + e / (nby * nbx)) * g.Hg + py0 + (e / nbx) % nby) * g.Wg + px0 + e % nbx;
+                return mb[tk] != 0 ? tk : -1;
+            },
+            std::true_type{}, kt == f);
+    }
+
+    if (key_ok) {
+        __bf16 *dst = (__bf16 *)(role_p ? a.dv : a.dk) + sample + (size_t)key * tok_stride;
+        store_row_t<__bf16, D>(dst, acc, role_p ? 1.0f : a.scale);
+    }
+}
+
 size_t backward_workspace_bytes(int batch, int heads, int n) {
     return 2 * (size_t)batch * heads * n * sizeof(float);
 }
@@ -687,6 +1020,8 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
     const int x_groups = (g.tiles_x + kBwdWaves - 1) / kBwdWaves;
     const int key_units = a.batch * a.heads * g.T * g.tiles_y * x_groups;
     const bool sr16 = g.slot_row == 16;
+    const int n_kblocks = (a.n + 127) / 128;
+    const int kblock_units = a.batch * a.heads * n_kblocks;
 #define HET_BWD(T_, D_)                                                                                        \
     do {                                                                                                       \
         constexpr int kRowsPerBlock = 4 * (64 / ((D_) * (int)sizeof(T_) / 16));                               \
@@ -701,8 +1036,12 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
         else                                                                                                   \
             hipLaunchKernelGGL((bwd_dq_kernel<T_, D_, false, 32>), dim3(tile_units), dim3(64), 0, stream, a, g,  \
                                tile_units);                                                                    \
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T_, D_>), dim3(key_units), dim3(64 * kBwdWaves), 0, stream, a, g,   \
-                           x_groups, key_units);                                                               \
+        if constexpr (std::is_same<T_, __bf16>::value)                                                        \
+            hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D_>), dim3(kblock_units), dim3(512), 0, stream, a, g,     \
+                               n_kblocks, kblock_units);                                                       \
+        else                                                                                                   \
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T_, D_>), dim3(key_units), dim3(64 * kBwdWaves), 0, stream, a, \
+                               g, x_groups, key_units);                                                        \
     } while (0)
     if (a.bf16) {
         if (a.head_dim == 128) HET_BWD(__bf16, 128);
