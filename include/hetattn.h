@@ -200,8 +200,9 @@ int het_attn_local(const het_attn_shape *shape, const void *q, const void *k, co
                    const het_route *route, void *o, void *workspace, size_t workspace_bytes,
                    void *stream);
 
-/* Device workspace het_attn_backward needs for this shape, in bytes
- * (2 * B * heads * N fp32 values); 0 for an invalid shape. */
+/* Device workspace het_attn_backward needs for this shape, in bytes:
+ * 2 * B * heads * N fp32 values (row statistics) plus 4 * 1024 * 256 fp32
+ * values (partial statistics of the dense rows); 0 for an invalid shape. */
 size_t het_attn_backward_workspace_bytes(const het_attn_shape *shape);
 
 /* Backward pass of het_attn_forward with the route held fixed: the layer is

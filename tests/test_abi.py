@@ -229,7 +229,7 @@ def test_route_random_argument_errors(lib):
 def test_backward_argument_errors(lib):
     s = good_shape()  # B=1, N=256, heads=2, D=64, f32: 128 KiB per tensor
     ws_n = lib.het_attn_backward_workspace_bytes(ctypes.byref(s))
-    assert ws_n == 2 * 1 * 2 * 256 * 4
+    assert ws_n == 2 * 1 * 2 * 256 * 4 + 4 * 1024 * 256 * 4
     assert lib.het_attn_backward_workspace_bytes(ctypes.byref(good_shape(head_dim=96))) == 0
     span = 1 << 20
     base = {n: (i + 1) * span for i, n in enumerate(("q", "k", "v", "o", "dout", "dq", "dk", "dv", "ws"))}

@@ -327,6 +327,8 @@ int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k,
     }
     const size_t need = hetattn::backward_workspace_bytes((int)d.B, (int)d.H, (int)d.N);
     if (!workspace || workspace_bytes < need) return HET_ERR_WORKSPACE;
+    const int cus = current_cu_count();
+    if (cus <= 0) return HET_ERR_HIP;
     hetattn::BwdArgs a;
     a.q = q;
     a.k = k;
@@ -355,6 +357,9 @@ int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k,
     a.bf16 = shape->dtype == HET_BF16;
     a.scale = scale;
     a.max_dense = route->dense_count_host >= 0 ? route->dense_count_host : (int)d.N;
+    a.dense_exact = route->dense_count_host >= 0;
+    a.lse_part = (float *)workspace + 2 * (size_t)(d.B * d.H * d.N);
+    a.cu_count = cus < hetattn::kBwdMaxLseGroups ? cus : hetattn::kBwdMaxLseGroups;
     if (hetattn::launch_backward(a, (hipStream_t)stream) != hipSuccess) return HET_ERR_HIP;
     return HET_OK;
 }

@@ -330,6 +330,236 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dq_dense_kernel(BwdArgs a,
     if (valid) store_row_t<T, D>((T *)a.dq + sample + (size_t)tok * tok_stride, acc, a.scale);
 }
 
+// dQ of 128 dense rows (consecutive entries of the dense index list), bf16,
+// given their LSE (the dense forward kernel's statistics, launched in its
+// LSE form before this kernel).  Query group g (32 rows; this lane's row is
+// its column in every product) has two waves on one SIMD, g and g + 4,
+// which take the first and the second 32 keys of every 64-key tile, so that
+// the exponentials of one overlap the products of the other:
+//   S^T = K Q^T, dP^T = V dO^T, dS = P (dP - D), dQ^T += K^T dS^T (K read
+//   transposed); the two halves' partial dQ are added through LDS.
+// K and V tiles move global -> LDS by DMA (contiguous key rows, the
+// descriptor's range ending at key N so that the ragged last tile reads
+// zeros), chunk-swizzled as in the forward dense kernel, through rings of
+// three buffers (two tiles in flight), with one barrier per tile.
+template <int D>
+__global__ __launch_bounds__(512) void bwd_dq_dense_bf16_kernel(BwdArgs a, int n_units) {
+    constexpr int kBN = 64;                          // keys per tile
+    constexpr int kBM = 128;                         // dense rows per workgroup
+    constexpr int kCpr = D / 8;                      // 16-byte chunks per row
+    constexpr int kRowsPerLoad = 64 / kCpr;          // rows per wave DMA (1 KB)
+    constexpr int kLoads = kBN / kRowsPerLoad / 8;   // DMAs per wave and tensor
+    constexpr int NC = D / 16, NDB = D / 32;
+    static_assert(kLoads >= 1, "tile shape");
+    // LDS, in bytes: K and V through rings of three tile buffers of kBN key
+    // rows each; after the key loop the same bytes carry the second half's
+    // partial dQ.
+    constexpr uint32_t kTileB = kBN * D * 2;
+    constexpr uint32_t kK = 0, kV = 3 * kTileB;
+    constexpr uint32_t kLdsBytes = 6 * kTileB;
+    static_assert(4 * 64 * (D / 2) * 4 <= kLdsBytes, "dQ exchange fits the tile buffers");
+    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+    HET_LDS char *lds = (HET_LDS char *)smem;
+
+    const int unit = blockIdx.x;
+    if (unit >= n_units) return;
+    const int N = a.n, H = a.heads;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+    const int grp = wave & 3, kh = wave >> 2;  // query group, key half
+    const int groups = (a.max_dense + kBM - 1) / kBM;
+    const int qt = unit % groups, h = (unit / groups) % H, b = unit / groups / H;
+    const int cnt = a.counts[2 * b];
+    if (kBM * qt >= cnt) return;  // the whole workgroup
+    const int slot = kBM * qt + 32 * grp + col;
+    const bool valid = slot < cnt;
+    const int tok = valid ? a.dense_idx[(size_t)b * N + slot] : 0;
+    const int tok_stride = H * D;
+    const size_t sample = (size_t)b * N * tok_stride + (size_t)h * D;
+    const __bf16 *ksrc = (const __bf16 *)a.k + sample, *vsrc = (const __bf16 *)a.v + sample;
+    const size_t row_bh = ((size_t)b * H + h) * N;
+    const float sl2 = a.scale * kLog2e;
+    const int n_kt = (N + kBN - 1) / kBN;
+
+    bf16x8 qf[NC], df[NC];
+    {
+        const size_t off = sample + (size_t)tok * tok_stride + 8 * half;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            qf[c] = valid ? *(const bf16x8 *)((const __bf16 *)a.q + off + 16 * c) : bf16x8{};
+            df[c] = valid ? *(const bf16x8 *)((const __bf16 *)a.dout + off + 16 * c) : bf16x8{};
+        }
+    }
+    const float d_i = valid ? a.dsum[row_bh + tok] : 0.0f;
+
+    // DMA: load j of this wave fills key rows from (wave*kLoads + j)*kRowsPerLoad
+    // on; the descriptor base is the tile's first key row, so the offsets
+    // inside a tile are fixed.
+    int dma_voff[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int r = (wave * kLoads + j) * kRowsPerLoad + lane / kCpr;
+        dma_voff[j] = 2 * (r * tok_stride + 8 * ((lane % kCpr) ^ swz<D>(r)));
+    }
+    auto dma = [&](const __bf16 *src, uint32_t dst_base, int kt) HET_INLINE {
+        const int key0 = kt * kBN;
+        const uint32_t bytes = (uint32_t)(N - key0) * (uint32_t)tok_stride * 2u;
+        const __bf16 *base = src + (size_t)key0 * tok_stride;
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+            const uint32_t dst = dst_base + (wave * kLoads + j) * kRowsPerLoad * D * 2;
+            buffer_load_lds16(base, bytes, (HET_LDS void *)(lds + dst), dma_voff[j]);
+        }
+    };
+    // A operands (byte offsets in a tile): key rows 32*kh + col at chunk
+    // 2c + half, and the transposed K reads with the forward dense kernel's V
+    // offsets, from key row 32*kh on.
+    const int g16 = lane >> 4, j16 = lane & 15;
+    uint32_t r_off[NC], t_off[NDB][2];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) r_off[c] = 2 * ((32 * kh + col) * D + 8 * ((2 * c + half) ^ swz<D>(col)));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int lohi = 0; lohi < 2; ++lohi) {
+            const int row = 4 * half + (j16 >> 2) + 8 * lohi;
+            t_off[db][lohi] = 2 * ((32 * kh + row) * D +
+                                   8 * ((4 * db + 2 * (g16 & 1) + ((j16 & 3) >> 1)) ^ swz<D>(row)) + 4 * (j16 & 1));
+        }
+    auto ld128 = [&](uint32_t off) HET_INLINE -> bf16x8 { return *(const HET_LDS bf16x8 *)(lds + off); };
+    constexpr int kA = 4;  // A operands read ahead of their MFMA
+    // S^T (this wave's 32 keys x 32 rows) of the K tile at kbase, and, when
+    // vbase is given, dP^T of the V tile, as independent chains.
+    auto row_products = [&](uint32_t kbase, uint32_t vbase, bool with_dp, f32x16 &sc, f32x16 &dp) HET_INLINE {
+        sc = f32x16{};
+        dp = f32x16{};
+        uint32_t ka[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) ka[c] = kbase + r_off[c];
+        const uint32_t vdelta = vbase - kbase;
+        bf16x8 ring[kA];
+        if (with_dp) {
+            constexpr int n = 2 * NC;  // step i: K (even) or V (odd), k-chunk i>>1
+            auto op = [&](int i) HET_INLINE -> bf16x8 { return ld128(ka[i >> 1] + ((i & 1) ? vdelta : 0u)); };
+#pragma unroll
+            for (int x = 0; x < kA; ++x) ring[x] = op(x);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < n; ++i) {
+                if (i & 1) dp = mfma32_bf16(ring[i % kA], df[i >> 1], dp);
+                else sc = mfma32_bf16(ring[i % kA], qf[i >> 1], sc);
+                if (i + kA < n) ring[i % kA] = op(i + kA);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int x = 0; x < kA; ++x) ring[x] = ld128(ka[x]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                sc = mfma32_bf16(ring[i % kA], qf[i], sc);
+                if (i + kA < NC) ring[i % kA] = ld128(ka[i + kA]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    // Whether register i of a C-layout block of tile kt is a key below N.
+    auto key_in = [&](int kt, int i) HET_INLINE {
+        return kt * kBN + 32 * kh + 8 * (i / 4) + 4 * half + (i % 4) < N;
+    };
+
+    // s_waitcnt immediate: at most n vector-memory operations of this wave
+    // outstanding (no wait on the other counters).
+    auto vm_wait = [](int n) constexpr { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); };
+    const float lse2 = valid ? a.lse[row_bh + tok] : 0.0f;
+
+    // ---- dQ^T += K^T dS^T over this wave's key half
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+        if (x < n_kt) {
+            dma(ksrc, kK + x * kTileB, x);
+            dma(vsrc, kV + x * kTileB, x);
+        }
+    int cur = 0;  // kt % 3
+    for (int kt = 0; kt < n_kt; ++kt) {
+        if (kt + 1 < n_kt) __builtin_amdgcn_s_waitcnt(vm_wait(2 * kLoads));
+        else __builtin_amdgcn_s_waitcnt(vm_wait(0));
+        __syncthreads();  // tiles kt in LDS; tiles kt-1 done
+        const int nx2 = cur == 0 ? 2 : cur - 1;  // (kt + 2) % 3
+        if (kt + 2 < n_kt) {
+            dma(ksrc, kK + nx2 * kTileB, kt + 2);
+            dma(vsrc, kV + nx2 * kTileB, kt + 2);
+        }
+        f32x16 sc, dp;
+        row_products(kK + cur * kTileB, kV + cur * kTileB, true, sc, dp);
+        const uint32_t kb = kK + cur * kTileB;
+        auto op3 = [&](int i) HET_INLINE -> bf16x8 {
+            const int db = i % NDB, c2 = i / NDB;
+            const uint32_t o = kb + c2 * 16 * D * 2;
+            return concat8(lds_read_tr16((const HET_LDS void *)(lds + t_off[db][0] + o)),
+                           lds_read_tr16((const HET_LDS void *)(lds + t_off[db][1] + o)));
+        };
+        bf16x8 ring[kA];
+#pragma unroll
+        for (int x = 0; x < kA; ++x) ring[x] = op3(x);
+        // chunk c2 of the block = registers 8*c2 .. 8*c2+7
+        const bool ragged = kt * kBN + kBN > N;
+        bf16x8 sf[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            u32x4 ws;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                float s2[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int i = 8 * c2 + 2 * jj + e;
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], sl2, -lse2));
+                    if (ragged && !key_in(kt, i)) p = 0.0f;
+                    s2[e] = p * (dp[i] - d_i);
+                }
+                ws[jj] = pack_bf16x2(s2[0], s2[1]);
+            }
+            sf[c2] = __builtin_bit_cast(bf16x8, ws);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int n3 = 2 * NDB;
+#pragma unroll
+        for (int i = 0; i < n3; ++i) {
+            acc[i % NDB] = mfma32_bf16(ring[i % kA], sf[i / NDB], acc[i % NDB]);
+            if (i + kA < n3) ring[i % kA] = op3(i + kA);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        cur = cur == 2 ? 0 : cur + 1;
+    }
+
+    // the second key half's partial dQ through LDS, in [group][4 registers]
+    // [lane] f32x4 order (consecutive lanes, consecutive 16 bytes)
+    __syncthreads();  // every wave is done with the tile buffers
+    if (kh == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                *(HET_LDS f32x4 *)(lds + 16 * ((grp * (NDB * 4) + db * 4 + i4) * 64 + lane)) =
+                    f32x4{acc[db][4 * i4], acc[db][4 * i4 + 1], acc[db][4 * i4 + 2], acc[db][4 * i4 + 3]};
+    }
+    __syncthreads();
+    if (kh == 0 && valid) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x4 o = *(const HET_LDS f32x4 *)(lds + 16 * ((grp * (NDB * 4) + db * 4 + i4) * 64 + lane));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[db][4 * i4 + e] += o[e];
+            }
+        store_row_t<__bf16, D>((__bf16 *)a.dq + sample + (size_t)tok * tok_stride, acc, a.scale);
+    }
+}
+
 // dQ of 32 query rows (kDense: 32 consecutive entries of the dense index
 // list -- the one-wave form; the dense rows use bwd_dq_dense_kernel -- else
 // a 4x8 tile of local rows of one frame), and LSE of those rows.
@@ -998,7 +1228,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdArgs a, LocalGeom
 }
 
 size_t backward_workspace_bytes(int batch, int heads, int n) {
-    return 2 * (size_t)batch * heads * n * sizeof(float);
+    return 2 * (size_t)batch * heads * n * sizeof(float) + dense_lse_workspace_bytes(kBwdMaxLseGroups);
 }
 
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
@@ -1014,6 +1244,23 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
     g.cut = a.cut;
     if (kBwdQX + g.lw - 1 > 32) return hipErrorInvalidValue;  // rejected earlier by the ABI layer
 
+    // The dense rows' LSE (bf16) comes from the dense forward kernel in its
+    // statistics-only form.
+    AttnArgs fa{};
+    fa.q = a.q;
+    fa.k = a.k;
+    fa.dense_idx = a.dense_idx;
+    fa.counts = a.counts;
+    fa.batch = a.batch;
+    fa.n = a.n;
+    fa.heads = a.heads;
+    fa.head_dim = a.head_dim;
+    fa.bf16 = a.bf16;
+    fa.scale = a.scale;
+    fa.max_dense = a.max_dense;
+    fa.dense_exact = a.dense_exact;
+    fa.workspace = a.lse_part;
+    fa.cu_count = a.cu_count;
     const long rows = (long)a.batch * a.n * a.heads;
     const int dense_units = a.batch * a.heads * ((a.max_dense + 32 * kBwdWaves - 1) / (32 * kBwdWaves));
     const int tile_units = a.batch * a.heads * g.T * g.tiles_y * g.tiles_x;
@@ -1027,7 +1274,13 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
         constexpr int kRowsPerBlock = 4 * (64 / ((D_) * (int)sizeof(T_) / 16));                               \
         hipLaunchKernelGGL((bwd_prep_kernel<T_, D_>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), \
                            dim3(256), 0, stream, (const T_ *)a.o, (const T_ *)a.dout, a.dsum, rows, a.n, a.heads); \
-        if (dense_units > 0)                                                                                   \
+        if (dense_units > 0 && std::is_same<T_, __bf16>::value) {                                             \
+            const hipError_t e = launch_dense_lse(fa, a.lse, stream);                                          \
+            if (e != hipSuccess) return e;                                                                     \
+            hipLaunchKernelGGL((bwd_dq_dense_bf16_kernel<D_>), dim3(dense_units), dim3(512), 0, stream, a,      \
+                               dense_units);                                                                   \
+        }                                                                                                      \
+        else if (dense_units > 0)                                                                              \
             hipLaunchKernelGGL((bwd_dq_dense_kernel<T_, D_>), dim3(dense_units), dim3(64 * kBwdWaves), 0, stream, \
                                a, dense_units);                                                                \
         if (sr16)                                                                                              \

@@ -79,12 +79,15 @@ __device__ __forceinline__ int work_owner(int64_t W, int G, int64_t x) {
     return w;
 }
 
-template <int D>
+// kLse: only the row statistics -- no P*V, no V tiles -- and the output is
+// LSE_i = m_i + log2(l_i) (log2 units of scale * q.k) in lse[(b*H + h)*N + i]
+// for the gradient of the layer; the stream-K pieces then publish (m, l) only.
+template <int D, bool kLse>
 __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const int32_t *__restrict__ dense_idx,
     const int32_t *__restrict__ counts, int B, int N, int H, float scale_log2, int G,
-    float *__restrict__ ws_part) {
+    float *__restrict__ ws_part, float *__restrict__ lse) {
     using Gm = DenseBf16Geom<D>;
     constexpr int BN = Gm::BN;
     constexpr int BM = kDenseBM16;
@@ -337,9 +340,9 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
                             const float p0 = __builtin_amdgcn_exp2f(sc[kbk][8 * c2 + 2 * j]);
                             const float p1 = __builtin_amdgcn_exp2f(sc[kbk][8 * c2 + 2 * j + 1]);
                             tsum += p0 + p1;
-                            wv[j] = pack_bf16x2(p0, p1);
+                            if constexpr (!kLse) wv[j] = pack_bf16x2(p0, p1);
                         }
-                        pf[kbk][c2] = __builtin_bit_cast(bf16x8, wv);
+                        if constexpr (!kLse) pf[kbk][c2] = __builtin_bit_cast(bf16x8, wv);
                     }
                 return tsum;
             };
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         __builtin_amdgcn_s_barrier();
         // first round r = kt0
         if (kt0 + 1 < kt1) dma(kb, K1, kt0 + 1);
-        dma(vb, V0, kt0);
+        if constexpr (!kLse) dma(vb, V0, kt0);
         if (grp == 0) burst_ct(F_{}, T_{}, V1, K0);
         __builtin_amdgcn_s_barrier();
         if (grp == 0) softmax(kt0);
@@ -378,13 +381,15 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
         // rounds kt0+1 .. kt1-1: full bursts
+        // (kLse: S-only bursts, and no V tiles.)
+        using PV_ = std::integral_constant<bool, !kLse>;
         auto round = [&](int r, const __bf16 *Kc, __bf16 *Kn, const __bf16 *Vp, __bf16 *Vc) HET_INLINE {
             if (r + 1 < kt1) dma(kb, Kn, r + 1);
-            dma(vb, Vc, r);
-            if (grp == 0) burst_ct(T_{}, T_{}, Vp, Kc);
+            if constexpr (!kLse) dma(vb, Vc, r);
+            if (grp == 0) burst_ct(PV_{}, T_{}, Vp, Kc);
             else softmax(r - 1);
             if (grp == 0) softmax(r);
-            else burst_ct(T_{}, T_{}, Vp, Kc);
+            else burst_ct(PV_{}, T_{}, Vp, Kc);
             __builtin_amdgcn_s_waitcnt(0);
             __builtin_amdgcn_s_barrier();
         };
@@ -396,13 +401,19 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         // the buffer can be picked at run time.
         {
             const __bf16 *Vp = ((kt1 - 1 - kt0) & 1) ? V1 : V0;
-            if (grp == 0) burst_ct(T_{}, F_{}, Vp, K0);
+            if (grp == 0) burst_ct(PV_{}, F_{}, Vp, K0);
             else softmax(kt1 - 1);
             __builtin_amdgcn_s_barrier();
-            if (grp == 1) burst_ct(T_{}, F_{}, Vp, K0);
+            if (grp == 1) burst_ct(PV_{}, F_{}, Vp, K0);
         }
 
         const float l_tot = half_pair_sum(l_part);
+        if constexpr (kLse) {
+            if (kt0 == 0 && kt1 == n_kt) {
+                if (q_valid && half == 0) lse[((size_t)b * H + h) * N + tok] = m_ref + __builtin_log2f(l_tot);
+                continue;
+            }
+        }
         __bf16 *op = o + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
         auto store_out = [&](float inv_l) HET_INLINE {
             if (!q_valid) return;
@@ -417,25 +428,30 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
                     *(u32x2 *)(op + d) = wv;
                 }
         };
-        if (kt0 == 0 && kt1 == n_kt) {
-            store_out(1.0f / l_tot);
-            continue;
+        if constexpr (!kLse) {
+            if (kt0 == 0 && kt1 == n_kt) {
+                store_out(1.0f / l_tot);
+                continue;
+            }
         }
 
         // ---- a piece of a split unit: publish the partial state.  Each lane
         // stores its D/2 accumulators contiguously in register order (the
         // lane that merges reads them back in the same order).
-        const size_t slot_elems = (size_t)D * BM;
+        const size_t slot_elems = kLse ? 0 : (size_t)D * BM;  // kLse: no O partials
         const int my_slot = 2 * w + (unit == first_unit ? 0 : 1);
         const int qi = wave * 32 + col;  // query within the unit
         {
-            f32x4 *dst = (f32x4 *)(ws_part + (size_t)my_slot * slot_elems + (size_t)qi * D + (size_t)half * (D / 2));
+            if constexpr (!kLse) {
+                f32x4 *dst =
+                    (f32x4 *)(ws_part + (size_t)my_slot * slot_elems + (size_t)qi * D + (size_t)half * (D / 2));
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+                for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4)
-                    dst[db * 4 + i4] = f32x4{oacc[db][4 * i4], oacc[db][4 * i4 + 1], oacc[db][4 * i4 + 2],
-                                             oacc[db][4 * i4 + 3]};
+                    for (int i4 = 0; i4 < 4; ++i4)
+                        dst[db * 4 + i4] = f32x4{oacc[db][4 * i4], oacc[db][4 * i4 + 1], oacc[db][4 * i4 + 2],
+                                                 oacc[db][4 * i4 + 3]};
+            }
             float *part_ml = ws_part + (size_t)2 * G * slot_elems + (size_t)my_slot * 2 * BM;
             if (half == 0) {
                 part_ml[qi] = m_ref;
@@ -458,10 +474,11 @@ __device__ __forceinline__ int piece_slot(int64_t W, int G, int n_kt, int units_
 // 32*db + 8*i4 + 4*half + e (the accumulator order of the MFMA C layout).
 // The piece list of the unit (64-bit schedule arithmetic) is worked out by a
 // few threads per batch and shared through LDS.
-template <int D>
+// kLse: the pieces hold (m, l) only and the result is the LSE of each row.
+template <int D, bool kLse>
 __global__ __launch_bounds__(256) void dense_merge_kernel(
     __bf16 *__restrict__ o, const int32_t *__restrict__ dense_idx, const int32_t *__restrict__ counts,
-    int B, int N, int H, int G, const float *__restrict__ ws_part) {
+    int B, int N, int H, int G, const float *__restrict__ ws_part, float *__restrict__ lse) {
     constexpr int BM = kDenseBM16;
     constexpr int kSlices = D / 16;
     constexpr int kMergeQ = 256 / kSlices;
@@ -499,7 +516,7 @@ __global__ __launch_bounds__(256) void dense_merge_kernel(
     __syncthreads();
     const int w_first = s_range[0], w_last = s_range[1];
     if (w_first == w_last) return;  // one workgroup ran the whole unit and stored it
-    const size_t slot_elems = (size_t)D * BM;
+    const size_t slot_elems = kLse ? 0 : (size_t)D * BM;
     const float *ml = ws_part + (size_t)2 * G * slot_elems;
     // Pieces come from the non-empty workgroups owning the unit's items,
     // taken kMergeBatch at a time with all their loads in flight (the running
@@ -524,7 +541,7 @@ __global__ __launch_bounds__(256) void dense_merge_kernel(
             mp[j] = ok ? ml[(size_t)ps * 2 * BM + qi] : -__builtin_inff();
             lp[j] = ok ? ml[(size_t)ps * 2 * BM + BM + qi] : 0.0f;
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) pv[j][i4] = ok ? po[i4] : f32x4{};
+            for (int i4 = 0; i4 < 4; ++i4) pv[j][i4] = (ok && !kLse) ? po[i4] : f32x4{};
         }
         __syncthreads();  // s_slot is rewritten by the next batch
         float m_new = m_all;
@@ -546,9 +563,13 @@ __global__ __launch_bounds__(256) void dense_merge_kernel(
         }
     }
     if (!q_valid) return;
+    const int tok = dense_idx[(size_t)b * N + qrow];
+    if constexpr (kLse) {
+        if (slice == 0) lse[((size_t)b * H + h) * N + tok] = m_all + __builtin_log2f(l_all);
+        return;
+    }
     const float inv_l = 1.0f / l_all;
     const int half = slice / NDB, db = slice % NDB;
-    const int tok = dense_idx[(size_t)b * N + qrow];
     __bf16 *op = o + ((size_t)b * N + tok) * ((size_t)H * D) + (size_t)h * D;
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
@@ -704,6 +725,39 @@ __global__ __launch_bounds__(kDenseThreads) void dense_f32_kernel(
 
 int dense_persistent_groups(int cu_count) { return cu_count; }
 
+size_t dense_lse_workspace_bytes(int cu_count) {
+    return 2 * (size_t)dense_persistent_groups(cu_count) * 2 * kDenseBM16 * sizeof(float);
+}
+
+// Row statistics of the dense rows for the gradient (bf16): the persistent
+// kernel and merge in their kLse form; ws holds dense_lse_workspace_bytes().
+hipError_t launch_dense_lse(const AttnArgs &a, float *lse, hipStream_t stream) {
+    if (a.max_dense <= 0 || !a.bf16) return hipSuccess;
+    const float sl2 = a.scale * kLog2e;
+    auto q = (const __bf16 *)a.q, k = (const __bf16 *)a.k;
+    const int G = dense_persistent_groups(a.cu_count);
+    float *ws_part = (float *)a.workspace;
+    const dim3 g1d((G + 7) / 8 * 8);
+    const int units_ub = a.batch * a.heads * ((a.max_dense + kDenseBM16 - 1) / kDenseBM16);
+    const int units_sk_ub = a.dense_exact ? units_ub % G : (units_ub < G ? units_ub : G - 1);
+    const int merge_q = 256 / (a.head_dim / 16);
+    const dim3 gm((unsigned)units_sk_ub * (kDenseBM16 / merge_q));
+    if (a.head_dim == 128) {
+        hipLaunchKernelGGL((dense_bf16_kernel<128, true>), g1d, dim3(kDenseThreads16), 0, stream, q, k, nullptr,
+                           nullptr, a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, lse);
+        if (units_sk_ub > 0)
+            hipLaunchKernelGGL((dense_merge_kernel<128, true>), gm, dim3(256), 0, stream, nullptr, a.dense_idx,
+                               a.counts, a.batch, a.n, a.heads, G, (const float *)ws_part, lse);
+    } else {
+        hipLaunchKernelGGL((dense_bf16_kernel<64, true>), g1d, dim3(kDenseThreads16), 0, stream, q, k, nullptr,
+                           nullptr, a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, lse);
+        if (units_sk_ub > 0)
+            hipLaunchKernelGGL((dense_merge_kernel<64, true>), gm, dim3(256), 0, stream, nullptr, a.dense_idx,
+                               a.counts, a.batch, a.n, a.heads, G, (const float *)ws_part, lse);
+    }
+    return hipGetLastError();
+}
+
 size_t dense_workspace_bytes(int batch, int heads, int n, int head_dim, bool bf16, int cu_count) {
     if (!bf16) return 0;
     const size_t G = (size_t)dense_persistent_groups(cu_count);
@@ -730,17 +784,17 @@ hipError_t launch_dense(const AttnArgs &a, hipStream_t stream) {
         const int merge_q = 256 / (a.head_dim / 16);
         const dim3 gm((unsigned)units_sk_ub * (kDenseBM16 / merge_q));
         if (a.head_dim == 128) {
-            hipLaunchKernelGGL(dense_bf16_kernel<128>, g1d, dim3(kDenseThreads16), 0, stream, q, k, v, o,
-                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part);
+            hipLaunchKernelGGL((dense_bf16_kernel<128, false>), g1d, dim3(kDenseThreads16), 0, stream, q, k, v, o,
+                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, nullptr);
             if (units_sk_ub > 0)
-                hipLaunchKernelGGL(dense_merge_kernel<128>, gm, dim3(256), 0, stream, o, a.dense_idx, a.counts,
-                                   a.batch, a.n, a.heads, G, (const float *)ws_part);
+                hipLaunchKernelGGL((dense_merge_kernel<128, false>), gm, dim3(256), 0, stream, o, a.dense_idx,
+                                   a.counts, a.batch, a.n, a.heads, G, (const float *)ws_part, nullptr);
         } else {
-            hipLaunchKernelGGL(dense_bf16_kernel<64>, g1d, dim3(kDenseThreads16), 0, stream, q, k, v, o,
-                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part);
+            hipLaunchKernelGGL((dense_bf16_kernel<64, false>), g1d, dim3(kDenseThreads16), 0, stream, q, k, v, o,
+                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, nullptr);
             if (units_sk_ub > 0)
-                hipLaunchKernelGGL(dense_merge_kernel<64>, gm, dim3(256), 0, stream, o, a.dense_idx, a.counts,
-                                   a.batch, a.n, a.heads, G, (const float *)ws_part);
+                hipLaunchKernelGGL((dense_merge_kernel<64, false>), gm, dim3(256), 0, stream, o, a.dense_idx,
+                                   a.counts, a.batch, a.n, a.heads, G, (const float *)ws_part, nullptr);
         }
     } else {
         const dim3 grid((a.max_dense + kDenseBM - 1) / kDenseBM, a.heads, a.batch);

@@ -77,7 +77,10 @@ struct BwdArgs {
     int cut;
     bool bf16;
     float scale;
-    int max_dense;  // upper bound on any sample's dense count
+    int max_dense;     // upper bound on any sample's dense count
+    bool dense_exact;  // every sample has exactly max_dense dense tokens
+    void *lse_part;    // dense_lse_workspace_bytes(kBwdMaxLseGroups) bytes of device memory
+    int cu_count;      // persistent workgroups of the statistics kernel (<= kBwdMaxLseGroups)
 };
 
 // Largest effective window along w that the local kernel's key tiling holds.
@@ -89,8 +92,16 @@ size_t dense_workspace_bytes(int batch, int heads, int n, int head_dim, bool bf1
 hipError_t launch_route(const RouteArgs &a, hipStream_t stream);
 hipError_t launch_swap(const SwapArgs &a, int n_blocks, hipStream_t stream);
 hipError_t launch_dense(const AttnArgs &a, hipStream_t stream);
+// LSE of the dense rows (bf16 only) into lse[(b*heads + h)*n + token]; the
+// workspace holds dense_lse_workspace_bytes(cu_count).
+size_t dense_lse_workspace_bytes(int cu_count);
+hipError_t launch_dense_lse(const AttnArgs &a, float *lse, hipStream_t stream);
 hipError_t launch_local(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
+// The backward workspace holds the dense rows' partial statistics for at
+// most this many persistent workgroups, so that its size does not depend on
+// the device.
+constexpr int kBwdMaxLseGroups = 1024;
 size_t backward_workspace_bytes(int batch, int heads, int n);
 
 }  // namespace hetattn
