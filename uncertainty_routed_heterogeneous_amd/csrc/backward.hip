@@ -1244,11 +1244,22 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
     g.cut = a.cut;
     if (kBwdQX + g.lw - 1 > 32) return hipErrorInvalidValue;  // rejected earlier by the ABI layer
 
-    // The dense rows' LSE (bf16) comes from the dense forward kernel in its
-    // statistics-only form.
+    // bf16: the rows' LSE comes from the forward kernels in their
+    // statistics-only forms (dense rows: the persistent dense kernel; local
+    // rows: the band kernel), and the local rows' dQ from the band kernel's
+    // gradient form.
     AttnArgs fa{};
     fa.q = a.q;
     fa.k = a.k;
+    fa.v = a.v;
+    fa.mask = a.mask;
+    fa.grid_t = a.grid_t;
+    fa.grid_h = a.grid_h;
+    fa.grid_w = a.grid_w;
+    fa.win_t = a.win_t;
+    fa.win_h = a.win_h;
+    fa.win_w = a.win_w;
+    fa.cut = a.cut;
     fa.dense_idx = a.dense_idx;
     fa.counts = a.counts;
     fa.batch = a.batch;
@@ -1283,12 +1294,17 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
         else if (dense_units > 0)                                                                              \
             hipLaunchKernelGGL((bwd_dq_dense_kernel<T_, D_>), dim3(dense_units), dim3(64 * kBwdWaves), 0, stream, \
                                a, dense_units);                                                                \
-        if (sr16)                                                                                              \
+        if (std::is_same<T_, __bf16>::value) {                                                                \
+            hipError_t e = launch_local_lse(fa, a.lse, stream);                                               \
+            if (e == hipSuccess) e = launch_local_dq(fa, a.dout, a.lse, a.dsum, a.dq, stream);                 \
+            if (e != hipSuccess) return e;                                                                     \
+        } else if (sr16) {                                                                                     \
             hipLaunchKernelGGL((bwd_dq_kernel<T_, D_, false, 16>), dim3(tile_units), dim3(64), 0, stream, a, g,  \
                                tile_units);                                                                    \
-        else                                                                                                   \
+        } else {                                                                                               \
             hipLaunchKernelGGL((bwd_dq_kernel<T_, D_, false, 32>), dim3(tile_units), dim3(64), 0, stream, a, g,  \
                                tile_units);                                                                    \
+        }                                                                                                      \
         if constexpr (std::is_same<T_, __bf16>::value)                                                        \
             hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D_>), dim3(kblock_units), dim3(512), 0, stream, a, g,     \
                                n_kblocks, kblock_units);                                                       \

@@ -97,6 +97,11 @@ hipError_t launch_dense(const AttnArgs &a, hipStream_t stream);
 size_t dense_lse_workspace_bytes(int cu_count);
 hipError_t launch_dense_lse(const AttnArgs &a, float *lse, hipStream_t stream);
 hipError_t launch_local(const AttnArgs &a, hipStream_t stream);
+// bf16 only: LSE of the local rows into lse[(b*heads + h)*n + token], and dQ
+// of the local rows given that LSE and D = dO.O (dsum, same layout).
+hipError_t launch_local_lse(const AttnArgs &a, float *lse, hipStream_t stream);
+hipError_t launch_local_dq(const AttnArgs &a, const void *dout, const float *lse, const float *dsum, void *dq,
+                           hipStream_t stream);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 // The backward workspace holds the dense rows' partial statistics for at
 // most this many persistent workgroups, so that its size does not depend on

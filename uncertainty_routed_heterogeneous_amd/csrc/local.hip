@@ -306,11 +306,27 @@ struct BandGeom {
 };
 
 
-template <int D, int SR, int QY>
+// Extra operands of the statistics and gradient forms of the band kernel.
+struct BandGrad {
+    const __bf16 *dout;  // kMode 2: dL/dO
+    float *lse;          // kMode 1: written; kMode 2: read ([b][h][n], log2 units)
+    const float *dsum;   // kMode 2: D_i = dO_i . O_i ([b][h][n])
+    __bf16 *dq;          // kMode 2: dQ rows of the local tokens
+    float scale;         // kMode 2: softmax scale
+};
+
+// kMode 0: the layer's output O for the local tokens.
+// kMode 1: only the row statistics: LSE_i = m_i + log2(l_i) of each local
+//          row (no V, no P*V), for the gradient of the layer.
+// kMode 2: dQ of the local rows given their LSE and D (the gradient, with
+//          the route held fixed): per band S^T = K Q^T and dP^T = V dO^T
+//          (K and V rows as A operands), P = exp2(S - LSE) inside the
+//          window, dS = P (dP - D), dQ^T += K^T dS^T (K read transposed).
+template <int D, int SR, int QY, int kMode>
 __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const uint8_t *__restrict__ mask, int N, int H, float scale_log2, LocalGeom g,
-    int n_units, int x_blocks, int t_pairs) {
+    int n_units, int x_blocks, int t_pairs, BandGrad gr) {
     constexpr int QX = 32 / QY;
     using Bg = BandGeom<D, SR, QX>;
     constexpr int rpb = Bg::rpb, NC = D / 16, NDB = D / 32;
@@ -376,6 +392,17 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
 #pragma unroll
         for (int c = 0; c < NC; ++c) qf[c] = is_local ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
     }
+    const size_t row_bh = ((size_t)b * H + h) * N;
+    // kMode 2: this lane's dO row, LSE and D.
+    bf16x8 df[kMode == 2 ? NC : 1];
+    float lse_i = 0.0f, d_i = 0.0f;
+    if constexpr (kMode == 2) {
+        const __bf16 *dp_ = gr.dout + ((size_t)b * N + tok) * tok_stride + (size_t)h * D + 8 * half;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) df[c] = is_local ? *(const bf16x8 *)(dp_ + 16 * c) : bf16x8{};
+        lse_i = is_local ? gr.lse[row_bh + tok] : 0.0f;
+        d_i = is_local ? gr.dsum[row_bh + tok] : 0.0f;
+    }
 
     // LDS row of key slot s (0..31) of this wave's block: box row s/SR of the
     // band, column cw + s%SR, clamped to the box.
@@ -430,7 +457,8 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
             const int i = wave + kBandWaves * j;
             if (i < Bg::kLoads) {
                 buffer_load_lds16(kp, bytes, (HET_LDS void *)(Kd + i * Bg::kTokPerLoad * D), dma_voff[j]);
-                buffer_load_lds16(vp, bytes, (HET_LDS void *)(Vd + i * Bg::kTokPerLoad * D), dma_voff[j]);
+                if constexpr (kMode != 1)
+                    buffer_load_lds16(vp, bytes, (HET_LDS void *)(Vd + i * Bg::kTokPerLoad * D), dma_voff[j]);
             }
         }
     };
@@ -455,38 +483,93 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
         if (bi + 1 < n_bands) dma_band(bi + 1, Kn, Vn);
         const int f = F0 + bi / nb_f, yy0 = uy0 + (bi % nb_f) * rpb;
         if (!active || f < t0 || f >= t1) return;
+        // Register i holds slot 8(i/4) + 4*half + i%4 of the block: box row
+        // (i/4 >= 2 && SR == 16), column 8*((i/4) % (SR/8)) + 4*half + i%4;
+        // in_win(i): that key is inside this query's window.
+        const bool y_in0 = yy0 < uy0 + ny && yy0 >= ylo && yy0 < yhi;
+        const bool y_in1 = rpb > 1 && yy0 + 1 < uy0 + ny && yy0 + 1 >= ylo && yy0 + 1 < yhi;
+        auto in_win = [&](int i) HET_INLINE {
+            const int xo = 8 * ((i / 4) % (SR / 8)) + 4 * half + (i % 4);
+            const bool y_in = (SR == 16 && i >= 8) ? y_in1 : y_in0;
+            return y_in && xo >= xlo && xo < xhi;
+        };
+
+        if constexpr (kMode == 2) {
+            // S^T and dP^T of the block (K and V rows), then the transposed
+            // K reads land while dS is formed.
+            bf16x8 ka[NC], va[NC];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                ka[c] = *(const HET_LDS bf16x8 *)(Kc + k_off[c]);
+                va[c] = *(const HET_LDS bf16x8 *)(Vc + k_off[c]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                s = mfma32_bf16(ka[c], qf[c], s);
+                dp = mfma32_bf16(va[c], df[c], dp);
+            }
+            bf16x4 kr[2][2][NDB];
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+                for (int lohi = 0; lohi < 2; ++lohi)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        kr[c2][lohi][db] = lds_read_tr16((const HET_LDS void *)(Kc + v_off[c2][lohi][db]));
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 sf[2];
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                u32x4 w;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    float d2[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int i = 8 * c2 + 2 * jj + e;
+                        const float p =
+                            in_win(i) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, -lse_i)) : 0.0f;
+                        d2[e] = p * (dp[i] - d_i);
+                    }
+                    w[jj] = pack_bf16x2(d2[0], d2[1]);
+                }
+                sf[c2] = __builtin_bit_cast(bf16x8, w);
+            }
+            // dQ^T += K^T dS^T (accumulated in oacc).
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2)
+                    oacc[db] = mfma32_bf16(concat8(kr[c2][0][db], kr[c2][1][db]), sf[c2], oacc[db]);
+            return;
+        }
 
         // All LDS operands of the block are requested up front: the K reads
         // feed the QK product, the V reads land while the softmax runs.
         bf16x8 ka[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) ka[c] = *(const HET_LDS bf16x8 *)(Kc + k_off[c]);
-        bf16x4 vr[2][2][NDB];
+        bf16x4 vr[2][2][kMode == 0 ? NDB : 1];
+        if constexpr (kMode == 0) {
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
+            for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-            for (int lohi = 0; lohi < 2; ++lohi)
+                for (int lohi = 0; lohi < 2; ++lohi)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    vr[c2][lohi][db] = lds_read_tr16((const HET_LDS void *)(Vc + v_off[c2][lohi][db]));
+                    for (int db = 0; db < NDB; ++db)
+                        vr[c2][lohi][db] = lds_read_tr16((const HET_LDS void *)(Vc + v_off[c2][lohi][db]));
+        }
         __builtin_amdgcn_sched_barrier(0);
         // S^T = K Q^T for this wave's key block.
         f32x16 s = f32x16{};
 #pragma unroll
         for (int c = 0; c < NC; ++c) s = mfma32_bf16(ka[c], qf[c], s);
 
-        // Keep only keys inside this query's window.  Register i holds slot
-        // 8(i/4) + 4*half + i%4 of the block: box row (i/4 >= 2 && SR == 16),
-        // column 8*((i/4) % (SR/8)) + 4*half + i%4.
-        const bool y_in0 = yy0 < uy0 + ny && yy0 >= ylo && yy0 < yhi;
-        const bool y_in1 = rpb > 1 && yy0 + 1 < uy0 + ny && yy0 + 1 >= ylo && yy0 + 1 < yhi;
+        // Keep only keys inside this query's window.
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int xo = 8 * ((i / 4) % (SR / 8)) + 4 * half + (i % 4);
-            const bool y_in = (SR == 16 && i >= 8) ? y_in1 : y_in0;
-            const bool ok = y_in && xo >= xlo && xo < xhi;
-            s[i] = ok ? s[i] : -__builtin_inff();
-        }
+        for (int i = 0; i < 16; ++i) s[i] = in_win(i) ? s[i] : -__builtin_inff();
         // Online softmax in base 2 with a lazily moved reference max (see the
         // dense kernel): the reference is set on a query's first block with
         // keys and moves only when a block's exponentials ran large -- with
@@ -521,9 +604,9 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
                     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c2 + 2 * jj], scale_log2, neg_m));
                     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c2 + 2 * jj + 1], scale_log2, neg_m));
                     tsum += p0 + p1;
-                    w[jj] = pack_bf16x2(p0, p1);
+                    if constexpr (kMode == 0) w[jj] = pack_bf16x2(p0, p1);
                 }
-                pf[c2] = __builtin_bit_cast(bf16x8, w);
+                if constexpr (kMode == 0) pf[c2] = __builtin_bit_cast(bf16x8, w);
             }
             return tsum;
         };
@@ -536,11 +619,13 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
         }
         l_part += tsum;
         // O^T += V^T P^T.
+        if constexpr (kMode == 0) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2)
-                oacc[db] = mfma32_bf16(concat8(vr[c2][0][db], vr[c2][1][db]), pf[c2], oacc[db]);
+                for (int c2 = 0; c2 < 2; ++c2)
+                    oacc[db] = mfma32_bf16(concat8(vr[c2][0][db], vr[c2][1][db]), pf[c2], oacc[db]);
+        }
     };
 
     dma_band(0, Kb0, Vb0);
@@ -550,21 +635,28 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     }
 
     if (!is_local) return;
-    const float inv_l = 1.0f / half_pair_sum(l_part);
-    __bf16 *op = o + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
+    if constexpr (kMode == 1) {
+        const float l_tot = half_pair_sum(l_part);
+        if (half == 0) gr.lse[row_bh + tok] = m_run + __builtin_log2f(l_tot);
+        return;
+    }
+    const float mul = kMode == 2 ? gr.scale : 1.0f / half_pair_sum(l_part);
+    __bf16 *op = (kMode == 2 ? gr.dq : o) + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const int d = db * 32 + 8 * i4 + 4 * half;
             u32x2 w;
-            w[0] = pack_bf16x2(oacc[db][4 * i4 + 0] * inv_l, oacc[db][4 * i4 + 1] * inv_l);
-            w[1] = pack_bf16x2(oacc[db][4 * i4 + 2] * inv_l, oacc[db][4 * i4 + 3] * inv_l);
+            w[0] = pack_bf16x2(oacc[db][4 * i4 + 0] * mul, oacc[db][4 * i4 + 1] * mul);
+            w[1] = pack_bf16x2(oacc[db][4 * i4 + 2] * mul, oacc[db][4 * i4 + 3] * mul);
             *(u32x2 *)(op + d) = w;
         }
 }
 
-hipError_t launch_local(const AttnArgs &a, hipStream_t stream) {
+namespace {
+
+LocalGeom local_geom(const AttnArgs &a) {
     LocalGeom g;
     g.T = a.grid_t; g.Hg = a.grid_h; g.Wg = a.grid_w;
     g.wt = a.win_t; g.wh = a.win_h; g.ww = a.win_w;
@@ -574,9 +666,56 @@ hipError_t launch_local(const AttnArgs &a, hipStream_t stream) {
     g.cut = a.cut;
     g.tiles_y = (a.grid_h + kLocalQY - 1) / kLocalQY;
     g.tiles_x = (a.grid_w + kLocalQX - 1) / kLocalQX;
-    const int nx_max = kLocalQX + g.lw - 1;
-    g.slot_row = nx_max <= 16 ? 16 : 32;
-    if (nx_max > 32) return hipErrorInvalidValue;  // rejected earlier by the ABI layer
+    g.slot_row = kLocalQX + g.lw - 1 <= 16 ? 16 : 32;
+    return g;
+}
+
+// The band kernel (bf16) in form kMode over every local token.
+template <int kMode>
+hipError_t launch_band(const AttnArgs &a, const LocalGeom &g, const BandGrad &gr, hipStream_t stream) {
+    const float sl2 = a.scale * kLog2e;
+    // Tile shape: 4x8 or 8x4 queries, whichever needs fewer 32-key blocks
+    // per key frame (box rows / rows per block).
+    auto blocks_per_frame = [&](int qy) {
+        const int qx = 32 / qy, nx = qx + g.lw - 1, rows = qy + g.lh - 1;
+        const int rpb = nx <= 16 ? 2 : 1;
+        return nx > 32 ? 1 << 30 : (rows + rpb - 1) / rpb;
+    };
+    const int qy = blocks_per_frame(8) < blocks_per_frame(4) ? 8 : 4, qx = 32 / qy;
+    LocalGeom gb = g;
+    gb.tiles_y = (a.grid_h + qy - 1) / qy;
+    gb.tiles_x = (a.grid_w + qx - 1) / qx;
+    const bool b16 = qx + g.lw - 1 <= 16;
+    const int x_blocks = (gb.tiles_x + kBandNW - 1) / kBandNW, t_pairs = (g.T + 1) / 2;
+    const int band_units = a.batch * a.heads * t_pairs * gb.tiles_y * x_blocks;
+    const dim3 bgrid((band_units + 7) / 8 * 8), bblock(64 * kBandWaves);
+#define HET_BAND_LAUNCH(D_, SR_, QY_)                                                                        \
+    hipLaunchKernelGGL((local_band_kernel<D_, SR_, QY_, kMode>), bgrid, bblock, 0, stream, (const __bf16 *)a.q, \
+                       (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, a.mask, a.n, a.heads, sl2, gb,  \
+                       band_units, x_blocks, t_pairs, gr)
+    if (a.head_dim == 128) {
+        if (qy == 4) {
+            if (b16) HET_BAND_LAUNCH(128, 16, 4); else HET_BAND_LAUNCH(128, 32, 4);
+        } else {
+            if (b16) HET_BAND_LAUNCH(128, 16, 8); else HET_BAND_LAUNCH(128, 32, 8);
+        }
+    } else {
+        if (qy == 4) {
+            if (b16) HET_BAND_LAUNCH(64, 16, 4); else HET_BAND_LAUNCH(64, 32, 4);
+        } else {
+            if (b16) HET_BAND_LAUNCH(64, 16, 8); else HET_BAND_LAUNCH(64, 32, 8);
+        }
+    }
+#undef HET_BAND_LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_local(const AttnArgs &a, hipStream_t stream) {
+    const LocalGeom g = local_geom(a);
+    if (kLocalQX + g.lw - 1 > 32) return hipErrorInvalidValue;  // rejected earlier by the ABI layer
+    if (a.bf16) return launch_band<0>(a, g, BandGrad{}, stream);
     const int units = a.batch * a.heads * g.T * g.tiles_y * g.tiles_x;
     const dim3 grid((units + 7) / 8 * 8);
     const float sl2 = a.scale * kLog2e;
@@ -584,49 +723,28 @@ hipError_t launch_local(const AttnArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((local_kernel<T_, D_, SR_>), grid, dim3(64), 0, stream, (const T_ *)a.q,   \
                        (const T_ *)a.k, (const T_ *)a.v, (T_ *)a.o, a.mask, a.n, a.heads, sl2, g, units)
     const bool sr16 = g.slot_row == 16;
-    if (a.bf16) {
-        // Tile shape: 4x8 or 8x4 queries, whichever needs fewer 32-key blocks
-        // per key frame (box rows / rows per block).
-        auto blocks_per_frame = [&](int qy) {
-            const int qx = 32 / qy, nx = qx + g.lw - 1, rows = qy + g.lh - 1;
-            const int rpb = nx <= 16 ? 2 : 1;
-            return nx > 32 ? 1 << 30 : (rows + rpb - 1) / rpb;
-        };
-        const int qy = blocks_per_frame(8) < blocks_per_frame(4) ? 8 : 4, qx = 32 / qy;
-        LocalGeom gb = g;
-        gb.tiles_y = (a.grid_h + qy - 1) / qy;
-        gb.tiles_x = (a.grid_w + qx - 1) / qx;
-        const bool b16 = qx + g.lw - 1 <= 16;
-        const int x_blocks = (gb.tiles_x + kBandNW - 1) / kBandNW, t_pairs = (g.T + 1) / 2;
-        const int band_units = a.batch * a.heads * t_pairs * gb.tiles_y * x_blocks;
-        const dim3 bgrid((band_units + 7) / 8 * 8), bblock(64 * kBandWaves);
-#define HET_BAND_LAUNCH(D_, SR_, QY_)                                                                  \
-    hipLaunchKernelGGL((local_band_kernel<D_, SR_, QY_>), bgrid, bblock, 0, stream, (const __bf16 *)a.q, \
-                       (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, a.mask, a.n, a.heads, sl2, gb, \
-                       band_units, x_blocks, t_pairs)
-        if (a.head_dim == 128) {
-            if (qy == 4) {
-                if (b16) HET_BAND_LAUNCH(128, 16, 4); else HET_BAND_LAUNCH(128, 32, 4);
-            } else {
-                if (b16) HET_BAND_LAUNCH(128, 16, 8); else HET_BAND_LAUNCH(128, 32, 8);
-            }
-        } else {
-            if (qy == 4) {
-                if (b16) HET_BAND_LAUNCH(64, 16, 4); else HET_BAND_LAUNCH(64, 32, 4);
-            } else {
-                if (b16) HET_BAND_LAUNCH(64, 16, 8); else HET_BAND_LAUNCH(64, 32, 8);
-            }
-        }
-#undef HET_BAND_LAUNCH
+    if (a.head_dim == 128) {
+        if (sr16) HET_LOCAL_LAUNCH(float, 128, 16); else HET_LOCAL_LAUNCH(float, 128, 32);
     } else {
-        if (a.head_dim == 128) {
-            if (sr16) HET_LOCAL_LAUNCH(float, 128, 16); else HET_LOCAL_LAUNCH(float, 128, 32);
-        } else {
-            if (sr16) HET_LOCAL_LAUNCH(float, 64, 16); else HET_LOCAL_LAUNCH(float, 64, 32);
-        }
+        if (sr16) HET_LOCAL_LAUNCH(float, 64, 16); else HET_LOCAL_LAUNCH(float, 64, 32);
     }
 #undef HET_LOCAL_LAUNCH
     return hipGetLastError();
+}
+
+hipError_t launch_local_lse(const AttnArgs &a, float *lse, hipStream_t stream) {
+    const LocalGeom g = local_geom(a);
+    if (!a.bf16 || kLocalQX + g.lw - 1 > 32) return hipErrorInvalidValue;
+    return launch_band<1>(a, g, BandGrad{nullptr, lse, nullptr, nullptr, 0.0f}, stream);
+}
+
+hipError_t launch_local_dq(const AttnArgs &a, const void *dout, const float *lse, const float *dsum, void *dq,
+                           hipStream_t stream) {
+    const LocalGeom g = local_geom(a);
+    if (!a.bf16 || kLocalQX + g.lw - 1 > 32) return hipErrorInvalidValue;
+    return launch_band<2>(a, g,
+                          BandGrad{(const __bf16 *)dout, const_cast<float *>(lse), dsum, (__bf16 *)dq, a.scale},
+                          stream);
 }
 
 }  // namespace hetattn
