@@ -343,7 +343,10 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dq_dense_kernel(BwdArgs a,
 // zeros), chunk-swizzled as in the forward dense kernel, through rings of
 // three buffers (two tiles in flight), with one barrier per tile.
 template <int D>
-__global__ __launch_bounds__(512) void bwd_dq_dense_bf16_kernel(BwdArgs a, int n_units) {
+constexpr uint32_t dq_dense_lds_bytes() { return 6 * 64 * D * 2; }
+
+template <int D>
+__device__ __forceinline__ void bwd_dq_dense_bf16(const BwdArgs &a, int unit, HET_LDS char *lds) {
     constexpr int kBN = 64;                          // keys per tile
     constexpr int kBM = 128;                         // dense rows per workgroup
     constexpr int kCpr = D / 8;                      // 16-byte chunks per row
@@ -358,11 +361,8 @@ __global__ __launch_bounds__(512) void bwd_dq_dense_bf16_kernel(BwdArgs a, int n
     constexpr uint32_t kK = 0, kV = 3 * kTileB;
     constexpr uint32_t kLdsBytes = 6 * kTileB;
     static_assert(4 * 64 * (D / 2) * 4 <= kLdsBytes, "dQ exchange fits the tile buffers");
-    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
-    HET_LDS char *lds = (HET_LDS char *)smem;
+    static_assert(kLdsBytes == dq_dense_lds_bytes<D>(), "LDS size");
 
-    const int unit = blockIdx.x;
-    if (unit >= n_units) return;
     const int N = a.n, H = a.heads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
     const int grp = wave & 3, kh = wave >> 2;  // query group, key half
@@ -918,7 +918,13 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dkdv_kernel(BwdArgs a, Loc
 // the buffer's range) and has LSE = +inf, so its P and dS are 0.  Slot tokens
 // run two tiles ahead; one barrier per tile.
 template <int D>
-__global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdArgs a, LocalGeom g, int n_kblocks, int n_units) {
+constexpr uint32_t dkdv_lds_bytes() {
+    return 6 * (64 * D * 2) + 2 * (4 * 2 * 2 * 64 * 16) + 3 * 64 * 4 + 3 * 64 * 4 + 3 * 64 * 16;
+}
+
+template <int D>
+__device__ __forceinline__ void bwd_dkdv_bf16(const BwdArgs &a, const LocalGeom &g, int n_kblocks, int unit,
+                                              HET_LDS char *lds) {
     constexpr int kTile = 64;                         // query slots per tile
     constexpr int kCpr = D / 8;                       // 16-byte chunks per row
     constexpr int kRowsPerLoad = 64 / kCpr;           // rows per wave DMA (1 KB)
@@ -935,11 +941,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdArgs a, LocalGeom
     constexpr uint32_t kLse = kP + 2 * kPBuf, kDd = kLse + 3 * kTile * 4, kWin = kDd + 3 * kTile * 4;
     constexpr uint32_t kLdsBytes = kWin + 3 * kTile * 16;
     static_assert(kG + kTileB <= 65536, "dO reads take the Q offset plus an immediate");
-    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
-    HET_LDS char *lds = (HET_LDS char *)smem;
+    static_assert(kLdsBytes == dkdv_lds_bytes<D>(), "LDS size");
 
-    const int unit = blockIdx.x;
-    if (unit >= n_units) return;
     const int N = a.n, H = a.heads, HW = g.Hg * g.Wg;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
     const int grp = wave & 3;
@@ -1227,6 +1230,21 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdArgs a, LocalGeom
     }
 }
 
+// The dense rows' dQ (workgroups 0 .. n_dq-1) and dK/dV (the rest) in one
+// launch: the two are independent given the LSE, so the dK/dV workgroups
+// fill the CUs that the last round of dQ workgroups leaves idle.
+template <int D>
+__global__ __launch_bounds__(512) void bwd_dq_dkdv_bf16_kernel(BwdArgs a, LocalGeom g, int n_dq, int n_kblocks,
+                                                               int n_kv) {
+    constexpr uint32_t kBytes = dq_dense_lds_bytes<D>() > dkdv_lds_bytes<D>() ? dq_dense_lds_bytes<D>()
+                                                                                : dkdv_lds_bytes<D>();
+    __shared__ __attribute__((aligned(1024))) char smem[kBytes];
+    HET_LDS char *lds = (HET_LDS char *)smem;
+    const int bid = blockIdx.x;
+    if (bid < n_dq) bwd_dq_dense_bf16<D>(a, bid, lds);
+    else if (bid - n_dq < n_kv) bwd_dkdv_bf16<D>(a, g, n_kblocks, bid - n_dq, lds);
+}
+
 size_t backward_workspace_bytes(int batch, int heads, int n) {
     return 2 * (size_t)batch * heads * n * sizeof(float) + dense_lse_workspace_bytes(kBwdMaxLseGroups);
 }
@@ -1280,47 +1298,46 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
     const bool sr16 = g.slot_row == 16;
     const int n_kblocks = (a.n + 127) / 128;
     const int kblock_units = a.batch * a.heads * n_kblocks;
-#define HET_BWD(T_, D_)                                                                                        \
-    do {                                                                                                       \
-        constexpr int kRowsPerBlock = 4 * (64 / ((D_) * (int)sizeof(T_) / 16));                               \
-        hipLaunchKernelGGL((bwd_prep_kernel<T_, D_>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), \
-                           dim3(256), 0, stream, (const T_ *)a.o, (const T_ *)a.dout, a.dsum, rows, a.n, a.heads); \
-        if (dense_units > 0 && std::is_same<T_, __bf16>::value) {                                             \
-            const hipError_t e = launch_dense_lse(fa, a.lse, stream);                                          \
-            if (e != hipSuccess) return e;                                                                     \
-            hipLaunchKernelGGL((bwd_dq_dense_bf16_kernel<D_>), dim3(dense_units), dim3(512), 0, stream, a,      \
-                               dense_units);                                                                   \
-        }                                                                                                      \
-        else if (dense_units > 0)                                                                              \
-            hipLaunchKernelGGL((bwd_dq_dense_kernel<T_, D_>), dim3(dense_units), dim3(64 * kBwdWaves), 0, stream, \
-                               a, dense_units);                                                                \
-        if (std::is_same<T_, __bf16>::value) {                                                                \
-            hipError_t e = launch_local_lse(fa, a.lse, stream);                                               \
-            if (e == hipSuccess) e = launch_local_dq(fa, a.dout, a.lse, a.dsum, a.dq, stream);                 \
-            if (e != hipSuccess) return e;                                                                     \
-        } else if (sr16) {                                                                                     \
-            hipLaunchKernelGGL((bwd_dq_kernel<T_, D_, false, 16>), dim3(tile_units), dim3(64), 0, stream, a, g,  \
-                               tile_units);                                                                    \
-        } else {                                                                                               \
-            hipLaunchKernelGGL((bwd_dq_kernel<T_, D_, false, 32>), dim3(tile_units), dim3(64), 0, stream, a, g,  \
-                               tile_units);                                                                    \
-        }                                                                                                      \
-        if constexpr (std::is_same<T_, __bf16>::value)                                                        \
-            hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D_>), dim3(kblock_units), dim3(512), 0, stream, a, g,     \
-                               n_kblocks, kblock_units);                                                       \
-        else                                                                                                   \
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T_, D_>), dim3(key_units), dim3(64 * kBwdWaves), 0, stream, a, \
-                               g, x_groups, key_units);                                                        \
-    } while (0)
-    if (a.bf16) {
-        if (a.head_dim == 128) HET_BWD(__bf16, 128);
-        else HET_BWD(__bf16, 64);
-    } else {
-        if (a.head_dim == 128) HET_BWD(float, 128);
-        else HET_BWD(float, 64);
-    }
-#undef HET_BWD
-    return hipGetLastError();
+    // bf16: D, the rows' LSE (dense, local), the local rows' dQ, then the
+    // dense rows' dQ together with dK/dV in one launch.
+    auto bf16_path = [&](auto d_tag) -> hipError_t {
+        constexpr int D_ = decltype(d_tag)::value;
+        constexpr int kRowsPerBlock = 4 * (64 / (D_ * 2 / 16));
+        hipLaunchKernelGGL((bwd_prep_kernel<__bf16, D_>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                           dim3(256), 0, stream, (const __bf16 *)a.o, (const __bf16 *)a.dout, a.dsum, rows, a.n,
+                           a.heads);
+        hipError_t e = dense_units > 0 ? launch_dense_lse(fa, a.lse, stream) : hipSuccess;
+        if (e == hipSuccess) e = launch_local_lse(fa, a.lse, stream);
+        if (e == hipSuccess) e = launch_local_dq(fa, a.dout, a.lse, a.dsum, a.dq, stream);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_dq_dkdv_bf16_kernel<D_>), dim3((unsigned)(dense_units + kblock_units)), dim3(512), 0,
+                           stream, a, g, dense_units, n_kblocks, kblock_units);
+        return hipGetLastError();
+    };
+    // fp32: the staged-block kernels, each with its own LSE pass.
+    auto f32_path = [&](auto d_tag) -> hipError_t {
+        constexpr int D_ = decltype(d_tag)::value;
+        constexpr int kRowsPerBlock = 4 * (64 / (D_ * 4 / 16));
+        hipLaunchKernelGGL((bwd_prep_kernel<float, D_>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                           dim3(256), 0, stream, (const float *)a.o, (const float *)a.dout, a.dsum, rows, a.n,
+                           a.heads);
+        if (dense_units > 0)
+            hipLaunchKernelGGL((bwd_dq_dense_kernel<float, D_>), dim3(dense_units), dim3(64 * kBwdWaves), 0, stream,
+                               a, dense_units);
+        if (sr16)
+            hipLaunchKernelGGL((bwd_dq_kernel<float, D_, false, 16>), dim3(tile_units), dim3(64), 0, stream, a, g,
+                               tile_units);
+        else
+            hipLaunchKernelGGL((bwd_dq_kernel<float, D_, false, 32>), dim3(tile_units), dim3(64), 0, stream, a, g,
+                               tile_units);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<float, D_>), dim3(key_units), dim3(64 * kBwdWaves), 0, stream, a, g,
+                           x_groups, key_units);
+        return hipGetLastError();
+    };
+    using D128 = std::integral_constant<int, 128>;
+    using D64 = std::integral_constant<int, 64>;
+    if (a.bf16) return a.head_dim == 128 ? bf16_path(D128{}) : bf16_path(D64{});
+    return a.head_dim == 128 ? f32_path(D128{}) : f32_path(D64{});
 }
 
 }  // namespace hetattn
