@@ -92,6 +92,17 @@ def test_backward_cut_border(oracle_mod, dtype):
     full_check(oracle_mod, w, q, k, v, dout, r, "cut border", border="cut")
 
 
+@pytest.mark.parametrize("grid,window,head_dim", [
+    ((9, 3, 5), (3, 3, 3), 64),      # 15 positions per frame: a 128-key block spans 9 frames
+    ((3, 1, 200), (1, 1, 7), 128),   # one row per frame, 200 long
+    ((2, 13, 70), (3, 7, 7), 128),   # rows longer than a key block
+])
+def test_backward_key_block_layouts(oracle_mod, grid, window, head_dim):
+    w, q, k, v, dout, u = make_case(grid, 2, head_dim, "bf16", batch=2, seed=61 + grid[2], window=window)
+    r = gpu_route(u, w.grid, w.window, w.heads, w.head_dim, "bf16", rho=0.25)
+    full_check(oracle_mod, w, q, k, v, dout, r, f"key blocks {grid}")
+
+
 def test_backward_mean_std_and_swapped_routes(oracle_mod):
     import torch
     w, q, k, v, dout, u = make_case((6, 10, 20), 2, 128, "bf16", seed=41, u_kind="lognormal")
