@@ -400,14 +400,14 @@ __device__ __forceinline__ void bwd_dq_dense_bf16(const BwdArgs &a, int unit, HE
         const int r = (wave * kLoads + j) * kRowsPerLoad + lane / kCpr;
         dma_voff[j] = 2 * (r * tok_stride + 8 * ((lane % kCpr) ^ swz<D>(r)));
     }
-    auto dma = [&](const __bf16 *src, uint32_t dst_base, int kt) HET_INLINE {
+    auto dma = [&](HET_LDS char *wr, const __bf16 *src, uint32_t dst_base, int kt) HET_INLINE {
         const int key0 = kt * kBN;
         const uint32_t bytes = (uint32_t)(N - key0) * (uint32_t)tok_stride * 2u;
         const __bf16 *base = src + (size_t)key0 * tok_stride;
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
             const uint32_t dst = dst_base + (wave * kLoads + j) * kRowsPerLoad * D * 2;
-            buffer_load_lds16(base, bytes, (HET_LDS void *)(lds + dst), dma_voff[j]);
+            buffer_load_lds16(base, bytes, (HET_LDS void *)(wr + dst), dma_voff[j]);
         }
     };
     // A operands (byte offsets in a tile): key rows 32*kh + col at chunk
@@ -425,11 +425,14 @@ __device__ __forceinline__ void bwd_dq_dense_bf16(const BwdArgs &a, int unit, HE
             t_off[db][lohi] = 2 * ((32 * kh + row) * D +
                                    8 * ((4 * db + 2 * (g16 & 1) + ((j16 & 3) >> 1)) ^ swz<D>(row)) + 4 * (j16 & 1));
         }
-    auto ld128 = [&](uint32_t off) HET_INLINE -> bf16x8 { return *(const HET_LDS bf16x8 *)(lds + off); };
+    auto ld128 = [&](const HET_LDS char *rd, uint32_t off) HET_INLINE -> bf16x8 {
+        return *(const HET_LDS bf16x8 *)(rd + off);
+    };
     constexpr int kA = 4;  // A operands read ahead of their MFMA
     // S^T (this wave's 32 keys x 32 rows) of the K tile at kbase, and, when
     // vbase is given, dP^T of the V tile, as independent chains.
-    auto row_products = [&](uint32_t kbase, uint32_t vbase, bool with_dp, f32x16 &sc, f32x16 &dp) HET_INLINE {
+    auto row_products = [&](const HET_LDS char *rd, uint32_t kbase, uint32_t vbase, bool with_dp, f32x16 &sc,
+                            f32x16 &dp) HET_INLINE {
         sc = f32x16{};
         dp = f32x16{};
         uint32_t ka[NC];
@@ -439,7 +442,7 @@ __device__ __forceinline__ void bwd_dq_dense_bf16(const BwdArgs &a, int unit, HE
         bf16x8 ring[kA];
         if (with_dp) {
             constexpr int n = 2 * NC;  // step i: K (even) or V (odd), k-chunk i>>1
-            auto op = [&](int i) HET_INLINE -> bf16x8 { return ld128(ka[i >> 1] + ((i & 1) ? vdelta : 0u)); };
+            auto op = [&](int i) HET_INLINE -> bf16x8 { return ld128(rd, ka[i >> 1] + ((i & 1) ? vdelta : 0u)); };
 #pragma unroll
             for (int x = 0; x < kA; ++x) ring[x] = op(x);
             __builtin_amdgcn_sched_barrier(0);
@@ -452,12 +455,12 @@ __device__ __forceinline__ void bwd_dq_dense_bf16(const BwdArgs &a, int unit, HE
             }
         } else {
 #pragma unroll
-            for (int x = 0; x < kA; ++x) ring[x] = ld128(ka[x]);
+            for (int x = 0; x < kA; ++x) ring[x] = ld128(rd, ka[x]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < NC; ++i) {
                 sc = mfma32_bf16(ring[i % kA], qf[i], sc);
-                if (i + kA < NC) ring[i % kA] = ld128(ka[i + kA]);
+                if (i + kA < NC) ring[i % kA] = ld128(rd, ka[i + kA]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -479,27 +482,36 @@ __device__ __forceinline__ void bwd_dq_dense_bf16(const BwdArgs &a, int unit, HE
 #pragma unroll
     for (int x = 0; x < 2; ++x)
         if (x < n_kt) {
-            dma(ksrc, kK + x * kTileB, x);
-            dma(vsrc, kV + x * kTileB, x);
+            dma(lds, ksrc, kK + x * kTileB, x);
+            dma(lds, vsrc, kV + x * kTileB, x);
         }
+    // Nothing outside the loop's non-aliasing DMAs may be in flight when it
+    // starts, or the compiler waits for it inside every iteration.
+    __builtin_amdgcn_s_waitcnt(0);
     int cur = 0;  // kt % 3
     for (int kt = 0; kt < n_kt; ++kt) {
         if (kt + 1 < n_kt) __builtin_amdgcn_s_waitcnt(vm_wait(2 * kLoads));
         else __builtin_amdgcn_s_waitcnt(vm_wait(0));
         __syncthreads();  // tiles kt in LDS; tiles kt-1 done
         const int nx2 = cur == 0 ? 2 : cur - 1;  // (kt + 2) % 3
+        // The DMA into buffer nx2 and the reads of buffer cur go through
+        // pointers declared not to alias (their bytes are disjoint), so the
+        // compiler does not wait for the DMA before the transposed reads.
+        // (wr: K buffer nx2, rd: K buffer cur; the V buffers sit kV - kK
+        // bytes above their K buffers.)
+        auto tile = [&](HET_LDS char *__restrict__ wr, const HET_LDS char *__restrict__ rd) HET_INLINE {
         if (kt + 2 < n_kt) {
-            dma(ksrc, kK + nx2 * kTileB, kt + 2);
-            dma(vsrc, kV + nx2 * kTileB, kt + 2);
+            dma(wr, ksrc, 0, kt + 2);
+            dma(wr, vsrc, kV - kK, kt + 2);
         }
         f32x16 sc, dp;
-        row_products(kK + cur * kTileB, kV + cur * kTileB, true, sc, dp);
-        const uint32_t kb = kK + cur * kTileB;
+        row_products(rd, 0, kV - kK, true, sc, dp);
+        const uint32_t kb = 0;
         auto op3 = [&](int i) HET_INLINE -> bf16x8 {
             const int db = i % NDB, c2 = i / NDB;
             const uint32_t o = kb + c2 * 16 * D * 2;
-            return concat8(lds_read_tr16((const HET_LDS void *)(lds + t_off[db][0] + o)),
-                           lds_read_tr16((const HET_LDS void *)(lds + t_off[db][1] + o)));
+            return concat8(lds_read_tr16((const HET_LDS void *)(rd + t_off[db][0] + o)),
+                           lds_read_tr16((const HET_LDS void *)(rd + t_off[db][1] + o)));
         };
         bf16x8 ring[kA];
 #pragma unroll
@@ -532,6 +544,8 @@ __device__ __forceinline__ void bwd_dq_dense_bf16(const BwdArgs &a, int unit, HE
             if (i + kA < n3) ring[i % kA] = op3(i + kA);
             __builtin_amdgcn_sched_barrier(0);
         }
+        };
+        tile(lds + kK + nx2 * kTileB, lds + kK + cur * kTileB);
         cur = cur == 2 ? 0 : cur + 1;
     }
 
@@ -1002,9 +1016,11 @@ __device__ __forceinline__ void bwd_dkdv_bf16(const BwdArgs &a, const LocalGeom 
     const uint32_t p_lane = kP + grp * 4096 + lane * 16;  // + buffer, half, chunk
     const uint32_t rec_lane = 16 * half;                  // 4 slots of 4 bytes per half
 
-    auto ld128 = [&](uint32_t off) HET_INLINE -> bf16x8 { return *(const HET_LDS bf16x8 *)(lds + off); };
-    auto ldtr8 = [&](uint32_t lo, uint32_t hi) HET_INLINE -> bf16x8 {
-        return concat8(lds_read_tr16((const HET_LDS void *)(lds + lo)), lds_read_tr16((const HET_LDS void *)(lds + hi)));
+    auto ld128 = [&](const HET_LDS char *rd, uint32_t off) HET_INLINE -> bf16x8 {
+        return *(const HET_LDS bf16x8 *)(rd + off);
+    };
+    auto ldtr8 = [&](const HET_LDS char *rd, uint32_t lo, uint32_t hi) HET_INLINE -> bf16x8 {
+        return concat8(lds_read_tr16((const HET_LDS void *)(rd + lo)), lds_read_tr16((const HET_LDS void *)(rd + hi)));
     };
     constexpr int kA = 4;  // A operands read ahead of their MFMA
 
@@ -1013,7 +1029,7 @@ __device__ __forceinline__ void bwd_dkdv_bf16(const BwdArgs &a, const LocalGeom 
     // for S or dO rows for dP), the element-wise step, then the transposed
     // product of both halves into acc (A = dO^T for dV or Q^T for dK).
     // `elem` turns the two row products into the four B-operand chunks.
-    auto tile_products = [&](uint32_t row_base, uint32_t tr_base, auto &&elem) HET_INLINE {
+    auto tile_products = [&](const HET_LDS char *rd, uint32_t row_base, uint32_t tr_base, auto &&elem) HET_INLINE {
         uint32_t ra[NC], ta[NDB][2];
 #pragma unroll
         for (int c = 0; c < NC; ++c) ra[c] = row_base + r_off[c];
@@ -1025,7 +1041,7 @@ __device__ __forceinline__ void bwd_dkdv_bf16(const BwdArgs &a, const LocalGeom 
         f32x16 rp[2] = {f32x16{}, f32x16{}};
         bf16x8 ring[kA];
         constexpr int n1 = 2 * NC;  // step i: half i&1, k-chunk i>>1
-        auto op1 = [&](int i) HET_INLINE -> bf16x8 { return ld128(ra[i >> 1] + (i & 1) * kHalfB); };
+        auto op1 = [&](int i) HET_INLINE -> bf16x8 { return ld128(rd, ra[i >> 1] + (i & 1) * kHalfB); };
 #pragma unroll
         for (int x = 0; x < kA; ++x) ring[x] = op1(x);
         __builtin_amdgcn_sched_barrier(0);
@@ -1039,7 +1055,7 @@ __device__ __forceinline__ void bwd_dkdv_bf16(const BwdArgs &a, const LocalGeom 
         auto op3 = [&](int i) HET_INLINE -> bf16x8 {
             const int db = i % NDB, c2 = (i / NDB) & 1, qb2 = i / (2 * NDB);
             const uint32_t o = c2 * kChunkB + qb2 * kHalfB;
-            return ldtr8(ta[db][0] + o, ta[db][1] + o);
+            return ldtr8(rd, ta[db][0] + o, ta[db][1] + o);
         };
 #pragma unroll
         for (int x = 0; x < kA; ++x) ring[x] = op3(x);
@@ -1065,15 +1081,15 @@ __device__ __forceinline__ void bwd_dkdv_bf16(const BwdArgs &a, const LocalGeom 
             for (int j = 0; j < kLoads; ++j) dst[j] = meta(r, dma_slot[j]);
             dst[kLoads] = tid < kTile ? meta(r, tid) : -1;
         };
-        auto issue_dma = [&](int buf, const int(&tk)[kLoads + 1]) HET_INLINE {
+        auto issue_dma = [&](HET_LDS char *wr, int buf, const int(&tk)[kLoads + 1]) HET_INLINE {
 #pragma unroll
             for (int j = 0; j < kLoads; ++j) {
                 // unsigned: a row offset can pass 2^31 bytes (it stays below range)
                 const uint32_t voff =
                     tk[j] >= 0 ? (uint32_t)tk[j] * (uint32_t)tok_stride * 2u + (uint32_t)dma_byte[j] : range;
-                const uint32_t dst = buf * kTileB + (wave * kLoads + j) * kRowsPerLoad * D * 2;
-                buffer_load_lds16(qsrc, range, (HET_LDS void *)(lds + kQ + dst), (int)voff);
-                buffer_load_lds16(gsrc, range, (HET_LDS void *)(lds + kG + dst), (int)voff);
+                const uint32_t dst = (wave * kLoads + j) * kRowsPerLoad * D * 2;  // wr: Q buffer buf
+                buffer_load_lds16(qsrc, range, (HET_LDS void *)(wr + dst), (int)voff);
+                buffer_load_lds16(gsrc, range, (HET_LDS void *)(wr + (kG - kQ) + dst), (int)voff);
             }
         };
         float r_lse = 0.0f, r_d = 0.0f;
@@ -1100,8 +1116,9 @@ __device__ __forceinline__ void bwd_dkdv_bf16(const BwdArgs &a, const LocalGeom 
         };
         // Role P: P = exp2(S - LSE) (0 outside the window), published for
         // the partner wave, and dV^T += dO^T P.
-        auto compute_p = [&](int cur, int pb) HET_INLINE {
-            tile_products(kQ + cur * kTileB, kG + cur * kTileB, [&](const f32x16(&sc)[2], bf16x8(&pf)[2][2]) HET_INLINE {
+        // rd: Q buffer of the tile (its dO buffer sits kG - kQ bytes above)
+        auto compute_p = [&](const HET_LDS char *rd, int cur, int pb) HET_INLINE {
+            tile_products(rd, 0, kG - kQ, [&](const f32x16(&sc)[2], bf16x8(&pf)[2][2]) HET_INLINE {
 #pragma unroll
                 for (int qb2 = 0; qb2 < 2; ++qb2)
 #pragma unroll
@@ -1137,13 +1154,13 @@ __device__ __forceinline__ void bwd_dkdv_bf16(const BwdArgs &a, const LocalGeom 
             });
         };
         // Role dS: dS = P (dP - D) with the partner's P, and dK^T += Q^T dS.
-        auto compute_ds = [&](int cur, int pb) HET_INLINE {
-            tile_products(kG + cur * kTileB, kQ + cur * kTileB, [&](const f32x16(&dp)[2], bf16x8(&sf)[2][2]) HET_INLINE {
+        auto compute_ds = [&](const HET_LDS char *rd, int cur, int pb) HET_INLINE {
+            tile_products(rd, kG - kQ, 0, [&](const f32x16(&dp)[2], bf16x8(&sf)[2][2]) HET_INLINE {
 #pragma unroll
                 for (int qb2 = 0; qb2 < 2; ++qb2)
 #pragma unroll
                     for (int c2 = 0; c2 < 2; ++c2) {
-                        const bf16x8 pf = ld128(p_lane + pb * kPBuf + qb2 * 2048 + c2 * 1024);
+                        const bf16x8 pf = ld128(lds, p_lane + pb * kPBuf + qb2 * 2048 + c2 * 1024);
                         u32x4 ws;
 #pragma unroll
                         for (int g2 = 0; g2 < 2; ++g2) {
@@ -1164,7 +1181,7 @@ __device__ __forceinline__ void bwd_dkdv_bf16(const BwdArgs &a, const LocalGeom 
         fetch_meta(0, tk_next);
         if (n_tiles > 1) fetch_meta(1, tk_ahead);
         __syncthreads();  // the previous run is done with the buffers
-        issue_dma(0, tk_next);
+        issue_dma(lds + kQ, 0, tk_next);
         load_rec(tk_next);
         store_rec(0);
         // Iteration r: role P on tile r (buffer r % 3, P buffer r % 2), role
@@ -1174,18 +1191,25 @@ __device__ __forceinline__ void bwd_dkdv_bf16(const BwdArgs &a, const LocalGeom 
             const int nxt = cur == 2 ? 0 : cur + 1, prv = cur == 0 ? 2 : cur - 1;
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();  // tile r, its records and P of tile r-1 in LDS; tile r-2 done
-            if (r + 1 < n_tiles) {
+            // The DMA into buffer nxt and the reads of buffers cur and prv go
+            // through pointers declared not to alias (their bytes are
+            // disjoint), so the compiler does not wait for the DMA before the
+            // transposed reads.
+            auto iter = [&](HET_LDS char *__restrict__ wr, const HET_LDS char *__restrict__ rd) HET_INLINE {
+                if (r + 1 < n_tiles) {
 #pragma unroll
-                for (int j = 0; j <= kLoads; ++j) tk_next[j] = tk_ahead[j];
-                issue_dma(nxt, tk_next);
-                load_rec(tk_next);
-                if (r + 2 < n_tiles) fetch_meta(r + 2, tk_ahead);
-            }
-            if (role_p) {
-                if (r < n_tiles) compute_p(cur, r & 1);
-            } else if (r > 0) {
-                compute_ds(prv, (r - 1) & 1);
-            }
+                    for (int j = 0; j <= kLoads; ++j) tk_next[j] = tk_ahead[j];
+                    issue_dma(wr, nxt, tk_next);
+                    load_rec(tk_next);
+                    if (r + 2 < n_tiles) fetch_meta(r + 2, tk_ahead);
+                }
+                if (role_p) {
+                    if (r < n_tiles) compute_p(rd, cur, r & 1);
+                } else if (r > 0) {
+                    compute_ds(rd, prv, (r - 1) & 1);
+                }
+            };
+            iter(lds + kQ + nxt * kTileB, lds + kQ + (role_p ? cur : prv) * kTileB);
             if (r + 1 < n_tiles) store_rec(nxt);
             cur = nxt;
         }
