@@ -202,7 +202,9 @@ int het_attn_local(const het_attn_shape *shape, const void *q, const void *k, co
 
 /* Device workspace het_attn_backward needs for this shape, in bytes:
  * 2 * B * heads * N fp32 values (row statistics) plus 4 * 1024 * 256 fp32
- * values (partial statistics of the dense rows); 0 for an invalid shape. */
+ * values (partial statistics of the dense rows), and for bf16 inputs
+ * 2 * B * N * heads * head_dim fp32 values more (the local queries' part of
+ * dK and dV); 0 for an invalid shape. */
 size_t het_attn_backward_workspace_bytes(const het_attn_shape *shape);
 
 /* Backward pass of het_attn_forward with the route held fixed: the layer is

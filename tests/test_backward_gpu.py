@@ -95,7 +95,8 @@ def test_backward_cut_border(oracle_mod, dtype):
 @pytest.mark.parametrize("grid,window,head_dim", [
     ((9, 3, 5), (3, 3, 3), 64),      # 15 positions per frame: a 128-key block spans 9 frames
     ((3, 1, 200), (1, 1, 7), 128),   # one row per frame, 200 long
-    ((2, 13, 70), (3, 7, 7), 128),   # rows longer than a key block
+    ((2, 13, 70), (3, 7, 7), 128),   # rows longer than a key block; a column tile's queries span 17
+    ((2, 13, 71), (3, 7, 7), 128),   # three ragged column groups, each tile's queries within 16 columns
 ])
 def test_backward_key_block_layouts(oracle_mod, grid, window, head_dim):
     w, q, k, v, dout, u = make_case(grid, 2, head_dim, "bf16", batch=2, seed=61 + grid[2], window=window)

@@ -299,7 +299,7 @@ size_t het_attn_backward_workspace_bytes(const het_attn_shape *shape) {
     Dims d;
     float scale;
     if (check_shape(shape, d, scale) != HET_OK) return 0;
-    return hetattn::backward_workspace_bytes((int)d.B, (int)d.H, (int)d.N);
+    return hetattn::backward_workspace_bytes((int)d.B, (int)d.H, (int)d.N, (int)d.D, shape->dtype == HET_BF16);
 }
 
 int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k, const void *v,
@@ -325,7 +325,8 @@ int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k,
         for (int j = i + 1; j < 3; ++j)
             if (overlaps(outs[i], bytes, outs[j], bytes)) return HET_ERR_INVALID_ARG;
     }
-    const size_t need = hetattn::backward_workspace_bytes((int)d.B, (int)d.H, (int)d.N);
+    const size_t need =
+        hetattn::backward_workspace_bytes((int)d.B, (int)d.H, (int)d.N, (int)d.D, shape->dtype == HET_BF16);
     if (!workspace || workspace_bytes < need) return HET_ERR_WORKSPACE;
     const int cus = current_cu_count();
     if (cus <= 0) return HET_ERR_HIP;
@@ -359,6 +360,13 @@ int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k,
     a.max_dense = route->dense_count_host >= 0 ? route->dense_count_host : (int)d.N;
     a.dense_exact = route->dense_count_host >= 0;
     a.lse_part = (float *)workspace + 2 * (size_t)(d.B * d.H * d.N);
+    // bf16: the local dK and dV parts follow the statistics of the dense rows
+    a.dk_part = a.dv_part = nullptr;
+    if (shape->dtype == HET_BF16) {
+        float *parts = (float *)((char *)a.lse_part + hetattn::dense_lse_workspace_bytes(hetattn::kBwdMaxLseGroups));
+        a.dk_part = parts;
+        a.dv_part = parts + (size_t)(d.B * d.N * d.H * d.D);
+    }
     a.cu_count = cus < hetattn::kBwdMaxLseGroups ? cus : hetattn::kBwdMaxLseGroups;
     if (hetattn::launch_backward(a, (hipStream_t)stream) != hipSuccess) return HET_ERR_HIP;
     return HET_OK;

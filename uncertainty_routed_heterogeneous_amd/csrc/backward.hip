@@ -173,7 +173,7 @@ __device__ __forceinline__ void store_row_t(T *row, const f32x16 (&acc)[D / 32],
 // First and last position p of an axis whose window [lo(p), hi(p)) meets
 // the positions [j0, j1] (both ends are non-decreasing in p, and a position
 // lies in its own window, so p0 <= j0 and p1 >= j1).
-__device__ __forceinline__ void inverse_window(int j0, int j1, int k, int len, int S, int cut, int &p0,
+__host__ __device__ __forceinline__ void inverse_window(int j0, int j1, int k, int len, int S, int cut, int &p0,
                                                int &p1) {
     p0 = imax(0, j0 - k);
     while (win_hi(p0, k, len, S, cut) <= j0) ++p0;
@@ -1227,8 +1227,10 @@ __device__ __forceinline__ void bwd_dkdv_bf16(const BwdArgs &a, const LocalGeom 
     // Local queries, per frame the block touches: the box of positions whose
     // windows can hold a key of the block in that frame (rows y0..y1 of the
     // frame; columns x0..x1 when the block stays in one row, else all).
+    // (When the band kernel has taken the local queries, their part is in
+    // dk_part / dv_part and is added below.)
     const uint8_t *mb = a.mask + (size_t)b * N;
-    for (int f = key0 / HW; f <= (key1 - 1) / HW; ++f) {
+    for (int f = key0 / HW; !a.dk_part && f <= (key1 - 1) / HW; ++f) {
         const int lo = imax(key0, f * HW) - f * HW, hi = imin(key1, (f + 1) * HW) - 1 - f * HW;
         const int y0 = lo / g.Wg, y1 = hi / g.Wg;
         const int x0 = y0 == y1 ? lo % g.Wg : 0, x1 = y0 == y1 ? hi % g.Wg : g.Wg - 1;
@@ -1249,8 +1251,332 @@ __device__ __forceinline__ void bwd_dkdv_bf16(const BwdArgs &a, const LocalGeom 
     }
 
     if (key_ok) {
+        if (a.dk_part) {
+            const float *src = (role_p ? a.dv_part : a.dk_part) + (((size_t)b * N + key) * H + h) * D + 4 * half;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x4 pv = *(const f32x4 *)(src + db * 32 + 8 * i4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[db][4 * i4 + e] += pv[e];
+                }
+        }
         __bf16 *dst = (__bf16 *)(role_p ? a.dv : a.dk) + sample + (size_t)key * tok_stride;
         store_row_t<__bf16, D>(dst, acc, role_p ? 1.0f : a.scale);
+    }
+}
+
+// Local part of dK and dV (bf16) for grids that local_band_fits accepts
+// (windows at most 9 wide along the columns).  Workgroup = the
+// four 4x8 key tiles (ty, 4*xg .. 4*xg+3) of frame t, two waves per tile on
+// one SIMD, as in the dense pass (K side: S, P, dV; V side: dP, dS, dK one
+// band behind, P through LDS).  The queries whose windows can hold a key of
+// the tiles form a box (frames x rows x columns: the inverse windows of the
+// tiles' extent per axis).  It is streamed through LDS in bands of two box
+// rows of one frame: each box row is a run of consecutive tokens, so every
+// lane's DMA offset from the band's first token is fixed.  From each band a
+// tile takes the 16 columns x 2 rows of queries whose windows can reach it:
+// one 32 x 32 block.  A query sees a key when it is local and its position
+// lies, per axis, in the key's inverse window (computed once per lane).
+// Output: the fp32 partial dK (without the softmax scale) and dV of every
+// key of the tiles, which the dense pass adds before it stores dK and dV.
+constexpr int kLbCols = 40;  // LDS rows per box row of a band
+
+// Whether the band form holds the grid: every 8-column key tile takes its
+// queries from at most 16 columns, and every group of four tiles from at most
+// kLbCols.  A key tile's columns span 8 + k - 1 positions away from a border;
+// where windows are shifted inside the grid, the positions that see a key
+// near the border reach up to (k - 1) / 2 further, so the spans are taken
+// from the inverse windows tile by tile.
+static bool local_band_fits(const LocalGeom &g) {
+    for (int tx = 0; tx < g.tiles_x; ++tx) {
+        int c0, c1;
+        inverse_window(tx * kBwdQX, imin(tx * kBwdQX + kBwdQX - 1, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut, c0, c1);
+        if (c1 - c0 + 1 > 16) return false;
+        if (tx % 4 == 0) {
+            const int tx1 = imin(tx + 3, g.tiles_x - 1);
+            inverse_window(tx * kBwdQX, imin(tx1 * kBwdQX + kBwdQX - 1, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut, c0, c1);
+            if (c1 - c0 + 1 > kLbCols) return false;
+        }
+    }
+    return true;
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void bwd_dkdv_local_band_kernel(BwdArgs a, LocalGeom g, int x_groups,
+                                                                  int n_units) {
+    constexpr int kCpr = D / 8;
+    constexpr int kTokPerLoad = 64 / kCpr;                 // rows per wave DMA (1 KB)
+    constexpr int kBandRows = 2 * kLbCols;
+    constexpr int kLoadsTot = kBandRows / kTokPerLoad;     // wave DMAs per tensor and band
+    constexpr int kLoadsPerWave = (kLoadsTot + 7) / 8;
+    static_assert(kBandRows % kTokPerLoad == 0, "band rows in whole DMAs");
+    constexpr int NC = D / 16, NDB = D / 32;
+    constexpr uint32_t kBufB = kBandRows * D * 2;
+    constexpr uint32_t kQ = 0, kG = 3 * kBufB, kP = 6 * kBufB, kPBuf = 4 * 2 * 64 * 16;
+    constexpr uint32_t kLse = kP + 2 * kPBuf, kDd = kLse + 3 * 4 * 32 * 4;
+    constexpr uint32_t kLdsBytes = kDd + 3 * 4 * 32 * 4;
+    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+    HET_LDS char *lds = (HET_LDS char *)smem;
+
+    const int unit = blockIdx.x;
+    if (unit >= n_units) return;
+    const int N = a.n, H = a.heads;
+    int rest = unit;
+    const int xg = rest % x_groups;
+    rest /= x_groups;
+    const int ty = rest % g.tiles_y;
+    rest /= g.tiles_y;
+    const int t = rest % g.T;
+    rest /= g.T;
+    const int h = rest % H, b = rest / H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+    const int grp = wave & 3;
+    const bool role_p = wave < 4;
+    const int tok_stride = H * D;
+    const size_t sample = (size_t)b * N * tok_stride + (size_t)h * D;
+    const size_t row_bh = ((size_t)b * H + h) * N;
+    const float sl2 = a.scale * kLog2e;
+
+    // The box of query positions (uniform).
+    const int tx0 = 4 * xg, tx1 = imin(tx0 + 3, g.tiles_x - 1);
+    int pt0, pt1, py0, py1, px0, px1;
+    inverse_window(t, t, g.wt, g.lt, g.T, g.cut, pt0, pt1);
+    inverse_window(ty * kBwdQY, imin(ty * kBwdQY + kBwdQY - 1, g.Hg - 1), g.wh, g.lh, g.Hg, g.cut, py0, py1);
+    inverse_window(tx0 * kBwdQX, imin(tx1 * kBwdQX + kBwdQX - 1, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut, px0, px1);
+    const int C = px1 - px0 + 1;  // <= kLbCols
+    const int nb_f = (py1 - py0 + 2) / 2, n_bands = (pt1 - pt0 + 1) * nb_f;
+    // Columns of the box from which tile g' takes its 16 query columns.
+    auto tile_cw = [&](int gg) HET_INLINE -> int {
+        const int tx = imin(tx0 + gg, g.tiles_x - 1);
+        int c0, c1;
+        inverse_window(tx * kBwdQX, imin(tx * kBwdQX + kBwdQX - 1, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut, c0, c1);
+        return c0 - px0;
+    };
+    const int cw = tile_cw(grp);
+
+    // This lane's key and the intervals of query positions that see it.
+    const int tx = tx0 + grp;
+    const int ky = ty * kBwdQY + col / kBwdQX, kx = tx * kBwdQX + col % kBwdQX;
+    const bool key_ok = tx < g.tiles_x && ky < g.Hg && kx < g.Wg;
+    const int key = key_ok ? (t * g.Hg + ky) * g.Wg + kx : 0;
+    int it0, it1, iy0, iy1, ix0, ix1;
+    inverse_window(t, t, g.wt, g.lt, g.T, g.cut, it0, it1);
+    inverse_window(imin(ky, g.Hg - 1), imin(ky, g.Hg - 1), g.wh, g.lh, g.Hg, g.cut, iy0, iy1);
+    inverse_window(imin(kx, g.Wg - 1), imin(kx, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut, ix0, ix1);
+
+    bf16x8 kv[NC];
+    {
+        const __bf16 *src = (const __bf16 *)(role_p ? a.k : a.v) + sample + (size_t)key * tok_stride + 8 * half;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kv[c] = key_ok ? *(const bf16x8 *)(src + 16 * c) : bf16x8{};
+    }
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+    // Slot j (< 32) of this tile's block: box row j/16 of the band, column
+    // cw + j%16 (clamped to the LDS rows; a clamped slot is outside every
+    // key's interval, so it is masked).
+    auto slot_row = [&](int j) HET_INLINE -> int { return (j >> 4) * kLbCols + imin(cw + (j & 15), kLbCols - 1); };
+    const int g16 = lane >> 4, j16 = lane & 15;
+    uint32_t r_off[NC], t_off[2][NDB][2];
+    {
+        const int R = slot_row(col);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) r_off[c] = 2 * (R * D + 8 * ((2 * c + half) ^ swz<D>(R)));
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+            for (int lohi = 0; lohi < 2; ++lohi) {
+                const int Rt = slot_row(16 * c2 + 4 * half + (j16 >> 2) + 8 * lohi);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    t_off[c2][db][lohi] =
+                        2 * (Rt * D + 8 * ((4 * db + 2 * (g16 & 1) + ((j16 & 3) >> 1)) ^ swz<D>(Rt)) + 4 * (j16 & 1));
+            }
+    }
+    // DMA: wave load i (= wave + 8j) fills band rows i*kTokPerLoad ..; row R
+    // = rr*kLbCols + c holds box row rr, column c; columns past the box get
+    // an offset beyond any descriptor's range and read as zeros.
+    int dma_voff[kLoadsPerWave];
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j) {
+        const int i = wave + 8 * j;
+        const int R = i * kTokPerLoad + lane / kCpr;
+        const int rr = R / kLbCols, c = R % kLbCols;
+        dma_voff[j] = c < C ? 2 * ((rr * g.Wg + c) * tok_stride + 8 * ((lane % kCpr) ^ swz<D>(R))) : 0x7ffffff0;
+    }
+    const __bf16 *qbase = (const __bf16 *)a.q + sample, *gbase = (const __bf16 *)a.dout + sample;
+    auto band_tok0 = [&](int bi) HET_INLINE -> int {
+        const int f = pt0 + bi / nb_f, y0 = py0 + 2 * (bi % nb_f);
+        return (f * g.Hg + y0) * g.Wg + px0;
+    };
+    auto issue_dma = [&](HET_LDS char *wr, int bi) HET_INLINE {
+        const int tok0 = band_tok0(bi);
+        const uint32_t bytes = (uint32_t)(N - tok0) * (uint32_t)tok_stride * 2u;
+        const __bf16 *qp = qbase + (size_t)tok0 * tok_stride, *gp = gbase + (size_t)tok0 * tok_stride;
+#pragma unroll
+        for (int j = 0; j < kLoadsPerWave; ++j) {
+            const int i = wave + 8 * j;
+            if (i < kLoadsTot) {
+                const uint32_t dst = i * kTokPerLoad * D * 2;
+                buffer_load_lds16(qp, bytes, (HET_LDS void *)(wr + dst), dma_voff[j]);
+                buffer_load_lds16(gp, bytes, (HET_LDS void *)(wr + (kG - kQ) + dst), dma_voff[j]);
+            }
+        }
+    };
+    // Records of a band, per tile and slot: LSE (+inf for a slot without a
+    // local query in the box) and D.  Thread tid < 128 owns slot tid%32 of
+    // tile tid/32.
+    const int rec_g = (tid >> 5) & 3, rec_j = tid & 31;
+    const int rec_cw = tile_cw(rec_g);
+    const uint8_t *mb = a.mask + (size_t)b * N;
+    float r_lse = 0.0f, r_d = 0.0f;
+    auto load_rec = [&](int bi) HET_INLINE {
+        if (tid < 128) {
+            const int f = pt0 + bi / nb_f, y = py0 + 2 * (bi % nb_f) + (rec_j >> 4);
+            const int c = rec_cw + (rec_j & 15);
+            const bool in_box = y <= py1 && c < C;
+            const int tk = in_box ? (f * g.Hg + y) * g.Wg + px0 + c : 0;
+            const bool ok = in_box && mb[tk] != 0;
+            r_lse = ok ? a.lse[row_bh + tk] : __builtin_inff();
+            r_d = ok ? a.dsum[row_bh + tk] : 0.0f;
+        }
+    };
+    auto store_rec = [&](int buf) HET_INLINE {
+        if (tid < 128) {
+            *(HET_LDS float *)(lds + kLse + (buf * 128 + tid) * 4) = r_lse;
+            *(HET_LDS float *)(lds + kDd + (buf * 128 + tid) * 4) = r_d;
+        }
+    };
+    const uint32_t p_lane = kP + grp * 2048 + lane * 16;           // + buffer, chunk
+    const uint32_t rec_lane = (grp * 32 + 4 * half) * 4;           // + buffer, 8*(i/4) slots
+    // Window test of register i (slot 8(i/4) + 4*half + i%4): the band's
+    // frame and the slot's row and column against this key's intervals.
+    auto in_win = [&](int bi, int i) HET_INLINE -> bool {
+        const int f = pt0 + bi / nb_f, y = py0 + 2 * (bi % nb_f) + (i >> 3);
+        const int x = px0 + cw + 8 * ((i >> 2) & 1) + 4 * half + (i & 3);
+        return f >= it0 && f <= it1 && y >= iy0 && y <= iy1 && x >= ix0 && x <= ix1;
+    };
+
+    auto ld128 = [&](const HET_LDS char *rd, uint32_t off) HET_INLINE -> bf16x8 {
+        return *(const HET_LDS bf16x8 *)(rd + off);
+    };
+    constexpr int kA = 4;
+    // One block: row product (A = slot rows), element step, transposed
+    // product into acc (A = the other tensor's slots read transposed).
+    auto block = [&](const HET_LDS char *rd, uint32_t row_base, uint32_t tr_base, auto &&elem) HET_INLINE {
+        f32x16 rp = f32x16{};
+        bf16x8 ring[kA];
+        auto op1 = [&](int i) HET_INLINE -> bf16x8 { return ld128(rd, row_base + r_off[i]); };
+#pragma unroll
+        for (int x = 0; x < kA; ++x) ring[x] = op1(x);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            rp = mfma32_bf16(ring[i % kA], kv[i], rp);
+            if (i + kA < NC) ring[i % kA] = op1(i + kA);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        constexpr int n3 = 2 * NDB;  // step i: dim block i%NDB, chunk i/NDB
+        auto op3 = [&](int i) HET_INLINE -> bf16x8 {
+            const int db = i % NDB, c2 = i / NDB;
+            return concat8(lds_read_tr16((const HET_LDS void *)(rd + tr_base + t_off[c2][db][0])),
+                           lds_read_tr16((const HET_LDS void *)(rd + tr_base + t_off[c2][db][1])));
+        };
+#pragma unroll
+        for (int x = 0; x < kA; ++x) ring[x] = op3(x);
+        bf16x8 bf[2];
+        elem(rp, bf);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < n3; ++i) {
+            acc[i % NDB] = mfma32_bf16(ring[i % kA], bf[i / NDB], acc[i % NDB]);
+            if (i + kA < n3) ring[i % kA] = op3(i + kA);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto compute_p = [&](const HET_LDS char *rd, int bi, int cur, int pb) HET_INLINE {
+        block(rd, 0, kG - kQ, [&](const f32x16 &sc, bf16x8(&pf)[2]) HET_INLINE {
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                u32x4 wp;
+#pragma unroll
+                for (int g2 = 0; g2 < 2; ++g2) {
+                    const int g4 = 2 * c2 + g2;
+                    const f32x4 l4 = *(const HET_LDS f32x4 *)(lds + kLse + cur * 512 + rec_lane + 32 * g4);
+                    float p[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * g4 + e], sl2, -l4[e]));
+                        p[e] = in_win(bi, 4 * g4 + e) ? pe : 0.0f;
+                    }
+                    wp[2 * g2] = pack_bf16x2(p[0], p[1]);
+                    wp[2 * g2 + 1] = pack_bf16x2(p[2], p[3]);
+                }
+                pf[c2] = __builtin_bit_cast(bf16x8, wp);
+                *(HET_LDS bf16x8 *)(lds + p_lane + pb * kPBuf + c2 * 1024) = pf[c2];
+            }
+        });
+    };
+    auto compute_ds = [&](const HET_LDS char *rd, int cur, int pb) HET_INLINE {
+        block(rd, kG - kQ, 0, [&](const f32x16 &dp, bf16x8(&sf)[2]) HET_INLINE {
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const bf16x8 pf = ld128(lds, p_lane + pb * kPBuf + c2 * 1024);
+                u32x4 ws;
+#pragma unroll
+                for (int g2 = 0; g2 < 2; ++g2) {
+                    const int g4 = 2 * c2 + g2;
+                    const f32x4 d4 = *(const HET_LDS f32x4 *)(lds + kDd + cur * 512 + rec_lane + 32 * g4);
+                    float s[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[e] = (float)pf[4 * g2 + e] * (dp[4 * g4 + e] - d4[e]);
+                    ws[2 * g2] = pack_bf16x2(s[0], s[1]);
+                    ws[2 * g2 + 1] = pack_bf16x2(s[2], s[3]);
+                }
+                sf[c2] = __builtin_bit_cast(bf16x8, ws);
+            }
+        });
+    };
+
+    // Iteration r: K side on band r, V side on band r-1 (three band
+    // buffers, two P buffers, records three deep, one barrier per band).
+    issue_dma(lds + kQ, 0);
+    load_rec(0);
+    store_rec(0);
+    int cur = 0;
+    for (int r = 0; r <= n_bands; ++r) {
+        const int nxt = cur == 2 ? 0 : cur + 1, prv = cur == 0 ? 2 : cur - 1;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // band r, its records and P of band r-1 in LDS; band r-2 done
+        auto iter = [&](HET_LDS char *__restrict__ wr, const HET_LDS char *__restrict__ rd) HET_INLINE {
+            if (r + 1 < n_bands) {
+                issue_dma(wr, r + 1);
+                load_rec(r + 1);
+            }
+            if (role_p) {
+                if (r < n_bands) compute_p(rd, r, cur, r & 1);
+            } else if (r > 0) {
+                compute_ds(rd, prv, (r - 1) & 1);
+            }
+        };
+        iter(lds + kQ + nxt * kBufB, lds + kQ + (role_p ? cur : prv) * kBufB);
+        if (r + 1 < n_bands) store_rec(nxt);
+        cur = nxt;
+    }
+
+    // fp32 partials: dV (K side) and dK without the scale (V side).
+    if (key_ok) {
+        float *dst = (role_p ? a.dv_part : a.dk_part) + (((size_t)b * N + key) * H + h) * D + 4 * half;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                *(f32x4 *)(dst + db * 32 + 8 * i4) =
+                    f32x4{acc[db][4 * i4], acc[db][4 * i4 + 1], acc[db][4 * i4 + 2], acc[db][4 * i4 + 3]};
     }
 }
 
@@ -1269,8 +1595,10 @@ __global__ __launch_bounds__(512) void bwd_dq_dkdv_bf16_kernel(BwdArgs a, LocalG
     else if (bid - n_dq < n_kv) bwd_dkdv_bf16<D>(a, g, n_kblocks, bid - n_dq, lds);
 }
 
-size_t backward_workspace_bytes(int batch, int heads, int n) {
-    return 2 * (size_t)batch * heads * n * sizeof(float) + dense_lse_workspace_bytes(kBwdMaxLseGroups);
+size_t backward_workspace_bytes(int batch, int heads, int n, int head_dim, bool bf16) {
+    size_t bytes = 2 * (size_t)batch * heads * n * sizeof(float) + dense_lse_workspace_bytes(kBwdMaxLseGroups);
+    if (bf16) bytes += 2 * (size_t)batch * n * heads * head_dim * sizeof(float);  // local dK, dV parts
+    return bytes;
 }
 
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
@@ -1334,8 +1662,18 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
         if (e == hipSuccess) e = launch_local_lse(fa, a.lse, stream);
         if (e == hipSuccess) e = launch_local_dq(fa, a.dout, a.lse, a.dsum, a.dq, stream);
         if (e != hipSuccess) return e;
+        // Local part of dK/dV by key tiles over query bands when the tiles'
+        // query columns fit its slots (windows up to 9 wide, less near a
+        // shifted border); else the dense pass runs over the local queries.
+        BwdArgs a2 = a;
+        if (local_band_fits(g)) {
+            hipLaunchKernelGGL((bwd_dkdv_local_band_kernel<D_>), dim3((unsigned)key_units), dim3(512), 0, stream, a, g,
+                               x_groups, key_units);
+        } else {
+            a2.dk_part = a2.dv_part = nullptr;
+        }
         hipLaunchKernelGGL((bwd_dq_dkdv_bf16_kernel<D_>), dim3((unsigned)(dense_units + kblock_units)), dim3(512), 0,
-                           stream, a, g, dense_units, n_kblocks, kblock_units);
+                           stream, a2, g, dense_units, n_kblocks, kblock_units);
         return hipGetLastError();
     };
     // fp32: the staged-block kernels, each with its own LSE pass.

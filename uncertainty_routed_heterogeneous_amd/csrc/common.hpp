@@ -82,8 +82,8 @@ __device__ __forceinline__ bf16x8 concat8(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
-__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
+__host__ __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+__host__ __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 
 // Workgroup -> work unit.  The hardware deals consecutive workgroups to the 8
 // XCDs round-robin; this remap gives each XCD a contiguous run of units so
@@ -120,7 +120,7 @@ __device__ __forceinline__ int swz(int row) {
 }
 
 // Window start along one axis (shifted inside the grid), see hetattn.h.
-__device__ __forceinline__ int window_start(int pos, int k, int len, int S) {
+__host__ __device__ __forceinline__ int window_start(int pos, int k, int len, int S) {
     int s = pos - (k - 1) / 2;
     s = imin(s, S - len);
     return imax(s, 0);
@@ -132,10 +132,10 @@ __device__ __forceinline__ int window_start(int pos, int k, int len, int S) {
 // ends are non-decreasing in pos, so the union of the windows of the
 // positions p0 <= p <= p1 is [lo(p0), hi(p1)), and it is never wider than
 // p1 - p0 + len.
-__device__ __forceinline__ int win_lo(int pos, int k, int len, int S, int cut) {
+__host__ __device__ __forceinline__ int win_lo(int pos, int k, int len, int S, int cut) {
     return cut ? imax(pos - (k - 1) / 2, 0) : window_start(pos, k, len, S);
 }
-__device__ __forceinline__ int win_hi(int pos, int k, int len, int S, int cut) {
+__host__ __device__ __forceinline__ int win_hi(int pos, int k, int len, int S, int cut) {
     return cut ? imin(pos + (k - 1) / 2 + 1, S) : window_start(pos, k, len, S) + len;
 }
 

@@ -80,6 +80,7 @@ struct BwdArgs {
     int max_dense;     // upper bound on any sample's dense count
     bool dense_exact;  // every sample has exactly max_dense dense tokens
     void *lse_part;    // dense_lse_workspace_bytes(kBwdMaxLseGroups) bytes of device memory
+    float *dk_part, *dv_part;  // [batch, n, heads, head_dim] fp32 local parts (bf16 path)
     int cu_count;      // persistent workgroups of the statistics kernel (<= kBwdMaxLseGroups)
 };
 
@@ -107,6 +108,6 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 // most this many persistent workgroups, so that its size does not depend on
 // the device.
 constexpr int kBwdMaxLseGroups = 1024;
-size_t backward_workspace_bytes(int batch, int heads, int n);
+size_t backward_workspace_bytes(int batch, int heads, int n, int head_dim, bool bf16);
 
 }  // namespace hetattn
