@@ -210,9 +210,11 @@ def time_swap(layer, ratio: float, n_blocks: int, iters: int, warmup: int = 3):
     return ts[len(ts) // 2]
 
 
-def time_backward(layer, iters: int, warmup: int = 2):
-    """Median time of one het_attn_backward call on the layer's route and
-    output, with a seeded dO; per-kernel split from events is not possible
+def time_backward(layer, iters: int, warmup: int = 2, with_lse: bool = True):
+    """Median time of one backward call on the layer's route and output, with
+    a seeded dO: het_attn_backward_lse given the rows' LSE that
+    het_attn_forward_lse wrote (with_lse), else het_attn_backward, which
+    computes the LSE itself.  Per-kernel split from events is not possible
     inside one call, so only the whole call is timed here."""
     import torch
     het, w = layer.het, layer.w
@@ -221,15 +223,25 @@ def time_backward(layer, iters: int, warmup: int = 2):
     dq, dk, dv = (torch.empty_like(layer.q) for _ in range(3))
     ws_n = int(layer.lib.het_attn_backward_workspace_bytes(ctypes.byref(layer.shape)))
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
-    layer.route(); layer.local(); layer.dense()
+    lse = torch.empty((w.batch, w.heads, w.n_tokens), dtype=torch.float32, device="cuda")
+    layer.route()
+    st = layer.lib.het_attn_forward_lse(*layer.args[:6], lse.data_ptr(), *layer.args[6:])
+    if st != 0:
+        raise het.HetAttnError(st, "het_attn_forward_lse")
 
     def call():
-        st = layer.lib.het_attn_backward(ctypes.byref(layer.shape), layer.q.data_ptr(), layer.k.data_ptr(),
-                                         layer.v.data_ptr(), ctypes.byref(layer.rs), layer.o.data_ptr(),
-                                         dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                         ws.data_ptr(), ws_n, layer.stream)
+        if with_lse:
+            st = layer.lib.het_attn_backward_lse(ctypes.byref(layer.shape), layer.q.data_ptr(), layer.k.data_ptr(),
+                                                 layer.v.data_ptr(), ctypes.byref(layer.rs), layer.o.data_ptr(),
+                                                 dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                                 dv.data_ptr(), ws.data_ptr(), ws_n, layer.stream)
+        else:
+            st = layer.lib.het_attn_backward(ctypes.byref(layer.shape), layer.q.data_ptr(), layer.k.data_ptr(),
+                                             layer.v.data_ptr(), ctypes.byref(layer.rs), layer.o.data_ptr(),
+                                             dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                             ws.data_ptr(), ws_n, layer.stream)
         if st != 0:
-            raise het.HetAttnError(st, "het_attn_backward")
+            raise het.HetAttnError(st, "het_attn_backward" + ("_lse" if with_lse else ""))
 
     for _ in range(warmup):
         call()
@@ -475,8 +487,10 @@ def main():
 
     if not args.no_backward:
         bms = time_backward(layer, max(5, args.steps // 5))
+        bms_re = time_backward(layer, max(5, args.steps // 5), with_lse=False)
         bflop = 2.5 * eff_flop  # five products (S, dP, dV, dQ, dK) against the forward's two
-        out["backward"] = {"ms_median": round(bms, 4), "algorithmic_flop": bflop,
+        out["backward"] = {"ms_median": round(bms, 4), "lse": "from het_attn_forward_lse",
+                           "ms_median_lse_recomputed": round(bms_re, 4), "algorithmic_flop": bflop,
                            "TFLOPs": round(bflop / (bms * 1e-3) / 1e12, 2),
                            "frac_bf16_peak": round(bflop / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         log(f"[bench] backward: {out['backward']}")

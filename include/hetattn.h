@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define HETATTN_ABI_VERSION 2
+#define HETATTN_ABI_VERSION 3
 
 typedef enum {
     HET_OK = 0,
@@ -200,6 +200,19 @@ int het_attn_local(const het_attn_shape *shape, const void *q, const void *k, co
                    const het_route *route, void *o, void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/* het_attn_forward that also writes, for the gradient, the log-sum-exp of
+ * every row's softmax ([HetA §3.1.1 Eqs. 2-3] over the row's key set, the
+ * route held fixed as in het_attn_backward):
+ *   lse[(b * heads + h) * N + i] = log2( sum_j 2^(scale * log2(e) * q_i.k_j) ),
+ * j over the row's keys: all N for m_i = 0, the 3D window for m_i = 1.
+ *   lse      device, B * heads * N fp32, written once per row; must not
+ *            overlap q, k, v or o.  NULL is HET_ERR_INVALID_ARG.
+ * The other arguments and rules are het_attn_forward's; o is identical to
+ * het_attn_forward's.  bf16 only (fp32 inputs: HET_ERR_UNSUPPORTED). */
+int het_attn_forward_lse(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                         const het_route *route, void *o, float *lse, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
 /* Device workspace het_attn_backward needs for this shape, in bytes:
  * 2 * B * heads * N fp32 values (row statistics) plus 4 * 1024 * 256 fp32
  * values (partial statistics of the dense rows), and for bf16 inputs
@@ -226,6 +239,15 @@ size_t het_attn_backward_workspace_bytes(const het_attn_shape *shape);
 int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k, const void *v,
                       const het_route *route, const void *o, const void *dout, void *dq, void *dk,
                       void *dv, void *workspace, size_t workspace_bytes, void *stream);
+
+/* het_attn_backward given the row LSE that het_attn_forward_lse wrote for the
+ * same q, k, v and route (device, read only, must not overlap dq, dk, dv or
+ * the workspace; NULL is HET_ERR_INVALID_ARG): the rows' statistics are not
+ * computed again.  Same results as het_attn_backward, same workspace.
+ * bf16 only (fp32 inputs: HET_ERR_UNSUPPORTED). */
+int het_attn_backward_lse(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                          const het_route *route, const void *o, const void *dout, const float *lse, void *dq,
+                          void *dk, void *dv, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,8 @@ this module only marshals numpy arrays through ctypes.  Functions:
   all N keys, local rows use Eq. 3 over the 3D window ([HetA §3.1.1]).
 * :func:`forward`        -- :func:`attend_rows` over every token.
 * :func:`attention_weights` -- the softmax weights of one (row, head).
+* :func:`row_lse`        -- log of the softmax normaliser of chosen rows, the
+  statistic the gradient of the layer reuses.
 
 Parity pins for every function are in ``tests/test_oracle_*.py``.
 """
@@ -70,6 +72,8 @@ def _load():
                                            ctypes.c_double, P, P, ctypes.c_long, P, i]
         lib.oracle_attention_weights.argtypes = [P, P, i, i, i, i, i, i, i, i, i, i,
                                                  ctypes.c_double, P, ctypes.c_long, i, P]
+        lib.oracle_row_lse.argtypes = [P, P, i, i, i, i, i, i, i, i, i, i,
+                                       ctypes.c_double, P, P, ctypes.c_long, P, i]
         lib.oracle_route_uniform.argtypes = [i, i, ctypes.c_double, P, P, P, P]
         lib.oracle_attend_backward.argtypes = [P, P, P, P, i, i, i, i, i, i, i, i, i, i,
                                                ctypes.c_double, P, P, P, P, i]
@@ -87,7 +91,7 @@ def _load():
         for fn in (lib.oracle_route_top_rho, lib.oracle_route_mean_std, lib.oracle_window_axis,
                    lib.oracle_attend_rows, lib.oracle_attention_weights, lib.oracle_route_swap,
                    lib.oracle_window_axis_cut, lib.oracle_route_uniform, lib.oracle_route_random,
-                   lib.oracle_attend_backward, lib.oracle_attend_backward_dq_rows):
+                   lib.oracle_attend_backward, lib.oracle_attend_backward_dq_rows, lib.oracle_row_lse):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -237,6 +241,25 @@ def forward(q, k, v, grid, window, scale, mask, nthreads: int = 0,
     rows = np.arange(B * N, dtype=np.int64)
     return attend_rows(q, k, v, grid, window, scale, mask, rows, nthreads,
                        border).reshape(B, N, H, D)
+
+
+def row_lse(q, k, grid, window, scale, mask, rows, nthreads: int = 0, border: str = "shift") -> np.ndarray:
+    """[len(rows), heads] (float64): log sum_j exp(scale * q.k_j) over each
+    row's key set, natural log, for rows = b*N + n."""
+    q, k = _as_f32(q), _as_f32(k)
+    B, N, H, D = q.shape
+    T, Hg, Wg = grid
+    if T * Hg * Wg != N or k.shape != q.shape:
+        raise ValueError("shape mismatch")
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, H), np.float64)
+    wt, wh, ww = window
+    rc = _load().oracle_row_lse(_ptr(q), _ptr(k), B, H, D, T, Hg, Wg, wt, wh, ww, _BORDER[border],
+                                float(scale), _ptr(mask), _ptr(rows), rows.size, _ptr(out), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_row_lse rejected its arguments (rc={rc})")
+    return out
 
 
 def attention_weights(q, k, grid, window, scale, mask, row: int, head: int,

@@ -337,10 +337,12 @@ int oracle_window_axis_cut(int S, int k, int pos, int *start, int *len)
 /* Softmax attention of one query over an explicit key list, in double:
  * s_j = scale * q.k_j, a_j = exp(s_j - max s) / sum exp(s - max s),
  * o = sum_j a_j v_j ([HetA §3.1.1 Eqs. 2-3]).  Subtracting the maximum only
- * keeps exp() in range; it does not change a_j. */
+ * keeps exp() in range; it does not change a_j.  lse_out, if given, gets
+ * log sum_j exp(s_j) = max s + log sum exp(s - max s), the log of the
+ * softmax's normaliser. */
 static void attend_one(const float *qrow, const float *kbase, const float *vbase,
                        long key_stride, int D, const int *keys, int nkeys,
-                       double scale, double *s, double *o, double *w_out)
+                       double scale, double *s, double *o, double *w_out, double *lse_out)
 {
     double smax = -INFINITY;
     for (int j = 0; j < nkeys; j++) {
@@ -355,6 +357,7 @@ static void attend_one(const float *qrow, const float *kbase, const float *vbase
         s[j] = exp(s[j] - smax);
         denom += s[j];
     }
+    if (lse_out) *lse_out = smax + log(denom);
     for (int d = 0; d < D; d++) o[d] = 0.0;
     for (int j = 0; j < nkeys; j++) {
         double a = s[j] / denom;
@@ -440,12 +443,57 @@ int oracle_attend_rows(const float *q, const float *k, const float *v,
                     const float *kb = k + b * N * tok_stride + (long)h * D;
                     const float *vb = v + b * N * tok_stride + (long)h * D;
                     attend_one(qrow, kb, vb, tok_stride, D, keys, nk, scale, s,
-                               out + (r * heads + h) * (long)D, NULL);
+                               out + (r * heads + h) * (long)D, NULL, NULL);
                 }
             }
         }
         free(keys);
         free(s);
+    }
+    return err ? -2 : 0;
+}
+
+int oracle_row_lse(const float *q, const float *k,
+                   int B, int heads, int D,
+                   int T, int Hg, int Wg, int wt, int wh, int ww, int border,
+                   double scale, const unsigned char *mask,
+                   const long *rows, long nrows, double *out, int nthreads)
+{
+    if (!q || !k || !mask || !rows || !out) return -1;
+    if (check_shape(B, heads, D, T, Hg, Wg, wt, wh, ww, border)) return -1;
+    const long N = (long)T * Hg * Wg;
+    for (long r = 0; r < nrows; r++)
+        if (rows[r] < 0 || rows[r] >= (long)B * N) return -1;
+    const long tok_stride = (long)heads * D;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel reduction(| : err)
+    {
+        int *keys = (int *)malloc(sizeof(int) * (size_t)N);
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        double *o = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!keys || !s || !o) {
+            err = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long r = 0; r < nrows; r++) {
+                long b = rows[r] / N, n = rows[r] % N;
+                int nk = key_set((int)n, mask[b * N + n], T, Hg, Wg, wt, wh, ww, border, keys);
+                for (int h = 0; h < heads; h++) {
+                    const float *qrow = q + (b * N + n) * tok_stride + (long)h * D;
+                    const float *kb = k + b * N * tok_stride + (long)h * D;
+                    attend_one(qrow, kb, NULL, tok_stride, D, keys, nk, scale, s, o, NULL,
+                               out + r * heads + h);
+                }
+            }
+        }
+        free(keys);
+        free(s);
+        free(o);
     }
     return err ? -2 : 0;
 }
@@ -473,7 +521,7 @@ int oracle_attention_weights(const float *q, const float *k,
     int nk = key_set((int)n, mask[b * N + n], T, Hg, Wg, wt, wh, ww, border, keys);
     const float *qrow = q + (b * N + n) * tok_stride + (long)head * D;
     const float *kb = k + b * N * tok_stride + (long)head * D;
-    attend_one(qrow, kb, NULL, tok_stride, D, keys, nk, scale, s, o, w);
+    attend_one(qrow, kb, NULL, tok_stride, D, keys, nk, scale, s, o, w, NULL);
     for (long j = 0; j < N; j++) weights[j] = 0.0;
     for (int j = 0; j < nk; j++) weights[keys[j]] = w[j];
     free(keys); free(s); free(w); free(o);

@@ -114,6 +114,16 @@ int oracle_attend_rows(const float *q, const float *k, const float *v,
                        double scale, const unsigned char *mask,
                        const long *rows, long nrows, double *out, int nthreads);
 
+/* Log-sum-exp of each listed row's scores over its key set (the same key
+ * sets as oracle_attend_rows): out[r * heads + h] = log sum_j exp(scale *
+ * q.k_j), natural log, double -- the log of the softmax's normaliser
+ * ([HetA §3.1.1 Eqs. 2-3]), which the gradient of the layer reuses. */
+int oracle_row_lse(const float *q, const float *k,
+                   int B, int heads, int D,
+                   int T, int Hg, int Wg, int wt, int wh, int ww, int border,
+                   double scale, const unsigned char *mask,
+                   const long *rows, long nrows, double *out, int nthreads);
+
 /* Same as oracle_attend_rows, but also returns the attention weights of one
  * (row, head) pair over all N tokens of the row's sample (zero outside the
  * key set).  Used to check support and normalisation. */

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.het_attn_abi_version() == het.ABI_VERSION == 2
+    assert lib.het_attn_abi_version() == het.ABI_VERSION == 3
     for st in range(5):
         assert het.status_string(st)
     assert het.status_string(99) == "unknown status"
@@ -259,3 +259,18 @@ def test_backward_argument_errors(lib):
     # workspace
     assert call(ws_bytes=ws_n - 1) == het.HET_ERR_WORKSPACE
     assert call(ws=None) == het.HET_ERR_WORKSPACE
+
+
+def test_lse_entry_points_argument_errors(lib):
+    """The forms that hand the rows' LSE from the forward to the backward: a
+    NULL LSE is an argument error, and fp32 inputs are not supported (both
+    found before any device call)."""
+    s = good_shape()
+    r = fake_route()
+    args = (ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(r), FAKE)
+    assert lib.het_attn_forward_lse(*args, None, None, 0, None) == het.HET_ERR_INVALID_ARG
+    assert lib.het_attn_backward_lse(*args, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == het.HET_ERR_INVALID_ARG
+    s32 = good_shape()
+    s32.dtype = het.HET_F32
+    args32 = (ctypes.byref(s32), FAKE, FAKE, FAKE, ctypes.byref(r), FAKE)
+    assert lib.het_attn_forward_lse(*args32, FAKE + 4096, None, 0, None) == het.HET_ERR_UNSUPPORTED

@@ -152,3 +152,76 @@ def test_backward_full_size_sampled(oracle_mod):
     av = np.abs(dv.astype(np.float64)).sum(axis=1)
     assert np.all(np.abs(sv - so) <= 4e-3 * av + 1e-3), float((np.abs(sv - so) / av).max())
     assert np.isfinite(dk).all() and np.isfinite(dv).all()
+
+
+LOG2E = 1.4426950408889634
+
+
+@pytest.mark.parametrize("grid,window,head_dim,rho", [
+    ((6, 10, 20), (3, 7, 7), 128, 0.3),
+    ((6, 10, 20), (3, 7, 7), 64, 0.0),
+    ((6, 10, 20), (3, 7, 7), 64, 1.0),
+    ((2, 13, 70), (3, 7, 7), 128, 0.25),   # the dK/dV pass takes the local queries itself
+    ((9, 3, 5), (3, 3, 3), 64, 0.4),
+])
+def test_forward_lse_and_backward_lse(oracle_mod, grid, window, head_dim, rho):
+    """het_attn_forward_lse writes the same O as het_attn_forward and each row's
+    log2-sum-exp (checked against the oracle's normaliser); het_attn_backward_lse
+    given it returns exactly what het_attn_backward computes on its own."""
+    import torch
+    w, q, k, v, dout, u = make_case(grid, 2, head_dim, "bf16", batch=2, seed=91 + grid[2] + int(10 * rho),
+                                    window=window)
+    r = gpu_route(u, w.grid, w.window, w.heads, w.head_dim, "bf16", rho=rho)
+    qg, kg, vg, dg = (to_gpu(x, "bf16") for x in (q, k, v, dout))
+    log(f"[lse] grid={grid} win={window} D={head_dim} rho={rho}")
+    o = het.forward(qg, kg, vg, r)
+    o2, lse = het.forward(qg, kg, vg, r, return_lse=True)
+    g_ref = het.backward(qg, kg, vg, r, o, dg)
+    g_lse = het.backward(qg, kg, vg, r, o2, dg, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    B, N, H = w.batch, w.n_tokens, w.heads
+    mask = r.mask.cpu().numpy()
+    ref = oracle_mod.row_lse(q, k, w.grid, w.window, w.softmax_scale, mask, np.arange(B * N))
+    ref = ref.reshape(B, N, H).transpose(0, 2, 1) * LOG2E
+    got = lse.cpu().numpy()
+    err = np.abs(got - ref)
+    log(f"  lse: max {err.max():.2e} mean {err.mean():.2e} (log2 units)")
+    # scores from the bf16-rounded pre-scaled query: a few 2^-9 relative
+    assert np.isfinite(got).all() and err.max() < 2e-2 and err.mean() < 2e-3
+    for name, a, b in zip(("dQ", "dK", "dV"), g_ref, g_lse):
+        assert torch.equal(a, b), name
+
+
+def test_lse_forms_full_size():
+    """Wan-1.3B shape: the backward given the forward's LSE equals the backward
+    that computes it (the same kernels produce the same statistics)."""
+    import torch
+    w = W.WORKLOADS["wan13b"]
+    q, k, v = W.make_qkv(w)
+    u = W.make_u(w)
+    dout = W.round_to_bf16(np.random.default_rng(78).standard_normal(q.shape).astype(np.float32))
+    r = gpu_route(u, w.grid, w.window, w.heads, w.head_dim, "bf16", rho=w.rho)
+    qg, kg, vg, dg = (to_gpu(x, "bf16") for x in (q, k, v, dout))
+    log(f"[lse] full size {w.name}")
+    o, lse = het.forward(qg, kg, vg, r, return_lse=True)
+    g_ref = het.backward(qg, kg, vg, r, o, dg)
+    g_lse = het.backward(qg, kg, vg, r, o, dg, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lse).all()
+    for name, a, b in zip(("dQ", "dK", "dV"), g_ref, g_lse):
+        assert torch.equal(a, b), name
+
+
+def test_lse_forms_reject_fp32_and_bad_lse():
+    import torch
+    w, q, k, v, dout, u = make_case((3, 4, 5), 1, 64, "f32", batch=1, seed=5, window=(3, 3, 3))
+    r = gpu_route(u, w.grid, w.window, w.heads, w.head_dim, "f32", rho=0.3)
+    qg, kg, vg = (to_gpu(x, "f32") for x in (q, k, v))
+    with pytest.raises(het.HetAttnError):
+        het.forward(qg, kg, vg, r, return_lse=True)
+    qb, kb, vb, db = (to_gpu(x, "bf16") for x in (q, k, v, dout))
+    o, lse = het.forward(qb, kb, vb, r, return_lse=True)
+    with pytest.raises(ValueError):
+        het.backward(qb, kb, vb, r, o, db, lse=lse[:, :, :-1].contiguous())
+    torch.cuda.synchronize()

@@ -202,3 +202,57 @@ def test_attend_rows_subset_matches_forward(oracle_mod):
     rows = np.array([0, 5, 255, 256, 400, 511])
     got = oracle_mod.attend_rows(q, k, v, grid, (3, 3, 3), 0.125, mask, rows)
     np.testing.assert_array_equal(got, full[rows])
+
+
+def brute_row_lse(q, k, grid, window, scale, mask):
+    """log sum_j exp(s_j) over the allowed keys of every row, [B, N, heads]."""
+    B, N, H, D = q.shape
+    out = np.zeros((B, N, H))
+    for b in range(B):
+        allowed = brute_allowed(grid, window, mask[b])
+        for h in range(H):
+            s = scale * (q[b, :, h, :].astype(np.float64) @ k[b, :, h, :].astype(np.float64).T)
+            s = np.where(allowed, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            out[b, :, h] = (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
+    return out
+
+
+@pytest.mark.parametrize("grid,window", [((2, 3, 4), (1, 3, 3)), ((4, 8, 8), (3, 7, 7)), ((3, 5, 6), (3, 5, 1))])
+def test_row_lse_matches_bruteforce(oracle_mod, grid, window):
+    """The log of each row's softmax normaliser over an independently built key mask."""
+    T, Hg, Wg = grid
+    N = T * Hg * Wg
+    B, H, D = 2, 2, 16
+    q, k, _ = rand_qkv(B, N, H, D, seed=40 + N)
+    mask = (np.random.default_rng(41).random((B, N)) >= 0.3).astype(np.uint8)
+    rows = np.arange(B * N)
+    got = oracle_mod.row_lse(q, k, grid, window, 0.3, mask, rows).reshape(B, N, H)
+    np.testing.assert_allclose(got, brute_row_lse(q, k, grid, window, 0.3, mask), rtol=1e-12, atol=1e-12)
+
+
+def test_row_lse_all_dense_equals_library_logsumexp(oracle_mod):
+    B, H, D, grid = 1, 3, 32, (3, 4, 5)
+    N = 60
+    q, k, _ = rand_qkv(B, N, H, D, seed=42)
+    mask = np.zeros((B, N), np.uint8)
+    got = oracle_mod.row_lse(q, k, grid, (3, 3, 3), 0.2, mask, np.arange(N)).reshape(N, H)
+    s = 0.2 * torch.einsum("nhd,mhd->hnm", torch.from_numpy(q[0]).double(), torch.from_numpy(k[0]).double())
+    np.testing.assert_allclose(got, torch.logsumexp(s, dim=2).T.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_row_lse_closed_forms(oracle_mod):
+    """Q = 0: every score is 0, so the LSE is the log of the key count (N for
+    a dense row, the window's size for a local one); a 1x1x1 window: the
+    query's score against its own key."""
+    B, H, D, grid = 1, 2, 8, (4, 8, 8)
+    N = 256
+    q, k, _ = rand_qkv(B, N, H, D, seed=43)
+    mask = np.ones((B, N), np.uint8)
+    mask[0, ::5] = 0
+    got = oracle_mod.row_lse(np.zeros_like(q), k, grid, (3, 5, 7), 0.7, mask, np.arange(N))
+    want = np.where(mask[0] == 0, np.log(N), np.log(3 * 5 * 7))
+    np.testing.assert_allclose(got, np.repeat(want[:, None], H, axis=1), rtol=1e-13)
+    own = oracle_mod.row_lse(q, k, grid, (1, 1, 1), 0.7, np.ones((B, N), np.uint8), np.arange(N))
+    np.testing.assert_allclose(own, 0.7 * np.einsum("nhd,nhd->nh", q[0].astype(np.float64), k[0].astype(np.float64)),
+                               rtol=1e-12, atol=1e-12)

@@ -28,7 +28,7 @@ HET_OK, HET_ERR_INVALID_ARG, HET_ERR_UNSUPPORTED, HET_ERR_WORKSPACE, HET_ERR_HIP
 HET_BF16, HET_F32 = 0, 1
 HET_TOP_RHO, HET_MEAN_STD, HET_UNIFORM = 0, 1, 2
 HET_BORDER_SHIFT, HET_BORDER_CUT = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 _BORDERS = {"shift": HET_BORDER_SHIFT, "cut": HET_BORDER_CUT}
 
 
@@ -77,6 +77,9 @@ _ATTN_ARGS = [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_
               ctypes.c_void_p]
 for _name in ("het_attn_forward", "het_attn_dense", "het_attn_local"):
     SIGNATURES[_name] = (ctypes.c_int, _ATTN_ARGS)
+SIGNATURES["het_attn_forward_lse"] = (ctypes.c_int, _ATTN_ARGS[:6] + [ctypes.c_void_p] + _ATTN_ARGS[6:])
+SIGNATURES["het_attn_backward_lse"] = (ctypes.c_int, SIGNATURES["het_attn_backward"][1][:7] + [ctypes.c_void_p]
+                                       + SIGNATURES["het_attn_backward"][1][7:])
 
 _lib = None
 
@@ -251,12 +254,14 @@ def workspace_bytes(shape: Shape) -> int:
 
 
 def forward(q, k, v, r: Route, scale: float | None = None, out=None, stream=None,
-            part: str = "both", border: str = "shift"):
+            part: str = "both", border: str = "shift", return_lse: bool = False):
     """Heterogeneous attention for contiguous [B, N, heads, D] CUDA tensors.
 
     part = "both" (het_attn_forward), "dense" (het_attn_dense: rows with
     m_i = 0 only) or "local" (het_attn_local: rows with m_i = 1 only).
-    border = "shift" (window shifted inside the grid) or "cut" (cut at it)."""
+    border = "shift" (window shifted inside the grid) or "cut" (cut at it).
+    return_lse (part "both", bf16): also return the rows' log-sum-exp,
+    [B, heads, N] fp32 in log2 units (het_attn_forward_lse), for backward()."""
     import torch
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
@@ -270,6 +275,17 @@ def forward(q, k, v, r: Route, scale: float | None = None, out=None, stream=None
     ws_n = workspace_bytes(shape)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device) if ws_n else None
     rs = r.as_struct()
+    if return_lse:
+        if part != "both":
+            raise ValueError("return_lse needs part='both'")
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        st = load_library().het_attn_forward_lse(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                 ctypes.byref(rs), out.data_ptr(), lse.data_ptr(),
+                                                 ws.data_ptr() if ws is not None else None, ws_n,
+                                                 _stream_handle(stream))
+        if st != HET_OK:
+            raise HetAttnError(st, "het_attn_forward_lse")
+        return out, lse
     name = {"both": "het_attn_forward", "dense": "het_attn_dense", "local": "het_attn_local"}[part]
     st = getattr(load_library(), name)(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                        ctypes.byref(rs), out.data_ptr(),
@@ -280,8 +296,12 @@ def forward(q, k, v, r: Route, scale: float | None = None, out=None, stream=None
     return out
 
 
-def backward(q, k, v, r: Route, o, dout, scale: float | None = None, stream=None, border: str = "shift"):
-    """(dQ, dK, dV) of forward(q, k, v, r) = o for dL/dO = dout (het_attn_backward)."""
+def backward(q, k, v, r: Route, o, dout, scale: float | None = None, stream=None, border: str = "shift",
+             lse=None):
+    """(dQ, dK, dV) of forward(q, k, v, r) = o for dL/dO = dout (het_attn_backward).
+
+    lse: the rows' log-sum-exp from forward(..., return_lse=True) for the same
+    inputs (het_attn_backward_lse: not computed again)."""
     import torch
     for t in (q, k, v, o, dout):
         if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
@@ -293,6 +313,17 @@ def backward(q, k, v, r: Route, o, dout, scale: float | None = None, stream=None
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     rs = r.as_struct()
+    if lse is not None:
+        if (not lse.is_cuda or lse.dtype != torch.float32 or not lse.is_contiguous()
+                or tuple(lse.shape) != (B, H, N)):
+            raise ValueError("lse must be a contiguous [B, heads, N] float32 CUDA tensor")
+        st = lib.het_attn_backward_lse(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                       ctypes.byref(rs), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws_n,
+                                       _stream_handle(stream))
+        if st != HET_OK:
+            raise HetAttnError(st, "het_attn_backward_lse")
+        return dq, dk, dv
     st = lib.het_attn_backward(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(rs),
                                o.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                ws.data_ptr(), ws_n, _stream_handle(stream))

@@ -221,7 +221,7 @@ enum Part { kBoth = 3, kDenseOnly = 1, kLocalOnly = 2 };
 
 int run_attention(const het_attn_shape *shape, const void *q, const void *k, const void *v,
                   const het_route *route, void *o, void *workspace, size_t workspace_bytes,
-                  void *stream, int parts) {
+                  void *stream, int parts, float *lse = nullptr) {
     Dims d;
     float scale;
     const het_status st = check_shape(shape, d, scale);
@@ -229,6 +229,7 @@ int run_attention(const het_attn_shape *shape, const void *q, const void *k, con
     if (!q || !k || !v || !o || !route || !route->mask || !route->dense_idx || !route->counts)
         return HET_ERR_INVALID_ARG;
     if (route->dense_count_host < -1 || route->dense_count_host > d.N) return HET_ERR_INVALID_ARG;
+    if (lse && shape->dtype != HET_BF16) return HET_ERR_UNSUPPORTED;
     const int cus = current_cu_count();
     if (cus <= 0) return HET_ERR_HIP;
     const size_t need = hetattn::dense_workspace_bytes((int)d.B, (int)d.H, (int)d.N, (int)d.D,
@@ -261,6 +262,14 @@ int run_attention(const het_attn_shape *shape, const void *q, const void *k, con
     a.dense_exact = route->dense_count_host >= 0;
     a.workspace = workspace;
     a.cu_count = cus;
+    if (lse) {
+        const size_t lse_bytes = (size_t)(d.B * d.H * d.N) * sizeof(float);
+        const size_t io_bytes = (size_t)(d.B * d.N * d.H * d.D) * 2;
+        const void *ins[4] = {q, k, v, o};
+        for (int j = 0; j < 4; ++j)
+            if (overlaps(lse, lse_bytes, ins[j], io_bytes)) return HET_ERR_INVALID_ARG;
+        a.lse_out = lse;
+    }
 
     hipStream_t s = (hipStream_t)stream;
     // The two kernels write disjoint rows of o (Eq. 13 with m in {0, 1}).
@@ -291,6 +300,13 @@ int het_attn_local(const het_attn_shape *shape, const void *q, const void *k, co
     return run_attention(shape, q, k, v, route, o, workspace, workspace_bytes, stream, kLocalOnly);
 }
 
+int het_attn_forward_lse(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                         const het_route *route, void *o, float *lse, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    if (!lse) return HET_ERR_INVALID_ARG;
+    return run_attention(shape, q, k, v, route, o, workspace, workspace_bytes, stream, kBoth, lse);
+}
+
 }  // extern "C"
 
 extern "C" {
@@ -302,9 +318,10 @@ size_t het_attn_backward_workspace_bytes(const het_attn_shape *shape) {
     return hetattn::backward_workspace_bytes((int)d.B, (int)d.H, (int)d.N, (int)d.D, shape->dtype == HET_BF16);
 }
 
-int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k, const void *v,
-                      const het_route *route, const void *o, const void *dout, void *dq, void *dk,
-                      void *dv, void *workspace, size_t workspace_bytes, void *stream) {
+// lse: the forward's row LSE (bf16 only), or null to compute it here.
+static int run_backward(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                        const het_route *route, const void *o, const void *dout, const float *lse, void *dq,
+                        void *dk, void *dv, void *workspace, size_t workspace_bytes, void *stream) {
     Dims d;
     float scale;
     const het_status st = check_shape(shape, d, scale);
@@ -324,6 +341,12 @@ int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k,
             if (overlaps(outs[i], bytes, ins[j], bytes)) return HET_ERR_INVALID_ARG;
         for (int j = i + 1; j < 3; ++j)
             if (overlaps(outs[i], bytes, outs[j], bytes)) return HET_ERR_INVALID_ARG;
+    }
+    const size_t lse_bytes = (size_t)(d.B * d.H * d.N) * sizeof(float);
+    if (lse) {
+        if (shape->dtype != HET_BF16) return HET_ERR_UNSUPPORTED;
+        for (int i = 0; i < 3; ++i)
+            if (overlaps(outs[i], bytes, lse, lse_bytes)) return HET_ERR_INVALID_ARG;
     }
     const size_t need =
         hetattn::backward_workspace_bytes((int)d.B, (int)d.H, (int)d.N, (int)d.D, shape->dtype == HET_BF16);
@@ -368,8 +391,26 @@ int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k,
         a.dv_part = parts + (size_t)(d.B * d.N * d.H * d.D);
     }
     a.cu_count = cus < hetattn::kBwdMaxLseGroups ? cus : hetattn::kBwdMaxLseGroups;
+    if (lse) {
+        if (overlaps(workspace, need, lse, lse_bytes)) return HET_ERR_INVALID_ARG;
+        a.lse = const_cast<float *>(lse);  // read only when given
+        a.lse_given = true;
+    }
     if (hetattn::launch_backward(a, (hipStream_t)stream) != hipSuccess) return HET_ERR_HIP;
     return HET_OK;
+}
+
+int het_attn_backward(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                      const het_route *route, const void *o, const void *dout, void *dq, void *dk,
+                      void *dv, void *workspace, size_t workspace_bytes, void *stream) {
+    return run_backward(shape, q, k, v, route, o, dout, nullptr, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+int het_attn_backward_lse(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                          const het_route *route, const void *o, const void *dout, const float *lse, void *dq,
+                          void *dk, void *dv, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!lse) return HET_ERR_INVALID_ARG;
+    return run_backward(shape, q, k, v, route, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

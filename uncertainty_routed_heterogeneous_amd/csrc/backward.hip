@@ -1658,8 +1658,11 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((bwd_prep_kernel<__bf16, D_>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
                            dim3(256), 0, stream, (const __bf16 *)a.o, (const __bf16 *)a.dout, a.dsum, rows, a.n,
                            a.heads);
-        hipError_t e = dense_units > 0 ? launch_dense_lse(fa, a.lse, stream) : hipSuccess;
-        if (e == hipSuccess) e = launch_local_lse(fa, a.lse, stream);
+        hipError_t e = hipSuccess;
+        if (!a.lse_given) {
+            if (dense_units > 0) e = launch_dense_lse(fa, a.lse, stream);
+            if (e == hipSuccess) e = launch_local_lse(fa, a.lse, stream);
+        }
         if (e == hipSuccess) e = launch_local_dq(fa, a.dout, a.lse, a.dsum, a.dq, stream);
         if (e != hipSuccess) return e;
         // Local part of dK/dV by key tiles over query bands when the tiles'

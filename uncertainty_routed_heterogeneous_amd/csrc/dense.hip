@@ -82,6 +82,7 @@ __device__ __forceinline__ int work_owner(int64_t W, int G, int64_t x) {
 // kLse: only the row statistics -- no P*V, no V tiles -- and the output is
 // LSE_i = m_i + log2(l_i) (log2 units of scale * q.k) in lse[(b*H + h)*N + i]
 // for the gradient of the layer; the stream-K pieces then publish (m, l) only.
+// !kLse: the output O, and the same LSE too when lse is not null.
 template <int D, bool kLse>
 __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
@@ -431,6 +432,9 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         if constexpr (!kLse) {
             if (kt0 == 0 && kt1 == n_kt) {
                 store_out(1.0f / l_tot);
+                // The row's LSE for the gradient, when asked for.
+                if (lse != nullptr && q_valid && half == 0)
+                    lse[((size_t)b * H + h) * N + tok] = m_ref + __builtin_log2f(l_tot);
                 continue;
             }
         }
@@ -568,6 +572,7 @@ __global__ __launch_bounds__(256) void dense_merge_kernel(
         if (slice == 0) lse[((size_t)b * H + h) * N + tok] = m_all + __builtin_log2f(l_all);
         return;
     }
+    if (lse != nullptr && slice == 0) lse[((size_t)b * H + h) * N + tok] = m_all + __builtin_log2f(l_all);
     const float inv_l = 1.0f / l_all;
     const int half = slice / NDB, db = slice % NDB;
     __bf16 *op = o + ((size_t)b * N + tok) * ((size_t)H * D) + (size_t)h * D;
@@ -785,16 +790,16 @@ hipError_t launch_dense(const AttnArgs &a, hipStream_t stream) {
         const dim3 gm((unsigned)units_sk_ub * (kDenseBM16 / merge_q));
         if (a.head_dim == 128) {
             hipLaunchKernelGGL((dense_bf16_kernel<128, false>), g1d, dim3(kDenseThreads16), 0, stream, q, k, v, o,
-                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, nullptr);
+                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, a.lse_out);
             if (units_sk_ub > 0)
                 hipLaunchKernelGGL((dense_merge_kernel<128, false>), gm, dim3(256), 0, stream, o, a.dense_idx,
-                                   a.counts, a.batch, a.n, a.heads, G, (const float *)ws_part, nullptr);
+                                   a.counts, a.batch, a.n, a.heads, G, (const float *)ws_part, a.lse_out);
         } else {
             hipLaunchKernelGGL((dense_bf16_kernel<64, false>), g1d, dim3(kDenseThreads16), 0, stream, q, k, v, o,
-                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, nullptr);
+                               a.dense_idx, a.counts, a.batch, a.n, a.heads, sl2, G, ws_part, a.lse_out);
             if (units_sk_ub > 0)
                 hipLaunchKernelGGL((dense_merge_kernel<64, false>), gm, dim3(256), 0, stream, o, a.dense_idx,
-                                   a.counts, a.batch, a.n, a.heads, G, (const float *)ws_part, nullptr);
+                                   a.counts, a.batch, a.n, a.heads, G, (const float *)ws_part, a.lse_out);
         }
     } else {
         const dim3 grid((a.max_dense + kDenseBM - 1) / kDenseBM, a.heads, a.batch);

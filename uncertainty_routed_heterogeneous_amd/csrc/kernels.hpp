@@ -50,6 +50,7 @@ struct AttnArgs {
     bool dense_exact;          // every sample has exactly max_dense dense tokens
     void *workspace;           // dense_workspace_bytes() bytes of device memory
     int cu_count;              // compute units of the device the launch runs on
+    float *lse_out = nullptr;  // bf16, optional: each written row's LSE, [batch][heads][n], log2 units
 };
 
 // Grid and window of the local kernels and the backward pass (query tiles of
@@ -82,6 +83,7 @@ struct BwdArgs {
     void *lse_part;    // dense_lse_workspace_bytes(kBwdMaxLseGroups) bytes of device memory
     float *dk_part, *dv_part;  // [batch, n, heads, head_dim] fp32 local parts (bf16 path)
     int cu_count;      // persistent workgroups of the statistics kernel (<= kBwdMaxLseGroups)
+    bool lse_given = false;  // bf16: lse holds the forward's row LSE; skip the statistics passes
 };
 
 // Largest effective window along w that the local kernel's key tiling holds.

@@ -309,13 +309,15 @@ struct BandGeom {
 // Extra operands of the statistics and gradient forms of the band kernel.
 struct BandGrad {
     const __bf16 *dout;  // kMode 2: dL/dO
-    float *lse;          // kMode 1: written; kMode 2: read ([b][h][n], log2 units)
+    float *lse;          // kMode 1: written; kMode 0: written when not null; kMode 2: read
+                         // ([b][h][n], log2 units)
     const float *dsum;   // kMode 2: D_i = dO_i . O_i ([b][h][n])
     __bf16 *dq;          // kMode 2: dQ rows of the local tokens
     float scale;         // kMode 2: softmax scale
 };
 
-// kMode 0: the layer's output O for the local tokens.
+// kMode 0: the layer's output O for the local tokens (and their LSE when
+//          gr.lse is given).
 // kMode 1: only the row statistics: LSE_i = m_i + log2(l_i) of each local
 //          row (no V, no P*V), for the gradient of the layer.
 // kMode 2: dQ of the local rows given their LSE and D (the gradient, with
@@ -640,7 +642,10 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
         if (half == 0) gr.lse[row_bh + tok] = m_run + __builtin_log2f(l_tot);
         return;
     }
-    const float mul = kMode == 2 ? gr.scale : 1.0f / half_pair_sum(l_part);
+    const float l_tot = half_pair_sum(l_part);
+    // kMode 0: the row's LSE for the gradient, when asked for.
+    if (kMode == 0 && gr.lse != nullptr && half == 0) gr.lse[row_bh + tok] = m_run + __builtin_log2f(l_tot);
+    const float mul = kMode == 2 ? gr.scale : 1.0f / l_tot;
     __bf16 *op = (kMode == 2 ? gr.dq : o) + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -715,7 +720,7 @@ hipError_t launch_band(const AttnArgs &a, const LocalGeom &g, const BandGrad &gr
 hipError_t launch_local(const AttnArgs &a, hipStream_t stream) {
     const LocalGeom g = local_geom(a);
     if (kLocalQX + g.lw - 1 > 32) return hipErrorInvalidValue;  // rejected earlier by the ABI layer
-    if (a.bf16) return launch_band<0>(a, g, BandGrad{}, stream);
+    if (a.bf16) return launch_band<0>(a, g, BandGrad{nullptr, a.lse_out, nullptr, nullptr, 0.0f}, stream);
     const int units = a.batch * a.heads * g.T * g.tiles_y * g.tiles_x;
     const dim3 grid((units + 7) / 8 * 8);
     const float sl2 = a.scale * kLog2e;
