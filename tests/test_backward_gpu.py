@@ -193,6 +193,33 @@ def test_forward_lse_and_backward_lse(oracle_mod, grid, window, head_dim, rho):
         assert torch.equal(a, b), name
 
 
+@pytest.mark.parametrize("router,border", [("mean_std", "shift"), ("top_rho", "cut")])
+def test_lse_forms_other_routes_and_border(oracle_mod, router, border):
+    """Dense counts unknown to the host (mean-std threshold: the merge of the
+    dense kernel's split units runs over device-side counts) and the cut
+    border: the forward's LSE against the oracle, the backward given it
+    against the oracle's gradients."""
+    import torch
+    w, q, k, v, dout, u = make_case((6, 10, 20), 2, 128, "bf16", batch=2, seed=97, window=(3, 7, 9),
+                                    u_kind="lognormal")
+    r = (gpu_route(u, w.grid, w.window, w.heads, w.head_dim, "bf16", c=0.9) if router == "mean_std"
+         else gpu_route(u, w.grid, w.window, w.heads, w.head_dim, "bf16", rho=0.2))
+    qg, kg, vg, dg = (to_gpu(x, "bf16") for x in (q, k, v, dout))
+    log(f"[lse] {router} border={border}")
+    o, lse = het.forward(qg, kg, vg, r, return_lse=True, border=border)
+    grads = het.backward(qg, kg, vg, r, o, dg, lse=lse, border=border)
+    torch.cuda.synchronize()
+    B, N, H = w.batch, w.n_tokens, w.heads
+    mask = r.mask.cpu().numpy()
+    ref = oracle_mod.row_lse(q, k, w.grid, w.window, w.softmax_scale, mask, np.arange(B * N), border=border)
+    err = np.abs(lse.cpu().numpy() - ref.reshape(B, N, H).transpose(0, 2, 1) * LOG2E)
+    log(f"  lse: max {err.max():.2e} mean {err.mean():.2e} (log2 units)")
+    assert err.max() < 2e-2 and err.mean() < 2e-3
+    refs = oracle_mod.backward(q, k, v, dout, w.grid, w.window, w.softmax_scale, mask, border=border)
+    for name, g, rf in zip(("dQ", "dK", "dV"), grads, refs):
+        rel_check(g.float().cpu().numpy(), rf, "bf16", f"{router} {border} {name}")
+
+
 def test_lse_forms_full_size():
     """Wan-1.3B shape: the backward given the forward's LSE equals the backward
     that computes it (the same kernels produce the same statistics)."""
