@@ -381,7 +381,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(the layer shards by (sample, head) with no collectives; see DESIGN.md)",
+              "(the layer shards by (sample, head) with no collectives between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
