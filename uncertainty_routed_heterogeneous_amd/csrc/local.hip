@@ -447,10 +447,21 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     }
     const __bf16 *kbase = k + (size_t)b * N * tok_stride + (size_t)h * D;
     const __bf16 *vbase = v + (size_t)b * N * tok_stride + (size_t)h * D;
-    // Band bi -> LDS.  The descriptors end at token N of this sample, so a
-    // second band row past the grid reads zeros (its slots are masked).
-    auto dma_band = [&](int bi, __bf16 *Kd, __bf16 *Vd) HET_INLINE {
-        const int f = F0 + bi / nb_f, yy0 = uy0 + (bi % nb_f) * rpb;
+    // Bands go (frame, row of bands) in order; (c_f, c_r) is the band being
+    // computed and (d_f, d_r) the next one to fetch, advanced step by step
+    // (no division in the loop).
+    int c_f = F0, c_r = 0, d_f = F0, d_r = 0;
+    auto next_band = [&](int &f, int &r) HET_INLINE {
+        if (++r == nb_f) {
+            r = 0;
+            ++f;
+        }
+    };
+    // The next band -> LDS.  The descriptors end at token N of this sample,
+    // so a second band row past the grid reads zeros (its slots are masked).
+    auto dma_band = [&](__bf16 *Kd, __bf16 *Vd) HET_INLINE {
+        const int f = d_f, yy0 = uy0 + d_r * rpb;
+        next_band(d_f, d_r);
         const int tok0 = (f * g.Hg + yy0) * g.Wg + ux0;
         const uint32_t bytes = (uint32_t)((N - tok0) * (int)tok_stride) * 2u;
         const __bf16 *kp = kbase + (size_t)tok0 * tok_stride, *vp = vbase + (size_t)tok0 * tok_stride;
@@ -482,8 +493,9 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
         // band bi-1, whose buffers the next DMA refills.
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
-        if (bi + 1 < n_bands) dma_band(bi + 1, Kn, Vn);
-        const int f = F0 + bi / nb_f, yy0 = uy0 + (bi % nb_f) * rpb;
+        if (bi + 1 < n_bands) dma_band(Kn, Vn);
+        const int f = c_f, yy0 = uy0 + c_r * rpb;
+        next_band(c_f, c_r);
         if (!active || f < t0 || f >= t1) return;
         // Register i holds slot 8(i/4) + 4*half + i%4 of the block: box row
         // (i/4 >= 2 && SR == 16), column 8*((i/4) % (SR/8)) + 4*half + i%4;
@@ -630,7 +642,7 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
         }
     };
 
-    dma_band(0, Kb0, Vb0);
+    dma_band(Kb0, Vb0);
     for (int bi = 0; bi < n_bands; bi += 2) {
         step(bi, Kb0, Vb0, Kb1, Vb1);
         if (bi + 1 < n_bands) step(bi + 1, Kb1, Vb1, Kb0, Vb0);
