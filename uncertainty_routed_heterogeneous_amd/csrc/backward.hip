@@ -1409,12 +1409,16 @@ __global__ __launch_bounds__(512) void bwd_dkdv_local_band_kernel(BwdArgs a, Loc
         dma_voff[j] = c < C ? 2 * ((rr * g.Wg + c) * tok_stride + 8 * ((lane % kCpr) ^ swz<D>(R))) : 0x7ffffff0;
     }
     const __bf16 *qbase = (const __bf16 *)a.q + sample, *gbase = (const __bf16 *)a.dout + sample;
-    auto band_tok0 = [&](int bi) HET_INLINE -> int {
-        const int f = pt0 + bi / nb_f, y0 = py0 + 2 * (bi % nb_f);
-        return (f * g.Hg + y0) * g.Wg + px0;
+    // A band is named by its frame f and its row of bands rb (box rows
+    // py0 + 2 rb and the next); the loop advances both by counters.
+    auto next_band = [&](int &f, int &rb) HET_INLINE {
+        if (++rb == nb_f) {
+            rb = 0;
+            ++f;
+        }
     };
-    auto issue_dma = [&](HET_LDS char *wr, int bi) HET_INLINE {
-        const int tok0 = band_tok0(bi);
+    auto issue_dma = [&](HET_LDS char *wr, int f, int rb) HET_INLINE {
+        const int tok0 = (f * g.Hg + py0 + 2 * rb) * g.Wg + px0;
         const uint32_t bytes = (uint32_t)(N - tok0) * (uint32_t)tok_stride * 2u;
         const __bf16 *qp = qbase + (size_t)tok0 * tok_stride, *gp = gbase + (size_t)tok0 * tok_stride;
 #pragma unroll
@@ -1434,9 +1438,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_local_band_kernel(BwdArgs a, Loc
     const int rec_cw = tile_cw(rec_g);
     const uint8_t *mb = a.mask + (size_t)b * N;
     float r_lse = 0.0f, r_d = 0.0f;
-    auto load_rec = [&](int bi) HET_INLINE {
+    auto load_rec = [&](int f, int rb) HET_INLINE {
         if (tid < 128) {
-            const int f = pt0 + bi / nb_f, y = py0 + 2 * (bi % nb_f) + (rec_j >> 4);
+            const int y = py0 + 2 * rb + (rec_j >> 4);
             const int c = rec_cw + (rec_j & 15);
             const bool in_box = y <= py1 && c < C;
             const int tk = in_box ? (f * g.Hg + y) * g.Wg + px0 + c : 0;
@@ -1455,8 +1459,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_local_band_kernel(BwdArgs a, Loc
     const uint32_t rec_lane = (grp * 32 + 4 * half) * 4;           // + buffer, 8*(i/4) slots
     // Window test of register i (slot 8(i/4) + 4*half + i%4): the band's
     // frame and the slot's row and column against this key's intervals.
-    auto in_win = [&](int bi, int i) HET_INLINE -> bool {
-        const int f = pt0 + bi / nb_f, y = py0 + 2 * (bi % nb_f) + (i >> 3);
+    auto in_win = [&](int f, int rb, int i) HET_INLINE -> bool {
+        const int y = py0 + 2 * rb + (i >> 3);
         const int x = px0 + cw + 8 * ((i >> 2) & 1) + 4 * half + (i & 3);
         return f >= it0 && f <= it1 && y >= iy0 && y <= iy1 && x >= ix0 && x <= ix1;
     };
@@ -1498,7 +1502,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_local_band_kernel(BwdArgs a, Loc
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto compute_p = [&](const HET_LDS char *rd, int bi, int cur, int pb) HET_INLINE {
+    auto compute_p = [&](const HET_LDS char *rd, int bf, int brb, int cur, int pb) HET_INLINE {
         block(rd, 0, kG - kQ, [&](const f32x16 &sc, bf16x8(&pf)[2]) HET_INLINE {
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
@@ -1511,7 +1515,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_local_band_kernel(BwdArgs a, Loc
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * g4 + e], sl2, -l4[e]));
-                        p[e] = in_win(bi, 4 * g4 + e) ? pe : 0.0f;
+                        p[e] = in_win(bf, brb, 4 * g4 + e) ? pe : 0.0f;
                     }
                     wp[2 * g2] = pack_bf16x2(p[0], p[1]);
                     wp[2 * g2 + 1] = pack_bf16x2(p[2], p[3]);
@@ -1544,21 +1548,23 @@ __global__ __launch_bounds__(512) void bwd_dkdv_local_band_kernel(BwdArgs a, Loc
 
     // Iteration r: K side on band r, V side on band r-1 (three band
     // buffers, two P buffers, records three deep, one barrier per band).
-    issue_dma(lds + kQ, 0);
-    load_rec(0);
+    issue_dma(lds + kQ, pt0, 0);
+    load_rec(pt0, 0);
     store_rec(0);
     int cur = 0;
+    int c_f = pt0, c_rb = 0, n_f = pt0, n_rb = 0;  // bands r and r + 1
+    next_band(n_f, n_rb);
     for (int r = 0; r <= n_bands; ++r) {
         const int nxt = cur == 2 ? 0 : cur + 1, prv = cur == 0 ? 2 : cur - 1;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // band r, its records and P of band r-1 in LDS; band r-2 done
         auto iter = [&](HET_LDS char *__restrict__ wr, const HET_LDS char *__restrict__ rd) HET_INLINE {
             if (r + 1 < n_bands) {
-                issue_dma(wr, r + 1);
-                load_rec(r + 1);
+                issue_dma(wr, n_f, n_rb);
+                load_rec(n_f, n_rb);
             }
             if (role_p) {
-                if (r < n_bands) compute_p(rd, r, cur, r & 1);
+                if (r < n_bands) compute_p(rd, c_f, c_rb, cur, r & 1);
             } else if (r > 0) {
                 compute_ds(rd, prv, (r - 1) & 1);
             }
@@ -1566,6 +1572,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_local_band_kernel(BwdArgs a, Loc
         iter(lds + kQ + nxt * kBufB, lds + kQ + (role_p ? cur : prv) * kBufB);
         if (r + 1 < n_bands) store_rec(nxt);
         cur = nxt;
+        next_band(c_f, c_rb);
+        next_band(n_f, n_rb);
     }
 
     // fp32 partials: dV (K side) and dK without the scale (V side).
