@@ -275,30 +275,35 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
 }
 
 // ------------------------------------------------------------ bf16 path ----
-// One workgroup = kBandWaves waves = 2 query frames (t, t+1) x kBandNW
-// x-tiles of QY (h) x QX (w) = 32 queries, all on the rows ybase ..
-// ybase+QY-1 (QY = 4 or 8, chosen per window: the tile whose key box takes
-// the fewest 32-key blocks per frame).  The
-// tiles of a workgroup share one key box: the frames [F0, F1) that the two
-// frames' windows cover x ny rows x C columns (the union of the tiles' column
-// windows).  The box goes through LDS in bands of rpb = 32/SR rows of one
+// One workgroup = kBandWaves waves = NF query frames x NW x-tiles of QY (h)
+// x QX (w) = 32 queries, all on the rows ybase .. ybase+QY-1 (QY = 4 or 8,
+// chosen per window: the tile whose key box takes the fewest 32-key blocks
+// per frame).  The forward and statistics forms take one frame and 8
+// x-tiles, so that every wave has work in every band; the gradient form
+// takes two frames (t, t+1) and 4 x-tiles, whose smaller box keeps its
+// buffers' offsets within the LDS instructions' immediates.  The tiles of a
+// workgroup share one key box: the frames [F0, F1) that the frames' windows
+// cover x ny rows x C columns (the union of the tiles' column windows).  The box goes through LDS in bands of rpb = 32/SR rows of one
 // frame (one MFMA key block per wave and band), double-buffered: the DMA of
 // band i+1 runs while the waves work on band i.  Every K/V row of the box is
 // read from L2 once per workgroup instead of once per tile.  A wave takes
 // from each band the SR columns of its own tile's box (clamped at the edge of
 // the workgroup box; such slots are masked) and skips bands outside its
 // frame's window.
-constexpr int kBandNW = 4;
-constexpr int kBandWaves = 2 * kBandNW;
+constexpr int kBandWaves = 8;
+// x-tiles per workgroup (NW) of the band kernel in form kMode; the
+// workgroup's query frames are kBandWaves / NW.
+template <int kMode>
+constexpr int band_nw() { return kMode == 2 ? 4 : 8; }
 
-template <int D, int SR, int QX>
+template <int D, int SR, int QX, int NW>
 struct BandGeom {
     static constexpr int rpb = 32 / SR;                          // box rows per band
     static constexpr int kCpr = D / 8;                           // 16-byte chunks per token row
     static constexpr int kTokPerLoad = 64 / kCpr;                // token rows per wave DMA (1 KB)
     static constexpr int kMaxLw = SR == 16 ? 16 - QX + 1 : kLocalMaxWinW;
     // LDS rows per box row: the widest workgroup box, in whole DMA loads.
-    static constexpr int kCb = (kBandNW * QX + kMaxLw - 1 + kTokPerLoad - 1) / kTokPerLoad * kTokPerLoad;
+    static constexpr int kCb = (NW * QX + kMaxLw - 1 + kTokPerLoad - 1) / kTokPerLoad * kTokPerLoad;
     static constexpr int kBandRows = rpb * kCb;
     static constexpr int kLoads = kBandRows / kTokPerLoad;      // DMA loads per tensor and band
     static constexpr int kLoadsPerWave = (kLoads + kBandWaves - 1) / kBandWaves;
@@ -328,9 +333,10 @@ template <int D, int SR, int QY, int kMode>
 __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const uint8_t *__restrict__ mask, int N, int H, float scale_log2, LocalGeom g,
-    int n_units, int x_blocks, int t_pairs, BandGrad gr) {
+    int n_units, int x_blocks, int t_groups, BandGrad gr) {
     constexpr int QX = 32 / QY;
-    using Bg = BandGeom<D, SR, QX>;
+    constexpr int NW = band_nw<kMode>(), NF = kBandWaves / NW;
+    using Bg = BandGeom<D, SR, QX, NW>;
     constexpr int rpb = Bg::rpb, NC = D / 16, NDB = D / 32;
     __shared__ __attribute__((aligned(1024))) __bf16 Kb0[Bg::kBufElems];
     __shared__ __attribute__((aligned(1024))) __bf16 Kb1[Bg::kBufElems];
@@ -344,8 +350,8 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     rest /= x_blocks;
     const int ty = rest % g.tiles_y;
     rest /= g.tiles_y;
-    const int tp = rest % t_pairs;
-    rest /= t_pairs;
+    const int tp = rest % t_groups;
+    rest /= t_groups;
     const int h = rest % H, b = rest / H;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -356,18 +362,18 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     const int ybase = ty * QY;
     const int uy0 = win_lo(ybase, g.wh, g.lh, g.Hg, g.cut);
     const int ny = win_hi(imin(ybase + QY - 1, g.Hg - 1), g.wh, g.lh, g.Hg, g.cut) - uy0;
-    const int xt0 = xb * kBandNW, xt1 = imin(xt0 + kBandNW, g.tiles_x) - 1;
+    const int xt0 = xb * NW, xt1 = imin(xt0 + NW, g.tiles_x) - 1;
     const int ux0 = win_lo(xt0 * QX, g.ww, g.lw, g.Wg, g.cut);
     const int C = win_hi(imin(xt1 * QX + QX - 1, g.Wg - 1), g.ww, g.lw, g.Wg, g.cut) - ux0;
-    const int tA = 2 * tp, tB = imin(tA + 1, g.T - 1);
+    const int tA = NF * tp, tB = imin(tA + NF - 1, g.T - 1);
     const int F0 = win_lo(tA, g.wt, g.lt, g.T, g.cut);
     const int F1 = win_hi(tB, g.wt, g.lt, g.T, g.cut);
     const int nb_f = (ny + rpb - 1) / rpb;
     const int n_bands = (F1 - F0) * nb_f;
 
     // This wave's tile and this lane's query.
-    const int xt = xt0 + wave % kBandNW;
-    const int t = tA + wave / kBandNW;
+    const int xt = xt0 + wave % NW;
+    const int t = tA + wave / NW;
     const bool wave_on = t < g.T && xt < g.tiles_x;
     const int xbase = xt * QX;
     const int y = ybase + col / QX, x = xbase + col % QX;
@@ -703,13 +709,14 @@ hipError_t launch_band(const AttnArgs &a, const LocalGeom &g, const BandGrad &gr
     gb.tiles_y = (a.grid_h + qy - 1) / qy;
     gb.tiles_x = (a.grid_w + qx - 1) / qx;
     const bool b16 = qx + g.lw - 1 <= 16;
-    const int x_blocks = (gb.tiles_x + kBandNW - 1) / kBandNW, t_pairs = (g.T + 1) / 2;
-    const int band_units = a.batch * a.heads * t_pairs * gb.tiles_y * x_blocks;
+    constexpr int NW = band_nw<kMode>(), NF = kBandWaves / NW;
+    const int x_blocks = (gb.tiles_x + NW - 1) / NW, t_groups = (g.T + NF - 1) / NF;
+    const int band_units = a.batch * a.heads * t_groups * gb.tiles_y * x_blocks;
     const dim3 bgrid((band_units + 7) / 8 * 8), bblock(64 * kBandWaves);
 #define HET_BAND_LAUNCH(D_, SR_, QY_)                                                                        \
     hipLaunchKernelGGL((local_band_kernel<D_, SR_, QY_, kMode>), bgrid, bblock, 0, stream, (const __bf16 *)a.q, \
                        (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, a.mask, a.n, a.heads, sl2, gb,  \
-                       band_units, x_blocks, t_pairs, gr)
+                       band_units, x_blocks, t_groups, gr)
     if (a.head_dim == 128) {
         if (qy == 4) {
             if (b16) HET_BAND_LAUNCH(128, 16, 4); else HET_BAND_LAUNCH(128, 32, 4);
