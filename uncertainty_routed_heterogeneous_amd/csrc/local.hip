@@ -279,9 +279,10 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
 // x QX (w) = 32 queries, all on the rows ybase .. ybase+QY-1 (QY = 4 or 8,
 // chosen per window: the tile whose key box takes the fewest 32-key blocks
 // per frame).  The forward and statistics forms take one frame and 8
-// x-tiles, so that every wave has work in every band; the gradient form
-// takes two frames (t, t+1) and 4 x-tiles, whose smaller box keeps its
-// buffers' offsets within the LDS instructions' immediates.  The tiles of a
+// x-tiles where that fills the waves about as well as 4, so that every wave
+// has work in every band; else, and always in the gradient form (whose
+// smaller box keeps its buffers' offsets within the LDS instructions'
+// immediates), two frames (t, t+1) and 4 x-tiles.  The tiles of a
 // workgroup share one key box: the frames [F0, F1) that the frames' windows
 // cover x ny rows x C columns (the union of the tiles' column windows).  The box goes through LDS in bands of rpb = 32/SR rows of one
 // frame (one MFMA key block per wave and band), double-buffered: the DMA of
@@ -291,10 +292,8 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
 // the workgroup box; such slots are masked) and skips bands outside its
 // frame's window.
 constexpr int kBandWaves = 8;
-// x-tiles per workgroup (NW) of the band kernel in form kMode; the
+// x-tiles per workgroup (NW): 8 (one query frame) or 4 (two frames); the
 // workgroup's query frames are kBandWaves / NW.
-template <int kMode>
-constexpr int band_nw() { return kMode == 2 ? 4 : 8; }
 
 template <int D, int SR, int QX, int NW>
 struct BandGeom {
@@ -329,13 +328,13 @@ struct BandGrad {
 //          the route held fixed): per band S^T = K Q^T and dP^T = V dO^T
 //          (K and V rows as A operands), P = exp2(S - LSE) inside the
 //          window, dS = P (dP - D), dQ^T += K^T dS^T (K read transposed).
-template <int D, int SR, int QY, int kMode>
+template <int D, int SR, int QY, int kMode, int NW>
 __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const uint8_t *__restrict__ mask, int N, int H, float scale_log2, LocalGeom g,
     int n_units, int x_blocks, int t_groups, BandGrad gr) {
     constexpr int QX = 32 / QY;
-    constexpr int NW = band_nw<kMode>(), NF = kBandWaves / NW;
+    constexpr int NF = kBandWaves / NW;
     using Bg = BandGeom<D, SR, QX, NW>;
     constexpr int rpb = Bg::rpb, NC = D / 16, NDB = D / 32;
     __shared__ __attribute__((aligned(1024))) __bf16 Kb0[Bg::kBufElems];
@@ -709,14 +708,29 @@ hipError_t launch_band(const AttnArgs &a, const LocalGeom &g, const BandGrad &gr
     gb.tiles_y = (a.grid_h + qy - 1) / qy;
     gb.tiles_x = (a.grid_w + qx - 1) / qx;
     const bool b16 = qx + g.lw - 1 <= 16;
-    constexpr int NW = band_nw<kMode>(), NF = kBandWaves / NW;
+    // Workgroup shape: one frame x 8 x-tiles, unless 4 x-tiles (two frames)
+    // leave clearly fewer waves without a tile (the one-frame shape gains
+    // about 5 % by keeping every wave busy in every band); the gradient form
+    // always takes 4.
+    auto filled = [&](int nw) { return (double)gb.tiles_x / (nw * ((gb.tiles_x + nw - 1) / nw)); };
+    const bool nw8 = kMode != 2 && filled(8) >= filled(4) - 0.05;
+    const int NW = nw8 ? 8 : 4, NF = kBandWaves / NW;
     const int x_blocks = (gb.tiles_x + NW - 1) / NW, t_groups = (g.T + NF - 1) / NF;
     const int band_units = a.batch * a.heads * t_groups * gb.tiles_y * x_blocks;
     const dim3 bgrid((band_units + 7) / 8 * 8), bblock(64 * kBandWaves);
-#define HET_BAND_LAUNCH(D_, SR_, QY_)                                                                        \
-    hipLaunchKernelGGL((local_band_kernel<D_, SR_, QY_, kMode>), bgrid, bblock, 0, stream, (const __bf16 *)a.q, \
-                       (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, a.mask, a.n, a.heads, sl2, gb,  \
-                       band_units, x_blocks, t_groups, gr)
+#define HET_BAND_LAUNCH_NW(D_, SR_, QY_, NW_)                                                                 \
+    hipLaunchKernelGGL((local_band_kernel<D_, SR_, QY_, kMode, NW_>), bgrid, bblock, 0, stream,               \
+                       (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, a.mask, \
+                       a.n, a.heads, sl2, gb, band_units, x_blocks, t_groups, gr)
+#define HET_BAND_LAUNCH(D_, SR_, QY_)                                 \
+    do {                                                              \
+        if constexpr (kMode != 2) {                                   \
+            if (nw8) HET_BAND_LAUNCH_NW(D_, SR_, QY_, 8);              \
+            else HET_BAND_LAUNCH_NW(D_, SR_, QY_, 4);                  \
+        } else {                                                      \
+            HET_BAND_LAUNCH_NW(D_, SR_, QY_, 4);                      \
+        }                                                             \
+    } while (0)
     if (a.head_dim == 128) {
         if (qy == 4) {
             if (b16) HET_BAND_LAUNCH(128, 16, 4); else HET_BAND_LAUNCH(128, 32, 4);
@@ -731,6 +745,7 @@ hipError_t launch_band(const AttnArgs &a, const LocalGeom &g, const BandGrad &gr
         }
     }
 #undef HET_BAND_LAUNCH
+#undef HET_BAND_LAUNCH_NW
     return hipGetLastError();
 }
 
