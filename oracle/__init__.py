@@ -21,6 +21,9 @@ this module only marshals numpy arrays through ctypes.  Functions:
 * :func:`attention_weights` -- the softmax weights of one (row, head).
 * :func:`row_lse`        -- log of the softmax normaliser of chosen rows, the
   statistic the gradient of the layer reuses.
+* :func:`backward`, :func:`backward_dq_rows`, :func:`backward_kv_rows` -- the
+  gradients of the layer with the route held fixed: all of dQ, dK, dV; dQ of
+  chosen rows; dK and dV of chosen keys and heads.
 
 Parity pins for every function are in ``tests/test_oracle_*.py``.
 """
@@ -79,6 +82,8 @@ def _load():
                                                ctypes.c_double, P, P, P, P, i]
         lib.oracle_attend_backward_dq_rows.argtypes = [P, P, P, P, i, i, i, i, i, i, i, i, i, i,
                                                        ctypes.c_double, P, P, ctypes.c_long, P, i]
+        lib.oracle_attend_backward_kv_rows.argtypes = [P, P, P, P, i, i, i, i, i, i, i, i, i, i,
+                                                       ctypes.c_double, P, P, ctypes.c_long, P, i, P, P, i]
         lib.oracle_route_random.argtypes = [i, i, ctypes.c_double, ctypes.c_ulonglong, ctypes.c_uint,
                                             ctypes.c_uint, P, P, P, P]
         lib.oracle_philox4x32_10.argtypes = [P, P, P]
@@ -91,7 +96,8 @@ def _load():
         for fn in (lib.oracle_route_top_rho, lib.oracle_route_mean_std, lib.oracle_window_axis,
                    lib.oracle_attend_rows, lib.oracle_attention_weights, lib.oracle_route_swap,
                    lib.oracle_window_axis_cut, lib.oracle_route_uniform, lib.oracle_route_random,
-                   lib.oracle_attend_backward, lib.oracle_attend_backward_dq_rows, lib.oracle_row_lse):
+                   lib.oracle_attend_backward, lib.oracle_attend_backward_dq_rows, lib.oracle_row_lse,
+                   lib.oracle_attend_backward_kv_rows):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -312,3 +318,28 @@ def backward_dq_rows(q, k, v, dout, grid, window, scale, mask, rows, nthreads: i
     if rc != 0:
         raise ValueError(f"oracle_attend_backward_dq_rows rejected its arguments (rc={rc})")
     return out
+
+
+def backward_kv_rows(q, k, v, dout, grid, window, scale, mask, rows, heads=None, nthreads: int = 0,
+                     border: str = "shift"):
+    """dL/dK and dL/dV of the listed keys (rows = b*N + j, each once) for the
+    listed heads (default: all): two float64 arrays [len(rows), len(heads), D]
+    (oracle_attend_backward_kv_rows)."""
+    q, k, v, dout = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
+    B, N, H, D = q.shape
+    T, Hg, Wg = grid
+    if T * Hg * Wg != N or any(x.shape != q.shape for x in (k, v, dout)):
+        raise ValueError("shape mismatch")
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    hsel = np.ascontiguousarray(np.arange(H) if heads is None else heads, dtype=np.int32)
+    dk = np.empty((rows.size, hsel.size, D), np.float64)
+    dv = np.empty((rows.size, hsel.size, D), np.float64)
+    wt, wh, ww = window
+    rc = _load().oracle_attend_backward_kv_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, D, T, Hg, Wg,
+                                                wt, wh, ww, _BORDER[border], float(scale), _ptr(mask),
+                                                _ptr(rows), rows.size, _ptr(hsel), hsel.size, _ptr(dk), _ptr(dv),
+                                                int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_attend_backward_kv_rows rejected its arguments (rc={rc})")
+    return dk, dv

@@ -669,3 +669,157 @@ int oracle_attend_backward_dq_rows(const float *q, const float *k, const float *
     return err ? -2 : 0;
 }
 
+
+/* Whether token j lies in the key set of token n of the same sample: every
+ * token for a dense row (mask 0), else the 3D window of n along each axis,
+ * shifted (border 0) or cut (border 1) exactly as key_set builds it. */
+static int key_in_set(int n, int j, unsigned char is_local, int T, int Hg, int Wg,
+                      int wt, int wh, int ww, int border)
+{
+    if (!is_local) return 1;
+    const int pos_n[3] = {n / (Hg * Wg), (n / Wg) % Hg, n % Wg};
+    const int pos_j[3] = {j / (Hg * Wg), (j / Wg) % Hg, j % Wg};
+    const int ext[3] = {T, Hg, Wg}, win[3] = {wt, wh, ww};
+    for (int ax = 0; ax < 3; ax++) {
+        int start, len;
+        if (border == 0) oracle_window_axis(ext[ax], win[ax], pos_n[ax], &start, &len);
+        else oracle_window_axis_cut(ext[ax], win[ax], pos_n[ax], &start, &len);
+        if (pos_j[ax] < start || pos_j[ax] >= start + len) return 0;
+    }
+    return 1;
+}
+
+/* The two statistics of one row that its key gradients need, over its key
+ * list: lse = log sum_j exp(s_j) with s_j = scale * q.k_j, and
+ * dsum = sum_j p_j dP_j with p_j = exp(s_j - lse) and dP_j = dout.v_j.
+ * s is scratch of nkeys doubles. */
+static void row_grad_stats(const float *qrow, const float *dorow, const float *kbase,
+                           const float *vbase, long key_stride, int D, const int *keys, int nkeys,
+                           double scale, double *s, double *lse, double *dsum)
+{
+    double smax = -INFINITY;
+    for (int j = 0; j < nkeys; j++) {
+        const float *krow = kbase + keys[j] * key_stride;
+        double qk = 0.0;
+        for (int d = 0; d < D; d++) qk += (double)qrow[d] * (double)krow[d];
+        s[j] = scale * qk;
+        if (s[j] > smax) smax = s[j];
+    }
+    double denom = 0.0;
+    for (int j = 0; j < nkeys; j++) denom += exp(s[j] - smax);
+    *lse = smax + log(denom);
+    double acc = 0.0;
+    for (int j = 0; j < nkeys; j++) {
+        const float *vrow = vbase + keys[j] * key_stride;
+        double dp = 0.0;
+        for (int d = 0; d < D; d++) dp += (double)dorow[d] * (double)vrow[d];
+        acc += exp(s[j] - *lse) * dp;
+    }
+    *dsum = acc;
+}
+
+int oracle_attend_backward_kv_rows(const float *q, const float *k, const float *v,
+                                   const float *dout, int B, int heads, int D,
+                                   int T, int Hg, int Wg, int wt, int wh, int ww, int border,
+                                   double scale, const unsigned char *mask,
+                                   const long *rows, long nrows, const int *hsel, int nh,
+                                   double *dk, double *dv, int nthreads)
+{
+    if (!q || !k || !v || !dout || !mask || !rows || !hsel || !dk || !dv || nh <= 0) return -1;
+    if (check_shape(B, heads, D, T, Hg, Wg, wt, wh, ww, border)) return -1;
+    const long N = (long)T * Hg * Wg;
+    for (int i = 0; i < nh; i++)
+        if (hsel[i] < 0 || hsel[i] >= heads) return -1;
+    for (long r = 0; r < nrows; r++) {
+        if (rows[r] < 0 || rows[r] >= (long)B * N) return -1;
+        for (long r2 = 0; r2 < r; r2++)
+            if (rows[r2] == rows[r]) return -1; /* each key listed once */
+    }
+    const long tok_stride = (long)heads * D;
+    for (long e = 0; e < nrows * nh * D; e++) {
+        dk[e] = 0.0;
+        dv[e] = 0.0;
+    }
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    /* needed[n] = 1 when row n of sample b holds a listed key in its key set;
+     * lse and dsum are that row's statistics (per selected head). */
+    unsigned char *needed = (unsigned char *)malloc((size_t)N);
+    double *lse = (double *)malloc(sizeof(double) * (size_t)N * nh);
+    double *dsum = (double *)malloc(sizeof(double) * (size_t)N * nh);
+    int err = (!needed || !lse || !dsum);
+    for (long b = 0; b < B && !err; b++) {
+        int any = 0;
+        for (long r = 0; r < nrows; r++) any |= rows[r] / N == b;
+        if (!any) continue;
+        /* Which rows of sample b see a listed key. */
+#pragma omp parallel for schedule(dynamic, 64)
+        for (long n = 0; n < N; n++) {
+            needed[n] = 0;
+            for (long r = 0; r < nrows && !needed[n]; r++)
+                if (rows[r] / N == b &&
+                    key_in_set((int)n, (int)(rows[r] % N), mask[b * N + n], T, Hg, Wg, wt, wh, ww, border))
+                    needed[n] = 1;
+        }
+        /* Their statistics, each over the row's whole key set. */
+#pragma omp parallel reduction(| : err)
+        {
+            int *keys = (int *)malloc(sizeof(int) * (size_t)N);
+            double *s = (double *)malloc(sizeof(double) * (size_t)N);
+            if (!keys || !s) {
+                err = 1;
+            } else {
+#pragma omp for schedule(dynamic, 1)
+                for (long n = 0; n < N; n++) {
+                    if (!needed[n]) continue;
+                    int nk = key_set((int)n, mask[b * N + n], T, Hg, Wg, wt, wh, ww, border, keys);
+                    for (int i = 0; i < nh; i++) {
+                        const long base = b * N * tok_stride + (long)hsel[i] * D;
+                        row_grad_stats(q + base + n * tok_stride, dout + base + n * tok_stride, k + base,
+                                       v + base, tok_stride, D, keys, nk, scale, s, lse + n * nh + i,
+                                       dsum + n * nh + i);
+                    }
+                }
+            }
+            free(keys);
+            free(s);
+        }
+        /* Each listed key sums over the rows that see it, in row order:
+         * dS_nj = p_nj (dP_nj - dsum_n), dK_j += scale dS_nj q_n,
+         * dV_j += p_nj dout_n. */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (long r = 0; r < nrows; r++) {
+            if (rows[r] / N != b) continue;
+            const long j = rows[r] % N;
+            for (long n = 0; n < N; n++) {
+                if (!needed[n] ||
+                    !key_in_set((int)n, (int)j, mask[b * N + n], T, Hg, Wg, wt, wh, ww, border))
+                    continue;
+                for (int i = 0; i < nh; i++) {
+                    const long base = b * N * tok_stride + (long)hsel[i] * D;
+                    const float *qrow = q + base + n * tok_stride, *dorow = dout + base + n * tok_stride;
+                    const float *krow = k + base + j * tok_stride, *vrow = v + base + j * tok_stride;
+                    double qk = 0.0, dp = 0.0;
+                    for (int d = 0; d < D; d++) {
+                        qk += (double)qrow[d] * (double)krow[d];
+                        dp += (double)dorow[d] * (double)vrow[d];
+                    }
+                    const double p = exp(scale * qk - lse[n * nh + i]);
+                    const double ds = p * (dp - dsum[n * nh + i]);
+                    double *dkr = dk + (r * nh + i) * (long)D, *dvr = dv + (r * nh + i) * (long)D;
+                    for (int d = 0; d < D; d++) {
+                        dkr[d] += scale * ds * (double)qrow[d];
+                        dvr[d] += p * (double)dorow[d];
+                    }
+                }
+            }
+        }
+    }
+    free(needed);
+    free(lse);
+    free(dsum);
+    return err ? -2 : 0;
+}

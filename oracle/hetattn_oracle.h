@@ -153,6 +153,20 @@ int oracle_attend_backward_dq_rows(const float *q, const float *k, const float *
                                    double scale, const unsigned char *mask,
                                    const long *rows, long nrows, double *dq, int nthreads);
 
+/* dL/dK and dL/dV of the listed key rows only (rows[r] = b*N + j, each listed
+ * once) for the listed heads hsel[0 .. nh-1], into dk[(r*nh + i)*D + d] and
+ * dv[(r*nh + i)*D + d]: the sums of oracle_attend_backward over every row n
+ * of sample b whose key set holds token j (all dense rows; the local rows
+ * whose 3D window contains j), each row's softmax taken over its whole key
+ * set: p_nj = exp(s_nj - lse_n), dS_nj = p_nj (dP_nj - sum_j' p_nj' dP_nj'),
+ * dK_j = scale * sum_n dS_nj q_n, dV_j = sum_n p_nj dout_n. */
+int oracle_attend_backward_kv_rows(const float *q, const float *k, const float *v,
+                                   const float *dout, int B, int heads, int D,
+                                   int T, int Hg, int Wg, int wt, int wh, int ww, int border,
+                                   double scale, const unsigned char *mask,
+                                   const long *rows, long nrows, const int *hsel, int nh,
+                                   double *dk, double *dv, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -131,3 +131,66 @@ def test_equal_keys_give_zero_dq(oracle_mod):
     mask = (rng.random((1, N)) < 0.5).astype(np.uint8)
     dq, _, _ = oracle_mod.backward(q, k, v, do, grid, window, 1.0, mask)
     assert np.abs(dq).max() < 1e-14
+
+
+@pytest.mark.parametrize("border", ["shift", "cut"])
+@pytest.mark.parametrize("grid,window", [((3, 4, 5), (3, 3, 3)), ((2, 5, 6), (1, 3, 5))])
+def test_kv_rows_match_torch_autograd(oracle_mod, border, grid, window):
+    """dK, dV of listed keys and heads against torch autograd through the
+    brute-force masked softmax (every key of both samples, heads reordered)."""
+    rng = np.random.default_rng(3 * sum(grid) + (border == "cut"))
+    N = int(np.prod(grid))
+    q, k, v, do = (rng.standard_normal((2, N, 3, 8)).astype(np.float32) for _ in range(4))
+    mask = (rng.random((2, N)) < 0.7).astype(np.uint8)
+    rows = rng.permutation(2 * N).astype(np.int64)
+    heads = [2, 0]
+    dk, dv = oracle_mod.backward_kv_rows(q, k, v, do, grid, window, 0.4, mask, rows, heads=heads, border=border)
+    _, rk, rv = torch_grads(q, k, v, do, grid, window, 0.4, mask, border)
+    rk = rk.reshape(2 * N, 3, 8)[rows][:, heads]
+    rv = rv.reshape(2 * N, 3, 8)[rows][:, heads]
+    np.testing.assert_allclose(dk, rk, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, rv, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("border", ["shift", "cut"])
+def test_kv_rows_equal_full_backward(oracle_mod, border):
+    """On a 1200-token grid with borders in every axis: the listed keys' rows
+    of the full backward, whichever sample and head."""
+    grid, window = (6, 10, 20), (3, 7, 9)
+    N = 1200
+    rng = np.random.default_rng(17 + (border == "cut"))
+    q, k, v, do = (rng.standard_normal((2, N, 2, 16)).astype(np.float32) for _ in range(4))
+    mask = (rng.random((2, N)) < 0.8).astype(np.uint8)
+    _, fk, fv = oracle_mod.backward(q, k, v, do, grid, window, 0.21, mask, border=border)
+    rows = np.array([0, 19, 180, 599, 1199, 1200, 1201, 1719, 2399, 1500], dtype=np.int64)
+    dk, dv = oracle_mod.backward_kv_rows(q, k, v, do, grid, window, 0.21, mask, rows, heads=[1], border=border)
+    np.testing.assert_allclose(dk[:, 0], fk.reshape(2 * N, 2, 16)[rows, 1], rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dv[:, 0], fv.reshape(2 * N, 2, 16)[rows, 1], rtol=1e-10, atol=1e-13)
+
+
+def test_kv_rows_closed_forms(oracle_mod):
+    """All keys equal and all values equal: every weight is 1/|key set| and
+    dP_j is the same for every key, so dS = 0, dK = 0 and dV_j = sum over the
+    rows that see j of dO_n / |key set of n|."""
+    grid, window = (2, 4, 4), (1, 3, 3)
+    N = 32
+    rng = np.random.default_rng(9)
+    q, do = (rng.standard_normal((1, N, 1, 8)).astype(np.float32) for _ in range(2))
+    k, v = (np.broadcast_to(rng.standard_normal((1, 1, 1, 8)).astype(np.float32), (1, N, 1, 8)).copy()
+            for _ in range(2))
+    mask = (rng.random((1, N)) < 0.5).astype(np.uint8)
+    rows = np.arange(N, dtype=np.int64)
+    dk, dv = oracle_mod.backward_kv_rows(q, k, v, do, grid, window, 1.0, mask, rows)
+    assert np.abs(dk).max() < 1e-13
+    allowed = allowed_matrix(grid, window, mask[0], "shift")
+    expect = (allowed / allowed.sum(axis=1, keepdims=True)).T @ do[0, :, 0, :].astype(np.float64)
+    np.testing.assert_allclose(dv[:, 0], expect, rtol=1e-12, atol=1e-14)
+
+
+def test_kv_rows_rejects_bad_lists(oracle_mod):
+    grid, window = (2, 3, 4), (1, 3, 3)
+    q = np.zeros((1, 24, 2, 4), np.float32)
+    mask = np.ones((1, 24), np.uint8)
+    for rows, heads in (([3, 3], None), ([24], None), ([-1], None), ([1], [2]), ([1], [])):
+        with pytest.raises(ValueError):
+            oracle_mod.backward_kv_rows(q, q, q, q, grid, window, 1.0, mask, np.array(rows), heads=heads)

@@ -49,6 +49,9 @@ MUTANTS = {
     "backward_drops_row_term": ("const double ds = s[j] * (w[j] - Dsum);", "const double ds = s[j] * w[j];"),
     "backward_dk_without_scale": ("dkr[d] += scale * ds * (double)qrow[d];", "dkr[d] += ds * (double)qrow[d];"),
     "backward_dv_uses_ds": ("dvr[d] += s[j] * (double)dorow[d];", "dvr[d] += ds * (double)dorow[d];"),
+    "kv_rows_window_far_edge_included": ("if (pos_j[ax] < start || pos_j[ax] >= start + len) return 0;",
+                                         "if (pos_j[ax] < start || pos_j[ax] > start + len) return 0;"),
+    "kv_rows_drops_row_term": ("const double ds = p * (dp - dsum[n * nh + i]);", "const double ds = p * dp;"),
     "router_count_truncated": ("floor((double)N * rho + 0.5)", "floor((double)N * rho)"),
     "random_largest_draws": ("for (long j = 0; j < K; j++) dense[tok[j].idx] = 1;",
                              "for (long j = 0; j < K; j++) dense[tok[N - 1 - j].idx] = 1;"),
