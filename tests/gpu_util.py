@@ -53,10 +53,13 @@ def assert_route_equal(g: dict, o, exact_thresh: bool = True) -> None:
         np.testing.assert_array_equal(g["thresh"], o.thresh)
 
 
-def gpu_forward(q, k, v, r, dtype_name, scale=None):
+def gpu_forward(q, k, v, r, dtype_name, scale=None, prefill=None):
+    """het.forward on the GPU; with prefill, the output tensor starts filled
+    with that value (NaN shows a row the kernels did not write)."""
     import torch
     qg, kg, vg = to_gpu(q, dtype_name), to_gpu(k, dtype_name), to_gpu(v, dtype_name)
-    o = het.forward(qg, kg, vg, r, scale=scale)
+    out = torch.full_like(qg, prefill) if prefill is not None else None
+    o = het.forward(qg, kg, vg, r, scale=scale, out=out)
     torch.cuda.synchronize()
     return o.float().cpu().numpy()
 

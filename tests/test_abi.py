@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import uncertainty_routed_heterogeneous_amd as het
@@ -147,6 +148,68 @@ def test_binding_rejects_bad_tensors():
         het.route(u, (4, 8, 8), (3, 3, 3), 2, 64, torch.float32, rho=0.2)  # not on a GPU
     with pytest.raises(ValueError):
         het.route(u, (4, 8, 8), (3, 3, 3), 2, 64, torch.float32)  # neither rho nor c
+
+
+def cpu_route(B, grid, window=(3, 3, 3)):
+    """A Route of CPU tensors: the binding's shape checks run before any
+    device check, so each mismatch below is rejected without a GPU."""
+    import torch
+    N = int(np.prod(grid))
+    return het.Route(torch.zeros((B, N), dtype=torch.uint8), torch.zeros((B, N), dtype=torch.int32),
+                     torch.zeros((B, N), dtype=torch.int32), torch.zeros((B, 2), dtype=torch.int32),
+                     torch.zeros(B, dtype=torch.float64), -1, tuple(grid), tuple(window))
+
+
+@pytest.mark.parametrize("case", ["grid_vs_N", "batch_vs_route", "kv_shape", "kv_dtype", "not_4d",
+                                  "not_contiguous", "o_shape", "dout_dtype", "counts_shape", "cpu_tensors"])
+def test_binding_rejects_mismatched_shapes(case):
+    """A route made for another layer shape would send the kernels outside
+    the tensors (they size every index from the grid and the route's
+    buffers), so the binding refuses it before any launch."""
+    import torch
+    B, grid, H, D = 2, (2, 3, 4), 2, 64
+    N = 24
+    q = torch.zeros((B, N, H, D), dtype=torch.bfloat16)
+    k, v, o, do = (torch.zeros_like(q) for _ in range(4))
+    r = cpu_route(B, grid)
+    if case == "grid_vs_N":
+        r = cpu_route(B, (2, 3, 5))
+    elif case == "batch_vs_route":
+        r = cpu_route(1, grid)
+    elif case == "kv_shape":
+        k = torch.zeros((B, N, H + 1, D), dtype=torch.bfloat16)
+    elif case == "kv_dtype":
+        v = torch.zeros_like(q, dtype=torch.float32)
+    elif case == "not_4d":
+        q, k, v = (x.reshape(B, N, H * D) for x in (q, k, v))
+    elif case == "not_contiguous":
+        q = torch.zeros((B, N, D, H), dtype=torch.bfloat16).transpose(2, 3)
+    elif case == "o_shape":
+        o = torch.zeros((B, N - 1, H, D), dtype=torch.bfloat16)
+    elif case == "dout_dtype":
+        do = torch.zeros_like(q, dtype=torch.float32)
+    elif case == "counts_shape":
+        r.counts = torch.zeros((B, 3), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        het.backward(q, k, v, r, o, do)
+    if case not in ("o_shape", "dout_dtype"):
+        with pytest.raises(ValueError):
+            het.forward(q, k, v, r)
+
+
+def test_binding_rejects_bad_outputs():
+    import torch
+    B, grid, H, D = 1, (2, 3, 4), 2, 64
+    q = torch.zeros((B, 24, H, D), dtype=torch.bfloat16)
+    r = cpu_route(B, grid)
+    for out in (torch.zeros((B, 24, H, D), dtype=torch.float32), torch.zeros((B, 24, H, 2 * D))[..., ::2],
+                torch.zeros((B, 23, H, D), dtype=torch.bfloat16)):
+        with pytest.raises(ValueError):
+            het.forward(q, q, q, r, out=out)
+        with pytest.raises(ValueError):
+            het.backward(q, q, q, r, q, q, out=(out, torch.zeros_like(q), torch.zeros_like(q)))
+    with pytest.raises(ValueError):
+        het.backward(q, q, q, r, q, q, out=(torch.zeros_like(q), torch.zeros_like(q)))
 
 
 def call_swap(lib, shape, src=None, dst=None, r=0.07, n_blocks=1):

@@ -30,7 +30,7 @@ def full_parity(oracle_mod, w, q, k, v, u, rho=None, c=None, what=""):
     log(f"[forward] {what} grid={w.grid} win={w.window} B={w.batch} H={w.heads} D={w.head_dim} "
         f"{w.dtype} rho={rho} c={c}")
     r = gpu_route(u, w.grid, w.window, w.heads, w.head_dim, w.dtype, rho=rho, c=c)
-    got = gpu_forward(q, k, v, r, w.dtype)
+    got = gpu_forward(q, k, v, r, w.dtype, prefill=float("nan"))
     mask = r.mask.cpu().numpy()
     ref = oracle_mod.forward(q, k, v, w.grid, w.window, w.softmax_scale, mask)
     assert_close(got, ref, w.dtype, what)
@@ -139,14 +139,16 @@ def test_full_size_sampled_rows(oracle_mod, name, rho):
     u = W.make_u(w)
     log(f"[forward] full size {name} rho={rho} N={w.n_tokens}")
     r = gpu_route(u, w.grid, w.window, w.heads, w.head_dim, w.dtype, rho=rho)
-    got = gpu_forward(q, k, v, r, w.dtype)
+    # Output prefilled with NaN: every row must be written exactly once
+    # (Eq. 13), so no NaN may survive.
+    got = gpu_forward(q, k, v, r, w.dtype, prefill=float("nan"))
+    assert np.isfinite(got).all(), "an output element was not written"
     mask = r.mask.cpu().numpy()
     rng = np.random.default_rng(42)
     rows = np.concatenate([b * w.n_tokens + sampled_rows(mask[b], 40, rng) for b in range(w.batch)])
     ref = oracle_mod.attend_rows(q, k, v, w.grid, w.window, w.softmax_scale, mask, rows)
     got_rows = got.reshape(w.batch * w.n_tokens, w.heads, w.head_dim)[rows]
     assert_close(got_rows, ref, w.dtype, f"{name} sampled {rows.size} rows")
-    assert np.isfinite(got).all()
 
 
 def test_deterministic():

@@ -117,6 +117,53 @@ def _stream_handle(stream=None) -> int:
     return int(s.cuda_stream)
 
 
+def _on_stream(stream):
+    """Context for the allocations of a call that runs on `stream`: tensors
+    allocated inside belong to that stream in PyTorch's caching allocator, so
+    a workspace freed when the call returns is not handed to other work while
+    the call's kernels still use it."""
+    import contextlib
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _check_out(t, like, what: str) -> None:
+    if (tuple(t.shape) != tuple(like.shape) or t.dtype != like.dtype or t.device != like.device
+            or not t.is_contiguous()):
+        raise ValueError(f"{what} must be a contiguous tensor of q's shape, dtype and device")
+
+
+def _check_attn(q, k, v, r: "Route", tensors=()) -> None:
+    """Shape checks of an attention call, before anything touches a device:
+    the kernels size every index from the route's grid and read the route's
+    [B, N] buffers, so q must hold B samples of prod(grid) tokens."""
+    for t in (q, k, v) + tuple(tensors):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("q, k, v (and o, dout) must be contiguous [B, N, heads, D] tensors")
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    for t in tensors:
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("o and dout must have q's shape and dtype")
+    B, N = int(q.shape[0]), int(q.shape[1])
+    if math.prod(r.grid) != N:
+        raise ValueError(f"q holds {N} tokens per sample but the route's grid {tuple(r.grid)} "
+                         f"holds {math.prod(r.grid)}")
+    for name in ("mask", "dense_idx", "local_idx"):
+        if tuple(getattr(r, name).shape) != (B, N):
+            raise ValueError(f"route.{name} is {tuple(getattr(r, name).shape)}, not [B, N] = {(B, N)}")
+    if tuple(r.counts.shape) != (B, 2):
+        raise ValueError("route.counts must be [B, 2]")
+    for t in (q, k, v) + tuple(tensors):
+        if not t.is_cuda:
+            raise ValueError("q, k, v (and o, dout) must be CUDA tensors")
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    for name in ("mask", "dense_idx", "local_idx", "counts"):
+        if getattr(r, name).device != q.device:
+            raise ValueError(f"route.{name} is not on q's device")
+
+
 @dataclass
 class Route:
     """Result of :func:`route`: device tensors plus the host-side dense count."""
@@ -155,11 +202,12 @@ def route(u, grid, window, heads: int, head_dim: int, dtype, rho: float | None =
     if math.prod(grid) != N:
         raise ValueError("grid does not match N")
     dev = u.device
-    r = Route(torch.empty((B, N), dtype=torch.uint8, device=dev),
-              torch.empty((B, N), dtype=torch.int32, device=dev),
-              torch.empty((B, N), dtype=torch.int32, device=dev),
-              torch.empty((B, 2), dtype=torch.int32, device=dev),
-              torch.empty((B,), dtype=torch.float64, device=dev), -1, tuple(grid), tuple(window))
+    with _on_stream(stream):
+        r = Route(torch.empty((B, N), dtype=torch.uint8, device=dev),
+                  torch.empty((B, N), dtype=torch.int32, device=dev),
+                  torch.empty((B, N), dtype=torch.int32, device=dev),
+                  torch.empty((B, 2), dtype=torch.int32, device=dev),
+                  torch.empty((B,), dtype=torch.float64, device=dev), -1, tuple(grid), tuple(window))
     shape = make_shape(B, heads, head_dim, grid, window, _dtype_code(dtype))
     rs = r.as_struct()
     mode, param = (HET_TOP_RHO, rho) if rho is not None else (HET_MEAN_STD, c)
@@ -184,7 +232,8 @@ def route_uniform(batch: int, grid, window, rho: float, device=None, stream=None
     """Fixed uniform routing (HET_UNIFORM): the lattice floor(j*N/K), j < K."""
     import torch
     N = math.prod(grid)
-    bufs = [b[0] for b in _new_routes(1, batch, N, device or torch.device("cuda"))]
+    with _on_stream(stream):
+        bufs = [b[0] for b in _new_routes(1, batch, N, device or torch.device("cuda"))]
     r = Route(*bufs, -1, tuple(grid), tuple(window))
     shape = make_shape(batch, 1, 64, grid, window, HET_F32)
     rs = r.as_struct()
@@ -202,7 +251,8 @@ def route_random(batch: int, grid, window, rho: float, seed: int, step: int, blo
     Route objects viewing one allocation, route l for block `block + l`."""
     import torch
     N = math.prod(grid)
-    bufs = _new_routes(int(n_blocks), batch, N, device or torch.device("cuda"))
+    with _on_stream(stream):
+        bufs = _new_routes(int(n_blocks), batch, N, device or torch.device("cuda"))
     rs = RouteStruct(*[b.data_ptr() for b in bufs], -1)
     shape = make_shape(batch, 1, 64, grid, window, HET_F32)
     st = load_library().het_attn_route_random(ctypes.byref(shape), float(rho), int(seed) & (2**64 - 1),
@@ -231,7 +281,8 @@ def swap(r: Route, ratio: float, seed: int, step: int, block: int = 0, n_blocks:
         rs_out = r.as_struct()
     else:
         nb = int(n_blocks)
-        mask, di, li, cnt, th = _new_routes(nb, B, N, dev)
+        with _on_stream(stream):
+            mask, di, li, cnt, th = _new_routes(nb, B, N, dev)
         outs = [Route(mask[l], di[l], li[l], cnt[l], th[l], r.dense_count_host, r.grid, r.window)
                 for l in range(nb)]
         rs_out = RouteStruct(mask.data_ptr(), di.data_ptr(), li.data_ptr(), cnt.data_ptr(),
@@ -263,22 +314,21 @@ def forward(q, k, v, r: Route, scale: float | None = None, out=None, stream=None
     return_lse (part "both", bf16): also return the rows' log-sum-exp,
     [B, heads, N] fp32 in log2 units (het_attn_forward_lse), for backward()."""
     import torch
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError("q, k, v must be contiguous [B, N, heads, D] CUDA tensors")
-    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share shape and dtype")
+    _check_attn(q, k, v, r)
+    if out is not None:
+        _check_out(out, q, "out")
+    if return_lse and part != "both":
+        raise ValueError("return_lse needs part='both'")
     B, N, H, D = q.shape
     shape = make_shape(B, H, D, r.grid, r.window, _dtype_code(q.dtype), scale or 0.0, border)
-    if out is None:
-        out = torch.empty_like(q)
     ws_n = workspace_bytes(shape)
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device) if ws_n else None
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device) if ws_n else None
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
     rs = r.as_struct()
     if return_lse:
-        if part != "both":
-            raise ValueError("return_lse needs part='both'")
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
         st = load_library().het_attn_forward_lse(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                                  ctypes.byref(rs), out.data_ptr(), lse.data_ptr(),
                                                  ws.data_ptr() if ws is not None else None, ws_n,
@@ -297,24 +347,29 @@ def forward(q, k, v, r: Route, scale: float | None = None, out=None, stream=None
 
 
 def backward(q, k, v, r: Route, o, dout, scale: float | None = None, stream=None, border: str = "shift",
-             lse=None):
+             lse=None, out=None):
     """(dQ, dK, dV) of forward(q, k, v, r) = o for dL/dO = dout (het_attn_backward).
 
     lse: the rows' log-sum-exp from forward(..., return_lse=True) for the same
-    inputs (het_attn_backward_lse: not computed again)."""
+    inputs (het_attn_backward_lse: not computed again).
+    out: optional (dq, dk, dv) tensors of q's shape, dtype and device to write."""
     import torch
-    for t in (q, k, v, o, dout):
-        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError("q, k, v, o, dout must be contiguous CUDA tensors of one shape and dtype")
+    _check_attn(q, k, v, r, (o, dout))
+    if out is not None:
+        if len(out) != 3:
+            raise ValueError("out must be (dq, dk, dv)")
+        for t, name in zip(out, ("dq", "dk", "dv")):
+            _check_out(t, q, name)
     B, N, H, D = q.shape
     shape = make_shape(B, H, D, r.grid, r.window, _dtype_code(q.dtype), scale or 0.0, border)
     lib = load_library()
     ws_n = int(lib.het_attn_backward_workspace_bytes(ctypes.byref(shape)))
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    with _on_stream(stream):
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+        dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
     rs = r.as_struct()
     if lse is not None:
-        if (not lse.is_cuda or lse.dtype != torch.float32 or not lse.is_contiguous()
+        if (not lse.is_cuda or lse.device != q.device or lse.dtype != torch.float32 or not lse.is_contiguous()
                 or tuple(lse.shape) != (B, H, N)):
             raise ValueError("lse must be a contiguous [B, heads, N] float32 CUDA tensor")
         st = lib.het_attn_backward_lse(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),

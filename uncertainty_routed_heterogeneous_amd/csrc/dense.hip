@@ -186,31 +186,19 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         const __bf16 *kb = k + (size_t)b * N * tok_stride + (size_t)h * D;
         const __bf16 *vb = v + (size_t)b * N * tok_stride + (size_t)h * D;
 
-        // Gathered query of this lane.
+        // Gathered query of this lane, as stored: the MFMA forms q.k exactly
+        // (bf16 products, fp32 sums), and the softmax scale is applied in fp32
+        // with the exponent's FMA, so no rounding of the logits precedes the
+        // exponential (the logits of a peaked softmax reach tens of units).
         const int qrow = tile * BM + wave * 32 + col;
         const bool q_valid = qrow < n_dense;
         const int tok = q_valid ? dense_idx[(size_t)b * N + qrow] : 0;
-        // The query enters the MFMA pre-multiplied by scale*log2(e) (rounded
-        // to bf16), so that S comes out in the base-2 units of the softmax.
         bf16x8 qf[NC];
         {
             const __bf16 *qp = q + ((size_t)b * N + tok) * tok_stride + (size_t)h * D + 8 * half;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const bf16x8 raw = q_valid ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
-                u32x4 w;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = pack_bf16x2((float)raw[2 * e] * scale_log2, (float)raw[2 * e + 1] * scale_log2);
-                qf[c] = __builtin_bit_cast(bf16x8, w);
-            }
+            for (int c = 0; c < NC; ++c) qf[c] = q_valid ? *(const bf16x8 *)(qp + 16 * c) : bf16x8{};
         }
-        // One more k-step of the QK product adds -m_ref to every score: A is 1
-        // at k = 0 (every key row), B is -m_ref at k = 0 (this lane's query).
-        // m_ref is kept bf16-representable, so the term is exact; the first
-        // tile of a piece runs against reference 0.
-        bf16x8 ones_a = {}, neg_m_b = {};
-        if (half == 0) ones_a[0] = (__bf16)1.0f;
 
         // K or V tile kt -> LDS.  The descriptor covers the rows below N only:
         // a buffer load past its range returns zeros, so the ragged last tile
@@ -230,9 +218,9 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         f32x16 oacc[NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-        float m_ref = -__builtin_inff();  // reference max, log2 units
+        float m_ref = -__builtin_inff();  // reference max, log2 units (of scale * q.k * log2(e))
         float l_part = 0.0f;
-        f32x16 sc[2];                     // S^T of the current tile: key block x 32 queries
+        f32x16 sc[2];                     // S^T = q.k of the current tile: key block x 32 queries
         bf16x8 pf[2][2];                  // P of the current tile as the B operand
 
         // MFMA burst of round r: O^T += V(r-1)^T P(r-1)^T (steps 0..4*NDB-1),
@@ -257,10 +245,6 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
             constexpr bool kPv = decltype(pv_tag)::value, kQk = decltype(qk_tag)::value;
             constexpr int i0 = kPv ? 0 : kPvSteps, i1 = kQk ? kPvSteps + kQkSteps : kPvSteps;
             if constexpr (i0 < i1) {
-                if constexpr (kQk) {
-                    sc[0] = mfma32_bf16(ones_a, neg_m_b, f32x16{});
-                    sc[1] = mfma32_bf16(ones_a, neg_m_b, f32x16{});
-                }
                 bf16x8 ring[kAhead];
 #pragma unroll
                 for (int a = 0; a < kAhead; ++a)
@@ -273,8 +257,10 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
                         const int db = i % NDB, kbk = (i / NDB) >> 1, c2 = (i / NDB) & 1;
                         oacc[db] = mfma32_bf16(a, pf[kbk][c2], oacc[db]);
                     } else {
+                        // the first k-chunk of a key block starts from zero
+                        // (an inline constant, not zeroed registers)
                         const int j = i - kPvSteps, kbk = j & 1, c = j >> 1;
-                        sc[kbk] = mfma32_bf16(a, qf[c], sc[kbk]);
+                        sc[kbk] = mfma32_bf16(a, qf[c], c == 0 ? f32x16{} : sc[kbk]);
                     }
                     if (i + kAhead < i1) ring[(i - i0) % kAhead] = a_operand(i + kAhead, Vt, Kt);
                     __builtin_amdgcn_sched_barrier(0);
@@ -294,15 +280,24 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
                         sc[kbk][i] = key_off < lim ? sc[kbk][i] : -__builtin_inff();
                     }
             }
-            // Scores are already relative to the reference (base 2).  The
-            // reference moves (exactly as a running max would) only on the
-            // first tile of a piece and when a tile's exponentials ran
-            // large: with every score <= kRescaleSlack a lane's 32
-            // exponentials sum to at most 32 * 2^kRescaleSlack, so a larger
-            // sum (or a non-finite one) sends the tile through the exact max
-            // and its exponentials are taken again.  Without the max on
-            // every tile a score may exceed the reference by up to
-            // log2(32) + kRescaleSlack, well inside fp32 and bf16 range.
+            // Scores relative to the reference, in log2 units: one fp32 FMA
+            // per score, s * scale * log2(e) - m_ref (a piece's first tile
+            // is taken against 0).  The reference moves (exactly as a
+            // running max would) only on the first tile of a piece and when
+            // a tile's exponentials ran large: with every score <=
+            // kRescaleSlack a lane's 32 exponentials sum to at most
+            // 32 * 2^kRescaleSlack, so a larger sum (or a non-finite one)
+            // sends the tile through the exact max and its exponentials are
+            // taken again.  Without the max on every tile a score may exceed
+            // the reference by up to log2(32) + kRescaleSlack, well inside
+            // fp32 and bf16 range.
+            {
+                const float neg_m = m_ref == -__builtin_inff() ? 0.0f : -m_ref;
+#pragma unroll
+                for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sc[kbk][i] = __builtin_fmaf(sc[kbk][i], scale_log2, neg_m);
+            }
             auto rescale = [&]() HET_INLINE {
                 float mx = -__builtin_inff();
 #pragma unroll
@@ -313,18 +308,16 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
                 const bool first = m_ref == -__builtin_inff();  // first tile of the piece
                 const bool grow = first || mx > kRescaleSlack;
                 if (__builtin_expect(__any(grow), 0)) {
-                    // The new reference (bf16-representable) and how far it moved.
+                    // The new reference and how far it moved.
                     const float m_base = first ? 0.0f : m_ref;
-                    const float m_new = grow ? (float)(__bf16)(m_base + mx) : m_base;
-                    const float delta = m_new - m_base;
+                    const float delta = grow ? mx : 0.0f;
                     const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-delta);
-                    m_ref = m_new;
+                    m_ref = m_base + delta;
                     l_part *= alpha;
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
 #pragma unroll
                     for (int kbk = 0; kbk < 2; ++kbk) sc[kbk] -= delta;
-                    if (half == 0) neg_m_b[0] = (__bf16)(-m_ref);
                 }
             };
             // chunk c2 of key block kb = registers 8*c2 .. 8*c2+7, i.e. keys
