@@ -44,7 +44,8 @@
  * [0, S), so tokens near the border see fewer keys.
  *
  * Memory.  All tensor arguments are device pointers owned by the caller; the
- * library allocates and frees nothing and keeps no state between calls.
+ * library allocates and frees nothing and keeps no state between calls,
+ * except the static scratch array of het_attn_forward_noalloc (see there).
  * Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
  * return without waiting for it.  `shape` and `route` themselves are host
  * structs read during the call only.
@@ -64,7 +65,7 @@
 extern "C" {
 #endif
 
-#define HETATTN_ABI_VERSION 3
+#define HETATTN_ABI_VERSION 4
 
 typedef enum {
     HET_OK = 0,
@@ -185,6 +186,24 @@ int het_attn_swap(const het_attn_shape *shape, const het_route *in, double r, ui
 int het_attn_forward(const het_attn_shape *shape, const void *q, const void *k, const void *v,
                      const het_route *route, void *o, void *workspace, size_t workspace_bytes,
                      void *stream);
+
+/* het_attn_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same kernels and same results as het_attn_forward; the dense
+ * kernel's scratch (the partial outputs of query tiles split between
+ * workgroups) is taken from a static device array of the library instead of
+ * a caller's workspace.  That array holds 67.6 MB on each device the library
+ * runs on (kept until the process ends) and serves up to 256 persistent
+ * workgroups at head_dim 128; on a device with more compute units the dense
+ * kernel takes 256 workgroups.  The call allocates nothing; a shape whose
+ * scratch would exceed the array returns HET_ERR_WORKSPACE (none does with
+ * head_dim 64 or 128).  Every call on one device shares that device's
+ * array and leaves its contents behind: calls that overlap in time on one
+ * device (on different streams, or from different threads) race, and the
+ * caller must order them.  Nothing in the array needs clearing between
+ * calls.  q, k, v, route, o, stream: as het_attn_forward. */
+int het_attn_forward_noalloc(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                             const het_route *route, void *o, void *stream);
 
 /* The two halves of het_attn_forward, same arguments and rules.
  * het_attn_dense writes only the rows with m_i = 0 (dense attention over all

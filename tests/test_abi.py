@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.het_attn_abi_version() == het.ABI_VERSION == 3
+    assert lib.het_attn_abi_version() == het.ABI_VERSION == 4
     for st in range(5):
         assert het.status_string(st)
     assert het.status_string(99) == "unknown status"

@@ -28,7 +28,7 @@ HET_OK, HET_ERR_INVALID_ARG, HET_ERR_UNSUPPORTED, HET_ERR_WORKSPACE, HET_ERR_HIP
 HET_BF16, HET_F32 = 0, 1
 HET_TOP_RHO, HET_MEAN_STD, HET_UNIFORM = 0, 1, 2
 HET_BORDER_SHIFT, HET_BORDER_CUT = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 _BORDERS = {"shift": HET_BORDER_SHIFT, "cut": HET_BORDER_CUT}
 
 
@@ -77,6 +77,7 @@ _ATTN_ARGS = [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_
               ctypes.c_void_p]
 for _name in ("het_attn_forward", "het_attn_dense", "het_attn_local"):
     SIGNATURES[_name] = (ctypes.c_int, _ATTN_ARGS)
+SIGNATURES["het_attn_forward_noalloc"] = (ctypes.c_int, _ATTN_ARGS[:6] + [ctypes.c_void_p])
 SIGNATURES["het_attn_forward_lse"] = (ctypes.c_int, _ATTN_ARGS[:6] + [ctypes.c_void_p] + _ATTN_ARGS[6:])
 SIGNATURES["het_attn_backward_lse"] = (ctypes.c_int, SIGNATURES["het_attn_backward"][1][:7] + [ctypes.c_void_p]
                                        + SIGNATURES["het_attn_backward"][1][7:])
@@ -343,6 +344,23 @@ def forward(q, k, v, r: Route, scale: float | None = None, out=None, stream=None
                                        _stream_handle(stream))
     if st != HET_OK:
         raise HetAttnError(st, name)
+    return out
+
+
+def forward_noalloc(q, k, v, r: Route, out, scale: float | None = None, stream=None, border: str = "shift"):
+    """het_attn_forward_noalloc: het_attn_forward into the caller's `out`
+    with the library's static scratch, so that neither this call nor the
+    library allocates device memory.  Calls that overlap in time on one
+    device share that scratch and must be ordered by the caller."""
+    _check_attn(q, k, v, r)
+    _check_out(out, q, "out")
+    B, N, H, D = q.shape
+    shape = make_shape(B, H, D, r.grid, r.window, _dtype_code(q.dtype), scale or 0.0, border)
+    rs = r.as_struct()
+    st = load_library().het_attn_forward_noalloc(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                 ctypes.byref(rs), out.data_ptr(), _stream_handle(stream))
+    if st != HET_OK:
+        raise HetAttnError(st, "het_attn_forward_noalloc")
     return out
 
 

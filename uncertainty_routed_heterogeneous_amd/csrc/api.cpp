@@ -1,6 +1,7 @@
 // api.cpp -- the C ABI of include/hetattn.h: argument validation on the host,
-// then launches on the caller's stream.  No allocation, no state, no
-// device-to-host traffic.
+// then launches on the caller's stream.  No allocation and no device-to-host
+// traffic; the only state is the per-device address of the static scratch
+// that het_attn_forward_noalloc uses (kept in dense.hip).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -219,9 +220,12 @@ namespace {
 
 enum Part { kBoth = 3, kDenseOnly = 1, kLocalOnly = 2 };
 
+// no_alloc: run with the library's static scratch instead of the caller's
+// workspace (het_attn_forward_noalloc); the dense kernel then takes at most
+// kNoAllocGroups persistent workgroups, which that scratch holds.
 int run_attention(const het_attn_shape *shape, const void *q, const void *k, const void *v,
                   const het_route *route, void *o, void *workspace, size_t workspace_bytes,
-                  void *stream, int parts, float *lse = nullptr) {
+                  void *stream, int parts, float *lse = nullptr, bool no_alloc = false) {
     Dims d;
     float scale;
     const het_status st = check_shape(shape, d, scale);
@@ -230,8 +234,13 @@ int run_attention(const het_attn_shape *shape, const void *q, const void *k, con
         return HET_ERR_INVALID_ARG;
     if (route->dense_count_host < -1 || route->dense_count_host > d.N) return HET_ERR_INVALID_ARG;
     if (lse && shape->dtype != HET_BF16) return HET_ERR_UNSUPPORTED;
-    const int cus = current_cu_count();
+    int cus = current_cu_count();
     if (cus <= 0) return HET_ERR_HIP;
+    if (no_alloc) {
+        if (cus > hetattn::kNoAllocGroups) cus = hetattn::kNoAllocGroups;
+        if (hetattn::noalloc_scratch(&workspace) != hipSuccess) return HET_ERR_HIP;
+        workspace_bytes = hetattn::kNoAllocScratchBytes;
+    }
     const size_t need = hetattn::dense_workspace_bytes((int)d.B, (int)d.H, (int)d.N, (int)d.D,
                                                        shape->dtype == HET_BF16, cus);
     if (need > 0 && !workspace) return HET_ERR_INVALID_ARG;
@@ -298,6 +307,11 @@ int het_attn_local(const het_attn_shape *shape, const void *q, const void *k, co
                    const het_route *route, void *o, void *workspace, size_t workspace_bytes,
                    void *stream) {
     return run_attention(shape, q, k, v, route, o, workspace, workspace_bytes, stream, kLocalOnly);
+}
+
+int het_attn_forward_noalloc(const het_attn_shape *shape, const void *q, const void *k, const void *v,
+                             const het_route *route, void *o, void *stream) {
+    return run_attention(shape, q, k, v, route, o, nullptr, 0, stream, kBoth, nullptr, true);
 }
 
 int het_attn_forward_lse(const het_attn_shape *shape, const void *q, const void *k, const void *v,

@@ -19,6 +19,7 @@
 // previous tile, then S of this tile) with a VALU burst (softmax of this
 // tile), and the two groups run half a round apart, so while one wave of a
 // SIMD computes exponentials the other keeps the matrix unit busy.
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -754,6 +755,35 @@ hipError_t launch_dense_lse(const AttnArgs &a, float *lse, hipStream_t stream) {
                                a.counts, a.batch, a.n, a.heads, G, (const float *)ws_part, lse);
     }
     return hipGetLastError();
+}
+
+// Scratch of het_attn_forward_noalloc: the dense kernel's stream-K partials
+// for up to kNoAllocGroups persistent workgroups at head_dim <= 128, held in
+// a file-scope device array (one copy per device, allocated by the runtime
+// when the library's code object is loaded on that device, held until the
+// process ends).  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address comes from hipGetSymbolAddress, looked up
+// once per device below.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 size_t dense_workspace_bytes(int batch, int heads, int n, int head_dim, bool bf16, int cu_count) {

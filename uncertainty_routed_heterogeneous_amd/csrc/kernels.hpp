@@ -92,6 +92,16 @@ constexpr int kLocalMaxWinW = 25;
 // Device workspace of the dense kernel's stream-K pieces (fp32 partials).
 size_t dense_workspace_bytes(int batch, int heads, int n, int head_dim, bool bf16, int cu_count);
 
+// The allocation-free forward keeps the dense kernel's stream-K partials in a
+// static device array sized for kNoAllocGroups persistent workgroups at
+// head_dim 128 (the largest head size): 2 slots per workgroup of 256 queries
+// x (128 partial outputs + running max + row sum) fp32 values, 67.6 MB.
+constexpr int kNoAllocGroups = 256;
+constexpr size_t kNoAllocScratchBytes = 2ull * kNoAllocGroups * (128 * 256 + 2 * 256) * sizeof(float);
+// Device address of the current device's copy of that array (looked up once
+// per device with hipGetSymbolAddress).
+hipError_t noalloc_scratch(void **ptr);
+
 hipError_t launch_route(const RouteArgs &a, hipStream_t stream);
 hipError_t launch_swap(const SwapArgs &a, int n_blocks, hipStream_t stream);
 hipError_t launch_dense(const AttnArgs &a, hipStream_t stream);
