@@ -303,6 +303,7 @@ struct BandGeom {
     static constexpr int kMaxLw = SR == 16 ? 16 - QX + 1 : kLocalMaxWinW;
     // LDS rows per box row: the widest workgroup box, in whole DMA loads.
     static constexpr int kCb = (NW * QX + kMaxLw - 1 + kTokPerLoad - 1) / kTokPerLoad * kTokPerLoad;
+    static_assert(kCb % kTokPerLoad == 0, "a DMA load's rows stay in one box row");
     static constexpr int kBandRows = rpb * kCb;
     static constexpr int kLoads = kBandRows / kTokPerLoad;      // DMA loads per tensor and band
     static constexpr int kLoadsPerWave = (kLoads + kBandWaves - 1) / kBandWaves;
@@ -450,6 +451,18 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
         dma_voff[j] = c < C ? 2 * ((rr * g.Wg + c) * (int)tok_stride + 8 * ((lane % Bg::kCpr) ^ swz<D>(R)))
                             : 0x7ffffff0;
     }
+    // Loads whose rows all lie past the box's C columns are not issued (a
+    // load's rows are kTokPerLoad consecutive columns of one box row, since
+    // kCb is a multiple of kTokPerLoad); no read reaches those LDS rows.
+    uint32_t dma_live = 0;
+    {
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+        for (int j = 0; j < Bg::kLoadsPerWave; ++j) {
+            const int i = wv + kBandWaves * j;
+            if (i < Bg::kLoads && (i * Bg::kTokPerLoad) % Bg::kCb < C) dma_live |= 1u << j;
+        }
+    }
     const __bf16 *kbase = k + (size_t)b * N * tok_stride + (size_t)h * D;
     const __bf16 *vbase = v + (size_t)b * N * tok_stride + (size_t)h * D;
     // Bands go (frame, row of bands) in order; (c_f, c_r) is the band being
@@ -473,7 +486,7 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
 #pragma unroll
         for (int j = 0; j < Bg::kLoadsPerWave; ++j) {
             const int i = wave + kBandWaves * j;
-            if (i < Bg::kLoads) {
+            if ((dma_live >> j) & 1u) {
                 buffer_load_lds16(kp, bytes, (HET_LDS void *)(Kd + i * Bg::kTokPerLoad * D), dma_voff[j]);
                 if constexpr (kMode != 1)
                     buffer_load_lds16(vp, bytes, (HET_LDS void *)(Vd + i * Bg::kTokPerLoad * D), dma_voff[j]);
