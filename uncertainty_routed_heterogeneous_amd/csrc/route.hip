@@ -119,6 +119,18 @@ __device__ __forceinline__ void wave_excl_scan2(int x, int y, int *s_wave, int &
     __syncthreads();
 }
 
+// p[0 .. n) = -1, by the whole workgroup: 16-byte stores from the first
+// 16-byte boundary of p on (p is 4-byte aligned), single ones around them.
+__device__ __forceinline__ void fill_minus_one(int32_t *p, int n) {
+    const int tid = threadIdx.x;
+    const int head = imin(n, (int)(((16u - ((uint32_t)(uintptr_t)p & 15u)) & 15u) >> 2));
+    const int nv = (n - head) >> 2;
+    for (int i = tid; i < head; i += kRouteThreads) p[i] = -1;
+    i32x4 *pv = reinterpret_cast<i32x4 *>(p + head);
+    for (int i = tid; i < nv; i += kRouteThreads) pv[i] = i32x4{-1, -1, -1, -1};
+    for (int i = head + 4 * nv + tid; i < n; i += kRouteThreads) p[i] = -1;
+}
+
 // Number of lanes below this one whose bit is set in `bal`.
 __device__ __forceinline__ int lanes_below(uint64_t bal) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
@@ -134,6 +146,13 @@ constexpr int kHistStride = 257;
 constexpr int kHistWords = 64 * kHistStride;
 static_assert(kHistWords % 4 == 0, "the histogram is cleared in 16-byte words");
 
+// Candidate list of the radix select: after the first digit pass, the member
+// keys that carry the selected prefix are copied to LDS when at most
+// kCandCap of them do, and the later passes read that list instead of every
+// member's key (for a smooth u the selected digit holds a few hundred to a
+// few thousand tokens; the register pass over all of them cost about 3 us).
+constexpr int kCandCap = 8192;
+
 // MSB-first radix select over the keys of the members of one sample.
 // Precondition: 1 <= k <= the number of members, and [lo, hi] is the range of
 // the members' keys (workgroup-uniform).  Returns in tkey the k-th largest
@@ -142,26 +161,33 @@ static_assert(kHistWords % 4 == 0, "the histogram is cleared in 16-byte words");
 // above the highest bit in which lo and hi differ are shared by every member
 // and are skipped.  hcopy must be all zero on entry and is all zero on exit;
 // member(j) and key_at(j) describe row j of this wave's range as in
-// route_kernel.
+// route_kernel.  cand holds kCandCap keys and s_sel three ints (LDS).
 template <int kPer, typename KeyAt, typename Member>
 __device__ __forceinline__ void radix_select_largest(int k, uint32_t lo, uint32_t hi, int rows,
                                                      KeyAt &&key_at, Member &&member,
                                                      uint32_t *hcopy, uint32_t *hpart, int *s_sel,
-                                                     uint32_t &tkey, int &take_equal) {
+                                                     uint32_t *cand, uint32_t &tkey, int &take_equal) {
     const int tid = threadIdx.x, lane = tid & 63;
     int top_bit = (lo == hi) ? 0 : 32 - __builtin_clz(lo ^ hi);
     uint32_t pmask = (top_bit >= 32) ? 0u : ~((1u << top_bit) - 1u);
     uint32_t prefix = hi & pmask;
     int remaining = k;
     uint32_t *my_hist = hcopy + kHistStride * lane;
+    int n_cand = -1;  // < 0: the passes read every member's key
     while (top_bit > 0) {
         const int width = imin(8, top_bit);
         const int shift = top_bit - width;
         const uint32_t dmask = (1u << width) - 1u;
-        for_rows<kPer>(rows, [&](int j) HET_INLINE {
-            const uint32_t x = key_at(j);
-            if (member(j) && (x & pmask) == prefix) atomicAdd(&my_hist[(x >> shift) & dmask], 1u);
-        });
+        auto count = [&](uint32_t x) HET_INLINE {
+            if ((x & pmask) == prefix) atomicAdd(&my_hist[(x >> shift) & dmask], 1u);
+        };
+        if (n_cand < 0) {
+            for_rows<kPer>(rows, [&](int j) HET_INLINE {
+                if (member(j)) count(key_at(j));
+            });
+        } else {
+            for (int c = tid; c < n_cand; c += kRouteThreads) count(cand[c]);
+        }
         __syncthreads();
         {
             // Thread t sums bin t%256 over copies 16*(t/256) .. +15 and
@@ -193,12 +219,13 @@ __device__ __forceinline__ void radix_select_largest(int k, uint32_t lo, uint32_
             }
             const int excl = incl - mine;
             if (excl < remaining && remaining <= incl) {
-                int d = 255 - 4 * tid, before = excl;
-                if (before + c0 < remaining) { before += c0; d--;
-                    if (before + c1 < remaining) { before += c1; d--;
-                        if (before + c2 < remaining) { before += c2; d--; } } }
+                int d = 255 - 4 * tid, before = excl, in_bin = c0;
+                if (before + c0 < remaining) { before += c0; d--; in_bin = c1;
+                    if (before + c1 < remaining) { before += c1; d--; in_bin = c2;
+                        if (before + c2 < remaining) { before += c2; d--; in_bin = c3; } } }
                 s_sel[0] = d;
                 s_sel[1] = remaining - before;
+                s_sel[2] = in_bin;  // members with the new prefix
             }
         }
         __syncthreads();
@@ -206,6 +233,28 @@ __device__ __forceinline__ void radix_select_largest(int k, uint32_t lo, uint32_
         pmask |= dmask << shift;
         remaining = s_sel[1];
         top_bit = shift;
+        const int in_bin = s_sel[2];
+        if (n_cand < 0 && top_bit > 0 && in_bin <= kCandCap) {
+            // Copy the members with the new prefix to the candidate list:
+            // per row, the lowest matching lane reserves the row's run.
+            __syncthreads();  // every thread has read s_sel
+            if (tid == 0) s_sel[2] = 0;
+            __syncthreads();
+            for_rows<kPer>(rows, [&](int j) HET_INLINE {
+                const uint32_t x = key_at(j);
+                const bool m = member(j) && (x & pmask) == prefix;
+                const uint64_t bal = __ballot(m);
+                if (bal != 0ull) {
+                    const int leader = __builtin_ctzll(bal);
+                    int base = 0;
+                    if (lane == leader) base = atomicAdd(&s_sel[2], __popcll(bal));
+                    base = __shfl(base, leader);
+                    if (m) cand[base + lanes_below(bal)] = x;
+                }
+            });
+            __syncthreads();
+            n_cand = in_bin;
+        }
     }
     tkey = prefix;
     take_equal = remaining;
@@ -225,7 +274,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     __shared__ int s_wave[2 * kRouteWaves];
     __shared__ uint32_t s_mm[2 * kRouteWaves];
     __shared__ double s_part[kRouteWaves];
-    __shared__ int s_sel[2];
+    __shared__ int s_sel[3];
+    __shared__ uint32_t cand[kCandCap];
 
     // Row j of this wave is tokens w*C + 64*j + (0..63); `rows` rows hold
     // tokens below N.  Keys of tokens at or beyond N read as 0, which no
@@ -271,7 +321,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         __syncthreads();
         radix_select_largest<kPer>(
             a.k, lo, hi, rows, key_at, [&](int j) HET_INLINE { return key_at(j) != 0u; }, hcopy,
-            hpart, s_sel, tkey, take_equal);
+            hpart, s_sel, cand, tkey, take_equal);
         T = (double)key_to_float(tkey);
     } else if (!kUniform && a.mode == 1) {
         double s = 0.0;
@@ -339,8 +389,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         }
         d_seen += __popcll(bal);
     });
-    for (int i = n_dense + tid; i < N; i += kRouteThreads) dense_idx[i] = -1;
-    for (int i = (N - n_dense) + tid; i < N; i += kRouteThreads) local_idx[i] = -1;
+    fill_minus_one(dense_idx + n_dense, N - n_dense);
+    fill_minus_one(local_idx + (N - n_dense), n_dense);
     if (tid == 0) {
         a.counts[2 * b] = n_dense;
         a.counts[2 * b + 1] = N - n_dense;
@@ -425,7 +475,8 @@ __global__ __launch_bounds__(kRouteThreads) void swap_kernel(SwapArgs a) {
     __shared__ uint32_t hpart[4 * 256];
     __shared__ int s_wave[5 * kRouteWaves];
     __shared__ uint32_t s_mm[2 * kRouteWaves];
-    __shared__ int s_sel[2];
+    __shared__ int s_sel[3];
+    __shared__ uint32_t cand[kCandCap];
 
     const int per = kPer > 0 ? kPer : (N + kRouteThreads - 1) / kRouteThreads;
     const int w0 = wave * per * 64;
@@ -497,10 +548,10 @@ __global__ __launch_bounds__(kRouteThreads) void swap_kernel(SwapArgs a) {
         __syncthreads();
     }
     if (s_out > 0)
-        radix_select_largest<kPer>(s_out, dlo, dhi, rows, key_at, in_dense, hcopy, hpart, s_sel, tkd,
+        radix_select_largest<kPer>(s_out, dlo, dhi, rows, key_at, in_dense, hcopy, hpart, s_sel, cand, tkd,
                                    ted);
     if (s_in > 0)
-        radix_select_largest<kPer>(s_in, llo, lhi, rows, key_at, in_local, hcopy, hpart, s_sel, tkl,
+        radix_select_largest<kPer>(s_in, llo, lhi, rows, key_at, in_local, hcopy, hpart, s_sel, cand, tkl,
                                    tel);
 
     // Per wave: dense-set size, and in each set the tokens above the select
@@ -549,8 +600,8 @@ __global__ __launch_bounds__(kRouteThreads) void swap_kernel(SwapArgs a) {
         }
         d_seen += __popcll(bal);
     });
-    for (int i = n_dense + tid; i < N; i += kRouteThreads) dense_idx[i] = -1;
-    for (int i = (N - n_dense) + tid; i < N; i += kRouteThreads) local_idx[i] = -1;
+    fill_minus_one(dense_idx + n_dense, N - n_dense);
+    fill_minus_one(local_idx + (N - n_dense), n_dense);
     if (tid == 0) {
         a.counts[2 * r] = n_dense;
         a.counts[2 * r + 1] = N - n_dense;
