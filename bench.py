@@ -255,15 +255,28 @@ def time_backward(layer, iters: int, warmup: int = 2, with_lse: bool = True):
     return ts[len(ts) // 2]
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, q, k, v, u, rho, stride: int):
     """The fp64 oracle on the host cores, on a bounded sample of the same
-    layer: the full route plus every `stride`-th dense and local row."""
+    layer: the full route (timed by itself), then every `stride`-th dense and
+    local row of the layer (all heads), timed by itself; the rate is the
+    sample's effective FLOPs over the route and forward seconds."""
     import numpy as np
     import oracle
     import workloads as W
     threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     r = oracle.route_top_rho(u, rho)
+    t_route = time.perf_counter() - t0
     rows = []
     n_dense = n_local = 0
     for b in range(w.batch):
@@ -272,52 +285,60 @@ def cpu_baseline(w, q, k, v, u, rho, stride: int):
         n_dense += d.size
         n_local += l.size
         rows.append(b * w.n_tokens + np.concatenate([d, l]).astype(np.int64))
+    t1 = time.perf_counter()
     oracle.attend_rows(q, k, v, w.grid, w.window, w.softmax_scale, r.mask, np.concatenate(rows),
                        nthreads=threads)
-    sec = time.perf_counter() - t0
+    t_fwd = time.perf_counter() - t1
+    sec = t_route + t_fwd
     T, H, Wd = w.grid
     M = min(w.window[0], T) * min(w.window[1], H) * min(w.window[2], Wd)
     flop = 4.0 * w.head_dim * w.heads * (n_dense * w.n_tokens + n_local * M)
     return {"value": round(flop / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": (f"{w.name}: full route of {w.batch}x{w.n_tokens} tokens plus every "
-                       f"{stride}th dense and local row ({n_dense} dense, {n_local} local rows, "
-                       f"all {w.heads} heads) in fp64; {sec:.1f} s, effective FLOPs of the sample "
-                       f"per second; est. {W.effective_flops(w.with_(rho=rho)) / (flop / sec):.1f} s "
-                       f"for the whole layer")}
+            "kind": "oracle", "cpu": cpu_model(), "route_s": round(t_route, 3), "forward_s": round(t_fwd, 2),
+            "sample": (f"{w.name}: the full route of {w.batch}x{w.n_tokens} tokens ({t_route:.2f} s) plus every "
+                       f"{stride}th dense and local row ({n_dense} dense, {n_local} local rows, all {w.heads} "
+                       f"heads; {t_fwd:.1f} s) in fp64 on {threads} threads; effective FLOPs of the sample per "
+                       f"second; the whole layer would take about "
+                       f"{t_route + W.effective_flops(w.with_(rho=rho)) / (flop / t_fwd):.0f} s at this rate")}
 
 
-def run_sweep(het, W, torch, rho_main):
-    """Warm timings of the rho sweep on the Wan-1.3B shape and of the other
-    workloads at their own rho (medians of 20 steps after 5 warm-ups)."""
-    cases = ([("wan13b", r, None) for r in W.RHO_SWEEP] + [("wan5b", None, None), ("long", None, None)] +
-             [("wan13b", None, win) for win in W.WINDOW_SWEEP] + [("wan5b", None, (11, 11, 11))])
+def run_sweep(het, W, torch, main_inputs, steps: int, warmup: int):
+    """Warm timings (medians of `steps` steps after `warmup`) of the rho sweep
+    and the window ablation on the Wan-1.3B shape and of the other workloads
+    at their own rho: the inputs of each distinct workload are drawn once
+    (the Wan-1.3B ones are the main run's).  A compact row per config."""
+    cases = ([("wan13b", r, None) for r in W.RHO_SWEEP] +
+             [("wan13b", None, win) for win in W.WINDOW_SWEEP] +
+             [("wan5b", None, None), ("wan5b", None, (11, 11, 11)), ("long", None, None)])
     rows = []
+    cache = {"wan13b": main_inputs}
+    to_bf16 = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
     for name, r, win in cases:
         w = W.WORKLOADS[name]
+        if name not in cache:
+            cache.clear()
+            cache["wan13b"] = main_inputs
+            qn, kn, vn = W.make_qkv(w)
+            cache[name] = (to_bf16(qn), to_bf16(kn), to_bf16(vn), torch.from_numpy(W.make_u(w)).cuda())
+            del qn, kn, vn
+        q, k, v, u = cache[name]
         if win is not None:
             w = w.with_(window=win)
         rho = w.rho if r is None else r
-        qn, kn, vn = W.make_qkv(w)
-        un = W.make_u(w)
-        to_bf16 = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
-        q, k, v = to_bf16(qn), to_bf16(kn), to_bf16(vn)
-        u = torch.from_numpy(un).cuda()
         layer = Layer(het, w, q, k, v, u, rho)
-        res = time_layer(layer, 20, 5)
-        n_dense = [W.dense_count(w.n_tokens, rho)] * w.batch
-        eff = W.effective_flops(w, n_dense)
+        res = time_layer(layer, steps, warmup)
+        eff = W.effective_flops(w, [W.dense_count(w.n_tokens, rho)] * w.batch)
         ms = res["step_ms_median"]
-        row = {"workload": name, "rho": rho, "window": list(w.window), "tokens": w.n_tokens,
-               "batch": w.batch, "heads": w.heads,
-               "ms_per_layer": round(ms, 5), "route_ms": round(res["route_ms_median"], 5),
+        row = {"workload": name, "rho": rho, "window": list(w.window), "batch": w.batch, "heads": w.heads,
+               "tokens": w.n_tokens, "ms_per_layer": round(ms, 5), "route_ms": round(res["route_ms_median"], 5),
                "local_ms": round(res["local_ms_median"], 5), "dense_ms": round(res["dense_ms_median"], 5),
                "effective_TFLOPs": round(eff / (ms * 1e-3) / 1e12, 2),
                "pct_mfma_peak": round(100.0 * eff / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
         log(f"[bench] sweep {row}")
         rows.append(row)
-        del layer, q, k, v, u
-        torch.cuda.synchronize()
+        del layer
+    cache.clear()
+    torch.cuda.synchronize()
     return rows
 
 
@@ -364,8 +385,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (calibrates HBM counters)")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing")
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time the rho sweep on the Wan-1.3B shape and the other workloads")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the rho sweep, the window ablation and the other workloads")
     ap.add_argument("--router", default="top_rho", choices=["top_rho", "uniform", "random"],
                     help="routing of the timed layer (the ablation routers of the routing study)")
     ap.add_argument("--border", default="shift", choices=["shift", "cut"],
@@ -461,7 +482,8 @@ def main():
                    "window": list(w.window), "u": w.u_kind, "effective_flop": eff_flop,
                    "router": args.router, "border": args.border},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "kernel": "dense_bf16_kernel<128>",
+        "roofline": {"bound": "mfma",
+                     "kernel": "dense call: dense_bf16_kernel<128,false> + dense_merge_kernel<128,false>",
                      "achieved": round(dense_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dense_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "avg_launch_ms": round(res["dense_ms"], 5),
@@ -516,8 +538,8 @@ def main():
             f"({out['dense_rho1']['speedup_vs_rho1']}x slower than rho={rho})")
         del dl
 
-    if args.sweep:
-        out["sweep"] = run_sweep(het, W, torch, rho)
+    if not args.no_sweep and args.workload == "wan13b" and args.window is None and args.rho is None:
+        out["sweep"] = run_sweep(het, W, torch, (q, k, v, u), max(10, args.steps // 5), 3)
 
     if args.oracle_full:
         out["oracle_full"] = run_oracle_full(W)

@@ -46,7 +46,7 @@ _LIB_OVERRIDE = os.environ.get("HETATTN_ORACLE_LIB")
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (OpenMP, -O2, no fast-math)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
+        tmp = _LIB + f".tmp{os.getpid()}"  # several test workers may build at once
         subprocess.check_call(
             ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
              "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])

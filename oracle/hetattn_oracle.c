@@ -800,19 +800,19 @@ int oracle_attend_backward_kv_rows(const float *q, const float *k, const float *
                     continue;
                 for (int i = 0; i < nh; i++) {
                     const long base = b * N * tok_stride + (long)hsel[i] * D;
-                    const float *qrow = q + base + n * tok_stride, *dorow = dout + base + n * tok_stride;
+                    const float *qn = q + base + n * tok_stride, *don = dout + base + n * tok_stride;
                     const float *krow = k + base + j * tok_stride, *vrow = v + base + j * tok_stride;
                     double qk = 0.0, dp = 0.0;
                     for (int d = 0; d < D; d++) {
-                        qk += (double)qrow[d] * (double)krow[d];
-                        dp += (double)dorow[d] * (double)vrow[d];
+                        qk += (double)qn[d] * (double)krow[d];
+                        dp += (double)don[d] * (double)vrow[d];
                     }
                     const double p = exp(scale * qk - lse[n * nh + i]);
                     const double ds = p * (dp - dsum[n * nh + i]);
                     double *dkr = dk + (r * nh + i) * (long)D, *dvr = dv + (r * nh + i) * (long)D;
                     for (int d = 0; d < D; d++) {
-                        dkr[d] += scale * ds * (double)qrow[d];
-                        dvr[d] += p * (double)dorow[d];
+                        dkr[d] += scale * ds * (double)qn[d];
+                        dvr[d] += p * (double)don[d];
                     }
                 }
             }

@@ -134,6 +134,23 @@ def test_mean_std_gaussian_tail_matches_page_operating_point(oracle_mod):
     check_route_consistency(r, 1, N)
 
 
+def test_page_local_only_router(oracle_mod):
+    """The routing study's local-only row (§5.1, Routing Strategy, Table 6):
+    rho = 0 routes no token to dense attention, so the layer is pure local
+    attention (Eq. 13 with m = 1 everywhere)."""
+    with open(GOLDEN) as f:
+        rho = json.load(f)["local_only_router"]["rho"]
+    grid, window, N = (3, 4, 5), (3, 3, 3), 60
+    u = np.random.default_rng(21).random((2, N)).astype(np.float32)
+    r = oracle_mod.route_top_rho(u, rho)
+    assert (r.counts[:, 0] == 0).all() and (r.mask == 1).all() and (r.dense_idx == -1).all()
+    rng = np.random.default_rng(22)
+    q, k, v = (rng.standard_normal((2, N, 2, 8)).astype(np.float32) for _ in range(3))
+    got = oracle_mod.forward(q, k, v, grid, window, 0.3, r.mask)
+    local = oracle_mod.forward(q, k, v, grid, window, 0.3, np.ones((2, N), np.uint8))
+    np.testing.assert_array_equal(got, local)
+
+
 def test_mean_std_rejects_nonfinite_c(oracle_mod):
     u = np.zeros((1, 4), np.float32)
     for bad in (float("nan"), float("inf")):

@@ -6,10 +6,15 @@ Diffusion" (HetA-DiT): the swap of uncertain and certain tokens at each block
 Table 8).  Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel Random
 Numbers: As Easy as 1, 2, 3", SC'11.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 
 import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
 
 
 def test_philox_known_answers(oracle_mod):
@@ -151,6 +156,21 @@ def test_uniform_coverage_over_blocks(oracle_mod):
     mean = hits[local0].mean()
     assert abs(mean - blocks * p) < 0.02
     assert abs(hits[local0].var() - blocks * p * (1 - p)) < 0.1
+
+
+def test_page_coverage_figure_and_this_reading():
+    """App. B quotes a coverage of about 0.89 for r = 0.07 over B = 30 blocks,
+    i.e. 1-(1-r)^B with a certain token drawn with probability r per block.
+    Under this build's reading (S = round(rN) of the N - K certain tokens move
+    per block) a certain token is drawn with p = r/(1-rho), so its coverage is
+    higher: 0.936 at rho = 0.2 (test_uniform_coverage_over_blocks measures it
+    on the oracle's swaps)."""
+    with open(GOLDEN) as f:
+        g = json.load(f)["random_swap_coverage"]
+    r, blocks = g["r"], g["blocks"]
+    assert abs(1 - (1 - r) ** blocks - g["coverage_approx"]) < 0.005
+    p = r / (1 - 0.2)
+    assert abs(1 - (1 - p) ** blocks - 0.936) < 0.001
 
 
 def test_equal_draws_split_by_index(oracle_mod):

@@ -44,50 +44,32 @@ namespace {
 
 constexpr int kBwdQY = 4, kBwdQX = 8;  // query / key tile of the local rows: 4 (h) x 8 (w)
 
-template <typename T>
-struct Frag {
-    static constexpr bool kBf16 = std::is_same<T, __bf16>::value;
-    using type = typename std::conditional<kBf16, bf16x8, float>::type;
-    // MFMA k-steps over D: 16 bf16 or 2 fp32 per step.
-    template <int D>
-    static constexpr int steps() { return kBf16 ? D / 16 : D / 2; }
-};
+// The fp32 kernels' MFMA (v_mfma_f32_32x32x2_f32) takes one element per
+// lane and operand: k-step c of a D-element row is element 2c + half.
 
 // Fragment c of a row for a 32x32 MFMA operand (A: the lane's row; B: the
-// lane's column): bf16 elements 16c + 8*half .. +7, or fp32 element 2c + half.
-template <typename T>
-__device__ __forceinline__ typename Frag<T>::type load_frag(const T *row, int c, bool ok) {
+// lane's column), zero when !ok.
+__device__ __forceinline__ float load_frag(const float *row, int c, bool ok) {
     const int half = (threadIdx.x & 63) >> 5;
-    if constexpr (Frag<T>::kBf16) {
-        return ok ? *(const bf16x8 *)(row + 16 * c + 8 * half) : bf16x8{};
-    } else {
-        return ok ? row[2 * c + half] : 0.0f;
-    }
+    return ok ? row[2 * c + half] : 0.0f;
 }
 
-template <typename T>
-__device__ __forceinline__ f32x16 mma(const typename Frag<T>::type &a, const typename Frag<T>::type &b,
-                                      const f32x16 &c) {
-    if constexpr (Frag<T>::kBf16) return mfma32_bf16(a, b, c);
-    else return mfma32_f32(a, b, c);
-}
-
-// LDS slab of 32 rows of D elements (row pitch padded against bank
+// LDS slab of 32 fp32 rows of D elements (row pitch padded against bank
 // conflicts, as in the local kernel's V slab).
-template <typename T, int D>
+template <int D>
 struct Slab {
-    static constexpr int kPitch = Frag<T>::kBf16 ? D + 16 : D + 4;
-    static constexpr int kVec = 16 / sizeof(T);     // elements per 16-byte load
-    static constexpr int kChunks = D / kVec;        // 16-byte chunks per row
+    static constexpr int kPitch = D + 4;
+    static constexpr int kVec = 4;                   // elements per 16-byte load
+    static constexpr int kChunks = D / kVec;         // 16-byte chunks per row
     static constexpr int kStage = 32 * kChunks / 64; // chunks per lane
 };
 
 // Copies row `row_of(s)` (or zeros when !ok_of(s)) of each slot s < 32 into
 // the slab; the first kThreads threads of the workgroup move the 16-byte
 // chunks between them.
-template <typename T, int D, int kThreads = 64, typename RowOf, typename OkOf>
-__device__ __forceinline__ void stage_rows(T *slab, RowOf &&row_of, OkOf &&ok_of) {
-    using S = Slab<T, D>;
+template <int D, int kThreads = 64, typename RowOf, typename OkOf>
+__device__ __forceinline__ void stage_rows(float *slab, RowOf &&row_of, OkOf &&ok_of) {
+    using S = Slab<D>;
     constexpr int kTotal = 32 * S::kChunks;
     static_assert(kTotal % kThreads == 0, "chunks per thread");
     const int tid = threadIdx.x % kThreads;
@@ -100,51 +82,26 @@ __device__ __forceinline__ void stage_rows(T *slab, RowOf &&row_of, OkOf &&ok_of
 }
 
 // Fragment c of slab row l%32 as a 32x32 MFMA operand (as load_frag).
-template <typename T, int D>
-__device__ __forceinline__ typename Frag<T>::type lds_frag(const T *slab, int c) {
-    using S = Slab<T, D>;
+template <int D>
+__device__ __forceinline__ float lds_frag(const float *slab, int c) {
     const int lane = threadIdx.x & 63, half = lane >> 5, row = lane & 31;
-    if constexpr (Frag<T>::kBf16) return *(const bf16x8 *)(slab + row * S::kPitch + 16 * c + 8 * half);
-    else return slab[row * S::kPitch + 2 * c + half];
+    return slab[row * Slab<D>::kPitch + 2 * c + half];
 }
 
 // acc[db] += X^T B, X = the slab (32 slots x D, slot order of the B
 // operand's k index), B = the 16 per-lane values w[i] of a C-layout block
 // (lane: column l%32; w[i]: slot 8(i/4) + 4*half + i%4).  Result rows are
 // dims db*32 + l%32.
-template <typename T, int D>
-__device__ __forceinline__ void mma_slab_t(const T *slab, const float (&w)[16], f32x16 (&acc)[D / 32]) {
-    using S = Slab<T, D>;
+template <int D>
+__device__ __forceinline__ void mma_slab_t(const float *slab, const float (&w)[16], f32x16 (&acc)[D / 32]) {
     const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
-    if constexpr (Frag<T>::kBf16) {
-        bf16x8 wf[2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            u32x4 u;
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) u[jj] = pack_bf16x2(w[8 * c + 2 * jj], w[8 * c + 2 * jj + 1]);
-            wf[c] = __builtin_bit_cast(bf16x8, u);
+        for (int i = 0; i < 16; ++i) {
+            const float a = slab[(8 * (i / 4) + 4 * half + (i % 4)) * Slab<D>::kPitch + db * 32 + col];
+            acc[db] = mfma32_f32(a, w[i], acc[db]);
         }
-        const int gq = lane >> 4, j16 = lane & 15;
-        const int key_off = 4 * half + (j16 >> 2), col_off = 16 * (gq & 1) + 4 * (j16 & 3);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const __bf16 *base = (const __bf16 *)slab + (16 * c + key_off) * S::kPitch + db * 32 + col_off;
-                const bf16x4 lo = lds_read_tr16((const HET_LDS void *)base);
-                const bf16x4 hi = lds_read_tr16((const HET_LDS void *)(base + 8 * S::kPitch));
-                acc[db] = mfma32_bf16(concat8(lo, hi), wf[c], acc[db]);
-            }
-    } else {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float a = ((const float *)slab)[(8 * (i / 4) + 4 * half + (i % 4)) * S::kPitch + db * 32 + col];
-                acc[db] = mfma32_f32(a, w[i], acc[db]);
-            }
-    }
 }
 
 // Stores the C-layout accumulators (rows = dims) of this lane's column as one
@@ -157,7 +114,7 @@ __device__ __forceinline__ void store_row_t(T *row, const f32x16 (&acc)[D / 32],
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const int d = db * 32 + 8 * i4 + 4 * half;
-            if constexpr (Frag<T>::kBf16) {
+            if constexpr (std::is_same<T, __bf16>::value) {
                 u32x2 w;
                 w[0] = pack_bf16x2(acc[db][4 * i4 + 0] * mul, acc[db][4 * i4 + 1] * mul);
                 w[1] = pack_bf16x2(acc[db][4 * i4 + 2] * mul, acc[db][4 * i4 + 3] * mul);
@@ -213,11 +170,11 @@ constexpr int kBwdWaves = 4;  // waves of the dense-dQ and dK/dV workgroups
 // wave w takes 32 of them; the four waves share every 32-key block of K and
 // V, staged once into LDS (row reads for S and dP, transposed reads of K for
 // dQ += dS K).
-template <typename T, int D>
+template <int D>
 __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dq_dense_kernel(BwdArgs a, int n_units) {
-    using F = Frag<T>;
-    using S = Slab<T, D>;
-    constexpr int kSteps = F::template steps<D>();
+    using T = float;
+    using S = Slab<D>;
+    constexpr int kSteps = D / 2;
     __shared__ __attribute__((aligned(16))) T Ks[32 * S::kPitch];
     __shared__ __attribute__((aligned(16))) T Vs[32 * S::kPitch];
 
@@ -238,7 +195,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dq_dense_kernel(BwdArgs a,
     const size_t row_bh = ((size_t)b * H + h) * N;
     const float sl2 = a.scale * kLog2e;
 
-    typename F::type qf[kSteps], df[kSteps];
+    float qf[kSteps], df[kSteps];
 #pragma unroll
     for (int c = 0; c < kSteps; ++c) {
         qf[c] = load_frag(q + sample + (size_t)tok * tok_stride, c, valid);
@@ -283,7 +240,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dq_dense_kernel(BwdArgs a,
         if (kb + 1 < n_blocks) fetch(kb + 1, false);
         f32x16 sc = f32x16{};
 #pragma unroll
-        for (int c = 0; c < kSteps; ++c) sc = mma<T>(lds_frag<T, D>(Ks, c), qf[c], sc);
+        for (int c = 0; c < kSteps; ++c) sc = mfma32_f32(lds_frag<D>(Ks, c), qf[c], sc);
         float mx = -__builtin_inff();
 #pragma unroll
         for (int i = 0; i < 16; ++i)
@@ -316,8 +273,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dq_dense_kernel(BwdArgs a,
         f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int c = 0; c < kSteps; ++c) {
-            sc = mma<T>(lds_frag<T, D>(Ks, c), qf[c], sc);
-            dp = mma<T>(lds_frag<T, D>(Vs, c), df[c], dp);
+            sc = mfma32_f32(lds_frag<D>(Ks, c), qf[c], sc);
+            dp = mfma32_f32(lds_frag<D>(Vs, c), df[c], dp);
         }
         float ds[16];
 #pragma unroll
@@ -325,7 +282,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dq_dense_kernel(BwdArgs a,
             const float p = in_block(kb, i) ? __builtin_amdgcn_exp2f(sc[i] * sl2 - lse2) : 0.0f;
             ds[i] = p * (dp[i] - dq_i);
         }
-        mma_slab_t<T, D>(Ks, ds, acc);
+        mma_slab_t<D>(Ks, ds, acc);
     }
     if (valid) store_row_t<T, D>((T *)a.dq + sample + (size_t)tok * tok_stride, acc, a.scale);
 }
@@ -577,11 +534,11 @@ __device__ __forceinline__ void bwd_dq_dense_bf16(const BwdArgs &a, int unit, HE
 // dQ of 32 query rows (kDense: 32 consecutive entries of the dense index
 // list -- the one-wave form; the dense rows use bwd_dq_dense_kernel -- else
 // a 4x8 tile of local rows of one frame), and LSE of those rows.
-template <typename T, int D, bool kDense, int SR>
+template <int D, bool kDense, int SR>
 __global__ __launch_bounds__(64) void bwd_dq_kernel(BwdArgs a, LocalGeom g, int n_units) {
-    using F = Frag<T>;
-    using S = Slab<T, D>;
-    constexpr int kSteps = F::template steps<D>();
+    using T = float;
+    using S = Slab<D>;
+    constexpr int kSteps = D / 2;
     constexpr int rpb = 32 / SR;  // box rows per key block (local rows)
     __shared__ __attribute__((aligned(16))) T Ks[32 * S::kPitch];
 
@@ -666,7 +623,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BwdArgs a, LocalGeom g, int 
         }
     };
 
-    typename F::type qf[kSteps], df[kSteps];
+    float qf[kSteps], df[kSteps];
 #pragma unroll
     for (int c = 0; c < kSteps; ++c) {
         qf[c] = load_frag(q + sample + (size_t)tok * tok_stride, c, valid);
@@ -682,7 +639,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BwdArgs a, LocalGeom g, int 
         const bool kok = slot_ok(kb, col);
         f32x16 s = f32x16{};
 #pragma unroll
-        for (int c = 0; c < kSteps; ++c) s = mma<T>(load_frag(k + sample + (size_t)kt * tok_stride, c, kok), qf[c], s);
+        for (int c = 0; c < kSteps; ++c) s = mfma32_f32(load_frag(k + sample + (size_t)kt * tok_stride, c, kok), qf[c], s);
         return s;
     };
 
@@ -715,7 +672,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BwdArgs a, LocalGeom g, int 
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
     for (int kb = 0; kb < n_blocks; ++kb) {
-        stage_rows<T, D>(
+        stage_rows<D>(
             Ks, [&](int s) HET_INLINE { return k + sample + (size_t)slot_token(kb, s) * tok_stride; },
             [&](int s) HET_INLINE { return slot_ok(kb, s); });
         const f32x16 s = scores(kb);
@@ -723,7 +680,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BwdArgs a, LocalGeom g, int 
         const bool kok = slot_ok(kb, col);
         f32x16 dp = f32x16{};
 #pragma unroll
-        for (int c = 0; c < kSteps; ++c) dp = mma<T>(load_frag(v + sample + (size_t)kt * tok_stride, c, kok), df[c], dp);
+        for (int c = 0; c < kSteps; ++c) dp = mfma32_f32(load_frag(v + sample + (size_t)kt * tok_stride, c, kok), df[c], dp);
         float ds[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -731,7 +688,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BwdArgs a, LocalGeom g, int 
             ds[i] = p * (dp[i] - dq_i);
         }
         __syncthreads();  // the K slab is visible to the whole wave
-        mma_slab_t<T, D>(Ks, ds, acc);
+        mma_slab_t<D>(Ks, ds, acc);
         __syncthreads();  // slab free for the next block
     }
     if (valid) store_row_t<T, D>((T *)a.dq + sample + (size_t)tok * tok_stride, acc, a.scale);
@@ -742,12 +699,12 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BwdArgs a, LocalGeom g, int 
 // every 32-query block: Q and dO rows, LSE, D and the window of each query,
 // staged once into LDS (row reads for S and dP, transposed reads for dK and
 // dV).
-template <typename T, int D>
+template <int D>
 __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dkdv_kernel(BwdArgs a, LocalGeom g, int x_groups,
                                                                   int n_units) {
-    using F = Frag<T>;
-    using S = Slab<T, D>;
-    constexpr int kSteps = F::template steps<D>();
+    using T = float;
+    using S = Slab<D>;
+    constexpr int kSteps = D / 2;
     constexpr int kThreads = 64 * kBwdWaves;
     __shared__ __attribute__((aligned(16))) T Qs[32 * S::kPitch];
     __shared__ __attribute__((aligned(16))) T Ds[32 * S::kPitch];
@@ -779,7 +736,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dkdv_kernel(BwdArgs a, Loc
     const size_t row_bh = ((size_t)b * H + h) * N;
     const float sl2 = a.scale * kLog2e;
 
-    typename F::type kf[kSteps], vf[kSteps];
+    float kf[kSteps], vf[kSteps];
 #pragma unroll
     for (int c = 0; c < kSteps; ++c) {
         kf[c] = load_frag(k + sample + (size_t)ktok * tok_stride, c, key_ok);
@@ -857,8 +814,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dkdv_kernel(BwdArgs a, Loc
             f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int c = 0; c < kSteps; ++c) {
-                sc = mma<T>(lds_frag<T, D>(Qs, c), kf[c], sc);
-                dp = mma<T>(lds_frag<T, D>(Ds, c), vf[c], dp);
+                sc = mfma32_f32(lds_frag<D>(Qs, c), kf[c], sc);
+                dp = mfma32_f32(lds_frag<D>(Ds, c), vf[c], dp);
             }
             float p[16], ds[16];
 #pragma unroll
@@ -873,8 +830,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_dkdv_kernel(BwdArgs a, Loc
                 p[i] = in ? __builtin_amdgcn_exp2f(sc[i] * sl2 - __int_as_float(rec.w)) : 0.0f;
                 ds[i] = p[i] * (dp[i] - s_d[qs]);
             }
-            mma_slab_t<T, D>(Ds, p, dv);   // dV^T += dO^T P
-            mma_slab_t<T, D>(Qs, ds, dk);  // dK^T += Q^T dS
+            mma_slab_t<D>(Ds, p, dv);   // dV^T += dO^T P
+            mma_slab_t<D>(Qs, ds, dk);  // dK^T += Q^T dS
         }
     };
 
@@ -1695,15 +1652,15 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
                            dim3(256), 0, stream, (const float *)a.o, (const float *)a.dout, a.dsum, rows, a.n,
                            a.heads);
         if (dense_units > 0)
-            hipLaunchKernelGGL((bwd_dq_dense_kernel<float, D_>), dim3(dense_units), dim3(64 * kBwdWaves), 0, stream,
+            hipLaunchKernelGGL((bwd_dq_dense_kernel<D_>), dim3(dense_units), dim3(64 * kBwdWaves), 0, stream,
                                a, dense_units);
         if (sr16)
-            hipLaunchKernelGGL((bwd_dq_kernel<float, D_, false, 16>), dim3(tile_units), dim3(64), 0, stream, a, g,
+            hipLaunchKernelGGL((bwd_dq_kernel<D_, false, 16>), dim3(tile_units), dim3(64), 0, stream, a, g,
                                tile_units);
         else
-            hipLaunchKernelGGL((bwd_dq_kernel<float, D_, false, 32>), dim3(tile_units), dim3(64), 0, stream, a, g,
+            hipLaunchKernelGGL((bwd_dq_kernel<D_, false, 32>), dim3(tile_units), dim3(64), 0, stream, a, g,
                                tile_units);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<float, D_>), dim3(key_units), dim3(64 * kBwdWaves), 0, stream, a, g,
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D_>), dim3(key_units), dim3(64 * kBwdWaves), 0, stream, a, g,
                            x_groups, key_units);
         return hipGetLastError();
     };

@@ -579,14 +579,13 @@ __global__ __launch_bounds__(256) void dense_merge_kernel(
     }
 }
 
-// The f32 path below uses kDenseBM queries per workgroup and a plain grid.
-template <typename T, int D, int BN>
-struct DenseTile {
-    static constexpr int kPadK = (sizeof(T) == 2) ? 8 : 4;
-    static constexpr int kPadV = (sizeof(T) == 2) ? 16 : 4;
-    static constexpr int kPitchK = D + kPadK;     // elements
-    static constexpr int kPitchV = D + kPadV;
-    static constexpr int kVec = 16 / sizeof(T);   // elements per 16-byte load
+// The f32 path below uses kDenseBM queries per workgroup and a plain grid;
+// K and V tiles are staged in LDS with rows padded against bank conflicts.
+template <int D, int BN>
+struct DenseTileF32 {
+    static constexpr int kPitchK = D + 4;         // elements
+    static constexpr int kPitchV = D + 4;
+    static constexpr int kVec = 4;                // elements per 16-byte load
     static constexpr int kChunksPerRow = D / kVec;
     static constexpr int kRowsPerPass = kDenseThreads / kChunksPerRow;
     static constexpr int kPasses = BN / kRowsPerPass;
@@ -603,7 +602,7 @@ __global__ __launch_bounds__(kDenseThreads) void dense_f32_kernel(
     float *__restrict__ o, const int32_t *__restrict__ dense_idx,
     const int32_t *__restrict__ counts, int N, int H, float scale_log2) {
     constexpr int BN = 32;
-    using Tl = DenseTile<float, D, BN>;
+    using Tl = DenseTileF32<D, BN>;
     __shared__ __attribute__((aligned(16))) float Ks[BN * Tl::kPitchK];
     __shared__ __attribute__((aligned(16))) float Vs[BN * Tl::kPitchV];
 

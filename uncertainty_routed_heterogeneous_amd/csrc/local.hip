@@ -6,23 +6,20 @@
 // for the tokens with m_i = 1 (§3.2.2 Eqs. 12-13).  This is the
 // (1-rho)*N*M*d_h term of the cost model (§3.2.2 Eq. 14).
 //
-// One wave = one query tile of 4 (h) x 8 (w) grid positions at one t, for
-// one (sample, head).  Because the window is shifted rather than cut at the
-// border, the union of the tile's windows is a box: lt frames x ny rows x nx
-// columns.  That box is walked in key blocks of 32 slots, each block holding
-// 32/SR box rows of SR column slots (SR = 16 when nx <= 16, else 32), so every
-// key block is one 32x32 MFMA tile; per (query, key) a mask keeps only the
-// query's own window.  Dense tokens inside a tile ride along and are not
-// stored.
+// Query tiles are 32 grid positions of one frame of one (sample, head).
+// Because the window is shifted rather than cut at the border, the union of
+// a tile's windows is a box (frames x rows x columns); it is walked in key
+// blocks of 32 slots, each block holding 32/SR box rows of SR column slots,
+// so every key block is one 32x32 MFMA tile, and per (query, key) a mask
+// keeps only the query's own window.  Dense tokens inside a tile ride along
+// and are not stored.
 //
-// Memory: the layer is bandwidth-bound (about 65 flop per byte), so the
-// tiles are ordered (sample, head, t, y, x) and dealt to XCDs in contiguous
-// runs: neighbouring tiles, whose key boxes overlap, share one L2.  K rows
-// feed the MFMA straight from global memory; V goes through a per-wave LDS
-// slab and is read transposed.  The next key block's K and V are fetched into
-// registers while the current block computes.  Slots outside the box load a
-// clamped in-grid address and are zeroed (V) or masked (scores), so no load
-// is predicated.
+// local_band_kernel (bf16, the layer's local kernel and its statistics and
+// gradient forms): 8-wave workgroups share one key box streamed through LDS
+// in bands by buffer DMA; see its comment below.
+// local_f32_kernel (fp32 inputs, for fp32 parity): one wave per 4x8 tile, K
+// rows straight from global memory into the MFMA, V through a per-wave LDS
+// slab.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,19 +28,24 @@ namespace hetattn {
 constexpr int kLocalQY = 4;
 constexpr int kLocalQX = 8;
 
-
-
-template <typename T, int D, int SR>
-__global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
+// fp32 form: one wave = one query tile of 4 (h) x 8 (w) grid positions at
+// one t, v_mfma_f32_32x32x2_f32.  The tiles are ordered (sample, head, t, y,
+// x) and dealt to XCDs in contiguous runs, so that neighbouring tiles, whose
+// key boxes overlap, share one L2.  The next key block's K and V are fetched
+// into registers while the current block computes; slots outside the box
+// load a clamped in-grid address and are zeroed (V) or masked (scores), so
+// no load is predicated.
+template <int D, int SR>
+__global__ __launch_bounds__(64) void local_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v, float *__restrict__ o,
     const uint8_t *__restrict__ mask, int N, int H, float scale_log2, LocalGeom g, int n_units) {
-    constexpr bool kBf16 = sizeof(T) == 2;
     constexpr int rpb = 32 / SR;                  // box rows per key block
-    constexpr int kVec = 16 / sizeof(T);          // elements per 16-byte load
+    constexpr int kVec = 4;                       // floats per 16-byte load
     constexpr int kChunks = D / kVec;             // 16-byte chunks per row
     constexpr int kStage = 32 * kChunks / 64;     // V chunks staged per lane per block
-    constexpr int kPitchV = kBf16 ? D + 16 : D + 4;
-    __shared__ __attribute__((aligned(16))) T Vs[32 * kPitchV];
+    constexpr int kPitchV = D + 4;
+    constexpr int kKRegs = D / 2;
+    __shared__ __attribute__((aligned(16))) float Vs[32 * kPitchV];
 
     const int unit = xcd_remap(blockIdx.x, gridDim.x);
     if (unit >= n_units) return;
@@ -81,8 +83,8 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
     const int n_blocks = (rows + rpb - 1) / rpb;
 
     const size_t tok_stride = (size_t)H * D;
-    const T *kbase = k + (size_t)b * N * tok_stride + (size_t)h * D;
-    const T *vbase = v + (size_t)b * N * tok_stride + (size_t)h * D;
+    const float *kbase = k + (size_t)b * N * tok_stride + (size_t)h * D;
+    const float *vbase = v + (size_t)b * N * tok_stride + (size_t)h * D;
 
     // Box row r -> token of its first column (rows past the box clamp to the
     // last row).  r is the same for the whole wave, so this runs on the SALU.
@@ -99,25 +101,18 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
     float l_part = 0.0f;
 
     // Staging of one block: this lane's K row (A operand) and its share of V rows.
-    constexpr int kKRegs = kBf16 ? D / 16 : D / 2;
-    typedef typename std::conditional<kBf16, bf16x8, float>::type KFrag;
-    KFrag kf[kKRegs], kn[kKRegs];
+    float kf[kKRegs], kn[kKRegs];
     u32x4 vst[kStage];
     bool vok[kStage];
     // Slot s = rr*SR + xo of a block lies in box row rr of the block; slots
     // past the row (xo >= nx) or past the box load a clamped in-box address.
-    auto fetch = [&](int kb, KFrag *kdst) HET_INLINE {
+    auto fetch = [&](int kb, float *kdst) HET_INLINE {
         const int rt0 = row_token(kb * rpb), rt1 = row_token(kb * rpb + 1);
         const bool ok0 = kb * rpb < rows, ok1 = rpb > 1 && kb * rpb + 1 < rows;
         const int jk = ((col / SR) ? rt1 : rt0) + imin(col % SR, nx - 1);
-        const T *kp = kbase + (size_t)jk * tok_stride;
-        if constexpr (kBf16) {
+        const float *kp = kbase + (size_t)jk * tok_stride;
 #pragma unroll
-            for (int c = 0; c < kKRegs; ++c) kdst[c] = *(const bf16x8 *)((const __bf16 *)kp + 16 * c + 8 * half);
-        } else {
-#pragma unroll
-            for (int c = 0; c < kKRegs; ++c) kdst[c] = ((const float *)kp)[2 * c + half];
-        }
+        for (int c = 0; c < kKRegs; ++c) kdst[c] = kp[2 * c + half];
         // Lane stages slot (P*it + lane/kChunks), chunk lane%kChunks, P = 64/kChunks;
         // P*it % SR + P - 1 < SR, so the slot's row (P*it)/SR is known per it.
         constexpr int P = 64 / kChunks;
@@ -140,23 +135,12 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
     };
 
     // Query operand.
-    typedef typename std::conditional<kBf16, bf16x8, float>::type QFrag;
-    QFrag qf[kKRegs];
+    float qf[kKRegs];
     {
-        const T *qp = q + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
-        if constexpr (kBf16) {
+        const float *qp = q + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
 #pragma unroll
-            for (int c = 0; c < kKRegs; ++c)
-                qf[c] = is_local ? *(const bf16x8 *)((const __bf16 *)qp + 16 * c + 8 * half) : bf16x8{};
-        } else {
-#pragma unroll
-            for (int c = 0; c < kKRegs; ++c) qf[c] = is_local ? ((const float *)qp)[2 * c + half] : 0.0f;
-        }
+        for (int c = 0; c < kKRegs; ++c) qf[c] = is_local ? qp[2 * c + half] : 0.0f;
     }
-
-    const int gq = lane >> 4, j16 = lane & 15;
-    const int v_key_off = 4 * half + (j16 >> 2);
-    const int v_col_off = 16 * (gq & 1) + 4 * (j16 & 3);
 
     fetch(0, kf);
     for (int kb = 0; kb < n_blocks; ++kb) {
@@ -168,10 +152,7 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
         // S^T = K Q^T for this block.
         f32x16 s = f32x16{};
 #pragma unroll
-        for (int c = 0; c < kKRegs; ++c) {
-            if constexpr (kBf16) s = mfma32_bf16(kn[c], qf[c], s);
-            else s = mfma32_f32(kn[c], qf[c], s);
-        }
+        for (int c = 0; c < kKRegs; ++c) s = mfma32_f32(kn[c], qf[c], s);
 
         // Keep only keys inside this query's window.  Register i holds slot
         // 8(i/4) + 4*half + i%4 of the block: box row (i/4 >= 2 && SR == 16),
@@ -210,43 +191,18 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
         const float neg_m = -m_use;
 
         __syncthreads();  // V slab of this block visible to the whole wave
-        if constexpr (kBf16) {
-            bf16x8 pf[2];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                u32x4 w;
+        for (int i = 0; i < 16; ++i) {
+            s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, neg_m));
+            l_part += s[i];
+        }
+        // MFMA i: both halves contribute register i = key 8(i/4) + 4*half + i%4.
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + 2 * jj], scale_log2, neg_m));
-                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + 2 * jj + 1], scale_log2, neg_m));
-                    l_part += p0 + p1;
-                    w[jj] = pack_bf16x2(p0, p1);
-                }
-                pf[c] = __builtin_bit_cast(bf16x8, w);
-            }
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const __bf16 *base = (const __bf16 *)Vs + (16 * c + v_key_off) * kPitchV + db * 32 + v_col_off;
-                    const bf16x4 lo = lds_read_tr16((const HET_LDS void *)base);
-                    const bf16x4 hi = lds_read_tr16((const HET_LDS void *)(base + 8 * kPitchV));
-                    oacc[db] = mfma32_bf16(concat8(lo, hi), pf[c], oacc[db]);
-                }
-            }
-        } else {
+        for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, neg_m));
-                l_part += s[i];
-            }
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float a = ((const float *)Vs)[(8 * (i / 4) + 4 * half + (i % 4)) * kPitchV + db * 32 + col];
-                    oacc[db] = mfma32_f32(a, s[i], oacc[db]);
-                }
+                const float a = Vs[(8 * (i / 4) + 4 * half + (i % 4)) * kPitchV + db * 32 + col];
+                oacc[db] = mfma32_f32(a, s[i], oacc[db]);
             }
         }
         __syncthreads();  // slab free for the next block
@@ -254,22 +210,15 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void local_kernel(
 
     if (!is_local) return;
     const float inv_l = 1.0f / half_pair_sum(l_part);
-    T *op = o + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
+    float *op = o + ((size_t)b * N + tok) * tok_stride + (size_t)h * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const int d = db * 32 + 8 * i4 + 4 * half;
-            if constexpr (kBf16) {
-                u32x2 w;
-                w[0] = pack_bf16x2(oacc[db][4 * i4 + 0] * inv_l, oacc[db][4 * i4 + 1] * inv_l);
-                w[1] = pack_bf16x2(oacc[db][4 * i4 + 2] * inv_l, oacc[db][4 * i4 + 3] * inv_l);
-                *(u32x2 *)((__bf16 *)op + d) = w;
-            } else {
-                f32x4 w = {oacc[db][4 * i4 + 0] * inv_l, oacc[db][4 * i4 + 1] * inv_l,
-                           oacc[db][4 * i4 + 2] * inv_l, oacc[db][4 * i4 + 3] * inv_l};
-                *(f32x4 *)((float *)op + d) = w;
-            }
+            f32x4 w = {oacc[db][4 * i4 + 0] * inv_l, oacc[db][4 * i4 + 1] * inv_l,
+                       oacc[db][4 * i4 + 2] * inv_l, oacc[db][4 * i4 + 3] * inv_l};
+            *(f32x4 *)(op + d) = w;
         }
     }
 }
@@ -771,14 +720,14 @@ hipError_t launch_local(const AttnArgs &a, hipStream_t stream) {
     const int units = a.batch * a.heads * g.T * g.tiles_y * g.tiles_x;
     const dim3 grid((units + 7) / 8 * 8);
     const float sl2 = a.scale * kLog2e;
-#define HET_LOCAL_LAUNCH(T_, D_, SR_)                                                             \
-    hipLaunchKernelGGL((local_kernel<T_, D_, SR_>), grid, dim3(64), 0, stream, (const T_ *)a.q,   \
-                       (const T_ *)a.k, (const T_ *)a.v, (T_ *)a.o, a.mask, a.n, a.heads, sl2, g, units)
+#define HET_LOCAL_LAUNCH(D_, SR_)                                                                   \
+    hipLaunchKernelGGL((local_f32_kernel<D_, SR_>), grid, dim3(64), 0, stream, (const float *)a.q,  \
+                       (const float *)a.k, (const float *)a.v, (float *)a.o, a.mask, a.n, a.heads, sl2, g, units)
     const bool sr16 = g.slot_row == 16;
     if (a.head_dim == 128) {
-        if (sr16) HET_LOCAL_LAUNCH(float, 128, 16); else HET_LOCAL_LAUNCH(float, 128, 32);
+        if (sr16) HET_LOCAL_LAUNCH(128, 16); else HET_LOCAL_LAUNCH(128, 32);
     } else {
-        if (sr16) HET_LOCAL_LAUNCH(float, 64, 16); else HET_LOCAL_LAUNCH(float, 64, 32);
+        if (sr16) HET_LOCAL_LAUNCH(64, 16); else HET_LOCAL_LAUNCH(64, 32);
     }
 #undef HET_LOCAL_LAUNCH
     return hipGetLastError();
