@@ -342,13 +342,17 @@ def run_sweep(het, W, torch, main_inputs, steps: int, warmup: int):
     return rows
 
 
-def run_oracle_full(W):
+def run_oracle_full(W, everything: bool = False):
     """The fp64 oracle on whole layers (route + every dense and local row),
-    timed on the host cores."""
+    timed on the host cores: the tiny case and the Wan-1.3B layer at rho =
+    0.2 (about a minute on 16 threads), or with `everything` also the rho
+    sweep and the other workloads (tens of minutes)."""
     import numpy as np
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
-    cases = [("tiny", None)] + [("wan13b", r) for r in W.RHO_SWEEP] + [("wan5b", None), ("long", None)]
+    cases = [("tiny", None), ("wan13b", None)]
+    if everything:
+        cases += [("wan13b", r) for r in W.RHO_SWEEP if r != 0.2] + [("wan5b", None), ("long", None)]
     rows = []
     for name, r in cases:
         w = W.WORKLOADS[name]
@@ -363,7 +367,7 @@ def run_oracle_full(W):
         t2 = time.perf_counter()
         eff = W.effective_flops(w.with_(rho=rho))
         row = {"workload": name, "rho": rho, "route_s": round(t1 - t0, 3), "forward_s": round(t2 - t1, 2),
-               "effective_TFLOPs": round(eff / (t2 - t0) / 1e12, 5), "threads": threads}
+               "effective_TFLOPs": round(eff / (t2 - t0) / 1e12, 5), "threads": threads, "cpu": cpu_model()}
         log(f"[bench] oracle {row}")
         rows.append(row)
     return rows
@@ -396,7 +400,9 @@ def main():
     ap.add_argument("--swap-ratio", type=float, default=0.07,
                     help="ratio r of the per-block random swap timed beside the step (0 skips it)")
     ap.add_argument("--oracle-full", action="store_true",
-                    help="also time the fp64 oracle on whole layers (minutes of host time)")
+                    help="also time the fp64 oracle on the whole tiny and Wan-1.3B layers (about a minute)")
+    ap.add_argument("--oracle-full-all", action="store_true",
+                    help="with --oracle-full: also the rho sweep and the other workloads (tens of minutes)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -542,7 +548,7 @@ def main():
         out["sweep"] = run_sweep(het, W, torch, (q, k, v, u), max(10, args.steps // 5), 3)
 
     if args.oracle_full:
-        out["oracle_full"] = run_oracle_full(W)
+        out["oracle_full"] = run_oracle_full(W, args.oracle_full_all)
 
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 CPU oracle on a sample ...")
