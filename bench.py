@@ -87,6 +87,9 @@ class Layer:
         ws = het.workspace_bytes(self.shape)
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
         self.ws_bytes = ws
+        rws = int(self.lib.het_attn_route_workspace_bytes(ctypes.byref(self.shape)))
+        self.rws = torch.empty(max(rws, 1), dtype=torch.uint8, device=dev)
+        self.rws_bytes = rws
         self.args = (ctypes.byref(self.shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                      ctypes.byref(self.rs), self.o.data_ptr(), self.ws.data_ptr(), ws, self.stream)
 
@@ -97,7 +100,8 @@ class Layer:
         else:
             mode = self.het.HET_UNIFORM if self.router == "uniform" else self.het.HET_TOP_RHO
             st = self.lib.het_attn_route(ctypes.byref(self.shape), self.u.data_ptr(), mode, self.rho,
-                                         ctypes.byref(self.rs), self.stream)
+                                         ctypes.byref(self.rs), self.rws.data_ptr(), self.rws_bytes,
+                                         self.stream)
         if st != 0:
             raise self.het.HetAttnError(st, "route (" + self.router + ")")
 

@@ -45,7 +45,9 @@
  *
  * Memory.  All tensor arguments are device pointers owned by the caller; the
  * library allocates and frees nothing and keeps no state between calls,
- * except the static scratch array of het_attn_forward_noalloc (see there).
+ * except the static scratch array of het_attn_forward_noalloc (see there)
+ * and a count of het_attn_route calls (which tags the words each call
+ * exchanges through its workspace).
  * Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
  * return without waiting for it.  `shape` and `route` themselves are host
  * structs read during the call only.
@@ -65,7 +67,7 @@
 extern "C" {
 #endif
 
-#define HETATTN_ABI_VERSION 4
+#define HETATTN_ABI_VERSION 5
 
 typedef enum {
     HET_OK = 0,
@@ -121,15 +123,32 @@ const char *het_status_string(int status);
  * Returns 0 for an invalid shape as well; het_attn_forward reports that. */
 size_t het_attn_workspace_bytes(const het_attn_shape *shape);
 
+/* Device workspace het_attn_route needs in HET_TOP_RHO mode for this shape,
+ * in bytes (0: none; HET_MEAN_STD and HET_UNIFORM need none).  Samples of
+ * 8192 to 262144 tokens (at most 1024 workgroups of 2048 tokens in all) are
+ * routed by several workgroups per sample, which exchange histograms and
+ * counts through it.  0 for an invalid shape too. */
+size_t het_attn_route_workspace_bytes(const het_attn_shape *shape);
+
 /* Threshold selection, mask and stable compaction ([HetA §3.2.2 Eqs. 11-12]).
  *   u      device, float32 [B, N], read only (not read, and may be NULL, for
  *          HET_UNIFORM).
  *   mode   het_thresh_mode; param = rho (TOP_RHO) or c (MEAN_STD).
  *   out    host struct of caller-owned device buffers, all written;
  *          out->dense_count_host is written on the host.
- * Deterministic: the same u gives bit-identical outputs. */
+ *   workspace, workspace_bytes: device scratch of at least
+ *          het_attn_route_workspace_bytes(shape) bytes (NULL allowed when
+ *          that is 0), any contents: the call needs no clearing and leaves
+ *          only scratch there.  Calls that may run at the same time need
+ *          workspaces of their own.  Too small: HET_ERR_WORKSPACE.
+ * Deterministic: the same u gives bit-identical outputs, whichever of the
+ * two kernels routes the shape.  The workgroups of one sample wait for each
+ * other's data; each wait is bounded, and counts[2b] = counts[2b+1] = -1
+ * marks a sample whose workgroups were not all running at once within it or
+ * whose exchanged data failed their consistency check (neither seen on an
+ * otherwise idle device); its index lists are then not written. */
 int het_attn_route(const het_attn_shape *shape, const float *u, int mode, double param,
-                   het_route *out, void *stream);
+                   het_route *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Random routing per block, the other router of the routing ablation
  * ([HetA §5.1, Routing Strategy, Table 6]): for each block l in

@@ -19,6 +19,9 @@ extern hetattn::RouteArgs route;
 extern hetattn::AttnArgs attn;
 extern hetattn::BwdArgs bwd;
 extern int swap_blocks;
+extern int route_mb_launches;
+extern void *route_ws;
+extern uint32_t route_nonce;
 }  // namespace stub
 
 static int failures = 0;
@@ -50,26 +53,43 @@ int main() {
     het_route r = {(uint8_t *)fake(1), (int32_t *)fake(2), (int32_t *)fake(3), (int32_t *)fake(4),
                    (double *)fake(5), -1};
     // route: top-rho count, rejects
-    CHECK(het_attn_route(&s, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, nullptr) == HET_OK);
+    // top-rho at this size runs over several workgroups and needs the workspace
+    const size_t rws = het_attn_route_workspace_bytes(&s);
+    CHECK(rws > 0);
+    CHECK(het_attn_route(&s, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, nullptr, 0, nullptr) == HET_ERR_WORKSPACE);
+    CHECK(het_attn_route(&s, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, fake(7), rws - 1, nullptr) ==
+          HET_ERR_WORKSPACE);
+    int mb = stub::route_mb_launches;
+    CHECK(het_attn_route(&s, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, fake(7), rws, nullptr) == HET_OK);
+    CHECK(stub::route_mb_launches == mb + 1 && stub::route_ws == fake(7));
     CHECK(stub::route.k == (int)std::floor(0.2 * N + 0.5) && r.dense_count_host == stub::route.k);
-    CHECK(het_attn_route(&s, (const float *)fake(6), HET_MEAN_STD, 0.9, &r, nullptr) == HET_OK);
+    const uint32_t nonce0 = stub::route_nonce;
+    CHECK(het_attn_route(&s, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, fake(7), rws, nullptr) == HET_OK);
+    CHECK(stub::route_nonce == nonce0 + 1);
+    // small samples keep the one-workgroup route and need no workspace
+    het_attn_shape small = shape(2, 4, 64, 4, 8, 8);
+    CHECK(het_attn_route_workspace_bytes(&small) == 0);
+    mb = stub::route_mb_launches;
+    CHECK(het_attn_route(&small, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, nullptr, 0, nullptr) == HET_OK);
+    CHECK(stub::route_mb_launches == mb);
+    CHECK(het_attn_route(&s, (const float *)fake(6), HET_MEAN_STD, 0.9, &r, nullptr, 0, nullptr) == HET_OK);
     CHECK(r.dense_count_host == -1);
-    CHECK(het_attn_route(&s, nullptr, HET_UNIFORM, 0.3, &r, nullptr) == HET_OK);
-    CHECK(het_attn_route(&s, (const float *)fake(6), HET_TOP_RHO, 1.5, &r, nullptr) == HET_ERR_INVALID_ARG);
-    CHECK(het_attn_route(&s, (const float *)fake(6), HET_MEAN_STD, NAN, &r, nullptr) == HET_ERR_INVALID_ARG);
-    CHECK(het_attn_route(&s, nullptr, HET_TOP_RHO, 0.2, &r, nullptr) == HET_ERR_INVALID_ARG);
-    CHECK(het_attn_route(&s, (const float *)fake(6), 7, 0.2, &r, nullptr) == HET_ERR_INVALID_ARG);
-    CHECK(het_attn_route(nullptr, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, nullptr) == HET_ERR_INVALID_ARG);
+    CHECK(het_attn_route(&s, nullptr, HET_UNIFORM, 0.3, &r, nullptr, 0, nullptr) == HET_OK);
+    CHECK(het_attn_route(&s, (const float *)fake(6), HET_TOP_RHO, 1.5, &r, nullptr, 0, nullptr) == HET_ERR_INVALID_ARG);
+    CHECK(het_attn_route(&s, (const float *)fake(6), HET_MEAN_STD, NAN, &r, nullptr, 0, nullptr) == HET_ERR_INVALID_ARG);
+    CHECK(het_attn_route(&s, nullptr, HET_TOP_RHO, 0.2, &r, nullptr, 0, nullptr) == HET_ERR_INVALID_ARG);
+    CHECK(het_attn_route(&s, (const float *)fake(6), 7, 0.2, &r, nullptr, 0, nullptr) == HET_ERR_INVALID_ARG);
+    CHECK(het_attn_route(nullptr, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, nullptr, 0, nullptr) == HET_ERR_INVALID_ARG);
     het_attn_shape bad = s;
     bad.win_w = 4;
-    CHECK(het_attn_route(&bad, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, nullptr) == HET_ERR_INVALID_ARG);
+    CHECK(het_attn_route(&bad, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, nullptr, 0, nullptr) == HET_ERR_INVALID_ARG);
     bad = s;
     bad.head_dim = 96;
-    CHECK(het_attn_route(&bad, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, nullptr) == HET_ERR_UNSUPPORTED);
+    CHECK(het_attn_route(&bad, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, nullptr, 0, nullptr) == HET_ERR_UNSUPPORTED);
     bad = s;
     bad.grid_t = 1 << 20;
     bad.grid_h = 1 << 20;
-    CHECK(het_attn_route(&bad, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, nullptr) == HET_ERR_UNSUPPORTED);
+    CHECK(het_attn_route(&bad, (const float *)fake(6), HET_TOP_RHO, 0.2, &r, nullptr, 0, nullptr) == HET_ERR_UNSUPPORTED);
 
     // forward, halves, LSE and allocation-free forms
     r.dense_count_host = 6552;

@@ -13,6 +13,9 @@ hetattn::RouteArgs route;
 hetattn::AttnArgs attn;
 hetattn::BwdArgs bwd;
 int swap_blocks = 0;
+int route_mb_launches = 0;
+void *route_ws = nullptr;
+uint32_t route_nonce = 0;
 }  // namespace stub
 
 extern "C" hipError_t hipGetDevice(int *dev) {
@@ -44,6 +47,14 @@ hipError_t noalloc_scratch(void **ptr) {
 }
 hipError_t launch_route(const RouteArgs &a, hipStream_t) {
     stub::route = a;
+    ++stub::launches;
+    return hipSuccess;
+}
+hipError_t launch_route_mb(const RouteArgs &a, void *ws, uint32_t nonce, hipStream_t) {
+    stub::route = a;
+    stub::route_ws = ws;
+    stub::route_nonce = nonce;
+    ++stub::route_mb_launches;
     ++stub::launches;
     return hipSuccess;
 }

@@ -2,6 +2,7 @@
 host-side argument checks.  Nothing here launches a kernel: every call below
 is rejected on the host before any HIP call, so these run without a GPU."""
 import ctypes
+import math
 import os
 import re
 
@@ -37,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.het_attn_abi_version() == het.ABI_VERSION == 4
+    assert lib.het_attn_abi_version() == het.ABI_VERSION == 5
     for st in range(5):
         assert het.status_string(st)
     assert het.status_string(99) == "unknown status"
@@ -57,10 +58,10 @@ def fake_route():
     return het.RouteStruct(FAKE, FAKE, FAKE, FAKE, FAKE, -1)
 
 
-def call_route(lib, shape, mode=het.HET_TOP_RHO, param=0.2, u=FAKE, route=None):
+def call_route(lib, shape, mode=het.HET_TOP_RHO, param=0.2, u=FAKE, route=None, ws=None, ws_bytes=0):
     r = route if route is not None else fake_route()
     return lib.het_attn_route(ctypes.byref(shape) if shape is not None else None, u, mode, param,
-                              ctypes.byref(r), None)
+                              ctypes.byref(r), ws, ws_bytes, None)
 
 
 def call_forward(lib, shape, route=None, q=FAKE, o=FAKE, ws=None, ws_bytes=0):
@@ -88,6 +89,7 @@ def test_shape_errors(lib, bad, status):
     assert call_route(lib, s) == status
     assert call_forward(lib, s) == status
     assert lib.het_attn_workspace_bytes(ctypes.byref(s)) == 0
+    assert lib.het_attn_route_workspace_bytes(ctypes.byref(s)) == 0
 
 
 def test_null_and_bad_scale(lib):
@@ -139,6 +141,41 @@ def test_forward_argument_errors(lib):
 def test_workspace_size(lib):
     assert lib.het_attn_workspace_bytes(None) == 0
     assert lib.het_attn_workspace_bytes(ctypes.byref(good_shape())) >= 0
+
+
+def route_ws_expected(batch: int, n: int) -> int:
+    """The top-rho route's workspace as documented: per sample, two
+    [G][1024] arrays and [G] counts of 64-bit tagged words (G = ceil(N / 2048)
+    workgroups), rounded up to 256 bytes; none below 8192 tokens, above 128
+    workgroups per sample or 1024 per launch."""
+    g = -(-n // 2048)
+    if n < 8192 or g > 128 or batch * g > 1024:
+        return 0
+    per = (2 * g * 1024 + g) * 8
+    return batch * (-(-per // 256) * 256)
+
+
+@pytest.mark.parametrize("batch,grid", [(1, (4, 8, 8)), (1, (4, 32, 63)), (1, (4, 32, 64)),
+                                        (1, (21, 30, 52)), (2, (31, 22, 40)), (1, (39, 40, 41)),
+                                        (1, (64, 64, 64)), (1, (64, 64, 65)), (8, (64, 64, 64)),
+                                        (64, (21, 30, 52)), (65, (21, 30, 52))])
+def test_route_workspace_size(lib, batch, grid):
+    s = good_shape(batch=batch, grid=grid, head_dim=128, heads=1)
+    got = lib.het_attn_route_workspace_bytes(ctypes.byref(s))
+    assert got == route_ws_expected(batch, math.prod(grid))
+    assert lib.het_attn_route_workspace_bytes(None) == 0
+
+
+def test_route_workspace_errors(lib):
+    # 21x30x52 tokens: the top-rho route runs over 16 workgroups per sample.
+    s = good_shape(grid=(21, 30, 52), head_dim=128, heads=1)
+    need = lib.het_attn_route_workspace_bytes(ctypes.byref(s))
+    assert need > 0
+    assert call_route(lib, s) == het.HET_ERR_WORKSPACE
+    assert call_route(lib, s, ws=FAKE, ws_bytes=need - 1) == het.HET_ERR_WORKSPACE
+    assert call_route(lib, s, ws=None, ws_bytes=need) == het.HET_ERR_WORKSPACE
+    # argument errors still come first
+    assert call_route(lib, s, param=1.5) == het.HET_ERR_INVALID_ARG
 
 
 def test_binding_rejects_bad_tensors():

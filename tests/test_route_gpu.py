@@ -146,3 +146,92 @@ def test_route_deterministic():
     b = route_to_numpy(gpu_route(u, w.grid, w.window, w.heads, w.head_dim, w.dtype, rho=0.2))
     for key in a:
         np.testing.assert_array_equal(a[key], b[key])
+
+
+# ---- top-rho over several workgroups per sample (N >= 8192): the workgroups
+# exchange histograms and counts through the caller's workspace.
+
+def route_via_abi(u_gpu, grid, rho, ws):
+    """het_attn_route through the C ABI with a given workspace tensor."""
+    import ctypes
+    import torch
+    import uncertainty_routed_heterogeneous_amd as het
+    B, N = u_gpu.shape
+    dev = u_gpu.device
+    bufs = (torch.empty((B, N), dtype=torch.uint8, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
+            torch.empty((B, N), dtype=torch.int32, device=dev), torch.empty((B, 2), dtype=torch.int32, device=dev),
+            torch.empty((B,), dtype=torch.float64, device=dev))
+    rs = het.RouteStruct(*(b.data_ptr() for b in bufs), -1)
+    shape = het.make_shape(B, 2, 64, grid, (3, 3, 3), het.HET_F32)
+    lib = het.load_library()
+    need = int(lib.het_attn_route_workspace_bytes(ctypes.byref(shape)))
+    assert 0 < need <= ws.numel()
+    st = lib.het_attn_route(ctypes.byref(shape), u_gpu.data_ptr(), het.HET_TOP_RHO, float(rho), ctypes.byref(rs),
+                            ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+    assert st == het.HET_OK
+    torch.cuda.synchronize()
+    return dict(mask=bufs[0].cpu().numpy(), dense_idx=bufs[1].cpu().numpy(), local_idx=bufs[2].cpu().numpy(),
+                counts=bufs[3].cpu().numpy(), thresh=bufs[4].cpu().numpy())
+
+
+def test_route_workspace_reused_and_dirty(oracle_mod):
+    """The workspace needs no clearing: filled with 0xff, with random bytes,
+    and reused call after call (each call marks its barriers with a value of
+    its own), every route is the oracle's."""
+    import torch
+    rng = np.random.default_rng(11)
+    n = 21 * 30 * 52
+    ws = torch.full((2 * 1024 * 1024,), 255, dtype=torch.uint8, device="cuda")
+    for it, fill in enumerate(["ff", "random", "reuse", "reuse"]):
+        if fill == "random":
+            ws.copy_(torch.from_numpy(rng.integers(0, 256, ws.numel(), dtype=np.uint8)).cuda())
+        u = rng.standard_normal((2, n)).astype(np.float32)
+        rho = (0.2, 0.05, 0.6, 1.0 / n)[it]
+        log(f"[route] workspace {fill} rho={rho}")
+        g = route_via_abi(torch.from_numpy(u).cuda(), (21, 30, 52), rho, ws)
+        assert_route_equal(g, oracle_mod.route_top_rho(u, rho))
+
+
+@pytest.mark.parametrize("k", [2048, 4096, 4097, 6143, 12287])
+def test_route_k_at_workgroup_edges(oracle_mod, k):
+    """K at and next to multiples of the 2048 tokens a workgroup holds, with
+    every u equal (the dense tokens are the first K by index, so the tie rule
+    crosses workgroups) and with 40 distinct values."""
+    n = 12288
+    rng = np.random.default_rng(k)
+    u = np.empty((2, n), np.float32)
+    u[0] = 0.5
+    u[1] = np.round(rng.random(n) * 39) / 39
+    rho = (k - 0.25) / n  # floor(rho * n + 1/2) = k
+    log(f"[route] N={n} K={k}")
+    g = run_top_rho(oracle_mod, u, (1, 1, n), rho)
+    assert g["counts"][0, 0] == k
+    assert g["dense_idx"][0, :k].tolist() == list(range(k))
+
+
+def test_route_many_workgroups_special_values(oracle_mod):
+    """NaN (read as +inf), +-inf and -0 (read as +0) at a size routed by 12
+    workgroups; keys one ulp apart in the other sample (one 1-bit digit)."""
+    n = 24000
+    rng = np.random.default_rng(21)
+    u = rng.standard_normal((2, n)).astype(np.float32)
+    u[0, rng.choice(n, 50, replace=False)] = np.nan
+    u[0, rng.choice(n, 50, replace=False)] = np.inf
+    u[0, rng.choice(n, 50, replace=False)] = -np.inf
+    u[0, rng.choice(n, 300, replace=False)] = 0.0
+    u[0, rng.choice(n, 300, replace=False)] = -0.0
+    a = np.float32(1.0)
+    u[1] = np.where(rng.random(n) < 0.5, a, np.nextafter(a, np.float32(2.0)))
+    for rho in (0.001, 0.2, 0.5, 0.999):
+        log(f"[route] N={n} special values rho={rho}")
+        run_top_rho(oracle_mod, u, (1, 1, n), rho)
+
+
+def test_route_largest_launch(oracle_mod):
+    """1024 workgroups in one launch: 8 samples of 262144 tokens (128
+    workgroups each), the most the several-workgroup route takes."""
+    n = 64 * 64 * 64
+    rng = np.random.default_rng(31)
+    u = rng.lognormal(0.0, 1.0, (8, n)).astype(np.float32)
+    log(f"[route] B=8 N={n}")
+    run_top_rho(oracle_mod, u, (64, 64, 64), 0.2)

@@ -28,7 +28,7 @@ HET_OK, HET_ERR_INVALID_ARG, HET_ERR_UNSUPPORTED, HET_ERR_WORKSPACE, HET_ERR_HIP
 HET_BF16, HET_F32 = 0, 1
 HET_TOP_RHO, HET_MEAN_STD, HET_UNIFORM = 0, 1, 2
 HET_BORDER_SHIFT, HET_BORDER_CUT = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 _BORDERS = {"shift": HET_BORDER_SHIFT, "cut": HET_BORDER_CUT}
 
 
@@ -56,8 +56,10 @@ SIGNATURES = {
     "het_attn_abi_version": (ctypes.c_int, []),
     "het_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "het_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
+    "het_attn_route_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "het_attn_route": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_int,
-                                      ctypes.c_double, ctypes.POINTER(RouteStruct), ctypes.c_void_p]),
+                                      ctypes.c_double, ctypes.POINTER(RouteStruct), ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p]),
 }
 SIGNATURES["het_attn_backward_workspace_bytes"] = (ctypes.c_size_t, [ctypes.POINTER(Shape)])
 SIGNATURES["het_attn_backward"] = (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_void_p,
@@ -212,8 +214,16 @@ def route(u, grid, window, heads: int, head_dim: int, dtype, rho: float | None =
     shape = make_shape(B, heads, head_dim, grid, window, _dtype_code(dtype))
     rs = r.as_struct()
     mode, param = (HET_TOP_RHO, rho) if rho is not None else (HET_MEAN_STD, c)
-    st = load_library().het_attn_route(ctypes.byref(shape), u.data_ptr(), mode, float(param),
-                                       ctypes.byref(rs), _stream_handle(stream))
+    lib = load_library()
+    ws_bytes = int(lib.het_attn_route_workspace_bytes(ctypes.byref(shape))) if mode == HET_TOP_RHO else 0
+    ws = None
+    if ws_bytes:
+        # Stream-ordered scratch: freed after the launch, reused only by work
+        # that the caching allocator orders after it on the same stream.
+        with _on_stream(stream):
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = lib.het_attn_route(ctypes.byref(shape), u.data_ptr(), mode, float(param), ctypes.byref(rs),
+                            ws.data_ptr() if ws is not None else None, ws_bytes, _stream_handle(stream))
     if st != HET_OK:
         raise HetAttnError(st, "het_attn_route")
     r.dense_count_host = rs.dense_count_host
@@ -239,7 +249,7 @@ def route_uniform(batch: int, grid, window, rho: float, device=None, stream=None
     shape = make_shape(batch, 1, 64, grid, window, HET_F32)
     rs = r.as_struct()
     st = load_library().het_attn_route(ctypes.byref(shape), None, HET_UNIFORM, float(rho),
-                                       ctypes.byref(rs), _stream_handle(stream))
+                                       ctypes.byref(rs), None, 0, _stream_handle(stream))
     if st != HET_OK:
         raise HetAttnError(st, "het_attn_route")
     r.dense_count_host = rs.dense_count_host

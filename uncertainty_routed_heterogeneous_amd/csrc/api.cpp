@@ -1,9 +1,12 @@
 // api.cpp -- the C ABI of include/hetattn.h: argument validation on the host,
 // then launches on the caller's stream.  No allocation and no device-to-host
 // traffic; the only state is the per-device address of the static scratch
-// that het_attn_forward_noalloc uses (kept in dense.hip).
+// that het_attn_forward_noalloc uses (kept in dense.hip) and a counter of
+// het_attn_route calls, whose value tags the words a call exchanges through
+// the route workspace.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -116,8 +119,16 @@ size_t het_attn_workspace_bytes(const het_attn_shape *shape) {
     return hetattn::dense_workspace_bytes((int)d.B, (int)d.H, (int)d.N, (int)d.D, shape->dtype == HET_BF16, cus);
 }
 
+size_t het_attn_route_workspace_bytes(const het_attn_shape *shape) {
+    Dims d;
+    float scale;
+    if (check_shape(shape, d, scale) != HET_OK) return 0;
+    if (!hetattn::route_mb_applies(0, (int)d.N, (int)d.B)) return 0;
+    return (size_t)d.B * hetattn::route_mb_stride(hetattn::route_mb_groups((int)d.N));
+}
+
 int het_attn_route(const het_attn_shape *shape, const float *u, int mode, double param,
-                   het_route *out, void *stream) {
+                   het_route *out, void *workspace, size_t workspace_bytes, void *stream) {
     Dims d;
     float scale;
     const het_status st = check_shape(shape, d, scale);
@@ -147,7 +158,17 @@ int het_attn_route(const het_attn_shape *shape, const float *u, int mode, double
     } else {
         return HET_ERR_INVALID_ARG;
     }
-    if (hetattn::launch_route(a, (hipStream_t)stream) != hipSuccess) return HET_ERR_HIP;
+    if (hetattn::route_mb_applies(a.mode, a.n, a.batch)) {
+        const size_t need = (size_t)d.B * hetattn::route_mb_stride(hetattn::route_mb_groups(a.n));
+        if (!workspace || workspace_bytes < need) return HET_ERR_WORKSPACE;
+        // The call's number: the kernel tags the words it exchanges with a
+        // hash of it, so words of the previous 2^30 calls never match.
+        static std::atomic<uint32_t> calls{0};
+        const uint32_t nonce = calls.fetch_add(1, std::memory_order_relaxed) + 1u;
+        if (hetattn::launch_route_mb(a, workspace, nonce, (hipStream_t)stream) != hipSuccess) return HET_ERR_HIP;
+    } else if (hetattn::launch_route(a, (hipStream_t)stream) != hipSuccess) {
+        return HET_ERR_HIP;
+    }
     out->dense_count_host = (a.mode == 1) ? -1 : a.k;
     return HET_OK;
 }

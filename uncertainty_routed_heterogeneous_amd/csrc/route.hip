@@ -292,9 +292,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     uint32_t lo = 0xffffffffu, hi = 0u;
     uint32_t keys[kPer > 0 ? kPer : 1];
     if constexpr (kPer > 0) {
+        // Every lane loads (a clamped index past N), so the loads are in
+        // flight together instead of one branch and wait each.
+        float uv[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) uv[j] = uniform ? 0.0f : ub[imin(token(j), N - 1)];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            keys[j] = load_key(j);
+            keys[j] = (!uniform && token(j) < N) ? rank_key(uv[j]) : 0u;
             lo = min(lo, keys[j] ? keys[j] : 0xffffffffu);
             hi = max(hi, keys[j]);
         }
@@ -495,11 +500,20 @@ __global__ __launch_bounds__(kRouteThreads) void swap_kernel(SwapArgs a) {
     uint32_t keys[kPer > 0 ? kPer : 1];
     uint64_t dbits = 0;  // bit j: token(j) is in the dense set of the input route
     if constexpr (kPer > 0) {
+        // The mask bytes are loaded by every lane (a clamped index past N),
+        // all in flight together.
+        uint8_t mbyte[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) mbyte[j] = 1;
+        if (!a.random) {
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) mbyte[j] = min_b[imin(token(j), N - 1)];
+        }
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             if (j < rows) {
                 keys[j] = draw_key(j);
-                if (read_dense(j)) dbits |= 1ull << j;
+                if (token(j) < N && mbyte[j] == 0) dbits |= 1ull << j;
             } else {
                 keys[j] = 0u;
             }
@@ -607,6 +621,346 @@ __global__ __launch_bounds__(kRouteThreads) void swap_kernel(SwapArgs a) {
         a.counts[2 * r + 1] = N - n_dense;
         if (a.thresh) a.thresh[r] = (!a.random && a.thresh_in) ? a.thresh_in[b] : __builtin_nan("");
     }
+}
+
+// ---------------------------------------------------------------------------
+// Top-rho route over several workgroups per sample.  The one-workgroup route
+// runs its steps (load, radix passes, counts, compaction) on one CU; for a
+// sample of tens of thousands of tokens the same steps are spread over
+// G = ceil(N / kRouteMbChunk) workgroups of one sample, which exchange data
+// four times:
+//   - workgroup g holds tokens [2048 g, 2048 g + 2048), 8 per lane
+//     (wave w: rows 512 w + 64 j + lane, j < 8), as order-preserving keys;
+//   - three radix passes with fixed digits (key bits 31..21, 20..10, 9..0):
+//     each workgroup publishes the histogram of the digit over its keys that
+//     carry the prefix chosen so far, and every workgroup sums the G
+//     histograms and picks the same digit, the one that holds the K-th
+//     largest key; after the third pass the prefix is that key;
+//   - each workgroup publishes its counts of keys above and equal to the
+//     K-th key; from the counts of the workgroups before it, it places its
+//     dense and local tokens exactly as the one-workgroup route does (keys
+//     above are dense; of the keys equal to the K-th, the lowest indices
+//     are, up to K in all).
+// Exchange: every published 32-bit value travels with a 32-bit tag in one
+// 64-bit atomic store at device scope, and a reader loads words (64-bit
+// atomic loads at device scope) until each carries the tag it expects.  The
+// tag is a bijective 32-bit hash of (call number, exchange number), so a word
+// left by an earlier exchange or by one of the previous 2^30 calls never
+// passes, and no word needs to be ordered after another: no flag, no cache
+// write-back or invalidation, and no clearing of the workspace between calls.
+// What a reader assembles is also checked: the histogram of a pass holds as
+// many keys as the digit chosen before it (N for the first), and the counts
+// add up to K.  Every wait is bounded (kMbSpinLimit rounds of loads).  A
+// workgroup whose wait ran out or whose check failed writes no index (it
+// cannot know where its tokens go), and if it is workgroup 0 the sample's
+// counts read -1; the compaction's indices are clamped to the sample in any
+// case.
+constexpr int kMbThreads = 256;
+constexpr int kMbWaves = kMbThreads / 64;
+constexpr int kMbPer = kRouteMbChunk / kMbThreads;  // keys per lane
+constexpr int kMbSpinLimit = 1 << 20;
+constexpr int kMbSlotWords = kRouteMbBins / 2;  // one published histogram: two 16-bit counts a word
+constexpr int kMbBatch = 16;                     // histograms whose words are loaded together
+static_assert(kRouteMbBins == 8 * kMbThreads, "each thread sums eight bins");
+static_assert(kRouteMbChunk < 65536, "a workgroup's counts fit 16 bits");
+
+__device__ __forceinline__ uint64_t mb_tagged(uint32_t value, uint32_t tag) {
+    return (uint64_t)value | ((uint64_t)tag << 32);
+}
+__device__ __forceinline__ void mb_put(uint64_t *p, uint32_t value, uint32_t tag) {
+    __hip_atomic_store(p, mb_tagged(value, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t mb_get(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Tag of exchange e (0..3) of call number `call`: the finalizer of
+// MurmurHash3 (Appleby), a bijection of 32-bit words, on 4*call + e.
+__device__ __forceinline__ uint32_t mb_tag(uint32_t call, int e) {
+    uint32_t x = (call << 2) | (uint32_t)e;
+    x ^= x >> 16;
+    x *= 0x85ebca6bu;
+    x ^= x >> 13;
+    x *= 0xc2b2ae35u;
+    x ^= x >> 16;
+    return x;
+}
+
+// Cache policy of the 16-byte exchange loads: device-scope coherent (sc1),
+// as the compiler emits for the 64-bit atomic loads at that scope.
+constexpr int kMbCoherent = 16;
+
+// Wave 0 reads word 0 of each of the G slots (stride `stride` words) until
+// all carry `tag`; returns false for every thread when the wait ran out (and
+// does not wait once ok is false).  All threads of the workgroup call it.
+__device__ __forceinline__ bool mb_wait_words(const uint64_t *slots, int stride, int G, uint32_t tag, bool ok,
+                                              int *s_ok) {
+    const int tid = threadIdx.x;
+    ok = __syncthreads_and(ok);
+    if (tid < 64) {
+        bool seen = !ok;
+        for (int it = 0; !seen && it < kMbSpinLimit; ++it) {
+            const uint64_t w0 = tid < G ? mb_get(slots + (size_t)tid * stride) : mb_tagged(0u, tag);
+            const uint64_t w1 = tid + 64 < G ? mb_get(slots + (size_t)(tid + 64) * stride) : mb_tagged(0u, tag);
+            seen = __all((uint32_t)(w0 >> 32) == tag && (uint32_t)(w1 >> 32) == tag);
+            if (!seen) __builtin_amdgcn_s_sleep(1);
+        }
+        if (tid == 0) *s_ok = seen;
+    }
+    __syncthreads();
+    return ok && *s_ok != 0;
+}
+
+__global__ __launch_bounds__(kMbThreads) void route_mb_kernel(RouteArgs a, unsigned char *ws, size_t ws_stride,
+                                                            int G, uint32_t nonce) {
+    const int g = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int N = a.n, K = a.k;
+    unsigned char *wsb = ws + (size_t)b * ws_stride;
+    uint64_t *hist = reinterpret_cast<uint64_t *>(wsb);                       // [2][G][kMbSlotWords]
+    uint64_t *cnt = hist + 2 * (size_t)G * kMbSlotWords;                      // [G]
+    __shared__ __attribute__((aligned(16))) uint32_t h[kRouteMbBins];
+    __shared__ int s_red[2 * kMbWaves];
+    __shared__ int s_sel[4];
+    __shared__ int s_blk[4];
+    __shared__ int s_ok;
+
+    // Keys of tokens at or beyond N read as 0, which no token's key equals.
+    // Every lane loads (a clamped index past N), so the eight loads are in
+    // flight together instead of one branch and wait each.
+    const float *ub = a.u + (size_t)b * N;
+    const int w0 = g * kRouteMbChunk + wave * (kMbPer * 64);
+    auto token = [&](int j) HET_INLINE { return w0 + 64 * j + lane; };
+    float uv[kMbPer];
+#pragma unroll
+    for (int j = 0; j < kMbPer; ++j) uv[j] = ub[imin(token(j), N - 1)];
+    uint32_t keys[kMbPer];
+#pragma unroll
+    for (int j = 0; j < kMbPer; ++j) keys[j] = token(j) < N ? rank_key(uv[j]) : 0u;
+
+    bool ok = true;  // this thread's waits all ended with the expected words
+    uint32_t prefix = 0u, pmask = 0u;
+    int remaining = K;
+    int members = N;  // keys that carry the prefix chosen so far
+    if (K > 0) {
+#pragma unroll 1
+        for (int p = 0; p < 3; ++p) {
+            const int shift = p == 0 ? 21 : (p == 1 ? 10 : 0);
+            const uint32_t dmask = p == 2 ? 0x3ffu : 0x7ffu;
+            const uint32_t tag = mb_tag(nonce, p);
+            for (int i = tid; i < kRouteMbBins / 4; i += kMbThreads)
+                reinterpret_cast<u32x4 *>(h)[i] = u32x4{0u, 0u, 0u, 0u};
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < kMbPer; ++j) {
+                const uint32_t x = keys[j];
+                if (x != 0u && (x & pmask) == prefix) atomicAdd(&h[(x >> shift) & dmask], 1u);
+            }
+            __syncthreads();
+            // Thread t publishes bins 8t .. 8t+7 as four words of two 16-bit
+            // counts (a workgroup holds 2048 tokens).
+            uint64_t *slots = hist + (size_t)(p & 1) * G * kMbSlotWords;
+            {
+                const u32x4 lo = reinterpret_cast<const u32x4 *>(h)[2 * tid];
+                const u32x4 hi = reinterpret_cast<const u32x4 *>(h)[2 * tid + 1];
+                uint64_t *mine = slots + (size_t)g * kMbSlotWords + 4 * tid;
+                mb_put(mine + 0, lo[0] | (lo[1] << 16), tag);
+                mb_put(mine + 1, lo[2] | (lo[3] << 16), tag);
+                mb_put(mine + 2, hi[0] | (hi[1] << 16), tag);
+                mb_put(mine + 3, hi[2] | (hi[3] << 16), tag);
+            }
+            // Wave 0 first waits until word 0 of every histogram carries the
+            // tag (one word per workgroup, so the waiting costs little traffic).
+            ok = mb_wait_words(slots, kMbSlotWords, G, tag, ok, &s_ok);
+            // Thread t sums the same bins over the G histograms: 16-byte
+            // device-scope loads of kMbBatch histograms at a time, loaded again
+            // (rarely) while any of their words is stale.
+            int cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                slots, (short)0, (int)((size_t)G * kMbSlotWords * sizeof(uint64_t)), kBufferRsrcWord3);
+            for (int g0 = 0; g0 < G; g0 += kMbBatch) {
+                u32x4 v[kMbBatch][2];  // words 4t .. 4t+3 of histogram g0 + k: (value, tag) pairs
+                bool fresh = !ok;     // after a wait ran out, do not wait again
+                for (int it = 0; it < kMbSpinLimit; ++it) {
+#pragma unroll
+                    for (int k = 0; k < kMbBatch; ++k)
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const int off = (int)(((size_t)(g0 + k) * kMbSlotWords + 4 * tid + 2 * hh) * sizeof(uint64_t));
+                            v[k][hh] = g0 + k < G ? __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kMbCoherent)
+                                                  : u32x4{0u, tag, 0u, tag};
+                        }
+                    bool all = true;
+#pragma unroll
+                    for (int k = 0; k < kMbBatch; ++k)
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) all = all && v[k][hh][1] == tag && v[k][hh][3] == tag;
+                    if (all || fresh) {
+                        fresh = true;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                ok = ok && fresh;
+#pragma unroll
+                for (int k = 0; k < kMbBatch; ++k)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            cs[4 * hh + 2 * e] += (int)(v[k][hh][2 * e] & 0xffffu);
+                            cs[4 * hh + 2 * e + 1] += (int)(v[k][hh][2 * e] >> 16);
+                        }
+            }
+            int tot = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) tot += cs[i];
+            // Members in bins >= 8t: suffix sum over the threads t .. 255.
+            int suf = tot;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_down(suf, off);
+                if (lane + off < 64) suf += y;
+            }
+            if (lane == 0) s_red[wave] = suf;
+            __syncthreads();
+            int incl = suf;
+            for (int w = wave + 1; w < kMbWaves; ++w) incl += s_red[w];
+            const int excl = incl - tot;  // members in bins above 8t + 7
+            if (tid == 0) s_sel[3] = incl;  // all the histograms' keys
+            if (excl < remaining && remaining <= incl) {
+                // The digit d with count(> d) < remaining <= count(>= d).
+                int i = 7, before = excl;
+                while (i > 0 && before + cs[i] < remaining) before += cs[i--];
+                s_sel[0] = 8 * tid + i;
+                s_sel[1] = remaining - before;
+                s_sel[2] = cs[i];
+            }
+            __syncthreads();
+            ok = ok && s_sel[3] == members;
+            prefix |= (uint32_t)s_sel[0] << shift;
+            pmask |= dmask << shift;
+            remaining = s_sel[1];
+            members = s_sel[2];
+            __syncthreads();  // s_red and s_sel are rewritten by the next pass
+        }
+    }
+    // The K-th largest key and how many keys equal to it the K largest hold
+    // (K = 0: no key is larger, none equal is taken).
+    const uint32_t tkey = K > 0 ? prefix : 0xffffffffu;
+    const int take_equal = K > 0 ? remaining : 0;
+
+    // Counts of this wave and workgroup, published for the later workgroups.
+    int n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int j = 0; j < kMbPer; ++j) {
+        n_gt += __popcll(__ballot(keys[j] > tkey));
+        n_eq += __popcll(__ballot(keys[j] == tkey));
+    }
+    if (lane == 0) {
+        s_red[wave] = n_gt;
+        s_red[kMbWaves + wave] = n_eq;
+    }
+    __syncthreads();
+    int gt_w = 0, eq_w = 0, gt_b = 0, eq_b = 0;  // waves before this one; the workgroup
+#pragma unroll
+    for (int w = 0; w < kMbWaves; ++w) {
+        gt_w += w < wave ? s_red[w] : 0;
+        eq_w += w < wave ? s_red[kMbWaves + w] : 0;
+        gt_b += s_red[w];
+        eq_b += s_red[kMbWaves + w];
+    }
+    const uint32_t ctag = mb_tag(nonce, 3);
+    if (tid == 0) mb_put(cnt + g, (uint32_t)gt_b | ((uint32_t)eq_b << 16), ctag);
+    if (tid < 64) {
+        // Wave 0: the counts of the workgroups before this one, and the totals.
+        uint64_t c[2];
+        bool fresh = !ok;
+        for (int it = 0; it < kMbSpinLimit; ++it) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r) c[r] = tid + 64 * r < G ? mb_get(cnt + tid + 64 * r) : mb_tagged(0u, ctag);
+            if (fresh || ((uint32_t)(c[0] >> 32) == ctag && (uint32_t)(c[1] >> 32) == ctag)) {
+                fresh = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        ok = ok && fresh;
+        int gb = 0, eb = 0, gt = 0, et = 0;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int gg = tid + 64 * r;
+            const int x = (int)(c[r] & 0xffffu), y = (int)((c[r] >> 16) & 0xffffu);
+            gb += gg < g ? x : 0;
+            eb += gg < g ? y : 0;
+            gt += x;
+            et += y;
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            gb += __shfl_xor(gb, off);
+            eb += __shfl_xor(eb, off);
+            gt += __shfl_xor(gt, off);
+            et += __shfl_xor(et, off);
+        }
+        if (tid == 0) {
+            s_blk[0] = gb;
+            s_blk[1] = eb;
+            s_blk[2] = gt;
+            s_blk[3] = et;
+        }
+    }
+    // Every wait of every thread of the workgroup ended with the expected
+    // words, and the counts are those of K tokens.
+    ok = __syncthreads_and(ok);
+    ok = ok && s_blk[2] == K - take_equal && s_blk[3] >= take_equal && s_blk[2] + s_blk[3] <= N;
+    const int n_dense = s_blk[2] + imin(s_blk[3], take_equal);
+    int eq_run = s_blk[1] + eq_w;
+    int d_seen = s_blk[0] + gt_w + imin(eq_run, take_equal);
+
+    uint8_t *mask = a.mask + (size_t)b * N;
+    int32_t *dense_idx = a.dense_idx + (size_t)b * N;
+    int32_t *local_idx = a.local_idx + (size_t)b * N;
+    if (g == 0 && tid == 0) {
+        a.counts[2 * b] = ok ? n_dense : -1;
+        a.counts[2 * b + 1] = ok ? N - n_dense : -1;
+        a.thresh[b] = K > 0 ? (double)key_to_float(tkey) : __builtin_inf();
+    }
+    // After a wait that ran out the other workgroups' counts are not known,
+    // so no index may be trusted: nothing more is written.
+    if (!ok) return;
+#pragma unroll
+    for (int j = 0; j < kMbPer; ++j) {
+        uint64_t bal = __ballot(keys[j] > tkey);
+        const uint64_t eq_bal = __ballot(keys[j] == tkey);
+        if (eq_bal != 0ull) {
+            const bool eq = (eq_bal >> lane) & 1u;
+            bal |= __ballot(eq && eq_run + lanes_below(eq_bal) < take_equal);
+            eq_run += __popcll(eq_bal);
+        }
+        const int i = token(j);
+        const bool dn = (bal >> lane) & 1u;
+        // d <= i by construction; the clamps keep every store inside the
+        // sample whatever the exchanged data held.
+        const int d = imin(imax(d_seen + lanes_below(bal), 0), imin(i, N - 1));
+        if (i < N) {
+            mask[i] = dn ? 0 : 1;
+            *(dn ? dense_idx + d : local_idx + (i - d)) = i;
+        }
+        d_seen += __popcll(bal);
+    }
+    // -1 after the valid entries of both lists, over this workgroup's range.
+    const int lo = g * kRouteMbChunk, hi = imin(N, lo + kRouteMbChunk);
+    for (int i = lo + tid; i < hi; i += kMbThreads) {
+        if (i >= n_dense) dense_idx[i] = -1;
+        if (i >= N - n_dense) local_idx[i] = -1;
+    }
+}
+
+hipError_t launch_route_mb(const RouteArgs &a, void *ws, uint32_t nonce, hipStream_t stream) {
+    const int G = route_mb_groups(a.n);
+    hipLaunchKernelGGL(route_mb_kernel, dim3(G, a.batch), dim3(kMbThreads), 0, stream, a,
+                       static_cast<unsigned char *>(ws), route_mb_stride(G), G, nonce);
+    return hipGetLastError();
 }
 
 template <bool kUniform>
