@@ -158,9 +158,18 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
             v_off[db][lohi] = row * D + 8 * ((4 * db + v_chunk_off) ^ swz<D>(row)) + v_elem_off;
         }
 
+    // Stream-K pieces of the full length M = W / G visit their key tiles in
+    // the order of the tile index mod M (step i takes the tile t of the piece
+    // with t = i mod M), so every piece that holds a given key tile of a head
+    // reads it in the same round: the pieces of different units start at
+    // different tiles (n_kt mod M != 0 in general) but, like the whole units,
+    // run side by side on their XCD and share its L2.  Other pieces (the
+    // whole units, and the ends of units) keep the natural order.
+    const int piece_m = units_sk ? (int)(W / G) : 0;
     for (;;) {
         // ---- next task: a whole unit, then pieces of the stream-K units
         int unit, kt0, kt1;
+        int rot_m = 0;  // M when this piece visits its tiles in rotated order
         if (dp_unit < units_dp) {
             unit = dp_unit;
             kt0 = 0;
@@ -172,6 +181,7 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
             kt1 = (int)((x_end - (int64_t)sk * n_kt) < n_kt ? (x_end - (int64_t)sk * n_kt) : n_kt);
             x = (int64_t)sk * n_kt + kt1;
             unit = units_dp + sk;
+            if (piece_m > 1 && kt1 - kt0 == piece_m) rot_m = piece_m;
         } else {
             break;
         }
@@ -359,19 +369,27 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         // computes exponentials; only the end of a round is a barrier.
         // The first round has no P*V and the last no QK; in between, K(r)
         // lives in K0 for even r-kt0 and K1 for odd, V(r) likewise.
+        // Key tile of round r (rounds kt0 .. kt1-1): kt0 + (r - 2*kt0 mod M),
+        // from one remainder per piece and a compare per round.
+        const int rot0 = rot_m ? (rot_m - kt0 % rot_m) % rot_m : 0;
+        auto tile_at = [&](int r) HET_INLINE -> int {
+            if (rot_m == 0) return r;
+            const int d = r - kt0 + rot0;
+            return kt0 + (d >= rot_m ? d - rot_m : d);
+        };
         using T_ = std::true_type;
         using F_ = std::false_type;
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();  // previous piece is done with the buffers
-        dma(kb, K0, kt0);
+        dma(kb, K0, tile_at(kt0));
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
         // first round r = kt0
-        if (kt0 + 1 < kt1) dma(kb, K1, kt0 + 1);
-        if constexpr (!kLse) dma(vb, V0, kt0);
+        if (kt0 + 1 < kt1) dma(kb, K1, tile_at(kt0 + 1));
+        if constexpr (!kLse) dma(vb, V0, tile_at(kt0));
         if (grp == 0) burst_ct(F_{}, T_{}, V1, K0);
         __builtin_amdgcn_s_barrier();
-        if (grp == 0) softmax(kt0);
+        if (grp == 0) softmax(tile_at(kt0));
         else burst_ct(F_{}, T_{}, V1, K0);
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
@@ -379,11 +397,11 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         // (kLse: S-only bursts, and no V tiles.)
         using PV_ = std::integral_constant<bool, !kLse>;
         auto round = [&](int r, const __bf16 *Kc, __bf16 *Kn, const __bf16 *Vp, __bf16 *Vc) HET_INLINE {
-            if (r + 1 < kt1) dma(kb, Kn, r + 1);
-            if constexpr (!kLse) dma(vb, Vc, r);
+            if (r + 1 < kt1) dma(kb, Kn, tile_at(r + 1));
+            if constexpr (!kLse) dma(vb, Vc, tile_at(r));
             if (grp == 0) burst_ct(PV_{}, T_{}, Vp, Kc);
-            else softmax(r - 1);
-            if (grp == 0) softmax(r);
+            else softmax(tile_at(r - 1));
+            if (grp == 0) softmax(tile_at(r));
             else burst_ct(PV_{}, T_{}, Vp, Kc);
             __builtin_amdgcn_s_waitcnt(0);
             __builtin_amdgcn_s_barrier();
@@ -397,7 +415,7 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         {
             const __bf16 *Vp = ((kt1 - 1 - kt0) & 1) ? V1 : V0;
             if (grp == 0) burst_ct(PV_{}, F_{}, Vp, K0);
-            else softmax(kt1 - 1);
+            else softmax(tile_at(kt1 - 1));
             __builtin_amdgcn_s_barrier();
             if (grp == 1) burst_ct(PV_{}, F_{}, Vp, K0);
         }
