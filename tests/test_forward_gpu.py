@@ -118,6 +118,17 @@ def test_clustered_blobs(oracle_mod):
     full_parity(oracle_mod, w, q, k, v, u, rho=0.2, what="blobs")
 
 
+def test_medium_all_rows_split_units(oracle_mod):
+    """Every element at 8192 tokens x 12 heads: 84 dense units for 256
+    persistent workgroups, so every unit is cut into pieces of 42 key tiles
+    that visit their tiles in rotated order and are merged; the route runs
+    on 4 workgroups per sample."""
+    w = W.Workload("medium", 950, 1, 12, 128, (8, 32, 32), (3, 7, 7), 0.2, "bf16", "iid")
+    q, k, v = W.make_qkv(w)
+    log("[forward] medium 8x32x32, 12 heads, every row")
+    full_parity(oracle_mod, w, q, k, v, W.make_u(w), rho=0.2, what="medium")
+
+
 def sampled_rows(mask_b: np.ndarray, n_each: int, rng) -> np.ndarray:
     dense = np.nonzero(mask_b == 0)[0]
     local = np.nonzero(mask_b == 1)[0]
