@@ -126,8 +126,8 @@ size_t het_attn_workspace_bytes(const het_attn_shape *shape);
 /* Device workspace het_attn_route needs in HET_TOP_RHO mode for this shape,
  * in bytes (0: none; HET_MEAN_STD and HET_UNIFORM need none).  Samples of
  * 8192 to 262144 tokens (at most 1024 workgroups of 2048 tokens in all) are
- * routed by several workgroups per sample, which exchange histograms and
- * counts through it.  0 for an invalid shape too. */
+ * routed by several workgroups per sample, which exchange histograms, counts
+ * and candidate keys through it.  0 for an invalid shape too. */
 size_t het_attn_route_workspace_bytes(const het_attn_shape *shape);
 
 /* Threshold selection, mask and stable compaction ([HetA §3.2.2 Eqs. 11-12]).

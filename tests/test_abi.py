@@ -145,13 +145,14 @@ def test_workspace_size(lib):
 
 def route_ws_expected(batch: int, n: int) -> int:
     """The top-rho route's workspace as documented: per sample, two
-    [G][1024] arrays and [G] counts of 64-bit tagged words (G = ceil(N / 2048)
-    workgroups), rounded up to 256 bytes; none below 8192 tokens, above 128
-    workgroups per sample or 1024 per launch."""
+    [G][1024] arrays, [G] counts and [G][2056] candidate lists of 64-bit
+    tagged words (G = ceil(N / 2048) workgroups), rounded up to 256 bytes;
+    none below 8192 tokens, above 128 workgroups per sample or 1024 per
+    launch."""
     g = -(-n // 2048)
     if n < 8192 or g > 128 or batch * g > 1024:
         return 0
-    per = (2 * g * 1024 + g) * 8
+    per = (2 * g * 1024 + g + g * 2056) * 8
     return batch * (-(-per // 256) * 256)
 
 

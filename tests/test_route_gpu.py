@@ -235,3 +235,64 @@ def test_route_largest_launch(oracle_mod):
     u = rng.lognormal(0.0, 1.0, (8, n)).astype(np.float32)
     log(f"[route] B=8 N={n}")
     run_top_rho(oracle_mod, u, (64, 64, 64), 0.2)
+
+
+def top_bins(u, rho):
+    """Keys (the order-preserving map of float32 u) that share the K-th
+    largest key's top 11 and top 22 bits, per sample."""
+    b = np.ascontiguousarray(u, np.float32).view(np.uint32).astype(np.uint64)
+    b = np.where(np.isnan(u), np.uint64(0x7fc00000), b)
+    keys = np.where(b >> 31, ~b & 0xffffffff, b | 0x80000000)
+    out = []
+    for row in keys:
+        k = int(np.floor(rho * row.size + 0.5))
+        kth = np.sort(row)[::-1][k - 1]
+        out.append((int(np.sum(row >> 21 == kth >> 21)), int(np.sum(row >> 10 == kth >> 10))))
+    return out
+
+
+@pytest.mark.parametrize("case", ["bin_4096", "bin_4097", "narrow", "wide", "tied", "lists_whole_or_empty"])
+def test_route_selection_paths(oracle_mod, case):
+    """The several-workgroup top-rho select gathers the keys of the K-th
+    key's bin as candidates once at most 4096 share its top 11 bits, else
+    its top 22 bits, else it exchanges a third histogram and the counts.
+    Each case is built for one of those paths (checked on the host) at its
+    boundary: exactly 4096 and 4097 keys in the first bin, u spread wide
+    (Gaussian) or narrow (within one octave), all tied, and candidate lists
+    that are a whole workgroup's 2048 tokens or empty (4096 keys in all)."""
+    rng = np.random.default_rng(77)
+    n = 16384
+    if case in ("bin_4096", "bin_4097"):
+        m = 4096 if case == "bin_4096" else 4097
+        # m keys in [1, 1.25) (one top-11 bin), the rest in [4, 5), shuffled
+        u = np.where(np.arange(n) < m, 1.0 + 0.25 * rng.random(n), 4.0 + rng.random(n)).astype(np.float32)
+        u = u[rng.permutation(n)][None]
+        rho = (n - m + 100 - 0.25) / n
+        want = "first" if m <= 4096 else "second"
+    elif case == "narrow":
+        n = 32760
+        u = (1.0 + 0.01 * rng.standard_normal((2, n))).astype(np.float32)
+        rho, want = 0.2, "second"
+    elif case == "wide":
+        n = 32760
+        u = rng.standard_normal((2, n)).astype(np.float32)
+        rho, want = 0.2, "first"
+    elif case == "tied":
+        u = np.full((1, n), 0.75, np.float32)
+        u[0, rng.choice(n, 50, replace=False)] = 3.0
+        rho, want = 0.3, "histograms"
+    else:
+        # tokens 2048..4095 and 8192..10239 hold the bin's keys (two whole
+        # workgroups' lists), the others lie above or below it
+        u = np.where(rng.random(n) < 0.5, 0.1 * rng.random(n), 8.0 + rng.random(n)).astype(np.float32)
+        u[2048:4096] = 1.0 + 0.2 * rng.random(2048)
+        u[8192:10240] = 1.0 + 0.2 * rng.random(2048)
+        u = u[None]
+        above = int(np.sum(u >= 8.0))
+        rho = (above + 1000 - 0.25) / n
+        want = "first"
+    for first, second in top_bins(u, rho):
+        got = "first" if first <= 4096 else ("second" if second <= 4096 else "histograms")
+        assert got == want, (first, second)
+    log(f"[route] selection path {case} B={u.shape[0]} N={u.shape[1]} rho={rho:.4f}")
+    run_top_rho(oracle_mod, u, (1, 1, u.shape[1]), rho)

@@ -162,7 +162,7 @@ int het_attn_route(const het_attn_shape *shape, const float *u, int mode, double
         const size_t need = (size_t)d.B * hetattn::route_mb_stride(hetattn::route_mb_groups(a.n));
         if (!workspace || workspace_bytes < need) return HET_ERR_WORKSPACE;
         // The call's number: the kernel tags the words it exchanges with a
-        // hash of it, so words of the previous 2^30 calls never match.
+        // hash of it, so words of the previous 2^29 calls never match.
         static std::atomic<uint32_t> calls{0};
         const uint32_t nonce = calls.fetch_add(1, std::memory_order_relaxed) + 1u;
         if (hetattn::launch_route_mb(a, workspace, nonce, (hipStream_t)stream) != hipSuccess) return HET_ERR_HIP;

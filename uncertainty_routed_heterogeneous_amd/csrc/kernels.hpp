@@ -106,25 +106,29 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t stream);
 
 // Top-rho route over several workgroups per sample (route.hip): workgroup g
 // holds tokens [kRouteMbChunk*g, kRouteMbChunk*(g+1)), and the groups of a
-// sample exchange histograms and counts through a workspace of
-// route_mb_stride(G) bytes per sample: two [G][kRouteMbBins / 2] arrays and
-// [G] counts of 64-bit tagged words.  Samples of fewer than kRouteMbMinN
+// sample exchange histograms, counts and candidate keys through a workspace
+// of route_mb_stride(G) bytes per sample: two [G][kRouteMbBins / 2] arrays,
+// [G] counts and [G][kRouteMbCandWords] candidate lists of 64-bit tagged
+// words.  Samples of fewer than kRouteMbMinN
 // tokens or of more than kRouteMbMaxGroups groups, and launches of more than
-// kRouteMbMaxLaunch workgroups (which must all be running at once: 256-thread
-// workgroups, a quarter of what the device holds), keep the one-workgroup
-// route.
+// kRouteMbMaxLaunch workgroups, keep the one-workgroup route.  The G
+// workgroups of a sample wait for one another, so they must run at once: at
+// most 128 of them (a CU holds two), and the samples' workgroups are
+// dispatched in order, so a sample's are all placed once the samples before
+// it are.
 constexpr int kRouteMbChunk = 2048;
 constexpr int kRouteMbMaxGroups = 128;
 constexpr int kRouteMbMinN = 4 * kRouteMbChunk;
 constexpr int kRouteMbBins = 2048;
 constexpr int kRouteMbMaxLaunch = 1024;
+constexpr int kRouteMbCandWords = kRouteMbChunk + 8;  // a count word, then up to a chunk of keys
 inline int route_mb_groups(int n) { return (n + kRouteMbChunk - 1) / kRouteMbChunk; }
 inline bool route_mb_applies(int mode, int n, int batch) {
     return mode == 0 && n >= kRouteMbMinN && route_mb_groups(n) <= kRouteMbMaxGroups &&
            (int64_t)batch * route_mb_groups(n) <= kRouteMbMaxLaunch;
 }
 inline size_t route_mb_stride(int groups) {
-    const size_t bytes = (2ull * groups * (kRouteMbBins / 2) + groups) * sizeof(uint64_t);
+    const size_t bytes = (2ull * groups * (kRouteMbBins / 2) + groups + (size_t)groups * kRouteMbCandWords) * sizeof(uint64_t);
     return (bytes + 255) / 256 * 256;
 }
 // ws: batch * route_mb_stride(G) bytes, any contents; nonce: a value no

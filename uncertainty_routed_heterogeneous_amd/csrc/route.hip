@@ -628,33 +628,41 @@ __global__ __launch_bounds__(kRouteThreads) void swap_kernel(SwapArgs a) {
 // runs its steps (load, radix passes, counts, compaction) on one CU; for a
 // sample of tens of thousands of tokens the same steps are spread over
 // G = ceil(N / kRouteMbChunk) workgroups of one sample, which exchange data
-// four times:
+// twice (four times when many keys tie with the K-th):
 //   - workgroup g holds tokens [2048 g, 2048 g + 2048), 8 per lane
 //     (wave w: rows 512 w + 64 j + lane, j < 8), as order-preserving keys;
-//   - three radix passes with fixed digits (key bits 31..21, 20..10, 9..0):
-//     each workgroup publishes the histogram of the digit over its keys that
-//     carry the prefix chosen so far, and every workgroup sums the G
-//     histograms and picks the same digit, the one that holds the K-th
-//     largest key; after the third pass the prefix is that key;
-//   - each workgroup publishes its counts of keys above and equal to the
-//     K-th key; from the counts of the workgroups before it, it places its
+//   - the K-th largest key is found by radix passes with fixed digits (key
+//     bits 31..21, 20..10, 9..0).  In the first, each workgroup publishes the
+//     histogram of the top digit over its keys, and every workgroup sums the
+//     G histograms and picks the same digit, the bin that holds the K-th key;
+//   - when that bin holds at most kMbCandCap keys, each workgroup publishes
+//     its keys in the bin (in token order) and its count of keys above the
+//     bin.  Every workgroup gathers the lists into LDS, runs the two other
+//     passes there, and counts from them each workgroup's keys above and
+//     equal to the K-th key;
+//   - otherwise the two other passes exchange histograms as the first does
+//     (over the keys that carry the prefix chosen so far), and each
+//     workgroup then publishes its counts of keys above and equal to the
+//     K-th key;
+//   - from the counts of the workgroups before it, each workgroup places its
 //     dense and local tokens exactly as the one-workgroup route does (keys
 //     above are dense; of the keys equal to the K-th, the lowest indices
 //     are, up to K in all).
 // Exchange: every published 32-bit value travels with a 32-bit tag in one
 // 64-bit atomic store at device scope, and a reader loads words (64-bit
-// atomic loads at device scope) until each carries the tag it expects.  The
-// tag is a bijective 32-bit hash of (call number, exchange number), so a word
-// left by an earlier exchange or by one of the previous 2^30 calls never
-// passes, and no word needs to be ordered after another: no flag, no cache
+// loads at device scope) until each carries the tag it expects.  The tag is
+// a bijective 32-bit hash of (call number, exchange number), so a word left
+// by an earlier exchange or by one of the previous 2^29 calls never passes,
+// and no word needs to be ordered after another: no flag, no cache
 // write-back or invalidation, and no clearing of the workspace between calls.
 // What a reader assembles is also checked: the histogram of a pass holds as
-// many keys as the digit chosen before it (N for the first), and the counts
-// add up to K.  Every wait is bounded (kMbSpinLimit rounds of loads).  A
-// workgroup whose wait ran out or whose check failed writes no index (it
-// cannot know where its tokens go), and if it is workgroup 0 the sample's
-// counts read -1; the compaction's indices are clamped to the sample in any
-// case.
+// many keys as the digit chosen before it (N for the first), the candidate
+// lists as many as the chosen bin, the counts add up to K, and the counts a
+// workgroup derives for itself from the lists are its own.  Every wait is
+// bounded (kMbSpinLimit rounds of loads).  A workgroup whose wait ran out or
+// whose check failed writes no index (it cannot know where its tokens go),
+// and if it is workgroup 0 the sample's counts read -1; the compaction's
+// indices are clamped to the sample in any case.
 constexpr int kMbThreads = 256;
 constexpr int kMbWaves = kMbThreads / 64;
 constexpr int kMbPer = kRouteMbChunk / kMbThreads;  // keys per lane
@@ -663,6 +671,14 @@ constexpr int kMbSlotWords = kRouteMbBins / 2;  // one published histogram: two 
 constexpr int kMbBatch = 16;                     // histograms whose words are loaded together
 static_assert(kRouteMbBins == 8 * kMbThreads, "each thread sums eight bins");
 static_assert(kRouteMbChunk < 65536, "a workgroup's counts fit 16 bits");
+// The candidate path holds up to kMbCandCap keys in LDS (16 KiB), kMbCandPer
+// loads in flight a lane.  A larger list costs more than the histogram
+// exchange it saves: 5.7K candidates took 3 us longer than gathering a
+// second histogram and then a list of a few keys.
+constexpr int kMbCandPer = 16;
+constexpr int kMbCandCap = kMbCandPer * kMbThreads;
+static_assert(kRouteMbMaxGroups <= 256, "a workgroup number fits a byte");
+static_assert(kMbCandCap <= 4 * kRouteMbBins, "the owner table fits the histogram's memory");
 
 __device__ __forceinline__ uint64_t mb_tagged(uint32_t value, uint32_t tag) {
     return (uint64_t)value | ((uint64_t)tag << 32);
@@ -673,10 +689,10 @@ __device__ __forceinline__ void mb_put(uint64_t *p, uint32_t value, uint32_t tag
 __device__ __forceinline__ uint64_t mb_get(const uint64_t *p) {
     return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Tag of exchange e (0..3) of call number `call`: the finalizer of
-// MurmurHash3 (Appleby), a bijection of 32-bit words, on 4*call + e.
+// Tag of exchange e (0..7) of call number `call`: the finalizer of
+// MurmurHash3 (Appleby), a bijection of 32-bit words, on 8*call + e.
 __device__ __forceinline__ uint32_t mb_tag(uint32_t call, int e) {
-    uint32_t x = (call << 2) | (uint32_t)e;
+    uint32_t x = (call << 3) | (uint32_t)e;
     x ^= x >> 16;
     x *= 0x85ebca6bu;
     x ^= x >> 13;
@@ -716,13 +732,17 @@ __global__ __launch_bounds__(kMbThreads) void route_mb_kernel(RouteArgs a, unsig
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int N = a.n, K = a.k;
     unsigned char *wsb = ws + (size_t)b * ws_stride;
-    uint64_t *hist = reinterpret_cast<uint64_t *>(wsb);                       // [2][G][kMbSlotWords]
-    uint64_t *cnt = hist + 2 * (size_t)G * kMbSlotWords;                      // [G]
+    uint64_t *hist = reinterpret_cast<uint64_t *>(wsb);  // [2][G][kMbSlotWords]
+    uint64_t *cnt = hist + 2 * (size_t)G * kMbSlotWords;  // [G]
+    uint64_t *cands = cnt + G;                            // [G][kRouteMbCandWords]
     __shared__ __attribute__((aligned(16))) uint32_t h[kRouteMbBins];
+    __shared__ uint32_t cand[kMbCandCap];  // keys of the K-th key's 11-bit bin, workgroup by workgroup
     __shared__ int s_red[2 * kMbWaves];
     __shared__ int s_sel[4];
     __shared__ int s_blk[4];
     __shared__ int s_ok;
+    __shared__ int s_off[kRouteMbMaxGroups + 1];  // candidates of the workgroups before each
+    __shared__ int s_gt[kRouteMbMaxGroups], s_eq[kRouteMbMaxGroups];
 
     // Keys of tokens at or beyond N read as 0, which no token's key equals.
     // Every lane loads (a clamped index past N), so the eight loads are in
@@ -737,119 +757,307 @@ __global__ __launch_bounds__(kMbThreads) void route_mb_kernel(RouteArgs a, unsig
 #pragma unroll
     for (int j = 0; j < kMbPer; ++j) keys[j] = token(j) < N ? rank_key(uv[j]) : 0u;
 
-    bool ok = true;  // this thread's waits all ended with the expected words
+    bool ok = true;  // every wait ended with the expected words and every check held
     uint32_t prefix = 0u, pmask = 0u;
     int remaining = K;
     int members = N;  // keys that carry the prefix chosen so far
-    if (K > 0) {
-#pragma unroll 1
-        for (int p = 0; p < 3; ++p) {
-            const int shift = p == 0 ? 21 : (p == 1 ? 10 : 0);
-            const uint32_t dmask = p == 2 ? 0x3ffu : 0x7ffu;
-            const uint32_t tag = mb_tag(nonce, p);
-            for (int i = tid; i < kRouteMbBins / 4; i += kMbThreads)
-                reinterpret_cast<u32x4 *>(h)[i] = u32x4{0u, 0u, 0u, 0u};
-            __syncthreads();
+
+    // The next digit (bits shift .. shift + width of the key) from a
+    // histogram of the members' digits, thread t holding bins 8t .. 8t+7 in
+    // cs: the digit d with count(> d) < remaining <= count(>= d).  The
+    // histogram must hold every member.
+    auto choose_digit = [&](const int (&cs)[8], int shift, uint32_t dmask) HET_INLINE {
+        int tot = 0;
 #pragma unroll
-            for (int j = 0; j < kMbPer; ++j) {
-                const uint32_t x = keys[j];
-                if (x != 0u && (x & pmask) == prefix) atomicAdd(&h[(x >> shift) & dmask], 1u);
-            }
-            __syncthreads();
-            // Thread t publishes bins 8t .. 8t+7 as four words of two 16-bit
-            // counts (a workgroup holds 2048 tokens).
-            uint64_t *slots = hist + (size_t)(p & 1) * G * kMbSlotWords;
-            {
-                const u32x4 lo = reinterpret_cast<const u32x4 *>(h)[2 * tid];
-                const u32x4 hi = reinterpret_cast<const u32x4 *>(h)[2 * tid + 1];
-                uint64_t *mine = slots + (size_t)g * kMbSlotWords + 4 * tid;
-                mb_put(mine + 0, lo[0] | (lo[1] << 16), tag);
-                mb_put(mine + 1, lo[2] | (lo[3] << 16), tag);
-                mb_put(mine + 2, hi[0] | (hi[1] << 16), tag);
-                mb_put(mine + 3, hi[2] | (hi[3] << 16), tag);
-            }
-            // Wave 0 first waits until word 0 of every histogram carries the
-            // tag (one word per workgroup, so the waiting costs little traffic).
-            ok = mb_wait_words(slots, kMbSlotWords, G, tag, ok, &s_ok);
-            // Thread t sums the same bins over the G histograms: 16-byte
-            // device-scope loads of kMbBatch histograms at a time, loaded again
-            // (rarely) while any of their words is stale.
-            int cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                slots, (short)0, (int)((size_t)G * kMbSlotWords * sizeof(uint64_t)), kBufferRsrcWord3);
-            for (int g0 = 0; g0 < G; g0 += kMbBatch) {
-                u32x4 v[kMbBatch][2];  // words 4t .. 4t+3 of histogram g0 + k: (value, tag) pairs
-                bool fresh = !ok;     // after a wait ran out, do not wait again
-                for (int it = 0; it < kMbSpinLimit; ++it) {
+        for (int i = 0; i < 8; ++i) tot += cs[i];
+        // Members in bins >= 8t: suffix sum over the threads t .. 255.
+        int suf = tot;
 #pragma unroll
-                    for (int k = 0; k < kMbBatch; ++k)
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_down(suf, off);
+            if (lane + off < 64) suf += y;
+        }
+        if (lane == 0) s_red[wave] = suf;
+        __syncthreads();
+        int incl = suf;
+        for (int w = wave + 1; w < kMbWaves; ++w) incl += s_red[w];
+        const int excl = incl - tot;  // members in bins above 8t + 7
+        if (tid == 0) s_sel[3] = incl;  // all the histogram's keys
+        if (excl < remaining && remaining <= incl) {
+            int i = 7, before = excl;
+            while (i > 0 && before + cs[i] < remaining) before += cs[i--];
+            s_sel[0] = 8 * tid + i;
+            s_sel[1] = remaining - before;
+            s_sel[2] = cs[i];
+        }
+        __syncthreads();
+        ok = ok && s_sel[3] == members;
+        prefix |= (uint32_t)s_sel[0] << shift;
+        pmask |= dmask << shift;
+        remaining = s_sel[1];
+        members = s_sel[2];
+        __syncthreads();  // s_red and s_sel are rewritten by the next choice
+    };
+
+    // Radix pass p over the histograms all G workgroups publish (exchange p).
+    auto exchange_pass = [&](int p) HET_INLINE {
+        const int shift = p == 0 ? 21 : (p == 1 ? 10 : 0);
+        const uint32_t dmask = p == 2 ? 0x3ffu : 0x7ffu;
+        const uint32_t tag = mb_tag(nonce, p);
+        for (int i = tid; i < kRouteMbBins / 4; i += kMbThreads)
+            reinterpret_cast<u32x4 *>(h)[i] = u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();
 #pragma unroll
-                        for (int hh = 0; hh < 2; ++hh) {
-                            const int off = (int)(((size_t)(g0 + k) * kMbSlotWords + 4 * tid + 2 * hh) * sizeof(uint64_t));
-                            v[k][hh] = g0 + k < G ? __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kMbCoherent)
-                                                  : u32x4{0u, tag, 0u, tag};
-                        }
-                    bool all = true;
-#pragma unroll
-                    for (int k = 0; k < kMbBatch; ++k)
-#pragma unroll
-                        for (int hh = 0; hh < 2; ++hh) all = all && v[k][hh][1] == tag && v[k][hh][3] == tag;
-                    if (all || fresh) {
-                        fresh = true;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                ok = ok && fresh;
+        for (int j = 0; j < kMbPer; ++j) {
+            const uint32_t x = keys[j];
+            if (x != 0u && (x & pmask) == prefix) atomicAdd(&h[(x >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        // Thread t publishes bins 8t .. 8t+7 as four words of two 16-bit
+        // counts (a workgroup holds 2048 tokens).
+        uint64_t *slots = hist + (size_t)(p & 1) * G * kMbSlotWords;
+        {
+            const u32x4 lo = reinterpret_cast<const u32x4 *>(h)[2 * tid];
+            const u32x4 hi = reinterpret_cast<const u32x4 *>(h)[2 * tid + 1];
+            uint64_t *mine = slots + (size_t)g * kMbSlotWords + 4 * tid;
+            mb_put(mine + 0, lo[0] | (lo[1] << 16), tag);
+            mb_put(mine + 1, lo[2] | (lo[3] << 16), tag);
+            mb_put(mine + 2, hi[0] | (hi[1] << 16), tag);
+            mb_put(mine + 3, hi[2] | (hi[3] << 16), tag);
+        }
+        // Wave 0 first waits until word 0 of every histogram carries the
+        // tag (one word per workgroup, so the waiting costs little traffic).
+        ok = mb_wait_words(slots, kMbSlotWords, G, tag, ok, &s_ok);
+        // Thread t sums the same bins over the G histograms: 16-byte
+        // device-scope loads of kMbBatch histograms at a time, loaded again
+        // (rarely) while any of their words is stale.
+        int cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            slots, (short)0, (int)((size_t)G * kMbSlotWords * sizeof(uint64_t)), kBufferRsrcWord3);
+        for (int g0 = 0; g0 < G; g0 += kMbBatch) {
+            u32x4 v[kMbBatch][2];  // words 4t .. 4t+3 of histogram g0 + k: (value, tag) pairs
+            bool fresh = !ok;     // after a wait ran out, do not wait again
+            for (int it = 0; it < kMbSpinLimit; ++it) {
 #pragma unroll
                 for (int k = 0; k < kMbBatch; ++k)
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh)
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int off = (int)(((size_t)(g0 + k) * kMbSlotWords + 4 * tid + 2 * hh) * sizeof(uint64_t));
+                        v[k][hh] = g0 + k < G ? __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kMbCoherent)
+                                              : u32x4{0u, tag, 0u, tag};
+                    }
+                bool all = true;
 #pragma unroll
-                        for (int e = 0; e < 2; ++e) {
-                            cs[4 * hh + 2 * e] += (int)(v[k][hh][2 * e] & 0xffffu);
-                            cs[4 * hh + 2 * e + 1] += (int)(v[k][hh][2 * e] >> 16);
-                        }
+                for (int k = 0; k < kMbBatch; ++k)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) all = all && v[k][hh][1] == tag && v[k][hh][3] == tag;
+                if (all || fresh) {
+                    fresh = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
             }
-            int tot = 0;
+            ok = ok && fresh;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) tot += cs[i];
-            // Members in bins >= 8t: suffix sum over the threads t .. 255.
-            int suf = tot;
+            for (int k = 0; k < kMbBatch; ++k)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        cs[4 * hh + 2 * e] += (int)(v[k][hh][2 * e] & 0xffffu);
+                        cs[4 * hh + 2 * e + 1] += (int)(v[k][hh][2 * e] >> 16);
+                    }
+        }
+        choose_digit(cs, shift, dmask);
+    };
+
+    // Radix pass over the n candidates in LDS (no exchange).
+    auto local_pass = [&](int n, int shift, uint32_t dmask) HET_INLINE {
+        for (int i = tid; i < kRouteMbBins / 4; i += kMbThreads)
+            reinterpret_cast<u32x4 *>(h)[i] = u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();
+        for (int c = tid; c < n; c += kMbThreads) {
+            const uint32_t x = cand[c];
+            if ((x & pmask) == prefix) atomicAdd(&h[(x >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        int cs[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cs[i] = (int)h[8 * tid + i];
+        choose_digit(cs, shift, dmask);
+    };
+
+    // After the histogram exchange of pass first_local - 1 chose a bin of at
+    // most kMbCandCap keys: each workgroup publishes its keys in the bin (and
+    // its count of keys above it), and every workgroup gathers the lists in
+    // LDS, finishes the select there (passes first_local .. 2) and counts,
+    // per workgroup, the keys above and equal to the K-th key.
+    auto cand_select = [&](int first_local) HET_INLINE {
+        const uint32_t ctag = mb_tag(nonce, 4);
+        int nm = 0, na = 0;
+#pragma unroll
+        for (int j = 0; j < kMbPer; ++j) {
+            nm += __popcll(__ballot(keys[j] != 0u && (keys[j] & pmask) == prefix));
+            na += __popcll(__ballot((keys[j] & pmask) > prefix));
+        }
+        if (lane == 0) {
+            s_red[wave] = nm;
+            s_red[kMbWaves + wave] = na;
+        }
+        __syncthreads();
+        int run = 0, nm_b = 0, na_b = 0;
+#pragma unroll
+        for (int w = 0; w < kMbWaves; ++w) {
+            run += w < wave ? s_red[w] : 0;
+            nm_b += s_red[w];
+            na_b += s_red[kMbWaves + w];
+        }
+        __syncthreads();  // s_red is rewritten below
+        // Word 0: (keys in the bin, keys above it); words 1.. the keys in
+        // the bin in token order.
+        uint64_t *slot = cands + (size_t)g * kRouteMbCandWords;
+#pragma unroll
+        for (int j = 0; j < kMbPer; ++j) {
+            const bool m = keys[j] != 0u && (keys[j] & pmask) == prefix;
+            const uint64_t bal = __ballot(m);
+            if (m) mb_put(slot + 1 + run + lanes_below(bal), keys[j], ctag);
+            run += __popcll(bal);
+        }
+        if (tid == 0) mb_put(slot, (uint32_t)nm_b | ((uint32_t)na_b << 16), ctag);
+        ok = __syncthreads_and(ok);
+        if (tid < 64) {
+            // Wave 0: every count word, then where each list starts in
+            // the concatenation of the lists.
+            uint64_t c0 = 0ull, c1 = 0ull;
+            bool seen = !ok;
+            for (int it = 0; it < kMbSpinLimit; ++it) {
+                c0 = tid < G ? mb_get(cands + (size_t)tid * kRouteMbCandWords) : mb_tagged(0u, ctag);
+                c1 = tid + 64 < G ? mb_get(cands + (size_t)(tid + 64) * kRouteMbCandWords) : mb_tagged(0u, ctag);
+                seen = seen || __all((uint32_t)(c0 >> 32) == ctag && (uint32_t)(c1 >> 32) == ctag);
+                if (seen) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            const int n0 = tid < G ? (int)(c0 & 0xffffu) : 0;
+            const int n1 = tid + 64 < G ? (int)(c1 & 0xffffu) : 0;
+            int i0 = n0, i1 = n1;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
-                const int y = __shfl_down(suf, off);
-                if (lane + off < 64) suf += y;
+                const int y0 = __shfl_up(i0, off), y1 = __shfl_up(i1, off);
+                if (tid >= off) {
+                    i0 += y0;
+                    i1 += y1;
+                }
             }
-            if (lane == 0) s_red[wave] = suf;
-            __syncthreads();
-            int incl = suf;
-            for (int w = wave + 1; w < kMbWaves; ++w) incl += s_red[w];
-            const int excl = incl - tot;  // members in bins above 8t + 7
-            if (tid == 0) s_sel[3] = incl;  // all the histograms' keys
-            if (excl < remaining && remaining <= incl) {
-                // The digit d with count(> d) < remaining <= count(>= d).
-                int i = 7, before = excl;
-                while (i > 0 && before + cs[i] < remaining) before += cs[i--];
-                s_sel[0] = 8 * tid + i;
-                s_sel[1] = remaining - before;
-                s_sel[2] = cs[i];
+            const int t0 = __shfl(i0, 63), t1 = __shfl(i1, 63);
+            if (tid < G) {
+                s_off[tid] = i0 - n0;
+                s_gt[tid] = (int)((c0 >> 16) & 0xffffu);
             }
-            __syncthreads();
-            ok = ok && s_sel[3] == members;
-            prefix |= (uint32_t)s_sel[0] << shift;
-            pmask |= dmask << shift;
-            remaining = s_sel[1];
-            members = s_sel[2];
-            __syncthreads();  // s_red and s_sel are rewritten by the next pass
+            if (tid + 64 < G) {
+                s_off[tid + 64] = t0 + i1 - n1;
+                s_gt[tid + 64] = (int)((c1 >> 16) & 0xffffu);
+            }
+            if (tid == 0) {
+                s_off[G] = t0 + t1;
+                s_ok = seen;
+            }
         }
+        __syncthreads();
+        ok = ok && s_ok != 0 && s_off[G] == members;
+        // Candidate c of the concatenation belongs to workgroup owner[c]
+        // (the histogram's memory, free until the next pass).
+        const int n_cand = ok ? members : 0;
+        uint8_t *owner = reinterpret_cast<uint8_t *>(h);
+        if (n_cand > 0)
+            for (int w = wave; w < G; w += kMbWaves)
+                for (int c = s_off[w] + lane; c < s_off[w + 1]; c += 64) owner[c] = (uint8_t)w;
+        __syncthreads();
+        // The lists -> LDS: every lane loads kMbCandPer words at once
+        // (indices past the end load the last candidate again), and all
+        // of them again while any is still stale.
+        if (n_cand > 0) {
+            u32x2 v[kMbCandPer];
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                cands, (short)0, (int)((size_t)G * kRouteMbCandWords * sizeof(uint64_t)), kBufferRsrcWord3);
+            int off[kMbCandPer];
+#pragma unroll
+            for (int k = 0; k < kMbCandPer; ++k) {
+                const int c = imin(k * kMbThreads + tid, n_cand - 1);
+                const int w = owner[c];
+                off[k] = (int)(((size_t)w * kRouteMbCandWords + 1 + (c - s_off[w])) * sizeof(uint64_t));
+            }
+            bool fresh = false;
+            for (int it = 0; it < kMbSpinLimit; ++it) {
+#pragma unroll
+                for (int k = 0; k < kMbCandPer; ++k)
+                    v[k] = __builtin_amdgcn_raw_buffer_load_b64(rs, off[k], 0, kMbCoherent);
+                bool all = true;
+#pragma unroll
+                for (int k = 0; k < kMbCandPer; ++k) all = all && v[k][1] == ctag;
+                if (all) {
+                    fresh = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            ok = ok && fresh;
+#pragma unroll
+            for (int k = 0; k < kMbCandPer; ++k) {
+                const int c = k * kMbThreads + tid;
+                if (c < n_cand) cand[c] = v[k][0];
+            }
+        }
+        ok = __syncthreads_and(ok);
+        // The select's remaining digits on the candidates.
+        const int n_sel = ok ? n_cand : 0;
+#pragma unroll 1
+        for (int q = first_local; q < 3; ++q) local_pass(n_sel, q == 1 ? 10 : 0, q == 1 ? 0x7ffu : 0x3ffu);
+        // Each workgroup's keys above the K-th (above its bin, from its
+        // count word, and in its list) and equal to it.
+        if (n_sel > 0)
+            for (int w = wave; w < G; w += kMbWaves) {
+                int gt = 0, eq = 0;
+                for (int c0 = s_off[w]; c0 < s_off[w + 1]; c0 += 64) {
+                    const int c = c0 + lane;
+                    const uint32_t x = c < s_off[w + 1] ? cand[c] : 0u;
+                    gt += __popcll(__ballot(x > prefix));
+                    eq += __popcll(__ballot(x == prefix));
+                }
+                if (lane == 0) {
+                    s_gt[w] += gt;
+                    s_eq[w] = eq;
+                }
+            }
+        __syncthreads();
+    };
+
+    // Exchange 1 chooses the top 11 bits of the K-th key, and when more than
+    // kMbCandCap keys carry them, exchange 2 the next 11; the keys that carry
+    // the prefix chosen then are exchanged as candidates.  Only when more
+    // than kMbCandCap keys share the K-th key's top 22 bits do a third
+    // histogram exchange and one of the counts follow.
+    bool by_cand = false;
+    if (K > 0) {
+        // One copy of the pass in the code (a loop kept rolled), so that the
+        // kernel's instructions stay few.
+        int p = 0;
+#pragma unroll 1
+        for (;;) {
+            exchange_pass(p++);
+            if (p == 3) break;
+            if (members <= kMbCandCap) {  // workgroup-uniform (from LDS)
+                by_cand = true;
+                break;
+            }
+        }
+        if (by_cand) cand_select(p);
     }
     // The K-th largest key and how many keys equal to it the K largest hold
     // (K = 0: no key is larger, none equal is taken).
     const uint32_t tkey = K > 0 ? prefix : 0xffffffffu;
     const int take_equal = K > 0 ? remaining : 0;
 
-    // Counts of this wave and workgroup, published for the later workgroups.
+    // Counts of this wave and workgroup.
     int n_gt = 0, n_eq = 0;
 #pragma unroll
     for (int j = 0; j < kMbPer; ++j) {
@@ -869,31 +1077,48 @@ __global__ __launch_bounds__(kMbThreads) void route_mb_kernel(RouteArgs a, unsig
         gt_b += s_red[w];
         eq_b += s_red[kMbWaves + w];
     }
+    // Every workgroup's counts: from the candidate lists (exchange 2), else
+    // from one more exchange.
     const uint32_t ctag = mb_tag(nonce, 3);
-    if (tid == 0) mb_put(cnt + g, (uint32_t)gt_b | ((uint32_t)eq_b << 16), ctag);
+    if (!by_cand && tid == 0) mb_put(cnt + g, (uint32_t)gt_b | ((uint32_t)eq_b << 16), ctag);
     if (tid < 64) {
         // Wave 0: the counts of the workgroups before this one, and the totals.
-        uint64_t c[2];
-        bool fresh = !ok;
-        for (int it = 0; it < kMbSpinLimit; ++it) {
+        int x[2], y[2];
+        if (by_cand) {
 #pragma unroll
-            for (int r = 0; r < 2; ++r) c[r] = tid + 64 * r < G ? mb_get(cnt + tid + 64 * r) : mb_tagged(0u, ctag);
-            if (fresh || ((uint32_t)(c[0] >> 32) == ctag && (uint32_t)(c[1] >> 32) == ctag)) {
-                fresh = true;
-                break;
+            for (int r = 0; r < 2; ++r) {
+                const int gg = tid + 64 * r;
+                x[r] = gg < G ? s_gt[gg] : 0;
+                y[r] = gg < G ? s_eq[gg] : 0;
             }
-            __builtin_amdgcn_s_sleep(1);
+        } else {
+            uint64_t c[2];
+            bool fresh = !ok;
+            for (int it = 0; it < kMbSpinLimit; ++it) {
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+                    c[r] = tid + 64 * r < G ? mb_get(cnt + tid + 64 * r) : mb_tagged(0u, ctag);
+                if (fresh || ((uint32_t)(c[0] >> 32) == ctag && (uint32_t)(c[1] >> 32) == ctag)) {
+                    fresh = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            ok = ok && fresh;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                x[r] = (int)(c[r] & 0xffffu);
+                y[r] = (int)((c[r] >> 16) & 0xffffu);
+            }
         }
-        ok = ok && fresh;
         int gb = 0, eb = 0, gt = 0, et = 0;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int gg = tid + 64 * r;
-            const int x = (int)(c[r] & 0xffffu), y = (int)((c[r] >> 16) & 0xffffu);
-            gb += gg < g ? x : 0;
-            eb += gg < g ? y : 0;
-            gt += x;
-            et += y;
+            gb += gg < g ? x[r] : 0;
+            eb += gg < g ? y[r] : 0;
+            gt += x[r];
+            et += y[r];
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
@@ -909,10 +1134,11 @@ __global__ __launch_bounds__(kMbThreads) void route_mb_kernel(RouteArgs a, unsig
             s_blk[3] = et;
         }
     }
-    // Every wait of every thread of the workgroup ended with the expected
-    // words, and the counts are those of K tokens.
+    // Every wait of every thread ended with the expected words, and the
+    // counts are those of K tokens (this workgroup's own among them).
     ok = __syncthreads_and(ok);
     ok = ok && s_blk[2] == K - take_equal && s_blk[3] >= take_equal && s_blk[2] + s_blk[3] <= N;
+    if (by_cand) ok = ok && s_gt[g] == gt_b && s_eq[g] == eq_b;
     const int n_dense = s_blk[2] + imin(s_blk[3], take_equal);
     int eq_run = s_blk[1] + eq_w;
     int d_seen = s_blk[0] + gt_w + imin(eq_run, take_equal);
