@@ -224,7 +224,7 @@ __global__ __launch_bounds__(64) void local_f32_kernel(
 }
 
 // ------------------------------------------------------------ bf16 path ----
-// One workgroup = kBandWaves waves = NF query frames x NW x-tiles of QY (h)
+// One workgroup = WV waves = NF query frames x NW x-tiles of QY (h)
 // x QX (w) = 32 queries, all on the rows ybase .. ybase+QY-1 (QY = 4 or 8,
 // chosen per window: the tile whose key box takes the fewest 32-key blocks
 // per frame).  The forward and statistics forms take one frame and 8
@@ -240,11 +240,11 @@ __global__ __launch_bounds__(64) void local_f32_kernel(
 // from each band the SR columns of its own tile's box (clamped at the edge of
 // the workgroup box; such slots are masked) and skips bands outside its
 // frame's window.
-constexpr int kBandWaves = 8;
-// x-tiles per workgroup (NW): 8 (one query frame) or 4 (two frames); the
-// workgroup's query frames are kBandWaves / NW.
+// Waves per workgroup (WV) and x-tiles per workgroup (NW): 8 and 8 (one
+// query frame), 4 and 4 (one frame, two workgroups a CU) or 8 and 4 (two
+// frames); the workgroup's query frames are WV / NW.
 
-template <int D, int SR, int QX, int NW>
+template <int D, int SR, int QX, int NW, int WV>
 struct BandGeom {
     static constexpr int rpb = 32 / SR;                          // box rows per band
     static constexpr int kCpr = D / 8;                           // 16-byte chunks per token row
@@ -255,7 +255,7 @@ struct BandGeom {
     static_assert(kCb % kTokPerLoad == 0, "a DMA load's rows stay in one box row");
     static constexpr int kBandRows = rpb * kCb;
     static constexpr int kLoads = kBandRows / kTokPerLoad;      // DMA loads per tensor and band
-    static constexpr int kLoadsPerWave = (kLoads + kBandWaves - 1) / kBandWaves;
+    static constexpr int kLoadsPerWave = (kLoads + WV - 1) / WV;
     static constexpr int kBufElems = kBandRows * D;              // one tensor, one buffer
 };
 
@@ -278,14 +278,14 @@ struct BandGrad {
 //          the route held fixed): per band S^T = K Q^T and dP^T = V dO^T
 //          (K and V rows as A operands), P = exp2(S - LSE) inside the
 //          window, dS = P (dP - D), dQ^T += K^T dS^T (K read transposed).
-template <int D, int SR, int QY, int kMode, int NW>
-__global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
+template <int D, int SR, int QY, int kMode, int NW, int WV>
+__global__ __launch_bounds__(64 * WV, 2) void local_band_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const uint8_t *__restrict__ mask, int N, int H, float scale_log2, LocalGeom g,
     int n_units, int x_blocks, int t_groups, BandGrad gr) {
     constexpr int QX = 32 / QY;
-    constexpr int NF = kBandWaves / NW;
-    using Bg = BandGeom<D, SR, QX, NW>;
+    constexpr int NF = WV / NW;
+    using Bg = BandGeom<D, SR, QX, NW, WV>;
     constexpr int rpb = Bg::rpb, NC = D / 16, NDB = D / 32;
     __shared__ __attribute__((aligned(1024))) __bf16 Kb0[Bg::kBufElems];
     __shared__ __attribute__((aligned(1024))) __bf16 Kb1[Bg::kBufElems];
@@ -331,7 +331,18 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     const bool is_local = in_grid && mask[(size_t)b * N + tok] != 0;
     const bool active = __any(is_local);
     // A workgroup whose queries are all dense has nothing to do.
-    if (!__syncthreads_or(is_local)) return;
+    // (The flags go through the second K buffer, which no DMA fills before
+    // the first band's barrier; no other LDS, so that two four-wave
+    // workgroups fit a CU.)
+    {
+        uint32_t *flag = reinterpret_cast<uint32_t *>(Kb1);
+        if (lane == 0) flag[wave] = active ? 1u : 0u;
+        __syncthreads();
+        uint32_t any_local = 0u;
+#pragma unroll
+        for (int w = 0; w < WV; ++w) any_local |= flag[w];
+        if (any_local == 0u) return;
+    }
     const int t0 = win_lo(imin(t, g.T - 1), g.wt, g.lt, g.T, g.cut);
     const int t1 = win_hi(imin(t, g.T - 1), g.wt, g.lt, g.T, g.cut);
     const int ylo = win_lo(imin(y, g.Hg - 1), g.wh, g.lh, g.Hg, g.cut);
@@ -385,7 +396,7 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
                 v_off[c2][lohi][db] =
                     row * D + 8 * ((4 * db + 2 * (gq & 1) + ((j16 & 3) >> 1)) ^ swz<D>(row)) + 4 * (j16 & 1);
         }
-    // DMA: load i (i = wave + kBandWaves*j) fills LDS rows [i*kTokPerLoad, ..);
+    // DMA: load i (i = wave + WV*j) fills LDS rows [i*kTokPerLoad, ..);
     // this lane writes row R = i*kTokPerLoad + lane/kCpr at chunk position
     // lane%kCpr.  Row R = rr*kCb + c holds column c of band row rr; the byte
     // offset from the band's first token is fixed per lane.  Columns past
@@ -394,7 +405,7 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
     int dma_voff[Bg::kLoadsPerWave];
 #pragma unroll
     for (int j = 0; j < Bg::kLoadsPerWave; ++j) {
-        const int i = wave + kBandWaves * j;
+        const int i = wave + WV * j;
         const int R = i * Bg::kTokPerLoad + lane / Bg::kCpr;
         const int rr = R / Bg::kCb, c = R % Bg::kCb;
         dma_voff[j] = c < C ? 2 * ((rr * g.Wg + c) * (int)tok_stride + 8 * ((lane % Bg::kCpr) ^ swz<D>(R)))
@@ -408,7 +419,7 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
         const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
         for (int j = 0; j < Bg::kLoadsPerWave; ++j) {
-            const int i = wv + kBandWaves * j;
+            const int i = wv + WV * j;
             if (i < Bg::kLoads && (i * Bg::kTokPerLoad) % Bg::kCb < C) dma_live |= 1u << j;
         }
     }
@@ -434,7 +445,7 @@ __global__ __launch_bounds__(64 * kBandWaves) void local_band_kernel(
         const __bf16 *kp = kbase + (size_t)tok0 * tok_stride, *vp = vbase + (size_t)tok0 * tok_stride;
 #pragma unroll
         for (int j = 0; j < Bg::kLoadsPerWave; ++j) {
-            const int i = wave + kBandWaves * j;
+            const int i = wave + WV * j;
             if ((dma_live >> j) & 1u) {
                 buffer_load_lds16(kp, bytes, (HET_LDS void *)(Kd + i * Bg::kTokPerLoad * D), dma_voff[j]);
                 if constexpr (kMode != 1)
@@ -670,28 +681,36 @@ hipError_t launch_band(const AttnArgs &a, const LocalGeom &g, const BandGrad &gr
     gb.tiles_y = (a.grid_h + qy - 1) / qy;
     gb.tiles_x = (a.grid_w + qx - 1) / qx;
     const bool b16 = qx + g.lw - 1 <= 16;
-    // Workgroup shape: one frame x 8 x-tiles, unless 4 x-tiles (two frames)
-    // leave clearly fewer waves without a tile (the one-frame shape gains
-    // about 5 % by keeping every wave busy in every band); the gradient form
-    // always takes 4.
+    // Workgroup shape (x-tiles NW, waves WV).  One frame x 4 x-tiles in
+    // four-wave workgroups, two to a CU, so that one workgroup's waits (its
+    // first loads, the band barrier) overlap the other's work, where at least
+    // 3/4 of those waves have a tile; else one frame x 8 x-tiles in eight
+    // waves, unless 4 x-tiles in two frames leave clearly fewer waves without
+    // a tile (one frame keeps every wave busy in every band).  The gradient
+    // form, whose buffers must stay within the LDS instructions' offsets,
+    // never takes 8 x-tiles.
     auto filled = [&](int nw) { return (double)gb.tiles_x / (nw * ((gb.tiles_x + nw - 1) / nw)); };
-    const bool nw8 = kMode != 2 && filled(8) >= filled(4) - 0.05;
-    const int NW = nw8 ? 8 : 4, NF = kBandWaves / NW;
+    int shape = 2;  // 0: NW 8, WV 8; 1: NW 4, WV 4; 2: NW 4, WV 8
+    if (filled(4) >= 0.75 && (kMode == 2 || filled(4) >= filled(8) - 0.05)) shape = 1;
+    else if (kMode != 2 && filled(8) >= filled(4) - 0.05) shape = 0;
+    const int NW = shape == 0 ? 8 : 4, WV = shape == 1 ? 4 : 8, NF = WV / NW;
     const int x_blocks = (gb.tiles_x + NW - 1) / NW, t_groups = (g.T + NF - 1) / NF;
     const int band_units = a.batch * a.heads * t_groups * gb.tiles_y * x_blocks;
-    const dim3 bgrid((band_units + 7) / 8 * 8), bblock(64 * kBandWaves);
-#define HET_BAND_LAUNCH_NW(D_, SR_, QY_, NW_)                                                                 \
-    hipLaunchKernelGGL((local_band_kernel<D_, SR_, QY_, kMode, NW_>), bgrid, bblock, 0, stream,               \
+    const dim3 bgrid((band_units + 7) / 8 * 8), bblock(64 * WV);
+#define HET_BAND_LAUNCH_NW(D_, SR_, QY_, NW_, WV_)                                                           \
+    hipLaunchKernelGGL((local_band_kernel<D_, SR_, QY_, kMode, NW_, WV_>), bgrid, bblock, 0, stream,         \
                        (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, a.mask, \
                        a.n, a.heads, sl2, gb, band_units, x_blocks, t_groups, gr)
-#define HET_BAND_LAUNCH(D_, SR_, QY_)                                 \
-    do {                                                              \
-        if constexpr (kMode != 2) {                                   \
-            if (nw8) HET_BAND_LAUNCH_NW(D_, SR_, QY_, 8);              \
-            else HET_BAND_LAUNCH_NW(D_, SR_, QY_, 4);                  \
-        } else {                                                      \
-            HET_BAND_LAUNCH_NW(D_, SR_, QY_, 4);                      \
-        }                                                             \
+#define HET_BAND_LAUNCH(D_, SR_, QY_)                                   \
+    do {                                                                \
+        if constexpr (kMode != 2) {                                     \
+            if (shape == 0) HET_BAND_LAUNCH_NW(D_, SR_, QY_, 8, 8);      \
+            else if (shape == 1) HET_BAND_LAUNCH_NW(D_, SR_, QY_, 4, 4); \
+            else HET_BAND_LAUNCH_NW(D_, SR_, QY_, 4, 8);                 \
+        } else {                                                        \
+            if (shape == 1) HET_BAND_LAUNCH_NW(D_, SR_, QY_, 4, 4);      \
+            else HET_BAND_LAUNCH_NW(D_, SR_, QY_, 4, 8);                 \
+        }                                                               \
     } while (0)
     if (a.head_dim == 128) {
         if (qy == 4) {
