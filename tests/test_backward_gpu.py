@@ -210,6 +210,8 @@ LOG2E = 1.4426950408889634
     ((6, 10, 20), (3, 7, 7), 64, 1.0),
     ((2, 13, 70), (3, 7, 7), 128, 0.25),   # the dK/dV pass takes the local queries itself
     ((9, 3, 5), (3, 3, 3), 64, 0.4),
+    ((4, 9, 40), (3, 7, 7), 128, 0.2),     # local kernel: one frame x 8 x-tiles
+    ((4, 9, 14), (3, 7, 7), 128, 0.2),     # local kernel: two frames x 4 x-tiles
 ])
 def test_forward_lse_and_backward_lse(oracle_mod, grid, window, head_dim, rho):
     """het_attn_forward_lse writes the same O as het_attn_forward and each row's

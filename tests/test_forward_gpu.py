@@ -59,6 +59,16 @@ def test_window_shapes(oracle_mod, window):
     full_parity(oracle_mod, w, q, k, v, u, rho=0.2, what=f"window {window}")
 
 
+@pytest.mark.parametrize("grid", [(4, 9, 40), (4, 9, 14), (4, 9, 52)])
+def test_local_workgroup_shapes_all_rows(oracle_mod, grid):
+    """The local kernel's three workgroup shapes at the 3x7x7 window, each on
+    every row of a ragged grid: 5 column tiles of 8 take one frame x 8 x-tiles
+    in eight waves, 2 take two frames x 4 x-tiles, 7 take one frame x 4
+    x-tiles in four-wave workgroups, two to a CU."""
+    w, q, k, v, u = small_case(grid, 2, 128, "bf16", seed=300 + grid[2])
+    full_parity(oracle_mod, w, q, k, v, u, rho=0.2, what=f"workgroup shape, grid {grid}")
+
+
 @pytest.mark.parametrize("window", [(9, 9, 9), (11, 11, 11), (13, 13, 13)])
 @pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("f32", 64)])
 def test_cubic_windows_all_rows(oracle_mod, window, dtype, head_dim):

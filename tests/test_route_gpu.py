@@ -296,3 +296,23 @@ def test_route_selection_paths(oracle_mod, case):
         assert got == want, (first, second)
     log(f"[route] selection path {case} B={u.shape[0]} N={u.shape[1]} rho={rho:.4f}")
     run_top_rho(oracle_mod, u, (1, 1, u.shape[1]), rho)
+
+
+def test_route_selection_paths_mixed_in_one_launch(oracle_mod):
+    """Samples of one launch on different selection paths at once: all tied
+    (three histogram exchanges and the counts), spread wide (candidates after
+    the first exchange) and narrow (candidates after the second)."""
+    rng = np.random.default_rng(79)
+    n = 24576
+    u = np.empty((3, n), np.float32)
+    u[0] = 0.5
+    u[0, rng.choice(n, 40, replace=False)] = 2.0
+    u[1] = rng.standard_normal(n)
+    u[2] = 1.0 + 0.01 * rng.standard_normal(n)
+    rho = 0.25
+    paths = []
+    for first, second in top_bins(u, rho):
+        paths.append("first" if first <= 4096 else ("second" if second <= 4096 else "histograms"))
+    assert paths == ["histograms", "first", "second"], paths
+    log(f"[route] mixed selection paths B=3 N={n}")
+    run_top_rho(oracle_mod, u, (1, 1, n), rho)
