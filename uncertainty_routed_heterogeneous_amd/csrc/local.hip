@@ -303,7 +303,9 @@ __global__ __launch_bounds__(64 * WV, 2) void local_band_kernel(
     rest /= t_groups;
     const int h = rest % H, b = rest / H;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The wave index as a wave-uniform (scalar) value: the DMA's LDS addresses
+    // and the tile of each wave are then scalar too.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, col = lane & 31;
     const int gq = lane >> 4, j16 = lane & 15;
 
