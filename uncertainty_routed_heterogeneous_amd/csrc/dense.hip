@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kDenseThreads16) void dense_bf16_kernel(
         // then S(r) = K(r) Q^T (steps 4*NDB..4*NDB+2*NC-1).  The A operand of
         // step i is read from LDS kAhead steps before its MFMA, and
         // sched_barrier keeps the compiler from sinking the reads back.
-        constexpr int kPvSteps = 4 * NDB, kQkSteps = 2 * NC, kAhead = 6;
+        constexpr int kPvSteps = 4 * NDB, kQkSteps = 2 * NC, kAhead = 4;
         auto a_operand = [&](int i, const __bf16 *Vt, const __bf16 *Kt) HET_INLINE -> bf16x8 {
             if (i < kPvSteps) {
                 const int db = i % NDB, kbk = (i / NDB) >> 1, c2 = (i / NDB) & 1;
