@@ -471,9 +471,14 @@ __global__ __launch_bounds__(64 * WV, 2) void local_band_kernel(
     auto step = [&](int bi, const __bf16 *Kc, const __bf16 *Vc, __bf16 *Kn, __bf16 *Vn) HET_INLINE {
         // Band bi has landed for every wave, and every wave is done with
         // band bi-1, whose buffers the next DMA refills.
+        // A wave waits for the band at the lowest priority and computes it at
+        // a raised one, so that on a SIMD shared by two workgroups the wave
+        // that has its band goes first.
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
         if (bi + 1 < n_bands) dma_band(Kn, Vn);
+        __builtin_amdgcn_s_setprio(1);
         const int f = c_f, yy0 = uy0 + c_r * rpb;
         next_band(c_f, c_r);
         if (!active || f < t0 || f >= t1) return;
